@@ -1,0 +1,34 @@
+"""Plain CPU oracle for the DSA indexer + top-k + absorbed sparse-MLA path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or links
+this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+constant generator with the HIP library; both sides receive the same seeded
+inputs and compute independently.
+
+Everything here is written for a reader checking it against the pages by eye:
+NumPy, float64 arithmetic, no blocking, no fusion, no reordering beyond what a
+library primitive (matmul, lexsort) does.  Where the pages fix a precision
+(the FP8 cache write rounds in fp32 and e4m3) the oracle reproduces that
+rounding explicitly.
+
+Modules
+  codecs     bf16 and OCP e4m3fn value codecs
+  indexer    key-cache write, indexer score, deterministic top-k
+  mla        absorbed sparse MLA over selected latent rows, and a dense
+             causal MLA used only for the sparse == dense invariant
+  indexshare GLM-5.2 IndexShare source-layer resolution and layer stack
+
+Pins (what each function is checked against, in tests/test_oracle_*.py):
+  codecs      OCP e4m3fn end points and hand-decoded codes (tests/golden),
+              bf16 round-to-nearest-even examples
+  indexer     brute-force full sort with Python integer/tuple comparison on
+              tiny inputs, hand-computed worked example (tests/golden),
+              exact-integer scores, threshold certificate, invariants
+  mla         sparse == dense when k covers the context, pos == 0 row,
+              uniform-logit closed form, permutation invariance, convex hull
+  indexshare  hand-derived source maps and every rejection case
+No oracle function is "parity unpinned".
+"""
+
+from . import codecs, indexer, mla, indexshare  # noqa: F401

@@ -1,0 +1,303 @@
+"""Benchmark of the DSA decode hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. dsa_indexer_cache_write  - the step's new indexer keys into the cache
+  2. dsa_indexer_topk         - indexer score over every causal cached key,
+                                then the deterministic top-k per query token
+  3. sparse_mla_attn          - absorbed MLA over the selected latent rows
+Default workload ("decode_32k_mtp"): 64 requests x 32768 cached tokens, two
+query tokens per request (one plus one MTP draft), indexer 32 heads x 128
+dims bf16, top-k 2048, MLA 64 heads x (512 latent + 64 rope) bf16.  All
+inputs are resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is query tokens per second of the whole step.
+`roofline` is for the dominant call (the indexer: score + top-k kernels),
+algorithmic bytes / mean duration from HIP events on the launch stream.
+`cpu_baseline` times the plain CPU oracle on a bounded sample of the same
+workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+METRIC = "decode query-tokens/s (indexer+top-k+sparse MLA) and % HBM roofline, 32K ctx"
+
+
+def log(msg):
+    sys.stderr.write("[bench] %s\n" % msg)
+    sys.stderr.flush()
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode_32k_mtp",
+                   choices=["decode_32k_mtp", "fp8_decode_varlen",
+                            "indexshare_8layer", "prefill_16k"])
+    p.add_argument("--no-cpu", action="store_true",
+                   help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ bytes
+def indexer_bytes(b, cfg):
+    """Algorithmic bytes of one indexer + top-k call: every causal key read
+    once per request (+ its fp32 scale for an FP8 cache), queries and head
+    weights read once, indices written once, block tables read once."""
+    key_b = cfg.d_idx * (1 if cfg.idx_cache_dtype == "fp8" else 2)
+    if cfg.idx_cache_dtype == "fp8":
+        key_b += 4
+    keys = sum(b.seq_lens) * key_b
+    q = b.num_q_tokens * cfg.n_idx_heads * cfg.d_idx * 2
+    w = b.num_q_tokens * cfg.n_idx_heads * 4
+    out = b.num_q_tokens * cfg.topk * 4
+    bt = b.num_reqs * b.max_blocks * 4
+    return keys + q + w + out + bt
+
+
+def mla_bytes(b, cfg):
+    """One 1152-byte latent row per (query token, selected index), queries,
+    indices, bf16 output and fp32 lse."""
+    rows = 0
+    for bi in range(b.num_reqs):
+        for i in range(b.q_lens[bi]):
+            pos = b.seq_lens[bi] - b.q_lens[bi] + i
+            rows += min(cfg.topk, pos + 1)
+    N, H = b.num_q_tokens, cfg.n_heads
+    return (rows * cfg.d_latent * 2 + N * H * cfg.d_latent * 2 + N * cfg.topk * 4
+            + N * H * cfg.kv_lora_rank * 2 + N * H * 4)
+
+
+def cache_write_bytes(b, cfg):
+    per = cfg.d_idx * (1 if cfg.idx_cache_dtype == "fp8" else 2)
+    return b.num_q_tokens * (cfg.d_idx * 2 + per + 8)
+
+
+# ------------------------------------------------------------------ cpu leg
+def cpu_baseline(cfg, b, lay, k_cache, seconds):
+    """Time the oracle (as it stands) on whole query tokens of the same
+    workload until about `seconds` of compute have run."""
+    import numpy as np
+    import torch
+    from oracle import indexer as OI, mla as OM
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    spent = 0.0
+    tokens = 0
+    reqs = 0
+    bs = b.block_size
+    for bi in range(b.num_reqs):
+        if spent >= seconds:
+            break
+        L, ql = b.seq_lens[bi], b.q_lens[bi]
+        # host copies of this request's inputs (not timed)
+        slots = torch.as_tensor(OI.physical_slots(b.block_table_host[bi], bs, L),
+                                device=k_cache.device)
+        keys = k_cache[slots].cpu()
+        kv = lay.kv_cache[slots].cpu().float().numpy()
+        t0 = int(b.cu_q_host[bi])
+        q = lay.q_idx[t0:t0 + ql].float().cpu().numpy().astype(np.float64)
+        w = lay.w[t0:t0 + ql].cpu().numpy().astype(np.float64)
+        qm = lay.q_mla[t0:t0 + ql].float().cpu().numpy().astype(np.float64)
+        cache_np = keys.view(torch.int16).numpy().view(np.uint16)
+        ident = np.arange((L + bs - 1) // bs, dtype=np.int64)[None, :]
+        start = time.perf_counter()
+        idx = OI.indexer_topk([L], [0, ql], ident, bs, q, w, cache_np, None,
+                              OI.BF16, cfg.topk)
+        OM.sparse_mla([L], [0, ql], ident, bs, qm, lambda s: kv[s], idx,
+                      cfg.kv_lora_rank, cfg.softmax_scale)
+        spent += time.perf_counter() - start
+        tokens += ql
+        reqs += 1
+    return {"value": tokens / spent, "unit": "query-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d requests (%d query tokens) of %s, float64 NumPy "
+                      "oracle, compute only (%.1f s)" % (reqs, b.num_reqs, tokens,
+                                                         cfg.name, spent)}
+
+
+# ------------------------------------------------------------------ main
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(requests shard independently across GPUs; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sparse_attention_topk_amd as dsa
+    from synth import get_config, make_batch, make_layer
+    dsa.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    cfg = get_config(args.workload)
+    log("generating %s inputs" % cfg.name)
+    b = make_batch(cfg, dev)
+    bb = dsa.Batch.from_synth(b)
+    N = b.num_q_tokens
+    stream = torch.cuda.current_stream()
+
+    if cfg.name == "indexshare_8layer":
+        return bench_indexshare(args, cfg, b, bb, dsa, torch)
+
+    lay = make_layer(cfg, b, dev)
+    # the cache before this step: every slot populated through the cache write
+    if cfg.idx_cache_dtype == "fp8":
+        k_cache = torch.empty((b.num_slots, cfg.d_idx), dtype=torch.uint8, device=dev)
+        k_scale = torch.empty((b.num_slots,), dtype=torch.float32, device=dev)
+        all_slots = torch.arange(b.num_slots, dtype=torch.int64, device=dev)
+        dsa.dsa_indexer_cache_write(lay.k_src, all_slots, k_cache, k_scale)
+    else:
+        k_cache = lay.k_src
+        k_scale = None
+    k_new = lay.k_src[b.slot_mapping_t].contiguous()       # this step's keys
+    topk_idx = torch.empty((N, cfg.topk), dtype=torch.int32, device=dev)
+    out = torch.empty((N, cfg.n_heads, cfg.kv_lora_rank), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((N, cfg.n_heads), dtype=torch.float32, device=dev)
+    ws_bytes = max(dsa.dsa_indexer_topk_workspace_size(bb, cfg.topk),
+                   dsa.sparse_mla_attn_workspace_size(bb, cfg.n_heads, cfg.kv_lora_rank,
+                                                      cfg.rope_dim, cfg.topk, dsa.DSA_BF16))
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        dsa.dsa_indexer_cache_write(k_new, b.slot_mapping_t, k_cache, k_scale)
+        if ev is not None:
+            ev[1].record(stream)
+        dsa.dsa_indexer_topk(bb, lay.q_idx, lay.w, k_cache, k_scale, cfg.topk,
+                             topk_idx=topk_idx, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+        dsa.sparse_mla_attn(bb, lay.q_mla, lay.kv_cache, topk_idx, cfg.kv_lora_rank,
+                            cfg.softmax_scale, out=out, lse=lse, workspace=ws)
+        if ev is not None:
+            ev[3].record(stream)
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+           for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    cw = [e[0].elapsed_time(e[1]) for e in evs]
+    ix = [e[1].elapsed_time(e[2]) for e in evs]
+    ml = [e[2].elapsed_time(e[3]) for e in evs]
+    mean = lambda v: sum(v) / len(v)
+    ms_step = elapsed * 1e3 / args.steps
+    ib, mb, cb = indexer_bytes(b, cfg), mla_bytes(b, cfg), cache_write_bytes(b, cfg)
+    ix_gbs = ib / (mean(ix) * 1e-3) / 1e9
+    ml_gbs = mb / (mean(ml) * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": N / (ms_step * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.idx_cache_dtype != "fp8" else "bf16+fp8-cache",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "requests": b.num_reqs,
+                   "max_context": b.max_seq_len, "total_context": int(sum(b.seq_lens)),
+                   "query_tokens": N, "indexer_heads": cfg.n_idx_heads,
+                   "d_idx": cfg.d_idx, "topk": cfg.topk, "mla_heads": cfg.n_heads,
+                   "kv_lora_rank": cfg.kv_lora_rank, "rope_dim": cfg.rope_dim,
+                   "idx_cache": cfg.idx_cache_dtype, "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "kernel": "dsa_indexer_topk (score + top-k)",
+                     "achieved": ix_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ix_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "bytes_per_launch": ib, "mean_ms": mean(ix)},
+        "calls": {
+            "cache_write": {"mean_ms": mean(cw), "bytes": cb},
+            "indexer_topk": {"mean_ms": mean(ix), "bytes": ib, "GB/s": ix_gbs,
+                             "frac_hbm": ix_gbs / HBM_PEAK_GBS},
+            "sparse_mla_attn": {"mean_ms": mean(ml), "bytes": mb, "GB/s": ml_gbs,
+                                "frac_hbm": ml_gbs / HBM_PEAK_GBS},
+            "step_frac_hbm": (ib + mb + cb) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu and cfg.idx_cache_dtype != "fp8":
+        log("cpu oracle baseline (~%.0f s)" % args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cfg, b, lay, k_cache, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+def bench_indexshare(args, cfg, b, bb, dsa, torch):
+    """IndexShare stack: 8 layers, amortised time per layer."""
+    from synth import make_layer
+    from oracle import indexshare as OX  # noqa: F401  (type names only)
+    dev = "cuda"
+    types = cfg.indexer_types
+    src = []
+    last = None
+    for i, t in enumerate(types):
+        last = i if t == "full" else last
+        src.append(last)
+    N = b.num_q_tokens
+    layers = []
+    for i in range(len(types)):
+        full = src[i] == i
+        lay = make_layer(cfg, b, dev, layer=i, with_indexer=full)
+        layers.append(dsa.Layer(
+            q_mla=lay.q_mla, kv_cache=lay.kv_cache,
+            out=torch.empty((N, cfg.n_heads, cfg.kv_lora_rank), dtype=torch.bfloat16, device=dev),
+            lse=torch.empty((N, cfg.n_heads), dtype=torch.float32, device=dev),
+            q_idx=lay.q_idx if full else None, w=lay.w if full else None,
+            k_cache=lay.k_src if full else None,
+            topk_idx=torch.empty((N, cfg.topk), dtype=torch.int32, device=dev) if full else None))
+    dims = dsa.StackDims(cfg.n_idx_heads, cfg.d_idx, dsa.DSA_BF16, dsa.DSA_BF16, cfg.topk,
+                         cfg.n_heads, cfg.kv_lora_rank, cfg.rope_dim, dsa.DSA_BF16,
+                         cfg.softmax_scale)
+    codes = [dsa.DSA_LAYER_FULL if t == "full" else dsa.DSA_LAYER_SHARED for t in types]
+    ws = torch.empty(max(256, dsa.indexshare_forward_workspace_size(bb, dims)),
+                     dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        dsa.indexshare_forward(bb, codes, layers, dims, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dsa.indexshare_forward(bb, codes, layers, dims, workspace=ws)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    n_full = sum(1 for i in range(len(types)) if src[i] == i)
+    by = n_full * indexer_bytes(b, cfg) + len(types) * mla_bytes(b, cfg)
+    gbs = by / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "IndexShare stack ms and amortised us/layer", "value": ms * 1e3 / len(types),
+        "unit": "us/layer", "higher_is_better": False, "ms_per_step": ms,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "config": {"workload": cfg.name, "layers": types, "requests": b.num_reqs,
+                   "max_context": b.max_seq_len, "topk": cfg.topk},
+        "stack_bytes": by, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+        "data": "synthetic", "dtype": "bf16"}))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,258 @@
+/*
+ * dsa.h - C ABI of the MI355X (gfx950) DSA indexer + top-k + absorbed
+ * sparse-MLA library (libdsa.so).
+ *
+ * The method: for each query token, a light "lightning" indexer with H_I
+ * heads scores every causal cached token,
+ *     score[t, s] = sum_h w[t, h] * ReLU(q[t, h, :] . k[s, :]),
+ * the top `topk` positions are kept (ties go to the lower position), and
+ * absorbed multi-head latent attention then runs only over the latent rows
+ * cached at those positions.  With GLM-5.2 IndexShare, "shared" layers reuse
+ * the top-k of the nearest preceding "full" layer.
+ *
+ * Passages the operations follow (page "GLM5 TensorCast 适配设计", i.e. the
+ * GLM5 TensorCast adaptation design, unless another page is named):
+ *   - section "DSA Indexer fused semantic op": one op covers cache write,
+ *     scoring, head-weight mixing, head reduction and top-k; the indexer
+ *     cache is a mutable argument addressed by slot_mapping, block_tables and
+ *     seq_lens; the result has shape (batch, seq_len, min(topk_limit,
+ *     active_seq_len)) with a static width topk_limit; topk_limit and
+ *     topk_indices are handed to the MLA backend;
+ *   - section "Performance model design": score MMA, head-weight multiply /
+ *     head reduce / ReLU and scale shaping, top-k selection, key-cache and
+ *     FP8 scale-cache traffic; the sparse attention length is the top-k width;
+ *   - section "KV cache dtype and parallel-linear boundary fix": the indexer
+ *     cache is FP8 when attention is FP8, else the model dtype; only full
+ *     IndexShare layers own an indexer cache;
+ *   - section "GLM-5.2 IndexShare": full / shared layer types, the nearest
+ *     preceding full layer is the source, invalid type lists are rejected;
+ *   - page "GLM5 full-stack LoRA", section 1 and section 2.1: top-k must be
+ *     deterministic (torch.topk tie order differs between builds);
+ *     section 2.2: absorbed MLA over the latent rows.
+ *
+ * Conventions for every entry point
+ *   - Pointers are DEVICE pointers unless marked [host].  All device buffers
+ *     belong to the caller; the library never allocates or frees device
+ *     memory, never synchronises the device and keeps no state between calls
+ *     except the thread-local error text.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it; inputs must stay valid until that work completes.
+ *   - Return value: DSA_OK (0) or a negative dsa_status.  Every condition
+ *     that can be checked on the host (null pointers, sizes, dtypes, the
+ *     workspace size, IndexShare type lists) is checked BEFORE anything is
+ *     enqueued, so a failed call has no effect.  dsa_last_error() then
+ *     describes the failure.
+ *   - Device-resident metadata (seq_lens, cu_q, block_table, slot_mapping,
+ *     topk indices) must agree with the host-side bounds in dsa_batch.
+ *     Kernels clamp or skip values outside those bounds so that no memory
+ *     outside the given buffers is touched, but results are then unspecified.
+ *   - Row-major layouts throughout; "[A, B]" lists dims outer to inner.
+ *   - Positions are logical per-request positions 0..seq_len-1; the physical
+ *     cache row (slot) of position s of request b is
+ *         block_table[b * max_blocks + s / block_size] * block_size
+ *         + s % block_size.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage / arithmetic types */
+typedef enum {
+  DSA_F32 = 0,      /* IEEE binary32                                      */
+  DSA_BF16 = 1,     /* bfloat16 (upper half of binary32)                  */
+  DSA_FP8_E4M3 = 2  /* OCP e4m3fn: bias 7, max 448, 0x7F/0xFF = NaN       */
+} dsa_dtype;
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = -1,   /* null pointer, negative or inconsistent size */
+  DSA_ERR_UNSUPPORTED = -2,   /* valid but not implemented (dtype, shape)    */
+  DSA_ERR_INDEXER_TYPES = -3, /* bad IndexShare type list (the ValueError
+                                 case of section "GLM-5.2 IndexShare")       */
+  DSA_ERR_MISSING_TOPK = -4,  /* a full layer has no top-k buffer to fill    */
+  DSA_ERR_WORKSPACE = -5,     /* workspace null or smaller than required     */
+  DSA_ERR_HIP = -6            /* a HIP launch failed                         */
+} dsa_status;
+
+enum { DSA_LAYER_FULL = 0, DSA_LAYER_SHARED = 1 };
+
+/* Largest supported top-k width and the latent-row limits. */
+enum { DSA_MAX_TOPK = 4096 };
+
+/*
+ * Ragged batch and paged-cache geometry (section "DSA Indexer fused
+ * semantic op": slot_mapping / block_tables / seq_lens address the cache).
+ * Request b has q_len_b = cu_q[b+1] - cu_q[b] query tokens, the last q_len_b
+ * tokens of its seq_lens[b] cached tokens: query i sits at position
+ * seq_lens[b] - q_len_b + i and attends to positions 0..that position (the
+ * cache already holds this step's tokens).  Prefill is q_len_b = seq_lens[b].
+ */
+typedef struct dsa_batch {
+  int32_t num_reqs;            /* B >= 1                                    */
+  int32_t num_q_tokens;        /* N = cu_q[B]            (host copy)        */
+  int32_t max_q_len;           /* >= every q_len_b       (host copy)        */
+  int32_t max_seq_len;         /* >= every seq_lens[b]   (host copy)        */
+  int32_t max_blocks;          /* row length of block_table                 */
+  int32_t block_size;          /* tokens per cache block, multiple of 32    */
+  int64_t num_slots;           /* rows of every paged cache buffer          */
+  const int32_t* seq_lens;     /* [B]                                       */
+  const int32_t* cu_q;         /* [B+1], cu_q[0] = 0, non-decreasing        */
+  const int32_t* block_table;  /* [B, max_blocks] physical block ids        */
+} dsa_batch;
+
+/*
+ * Indexer key-cache write (section "DSA Indexer fused semantic op", the
+ * cache write of both paths; section "KV cache dtype ..." for the dtype).
+ *   k_new        [n_new, d_idx] new keys, k_dtype DSA_F32 or DSA_BF16
+ *   slot_mapping [n_new] int64 destination rows; -1 = padding token, skipped;
+ *                rows >= num_slots are skipped too
+ *   k_cache      [num_slots, d_idx] of cache_dtype
+ *   k_scale      [num_slots] fp32, required iff cache_dtype == DSA_FP8_E4M3,
+ *                else ignored
+ * F32 / BF16 cache: the key is stored unchanged (k_dtype must equal
+ * cache_dtype).  FP8 cache: per token amax = max_d |k_d| (in fp32),
+ * scale = fl32(amax / 448) (1 if amax == 0), code_d = e4m3(fl32(k_d / scale))
+ * with round-to-nearest-even, saturating at +-448, the sign kept; k_scale gets
+ * scale.  Only the listed rows are written.  d_idx: 1..1024.
+ */
+int dsa_indexer_cache_write(const void* k_new, int32_t k_dtype, int32_t n_new,
+                            int32_t d_idx, const int64_t* slot_mapping,
+                            int64_t num_slots, void* k_cache, float* k_scale,
+                            int32_t cache_dtype, void* stream);
+
+/*
+ * Indexer score + deterministic top-k (section "DSA Indexer fused semantic
+ * op"; section "Performance model design", score MMA, head mixing / reduce /
+ * ReLU shaping and top-k buckets; tie rule after page "GLM5 full-stack LoRA"
+ * section 1).
+ *   q        [N, n_heads, d_idx] query, q_dtype DSA_F32 or DSA_BF16
+ *   w        [N, n_heads] fp32 head weights
+ *   k_cache  [num_slots, d_idx] of cache_dtype (F32, BF16 or FP8_E4M3)
+ *   k_scale  [num_slots] fp32 for an FP8 cache (the key's value is
+ *            code * scale), else ignored
+ *   topk_idx [N, topk] int32 output: row t holds the n = min(topk, pos_t + 1)
+ *            selected positions in ascending order, then -1 up to topk.
+ *            Selection order is (score descending, position ascending), so
+ *            the set is unique.
+ * Scores use fp32 accumulation (bf16 / fp8 operands are widened exactly).
+ * Supported: q_dtype == cache_dtype for F32/BF16, q BF16 with an FP8 cache;
+ * n_heads 1..64 and d_idx 1..256 (the matrix-core path needs n_heads % 32 == 0
+ * and d_idx == 128; other shapes take a slower vector path); topk 1..4096.
+ * workspace: at least dsa_indexer_topk_workspace_size() bytes, 256-byte
+ * aligned; contents on entry are ignored.
+ */
+size_t dsa_indexer_topk_workspace_size(const dsa_batch* batch, int32_t topk);
+int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
+                     const float* w, int32_t n_heads, int32_t d_idx,
+                     const void* k_cache, const float* k_scale,
+                     int32_t cache_dtype, int32_t topk, int32_t* topk_idx,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Absorbed sparse MLA over the selected latent rows (section "DSA Indexer
+ * fused semantic op": topk_limit / topk_indices reach the MLA backend;
+ * section "Performance model design": attention length = top-k width; page
+ * "GLM5 full-stack LoRA" section 2.2: absorbed MLA).
+ *   q        [N, n_heads, R + P] absorbed queries (R = kv_lora_rank,
+ *            P = rope_dim)
+ *   kv_cache [num_slots, R + P] latent rows: R latent dims then P rope dims
+ *   topk_idx [N, topk] logical positions; entries < 0 are ignored; entries
+ *            beyond the token's position are out of contract
+ *   out      [N, n_heads, R] (same dtype as q): for each head
+ *            sum_j softmax_j(softmax_scale * q . kv_j) * kv_j[0:R]
+ *   lse      [N, n_heads] fp32 log-sum-exp of the scaled logits, or NULL
+ * A token with no valid index gets out = 0 and lse = -inf.
+ * Supported: dtype DSA_F32 or DSA_BF16.  The matrix-core path takes BF16
+ * with R = 512, P = 64 and n_heads % 16 == 0; other shapes (R + P <= 1024,
+ * n_heads <= 128) take a vector path.
+ * workspace: at least sparse_mla_attn_workspace_size() bytes (may be 0, in
+ * which case workspace may be NULL).
+ */
+size_t sparse_mla_attn_workspace_size(const dsa_batch* batch, int32_t n_heads,
+                                      int32_t kv_lora_rank, int32_t rope_dim,
+                                      int32_t topk, int32_t dtype);
+int sparse_mla_attn(const dsa_batch* batch, const void* q,
+                    const void* kv_cache, int32_t dtype, int32_t n_heads,
+                    int32_t kv_lora_rank, int32_t rope_dim,
+                    const int32_t* topk_idx, int32_t topk, float softmax_scale,
+                    void* out, float* lse, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * GLM-5.2 IndexShare source resolution (section "GLM-5.2 IndexShare";
+ * section "Configuration constraints", item 6).  Host only.
+ *   types [host] n_types values, DSA_LAYER_FULL or DSA_LAYER_SHARED
+ *   src   [host] out, n_layers entries: src[i] = i for a full layer, the
+ *         index of the nearest preceding full layer for a shared one
+ * DSA_ERR_INDEXER_TYPES if n_types < n_layers, any of the n_types values is
+ * unknown, or a shared layer among the first n_layers has no preceding full
+ * layer (src is then left unchanged).
+ */
+int dsa_resolve_indexer_sources(int32_t n_layers, const int32_t* types,
+                                int32_t n_types, int32_t* src);
+
+/* One decoder layer's tensors for indexshare_forward. */
+typedef struct dsa_layer {
+  const void* q_idx;     /* full: [N, n_idx_heads, d_idx]; shared: unused  */
+  const float* w;        /* full: [N, n_idx_heads];       shared: unused   */
+  const void* k_cache;   /* full: indexer cache [num_slots, d_idx]; shared:
+                            unused (shared layers own no indexer cache)     */
+  const float* k_scale;  /* full with an FP8 cache: [num_slots]             */
+  int32_t* topk_idx;     /* full: [N, topk] buffer to fill; shared: unused  */
+  const void* q_mla;     /* [N, n_heads, R + P]                             */
+  const void* kv_cache;  /* [num_slots, R + P]                              */
+  void* out;             /* [N, n_heads, R]                                 */
+  float* lse;            /* [N, n_heads] or NULL                            */
+} dsa_layer;
+
+/* Dimensions shared by every layer of the stack. */
+typedef struct dsa_stack_dims {
+  int32_t n_idx_heads, d_idx, q_idx_dtype, idx_cache_dtype, topk;
+  int32_t n_heads, kv_lora_rank, rope_dim, mla_dtype;
+  float softmax_scale;
+} dsa_stack_dims;
+
+/*
+ * IndexShare layer stack (section "GLM-5.2 IndexShare"; section "Trace and
+ * performance results": shared layers add no indexer op, latency or cache
+ * traffic).  For each layer i in order: a full layer runs
+ * dsa_indexer_topk into layers[i].topk_idx; a shared layer runs no indexer
+ * and uses the active top-k of its source layer unchanged; every layer then
+ * runs sparse_mla_attn with its own q_mla / kv_cache.
+ *   types       [host] as for dsa_resolve_indexer_sources
+ *   layers      [host] n_layers entries
+ *   active_topk [host] out, n_layers entries (may be NULL): the device
+ *               buffer each layer attended with (the source layer's buffer)
+ * Errors: DSA_ERR_INDEXER_TYPES as above; DSA_ERR_MISSING_TOPK if a full
+ * layer has topk_idx == NULL; the per-op argument errors otherwise.
+ * workspace: at least indexshare_forward_workspace_size() bytes.
+ */
+size_t indexshare_forward_workspace_size(const dsa_batch* batch,
+                                         const dsa_stack_dims* dims);
+int indexshare_forward(const dsa_batch* batch, int32_t n_layers,
+                       const int32_t* types, int32_t n_types,
+                       const dsa_layer* layers, const dsa_stack_dims* dims,
+                       const int32_t** active_topk, void* workspace,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * Diagnostic: decode n e4m3fn codes with the same device conversion the
+ * indexer's FP8 path uses (codes -> bf16 -> fp32).  For checking that
+ * conversion against the format definition; not on the hot path.
+ */
+int dsa_fp8_decode_check(const uint8_t* codes, float* out, int32_t n,
+                         void* stream);
+
+/* Text of the last error raised on the calling thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

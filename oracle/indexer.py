@@ -43,16 +43,25 @@ F32, BF16, FP8 = "f32", "bf16", "fp8"
 # --------------------------------------------------------------------------
 # key-cache write
 # --------------------------------------------------------------------------
+def fp8_quantize_rows(k32):
+    """Keys [n, d] (float32) -> (e4m3 codes [n, d], fp32 scales [n]).
+
+    Per row: amax = max |k| (exact), scale = fl32(amax / 448) or 1 when
+    amax == 0, code = e4m3(fl32(k / scale)).  NumPy float32 division is
+    IEEE round-to-nearest-even.
+    """
+    k32 = np.asarray(k32, dtype=np.float32)
+    amax = np.max(np.abs(k32), axis=1) if k32.shape[1] else np.zeros(k32.shape[0], np.float32)
+    scale = np.where(amax == 0, np.float32(1.0),
+                     (amax / np.float32(codecs.E4M3_MAX)).astype(np.float32)).astype(np.float32)
+    v = (k32 / scale[:, None]).astype(np.float32)
+    return codecs.f32_to_e4m3(v), scale
+
+
 def fp8_quantize_token(k32):
     """One token's key (float32 vector) -> (e4m3 codes, fp32 scale)."""
-    k32 = np.asarray(k32, dtype=np.float32)
-    amax = np.float32(np.max(np.abs(k32))) if k32.size else np.float32(0)
-    if amax == 0:
-        scale = np.float32(1.0)
-    else:
-        scale = np.float32(amax / np.float32(codecs.E4M3_MAX))
-    v = (k32 / scale).astype(np.float32)          # IEEE fp32 division
-    return codecs.f32_to_e4m3(v), scale
+    codes, scale = fp8_quantize_rows(np.asarray(k32, dtype=np.float32)[None, :])
+    return codes[0], scale[0]
 
 
 def cache_write(k_new, slot_mapping, cache, scale=None, cache_dtype=BF16):

@@ -1,0 +1,376 @@
+// Host side of the C ABI declared in include/dsa.h: argument validation,
+// workspace sizing, kernel dispatch, the IndexShare layer driver and the
+// thread-local error text.  Every host-checkable condition is checked before
+// anything is enqueued.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return DSA_OK;
+}
+
+// Prepends "<what>: " to the current error text.
+int prefix_error(int code, const char* what, int layer) {
+  char prev[sizeof(g_err)];
+  memcpy(prev, g_err, sizeof(prev));
+  char head[64];
+  snprintf(head, sizeof(head), what, layer);
+  return fail(code, "%s: %s", head, prev);
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+int check_batch(const dsa_batch* b) {
+  if (!b) return fail(DSA_ERR_INVALID_ARG, "batch is NULL");
+  if (b->num_reqs < 1) return fail(DSA_ERR_INVALID_ARG, "num_reqs must be >= 1");
+  if (b->num_q_tokens < 0 || b->max_q_len < 0 || b->max_seq_len < 0)
+    return fail(DSA_ERR_INVALID_ARG, "negative token count or length");
+  if (b->num_q_tokens > 0 && b->max_q_len < 1)
+    return fail(DSA_ERR_INVALID_ARG, "max_q_len must be >= 1");
+  if (b->max_q_len > b->max_seq_len)
+    return fail(DSA_ERR_INVALID_ARG, "max_q_len %d exceeds max_seq_len %d",
+                b->max_q_len, b->max_seq_len);
+  if (b->block_size < 1 || b->max_blocks < 1 || b->num_slots < 1)
+    return fail(DSA_ERR_INVALID_ARG, "block_size, max_blocks and num_slots must be >= 1");
+  if (b->block_size % 32 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "block_size %d is not a multiple of 32",
+                b->block_size);
+  if (static_cast<int64_t>(b->max_blocks) * b->block_size < b->max_seq_len)
+    return fail(DSA_ERR_INVALID_ARG,
+                "max_blocks * block_size (%lld) < max_seq_len (%d)",
+                static_cast<long long>(b->max_blocks) * b->block_size,
+                b->max_seq_len);
+  if (!b->seq_lens || !b->cu_q || !b->block_table)
+    return fail(DSA_ERR_INVALID_ARG, "batch device pointers must be non-NULL");
+  if (static_cast<int64_t>(b->num_q_tokens) * b->max_seq_len > (int64_t(1) << 40))
+    return fail(DSA_ERR_UNSUPPORTED, "num_q_tokens * max_seq_len too large");
+  return DSA_OK;
+}
+
+bool known_dtype(int d) {
+  return d == DSA_F32 || d == DSA_BF16 || d == DSA_FP8_E4M3;
+}
+
+size_t topk_ws(const dsa_batch* b) {
+  return round_up(static_cast<size_t>(b->num_q_tokens) *
+                  static_cast<size_t>(b->max_seq_len) * sizeof(float));
+}
+
+size_t mla_ws(const dsa_batch* b, int n_heads, int R, int P, int topk, int dtype) {
+  const int split = dsa::mla_choose_split(b, dtype, n_heads, R, P, topk);
+  if (split <= 1) return 0;
+  const size_t th = static_cast<size_t>(b->num_q_tokens) * split * n_heads;
+  return round_up(th * R * sizeof(float)) + round_up(th * sizeof(float));
+}
+
+int check_indexer(const dsa_batch* b, const void* q, int q_dtype,
+                  const float* w, int n_heads, int d_idx, const void* k_cache,
+                  const float* k_scale, int cache_dtype, int topk,
+                  const int32_t* topk_idx, const void* ws, size_t ws_bytes) {
+  int st = check_batch(b);
+  if (st) return st;
+  if (!q || !w || !k_cache || !topk_idx)
+    return fail(DSA_ERR_INVALID_ARG, "q, w, k_cache and topk_idx must be non-NULL");
+  if (!known_dtype(q_dtype) || !known_dtype(cache_dtype))
+    return fail(DSA_ERR_INVALID_ARG, "unknown dtype");
+  if (q_dtype == DSA_FP8_E4M3)
+    return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer queries are not supported");
+  if (cache_dtype == DSA_FP8_E4M3) {
+    if (q_dtype != DSA_BF16)
+      return fail(DSA_ERR_UNSUPPORTED, "an FP8 cache needs bf16 queries");
+    if (!k_scale) return fail(DSA_ERR_INVALID_ARG, "FP8 cache needs k_scale");
+  } else if (cache_dtype != q_dtype) {
+    return fail(DSA_ERR_UNSUPPORTED, "q dtype %d with cache dtype %d", q_dtype,
+                cache_dtype);
+  }
+  if (n_heads < 1 || n_heads > 64 || d_idx < 1 || d_idx > 256)
+    return fail(DSA_ERR_UNSUPPORTED, "n_heads %d / d_idx %d outside 1..64 / 1..256",
+                n_heads, d_idx);
+  if (n_heads * d_idx > 8192)
+    return fail(DSA_ERR_UNSUPPORTED, "n_heads * d_idx > 8192");
+  if (topk < 1 || topk > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "topk %d outside 1..%d", topk, DSA_MAX_TOPK);
+  if (b->num_q_tokens > 0 && (!ws || ws_bytes < topk_ws(b)))
+    return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", topk_ws(b),
+                ws ? ws_bytes : static_cast<size_t>(0));
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return DSA_OK;
+}
+
+int check_mla(const dsa_batch* b, const void* q, const void* kv, int dtype,
+              int n_heads, int R, int P, const int32_t* idx, int topk,
+              const void* out, const void* ws, size_t ws_bytes) {
+  int st = check_batch(b);
+  if (st) return st;
+  if (!q || !kv || !idx || !out)
+    return fail(DSA_ERR_INVALID_ARG, "q, kv_cache, topk_idx and out must be non-NULL");
+  if (dtype != DSA_F32 && dtype != DSA_BF16)
+    return fail(DSA_ERR_UNSUPPORTED, "sparse_mla_attn dtype must be F32 or BF16");
+  if (n_heads < 1 || n_heads > 128 || R < 1 || P < 0 || R + P > 1024)
+    return fail(DSA_ERR_UNSUPPORTED, "n_heads %d, kv_lora_rank %d, rope_dim %d",
+                n_heads, R, P);
+  if (topk < 1 || topk > DSA_MAX_TOPK)
+    return fail(DSA_ERR_UNSUPPORTED, "topk %d outside 1..%d", topk, DSA_MAX_TOPK);
+  const size_t need = mla_ws(b, n_heads, R, P, topk, dtype);
+  if (need && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  if (need && reinterpret_cast<uintptr_t>(ws) % kAlign)
+    return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  return DSA_OK;
+}
+
+int run_indexer(const dsa_batch* b, const void* q, int q_dtype, const float* w,
+                int n_heads, int d_idx, const void* k_cache, const float* k_scale,
+                int cache_dtype, int topk, int32_t* topk_idx, void* ws,
+                hipStream_t stream) {
+  dsa::IndexerArgs a;
+  a.b = *b;
+  a.q = q;
+  a.q_dtype = q_dtype;
+  a.w = w;
+  a.n_heads = n_heads;
+  a.d_idx = d_idx;
+  a.k_cache = k_cache;
+  a.k_scale = k_scale;
+  a.cache_dtype = cache_dtype;
+  a.topk = topk;
+  a.topk_idx = topk_idx;
+  a.scores = static_cast<float*>(ws);
+  a.row_stride = b->max_seq_len;
+  hipError_t e = dsa::launch_indexer_score(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer score launch");
+  e = dsa::launch_topk(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  return ok();
+}
+
+int run_mla(const dsa_batch* b, const void* q, const void* kv, int dtype,
+            int n_heads, int R, int P, const int32_t* idx, int topk, float scale,
+            void* out, float* lse, void* ws, hipStream_t stream) {
+  dsa::MlaArgs a;
+  a.b = *b;
+  a.q = q;
+  a.kv = kv;
+  a.dtype = dtype;
+  a.n_heads = n_heads;
+  a.R = R;
+  a.P = P;
+  a.idx = idx;
+  a.topk = topk;
+  a.scale = scale;
+  a.out = out;
+  a.lse = lse;
+  a.n_split = dsa::mla_choose_split(b, dtype, n_heads, R, P, topk);
+  a.part_o = nullptr;
+  a.part_lse = nullptr;
+  if (a.n_split > 1) {
+    const size_t th = static_cast<size_t>(b->num_q_tokens) * a.n_split * n_heads;
+    a.part_o = static_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                          round_up(th * R * sizeof(float)));
+  }
+  hipError_t e = dsa::launch_sparse_mla(a, stream);
+  if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");
+  return ok();
+}
+
+int resolve_sources(int32_t n_layers, const int32_t* types, int32_t n_types,
+                    int32_t* src) {
+  if (n_layers < 0) return fail(DSA_ERR_INVALID_ARG, "n_layers < 0");
+  if (n_layers > 0 && (!types || !src))
+    return fail(DSA_ERR_INVALID_ARG, "types and src must be non-NULL");
+  if (n_types < n_layers)
+    return fail(DSA_ERR_INDEXER_TYPES,
+                "indexer_types has %d entries for %d layers", n_types, n_layers);
+  for (int i = 0; i < n_types; ++i)
+    if (types[i] != DSA_LAYER_FULL && types[i] != DSA_LAYER_SHARED)
+      return fail(DSA_ERR_INDEXER_TYPES, "unknown indexer type %d at layer %d",
+                  types[i], i);
+  int last_full = -1;
+  for (int i = 0; i < n_layers; ++i) {
+    if (types[i] == DSA_LAYER_FULL) last_full = i;
+    else if (last_full < 0)
+      return fail(DSA_ERR_INDEXER_TYPES,
+                  "shared layer %d has no preceding full layer", i);
+  }
+  last_full = -1;
+  for (int i = 0; i < n_layers; ++i) {
+    if (types[i] == DSA_LAYER_FULL) last_full = i;
+    src[i] = last_full;
+  }
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_indexer_cache_write(const void* k_new, int32_t k_dtype, int32_t n_new,
+                            int32_t d_idx, const int64_t* slot_mapping,
+                            int64_t num_slots, void* k_cache, float* k_scale,
+                            int32_t cache_dtype, void* stream) {
+  if (n_new < 0 || d_idx < 1 || d_idx > 1024 || num_slots < 1)
+    return fail(DSA_ERR_INVALID_ARG, "n_new %d, d_idx %d, num_slots %lld", n_new,
+                d_idx, static_cast<long long>(num_slots));
+  if (n_new > 0 && (!k_new || !slot_mapping || !k_cache))
+    return fail(DSA_ERR_INVALID_ARG, "k_new, slot_mapping and k_cache must be non-NULL");
+  if (!known_dtype(k_dtype) || !known_dtype(cache_dtype))
+    return fail(DSA_ERR_INVALID_ARG, "unknown dtype");
+  if (k_dtype == DSA_FP8_E4M3)
+    return fail(DSA_ERR_UNSUPPORTED, "new keys must be F32 or BF16");
+  if (cache_dtype == DSA_FP8_E4M3) {
+    if (n_new > 0 && !k_scale)
+      return fail(DSA_ERR_INVALID_ARG, "FP8 cache needs k_scale");
+  } else if (cache_dtype != k_dtype) {
+    return fail(DSA_ERR_UNSUPPORTED, "a %s cache stores keys unchanged; key dtype differs",
+                cache_dtype == DSA_BF16 ? "BF16" : "F32");
+  }
+  hipError_t e = dsa::launch_cache_write(k_new, k_dtype, n_new, d_idx,
+                                         slot_mapping, num_slots, k_cache,
+                                         k_scale, cache_dtype,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache write launch");
+  return ok();
+}
+
+size_t dsa_indexer_topk_workspace_size(const dsa_batch* batch, int32_t topk) {
+  (void)topk;
+  if (!batch || batch->num_q_tokens < 0 || batch->max_seq_len < 0) return 0;
+  return topk_ws(batch);
+}
+
+int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
+                     const float* w, int32_t n_heads, int32_t d_idx,
+                     const void* k_cache, const float* k_scale,
+                     int32_t cache_dtype, int32_t topk, int32_t* topk_idx,
+                     void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_indexer(batch, q, q_dtype, w, n_heads, d_idx, k_cache, k_scale,
+                         cache_dtype, topk, topk_idx, workspace, ws_bytes);
+  if (st) return st;
+  return run_indexer(batch, q, q_dtype, w, n_heads, d_idx, k_cache, k_scale,
+                     cache_dtype, topk, topk_idx, workspace,
+                     static_cast<hipStream_t>(stream));
+}
+
+size_t sparse_mla_attn_workspace_size(const dsa_batch* batch, int32_t n_heads,
+                                      int32_t kv_lora_rank, int32_t rope_dim,
+                                      int32_t topk, int32_t dtype) {
+  if (!batch || batch->num_q_tokens < 0) return 0;
+  return mla_ws(batch, n_heads, kv_lora_rank, rope_dim, topk, dtype);
+}
+
+int sparse_mla_attn(const dsa_batch* batch, const void* q, const void* kv_cache,
+                    int32_t dtype, int32_t n_heads, int32_t kv_lora_rank,
+                    int32_t rope_dim, const int32_t* topk_idx, int32_t topk,
+                    float softmax_scale, void* out, float* lse, void* workspace,
+                    size_t ws_bytes, void* stream) {
+  int st = check_mla(batch, q, kv_cache, dtype, n_heads, kv_lora_rank, rope_dim,
+                     topk_idx, topk, out, workspace, ws_bytes);
+  if (st) return st;
+  return run_mla(batch, q, kv_cache, dtype, n_heads, kv_lora_rank, rope_dim,
+                 topk_idx, topk, softmax_scale, out, lse, workspace,
+                 static_cast<hipStream_t>(stream));
+}
+
+int dsa_resolve_indexer_sources(int32_t n_layers, const int32_t* types,
+                                int32_t n_types, int32_t* src) {
+  int st = resolve_sources(n_layers, types, n_types, src);
+  return st ? st : ok();
+}
+
+size_t indexshare_forward_workspace_size(const dsa_batch* batch,
+                                         const dsa_stack_dims* d) {
+  if (!batch || !d || batch->num_q_tokens < 0) return 0;
+  size_t a = topk_ws(batch);
+  size_t m = mla_ws(batch, d->n_heads, d->kv_lora_rank, d->rope_dim, d->topk,
+                    d->mla_dtype);
+  return a > m ? a : m;
+}
+
+int indexshare_forward(const dsa_batch* batch, int32_t n_layers,
+                       const int32_t* types, int32_t n_types,
+                       const dsa_layer* layers, const dsa_stack_dims* d,
+                       const int32_t** active_topk, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  if (!d) return fail(DSA_ERR_INVALID_ARG, "dims is NULL");
+  if (n_layers < 1) return fail(DSA_ERR_INVALID_ARG, "n_layers must be >= 1");
+  if (!layers) return fail(DSA_ERR_INVALID_ARG, "layers is NULL");
+  int32_t src_stack[256];
+  if (n_layers > 256) return fail(DSA_ERR_UNSUPPORTED, "more than 256 layers");
+  int st = resolve_sources(n_layers, types, n_types, src_stack);
+  if (st) return st;
+  // validate every layer before enqueuing anything
+  for (int i = 0; i < n_layers; ++i) {
+    const dsa_layer& L = layers[i];
+    if (src_stack[i] == i) {
+      if (!L.topk_idx)
+        return fail(DSA_ERR_MISSING_TOPK, "full layer %d has no topk_idx buffer", i);
+      st = check_indexer(batch, L.q_idx, d->q_idx_dtype, L.w, d->n_idx_heads,
+                         d->d_idx, L.k_cache, L.k_scale, d->idx_cache_dtype,
+                         d->topk, L.topk_idx, workspace, ws_bytes);
+      if (st) return prefix_error(st, "layer %d indexer", i);
+    }
+    st = check_mla(batch, L.q_mla, L.kv_cache, d->mla_dtype, d->n_heads,
+                   d->kv_lora_rank, d->rope_dim, layers[src_stack[i]].topk_idx,
+                   d->topk, L.out, workspace, ws_bytes);
+    if (st) return prefix_error(st, "layer %d attention", i);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t* active = nullptr;
+  for (int i = 0; i < n_layers; ++i) {
+    const dsa_layer& L = layers[i];
+    if (src_stack[i] == i) {
+      st = run_indexer(batch, L.q_idx, d->q_idx_dtype, L.w, d->n_idx_heads,
+                       d->d_idx, L.k_cache, L.k_scale, d->idx_cache_dtype,
+                       d->topk, L.topk_idx, workspace, s);
+      if (st) return st;
+      active = L.topk_idx;
+    }
+    // a shared layer keeps `active`, the buffer of layer src_stack[i]
+    if (active_topk) active_topk[i] = active;
+    st = run_mla(batch, L.q_mla, L.kv_cache, d->mla_dtype, d->n_heads,
+                 d->kv_lora_rank, d->rope_dim, active, d->topk,
+                 d->softmax_scale, L.out, L.lse, workspace, s);
+    if (st) return st;
+  }
+  return ok();
+}
+
+int dsa_fp8_decode_check(const uint8_t* codes, float* out, int32_t n,
+                         void* stream) {
+  if (n < 0 || n % 8 != 0)
+    return fail(DSA_ERR_INVALID_ARG, "n must be a non-negative multiple of 8");
+  if (n > 0 && (!codes || !out))
+    return fail(DSA_ERR_INVALID_ARG, "codes and out must be non-NULL");
+  hipError_t e = dsa::launch_fp8_decode_check(codes, out, n,
+                                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "fp8 decode launch");
+  return ok();
+}
+
+const char* dsa_last_error(void) { return g_err; }
+
+}  // extern "C"

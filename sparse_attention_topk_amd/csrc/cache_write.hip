@@ -1,0 +1,136 @@
+// Indexer key-cache write (page "GLM5 TensorCast 适配设计", section "DSA
+// Indexer fused semantic op": the op writes new keys into the paged indexer
+// cache addressed by slot_mapping; on the FP8 path it writes e4m3 key codes
+// plus a per-token scale; section "KV cache dtype and parallel-linear
+// boundary fix": the cache dtype follows attention quantisation).
+//
+// One 64-lane wave per token.  F32/BF16: a straight copy.  FP8: the wave
+// reduces amax = max |k| exactly, scale = fl32(amax / 448) (1 if amax == 0),
+// each lane divides its elements by scale (IEEE fp32 division) and rounds to
+// e4m3fn with round-to-nearest-even and saturation at +-448.
+#include "common.h"
+
+namespace dsa {
+namespace {
+
+// fp32 -> OCP e4m3fn, round to nearest even, saturating, sign kept.
+// NaN is outside the contract (it saturates like a large value).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  uint32_t bits = __float_as_uint(v);
+  uint32_t sign = (bits >> 24) & 0x80u;
+  uint32_t a = bits & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;          // |v| >= 448
+  if (a >= 0x3C800000u) {                             // |v| >= 2^-6: normal
+    // keep 3 mantissa bits: round the 20 dropped bits to nearest even; a
+    // carry moves into the exponent, which is the right result
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sign | ((r >> 20) - (120u << 3));          // rebias 127 -> 7
+  }
+  // subnormal: value = m * 2^-9 with m = rne(|v| * 512) in 0..8
+  // (m == 8 is the smallest normal, code 0x08, which is also correct)
+  float m = rintf(__uint_as_float(a) * 512.0f);
+  return sign | static_cast<uint32_t>(m);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, int64_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p,
+                                                       int64_t i) {
+  return bf16_bits_to_f32(p[i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_copy_keys(const T* __restrict__ k_new,
+                                                   int n_new, int d,
+                                                   const int64_t* __restrict__ slots,
+                                                   int64_t num_slots,
+                                                   T* __restrict__ cache) {
+  int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (tok >= n_new) return;
+  int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  for (int e = lane; e < d; e += kWave)
+    cache[slot * d + e] = k_new[static_cast<int64_t>(tok) * d + e];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant_keys(const T* __restrict__ k_new,
+                                                    int n_new, int d,
+                                                    const int64_t* __restrict__ slots,
+                                                    int64_t num_slots,
+                                                    uint8_t* __restrict__ cache,
+                                                    float* __restrict__ scale) {
+  int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int lane = threadIdx.x & 63;
+  if (tok >= n_new) return;
+  int64_t slot = slots[tok];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t src = static_cast<int64_t>(tok) * d;
+  float amax = 0.0f;
+  for (int e = lane; e < d; e += kWave)
+    amax = fmaxf(amax, fabsf(load_as_f32(k_new, src + e)));
+  for (int off = 32; off > 0; off >>= 1)
+    amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  for (int e = lane; e < d; e += kWave) {
+    float v = load_as_f32(k_new, src + e) / s;
+    cache[slot * d + e] = static_cast<uint8_t>(f32_to_e4m3(v));
+  }
+  if (lane == 0) scale[slot] = s;
+}
+
+// Decodes e4m3 codes, 8 per thread, with the conversion and byte packing
+// the indexer's FP8 path uses (n is a multiple of 8).
+__global__ void k_fp8_decode_check(const uint8_t* __restrict__ codes,
+                                   float* __restrict__ out, int n) {
+  int i = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i >= n) return;
+  const u32x2 raw = *reinterpret_cast<const u32x2*>(codes + i);
+  bf16x8 v = fp8x8_to_bf16x8(raw[0], raw[1]);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[i + e] = static_cast<float>(v[e]);
+}
+
+}  // namespace
+
+hipError_t launch_cache_write(const void* k_new, int k_dtype, int n_new,
+                              int d, const int64_t* slots, int64_t num_slots,
+                              void* k_cache, float* k_scale, int cache_dtype,
+                              hipStream_t stream) {
+  if (n_new == 0) return hipSuccess;
+  dim3 grid((n_new + 3) / 4), block(256);
+  if (cache_dtype == DSA_FP8_E4M3) {
+    if (k_dtype == DSA_BF16)
+      k_quant_keys<uint16_t><<<grid, block, 0, stream>>>(
+          static_cast<const uint16_t*>(k_new), n_new, d, slots, num_slots,
+          static_cast<uint8_t*>(k_cache), k_scale);
+    else
+      k_quant_keys<float><<<grid, block, 0, stream>>>(
+          static_cast<const float*>(k_new), n_new, d, slots, num_slots,
+          static_cast<uint8_t*>(k_cache), k_scale);
+  } else if (cache_dtype == DSA_BF16) {
+    k_copy_keys<uint16_t><<<grid, block, 0, stream>>>(
+        static_cast<const uint16_t*>(k_new), n_new, d, slots, num_slots,
+        static_cast<uint16_t*>(k_cache));
+  } else {
+    k_copy_keys<float><<<grid, block, 0, stream>>>(
+        static_cast<const float*>(k_new), n_new, d, slots, num_slots,
+        static_cast<float*>(k_cache));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_decode_check(const uint8_t* codes, float* out, int n,
+                                   hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  k_fp8_decode_check<<<(n / 8 + 255) / 256, 256, 0, stream>>>(codes, out, n);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,121 @@
+// Shared device helpers and internal launch declarations for libdsa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa.h"
+
+namespace dsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// e4m3fn x8 (two dwords, byte order = element order) -> bf16 x8.  Exact:
+// every e4m3 value is a bf16 value.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  auto c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ float fp8_to_f32(uint8_t code) {
+  auto v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<uint32_t>(code),
+                                                      1.0f, false);
+  return static_cast<float>(v[0]);
+}
+
+// Physical cache row of logical position s of a request, or -1 when the
+// block id or slot falls outside the cache (treated as "no key").
+__device__ __forceinline__ int64_t slot_of(const int32_t* bt_row, int32_t s,
+                                           int32_t block_size,
+                                           int32_t max_blocks,
+                                           int64_t num_slots) {
+  int32_t blk = s / block_size;
+  if (s < 0 || blk >= max_blocks) return -1;
+  int64_t slot = static_cast<int64_t>(bt_row[blk]) * block_size + s % block_size;
+  return (slot >= 0 && slot < num_slots) ? slot : -1;
+}
+
+// Request that owns query token t: the largest b with cu_q[b] <= t.
+__device__ __forceinline__ int request_of(const int32_t* cu_q, int32_t B,
+                                          int32_t t) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Position of query token t of request b, clamped into [-1, max_seq_len-1].
+__device__ __forceinline__ int32_t query_pos(const int32_t* seq_lens,
+                                             const int32_t* cu_q, int b,
+                                             int32_t t, int32_t max_seq_len) {
+  int32_t L = min(seq_lens[b], max_seq_len);
+  int32_t qlen = cu_q[b + 1] - cu_q[b];
+  return min(L - qlen + (t - cu_q[b]), L - 1);
+}
+
+// Launchers (each returns hipGetLastError() after its launches).
+hipError_t launch_cache_write(const void* k_new, int k_dtype, int n_new,
+                              int d_idx, const int64_t* slot_mapping,
+                              int64_t num_slots, void* k_cache, float* k_scale,
+                              int cache_dtype, hipStream_t stream);
+
+struct IndexerArgs {
+  dsa_batch b;
+  const void* q;
+  int q_dtype;
+  const float* w;
+  int n_heads, d_idx;
+  const void* k_cache;
+  const float* k_scale;
+  int cache_dtype;
+  int topk;
+  int32_t* topk_idx;
+  float* scores;          // workspace [N, max_seq_len]
+  int64_t row_stride;
+};
+bool indexer_mfma_ok(const IndexerArgs& a);
+hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t stream);
+hipError_t launch_topk(const IndexerArgs& a, hipStream_t stream);
+
+struct MlaArgs {
+  dsa_batch b;
+  const void* q;
+  const void* kv;
+  int dtype;
+  int n_heads, R, P;
+  const int32_t* idx;
+  int topk;
+  float scale;
+  void* out;
+  float* lse;
+  float* part_o;          // workspace [N, n_split, H, R] when n_split > 1
+  float* part_lse;        // workspace [N, n_split, H]
+  int n_split;
+};
+bool mla_mfma_ok(int dtype, int n_heads, int R, int P);
+int mla_choose_split(const dsa_batch* b, int dtype, int n_heads, int R, int P,
+                     int topk);
+hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);
+
+hipError_t launch_fp8_decode_check(const uint8_t* codes, float* out, int n,
+                                   hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,285 @@
+// Indexer score (page "GLM5 TensorCast 适配设计", section "DSA Indexer fused
+// semantic op": cache scoring, head-weight mixing and head reduction;
+// section "Performance model design", buckets "q-k index score MMA" and
+// "head weight multiply, head reduce, relu / q-scale / k-scale shaping"):
+//
+//     score[t, s] = kscale[s] * sum_h w[t, h] * max(q[t, h, :] . k[s, :], 0)
+//
+// for every causal key s <= pos(t), written as fp32 into a [N, row_stride]
+// scratch matrix that the top-k kernel reads.  kscale is 1 except for an
+// FP8 cache, whose key value is code * scale; the scale is positive, so it is
+// applied after the head sum.
+//
+// Matrix-core path (bf16 query, bf16 or e4m3 keys, n_heads % 32 == 0,
+// d_idx == 128): one v_mfma_f32_32x32x16_bf16 tile has the 32 heads of one
+// query token on M and 32 keys on N, contracting 16 of the 128 dims per
+// instruction.  The 32x32 accumulator leaves each lane with one key column
+// and 16 of the 32 head rows, so ReLU * w and 16 of the 32 head terms are
+// summed in-lane and one cross-half exchange finishes the head reduction.
+// A workgroup is 4 waves sharing one query block (1 or 2 tokens of a
+// request) and one key chunk; each wave streams 32-key tiles of the paged
+// cache straight from HBM into MFMA operand registers, prefetching the next
+// tile while the current one is multiplied.  Keys of an e4m3 cache are
+// widened exactly to bf16 with the hardware conversion.
+//
+// Vector path: any dtype / shape within the documented limits, one thread
+// per (query token, key), fp32 arithmetic.
+#include "common.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kTile = 32;      // keys per MFMA tile
+constexpr int kWaves = 4;      // waves per workgroup
+constexpr int kChunkTiles = 8; // tiles per wave per workgroup
+constexpr int kChunk = kTile * kWaves * kChunkTiles;   // keys per workgroup
+
+// Dim mapping of the MFMA operands.  Lane half hf = lane / 32 and K-step s
+// (0..7) hold 8 consecutive dims starting at:
+//   bf16 keys: 16 s + 8 hf   (one 16-byte load per step, natural order)
+//   fp8 keys:  64 hf + 8 s   (each lane half reads 64 contiguous bytes)
+// The query operand uses the same mapping, so every product pairs q[d]
+// with k[d].
+template <bool FP8>
+__device__ __forceinline__ int dim_of(int hf, int s) {
+  return FP8 ? (64 * hf + 8 * s) : (16 * s + 8 * hf);
+}
+
+template <bool FP8>
+struct KeyTile {
+  bf16x8 v[8];
+};
+
+template <bool FP8>
+__device__ __forceinline__ void load_key_tile(KeyTile<FP8>& kt,
+                                              const uint8_t* __restrict__ kc,
+                                              int64_t slot, int hf) {
+  if (slot < 0) {
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      kt.v[s] = bf16x8{};
+    return;
+  }
+  if constexpr (!FP8) {
+    const uint8_t* row = kc + slot * 256;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      kt.v[s] = *reinterpret_cast<const bf16x8*>(row + 2 * dim_of<false>(hf, s));
+  } else {
+    const u32x4* row = reinterpret_cast<const u32x4*>(kc + slot * 128 + 64 * hf);
+    u32x4 raw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) raw[j] = row[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      kt.v[2 * j] = fp8x8_to_bf16x8(raw[j][0], raw[j][1]);
+      kt.v[2 * j + 1] = fp8x8_to_bf16x8(raw[j][2], raw[j][3]);
+    }
+  }
+}
+
+// TQ: query tokens per workgroup (1 or 2).  MT: 32-head M-tiles (H / 32).
+template <int TQ, int MT, bool FP8>
+__global__ __launch_bounds__(256, (TQ * MT > 2) ? 1 : 2) void k_score_mfma(
+    const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint8_t* __restrict__ kc, const float* __restrict__ kscale,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ block_table, int32_t max_blocks,
+    int32_t block_size, int64_t num_slots, int32_t max_seq_len,
+    int32_t qblocks_per_req, int32_t nchunks, float* __restrict__ scores,
+    int64_t row_stride) {
+  constexpr int H = 32 * MT;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+
+  const int chunk = blockIdx.x % nchunks;
+  const int qbg = blockIdx.x / nchunks;
+  const int b = qbg / qblocks_per_req;
+  const int qb = qbg % qblocks_per_req;
+
+  const int32_t L = min(seq_lens[b], max_seq_len);
+  const int32_t tbeg = cu_q[b];
+  const int32_t qlen = min(cu_q[b + 1] - tbeg, L);
+  const int32_t t0 = qb * TQ;
+  if (t0 >= qlen) return;
+  const int nt = min(TQ, qlen - t0);
+  const int32_t pos0 = L - qlen + t0;            // position of the first token
+  const int32_t key_end = min(pos0 + nt, (chunk + 1) * kChunk);   // exclusive
+  const int32_t key_beg = chunk * kChunk;
+  if (key_beg >= key_end) return;
+  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
+
+  // query operand and head weights, per token and M-tile
+  bf16x8 qa[TQ][MT][8];
+  float wr[TQ][MT][16];
+#pragma unroll
+  for (int tt = 0; tt < TQ; ++tt) {
+    const bool live = tt < nt;
+    const int64_t tok = tbeg + t0 + (live ? tt : 0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int head = mt * 32 + col;
+      const uint16_t* qrow = q + (tok * H + head) * 128;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        qa[tt][mt][s] = live ? *reinterpret_cast<const bf16x8*>(
+                                   qrow + dim_of<FP8>(hf, s))
+                             : bf16x8{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        // accumulator register r of a 32x32 tile holds row
+        // 8 * (r / 4) + 4 * hf + r % 4 of column `col`
+        const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+        wr[tt][mt][r] = live ? w[tok * H + mt * 32 + row] : 0.0f;
+      }
+    }
+  }
+
+  const int first_tile = key_beg / kTile + wave;
+  const int end_tile = (key_end + kTile - 1) / kTile;
+
+  KeyTile<FP8> cur, nxt;
+  int64_t slot_cur = -1;
+  if (first_tile < end_tile) {
+    const int32_t s = first_tile * kTile + col;
+    slot_cur = s < key_end ? slot_of(bt_row, s, block_size, max_blocks, num_slots) : -1;
+    load_key_tile<FP8>(cur, kc, slot_cur, hf);
+  }
+  for (int tile = first_tile; tile < end_tile; tile += kWaves) {
+    const int nxt_tile = tile + kWaves;
+    int64_t slot_nxt = -1;
+    if (nxt_tile < end_tile) {
+      const int32_t s = nxt_tile * kTile + col;
+      slot_nxt = s < key_end ? slot_of(bt_row, s, block_size, max_blocks, num_slots) : -1;
+      load_key_tile<FP8>(nxt, kc, slot_nxt, hf);
+    }
+    float part[TQ];
+#pragma unroll
+    for (int tt = 0; tt < TQ; ++tt) {
+      part[tt] = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[tt][mt][s], cur.v[s],
+                                                        acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          part[tt] = fmaf(wr[tt][mt][r], fmaxf(acc[r], 0.0f), part[tt]);
+      }
+      part[tt] += __shfl_xor(part[tt], 32);
+    }
+    const int32_t s = tile * kTile + col;
+    float ks = 1.0f;
+    if constexpr (FP8) ks = slot_cur >= 0 ? kscale[slot_cur] : 0.0f;
+    // lane half hf stores token hf's score for key s
+    if (hf < nt) {
+      const int32_t pos = pos0 + hf;
+      float v = part[0];
+      if constexpr (TQ > 1) v = hf ? part[1] : part[0];
+      if (s <= pos && s < key_end)
+        scores[(tbeg + t0 + hf) * row_stride + s] = v * ks;
+    }
+    if (nxt_tile < end_tile) {
+      cur = nxt;
+      slot_cur = slot_nxt;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- vector path
+__device__ __forceinline__ float ld(const void* p, int64_t i, int dt) {
+  if (dt == DSA_F32) return static_cast<const float*>(p)[i];
+  if (dt == DSA_BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+  return fp8_to_f32(static_cast<const uint8_t*>(p)[i]);
+}
+
+// one thread per (token, key); the token's query and weights sit in LDS
+__global__ __launch_bounds__(256) void k_score_vector(
+    const void* __restrict__ q, int q_dtype, const float* __restrict__ w,
+    const void* __restrict__ kc, const float* __restrict__ kscale,
+    int cache_dtype, int H, int D, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ cu_q, int32_t B,
+    const int32_t* __restrict__ block_table, int32_t max_blocks,
+    int32_t block_size, int64_t num_slots, int32_t max_seq_len,
+    int32_t key_blocks, float* __restrict__ scores, int64_t row_stride) {
+  __shared__ float sq[8192];
+  __shared__ float sw[64];
+  const int t = blockIdx.x / key_blocks;
+  const int kb = blockIdx.x % key_blocks;
+  const int b = request_of(cu_q, B, t);
+  const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
+  if (kb * 256 > pos) return;
+  for (int i = threadIdx.x; i < H * D; i += 256)
+    sq[i] = ld(q, static_cast<int64_t>(t) * H * D + i, q_dtype);
+  for (int i = threadIdx.x; i < H; i += 256) sw[i] = w[static_cast<int64_t>(t) * H + i];
+  __syncthreads();
+  const int32_t s = kb * 256 + threadIdx.x;
+  if (s > pos) return;
+  const int64_t slot = slot_of(block_table + static_cast<int64_t>(b) * max_blocks,
+                               s, block_size, max_blocks, num_slots);
+  float score = 0.0f;
+  if (slot >= 0) {
+    for (int h = 0; h < H; ++h) {
+      float dot = 0.0f;
+      for (int d = 0; d < D; ++d)
+        dot = fmaf(sq[h * D + d], ld(kc, slot * D + d, cache_dtype), dot);
+      score = fmaf(sw[h], fmaxf(dot, 0.0f), score);
+    }
+    if (cache_dtype == DSA_FP8_E4M3) score *= kscale[slot];
+  }
+  scores[static_cast<int64_t>(t) * row_stride + s] = score;
+}
+
+template <int TQ, int MT, bool FP8>
+hipError_t launch_mfma(const IndexerArgs& a, hipStream_t stream) {
+  const dsa_batch& b = a.b;
+  const int qbpr = (b.max_q_len + TQ - 1) / TQ;
+  const int nchunks = (b.max_seq_len + kChunk - 1) / kChunk;
+  const int64_t grid = static_cast<int64_t>(b.num_reqs) * qbpr * nchunks;
+  if (grid == 0) return hipSuccess;
+  k_score_mfma<TQ, MT, FP8><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
+      static_cast<const uint16_t*>(a.q), a.w,
+      static_cast<const uint8_t*>(a.k_cache), a.k_scale, b.seq_lens, b.cu_q,
+      b.block_table, b.max_blocks, b.block_size, b.num_slots, b.max_seq_len,
+      qbpr, nchunks, a.scores, a.row_stride);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool indexer_mfma_ok(const IndexerArgs& a) {
+  return a.q_dtype == DSA_BF16 &&
+         (a.cache_dtype == DSA_BF16 || a.cache_dtype == DSA_FP8_E4M3) &&
+         a.d_idx == 128 && (a.n_heads == 32 || a.n_heads == 64) &&
+         a.b.block_size % kTile == 0;
+}
+
+hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t stream) {
+  const dsa_batch& b = a.b;
+  if (b.num_q_tokens == 0) return hipSuccess;
+  if (indexer_mfma_ok(a)) {
+    const bool fp8 = a.cache_dtype == DSA_FP8_E4M3;
+    const bool one = b.max_q_len == 1;
+    const bool mt2 = a.n_heads == 64;
+    if (one) {
+      if (mt2) return fp8 ? launch_mfma<1, 2, true>(a, stream) : launch_mfma<1, 2, false>(a, stream);
+      return fp8 ? launch_mfma<1, 1, true>(a, stream) : launch_mfma<1, 1, false>(a, stream);
+    }
+    if (mt2) return fp8 ? launch_mfma<2, 2, true>(a, stream) : launch_mfma<2, 2, false>(a, stream);
+    return fp8 ? launch_mfma<2, 1, true>(a, stream) : launch_mfma<2, 1, false>(a, stream);
+  }
+  const int key_blocks = (b.max_seq_len + 255) / 256;
+  const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * key_blocks;
+  k_score_vector<<<static_cast<unsigned>(grid), 256, 0, stream>>>(
+      a.q, a.q_dtype, a.w, a.k_cache, a.k_scale, a.cache_dtype, a.n_heads,
+      a.d_idx, b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
+      b.block_size, b.num_slots, b.max_seq_len, key_blocks, a.scores,
+      a.row_stride);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,311 @@
+// Deterministic per-row top-k (page "GLM5 TensorCast 适配设计", section "DSA
+// Indexer fused semantic op": top-k selection, output width topk_limit, or
+// min(topk_limit, active length); page "GLM5 full-stack LoRA", section 1:
+// the selection must not depend on an unspecified tie order).
+//
+// Row t holds the scores of query token t over positions 0..pos(t).  The
+// kernel selects the n = min(topk, pos + 1) positions that come first in the
+// order (score descending, position ascending) and writes them in ascending
+// position order, then -1 up to topk.
+//
+// One 1024-thread workgroup per row.  Scores become order-preserving 32-bit
+// keys (-0.0 is folded into +0.0 first, so the two zeros tie and fall to the
+// position rule).  The selection finds the threshold key T = the topk-th
+// largest key and the count c_gt of keys strictly above it; the output is
+// then every position with key > T plus the first topk - c_gt positions with
+// key == T, in position order.
+//
+//  1. load: the row is read once from HBM, into LDS when it fits
+//     (<= 32768 keys), tracking the value range [vmin, vmax];
+//  2. histogram over 2048 value-linear bins of [vmin, vmax] (the bin map is
+//     monotone in the value, so every key in a higher bin is strictly
+//     larger), LDS atomics;
+//  3. the bin holding the threshold is found by a suffix scan; its keys are
+//     gathered into a candidate list;
+//  4. an exact 4 x 8-bit radix select over the candidates (or over the whole
+//     row when the bin is too large) gives T and c_gt;
+//  5. ordered compaction: each wave owns a contiguous span of the row,
+//     counts keys > T and == T with wave ballots, the per-wave counts are
+//     scanned across waves, then each wave emits its positions in order
+//     using ballot prefix counts.
+#include "common.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kBins = 2048;
+constexpr int kRowCap = 32768;    // keys kept in LDS
+constexpr int kCandCap = 4096;
+
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7FFFFFFFu) == 0) b = 0;                 // -0.0 -> +0.0
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+struct Shared {
+  uint32_t row[kRowCap];
+  uint32_t hist[kBins];
+  uint32_t cand[kCandCap];
+  uint32_t wave_a[kWaves];
+  uint32_t wave_b[kWaves];
+  float red_min[kWaves];
+  float red_max[kWaves];
+  uint32_t ncand;
+  uint32_t sel_bin;       // threshold bin
+  uint32_t above_bin;     // keys in bins above it
+  uint32_t digit;         // radix step result
+  uint32_t digit_above;
+};
+
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Suffix scan helper: for a 256-bin histogram find digit d with
+// above(d) < r <= above(d) + h[d] (above = sum of higher bins).  Wave 0
+// scans; results land in s.digit / s.digit_above.
+__device__ void find_digit(Shared& s, uint32_t r) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    // lane owns digits 255 - 4*lane - i, i = 0..3 (top-down)
+    uint32_t c[4];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[i] = s.hist[255 - 4 * lane - i];
+      tot += c[i];
+    }
+    uint32_t incl = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      uint32_t v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    uint32_t above = incl - tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (above < r && r <= above + c[i]) {
+        s.digit = 255 - 4 * lane - i;
+        s.digit_above = above;
+      }
+      above += c[i];
+    }
+  }
+}
+
+template <bool IN_LDS>
+__device__ __forceinline__ uint32_t row_key(const Shared& s,
+                                            const float* __restrict__ src,
+                                            int i) {
+  if constexpr (IN_LDS) return s.row[i];
+  return float_key(src[i]);
+}
+
+__device__ __forceinline__ int bin_of(float v, float vmin, float inv) {
+  float t = (v - vmin) * inv;
+  // NaN (0 * inf when the range underflows) compares false -> bin 0;
+  // the map stays monotone in v
+  int b = t > 0.0f ? (t >= static_cast<float>(kBins) ? kBins - 1 : static_cast<int>(t)) : 0;
+  return b;
+}
+
+template <bool IN_LDS>
+__device__ void select_row(Shared& s, const float* __restrict__ src, int L,
+                           int topk, int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // ---- 1. load + range
+  float vmin = INFINITY, vmax = -INFINITY;
+  for (int i = tid; i < L; i += kThreads) {
+    const uint32_t k = float_key(src[i]);
+    if constexpr (IN_LDS) s.row[i] = k;
+    const float f = key_float(k);
+    vmin = fminf(vmin, f);
+    vmax = fmaxf(vmax, f);
+  }
+  for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    vmin = fminf(vmin, __shfl_xor(vmin, off));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+  }
+  if (lane == 0) {
+    s.red_min[wave] = vmin;
+    s.red_max[wave] = vmax;
+  }
+  if (tid == 0) s.ncand = 0;
+  __syncthreads();
+  vmin = s.red_min[0];
+  vmax = s.red_max[0];
+#pragma unroll
+  for (int wv = 1; wv < kWaves; ++wv) {
+    vmin = fminf(vmin, s.red_min[wv]);
+    vmax = fmaxf(vmax, s.red_max[wv]);
+  }
+
+  uint32_t T;
+  uint32_t c_gt;
+  if (!(vmax > vmin)) {
+    // every key is equal: positions decide
+    T = float_key(vmax);
+    c_gt = 0;
+  } else {
+    // ---- 2. histogram
+    const float inv = static_cast<float>(kBins) / (vmax - vmin);
+    for (int i = tid; i < L; i += kThreads) {
+      const float f = key_float(row_key<IN_LDS>(s, src, i));
+      atomicAdd(&s.hist[bin_of(f, vmin, inv)], 1u);
+    }
+    __syncthreads();
+    // ---- 3. threshold bin: thread tid owns bins 2047-2tid, 2046-2tid
+    {
+      const uint32_t h0 = s.hist[kBins - 1 - 2 * tid];
+      const uint32_t h1 = s.hist[kBins - 2 - 2 * tid];
+      const uint32_t tot = h0 + h1;
+      uint32_t incl = tot;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        uint32_t v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      if (lane == 63) s.wave_a[wave] = incl;
+      __syncthreads();
+      uint32_t base = 0;
+      for (int wv = 0; wv < wave; ++wv) base += s.wave_a[wv];
+      const uint32_t above0 = base + incl - tot;    // above bin 2047-2tid
+      const uint32_t r = static_cast<uint32_t>(topk);
+      if (above0 < r && r <= above0 + h0) {
+        s.sel_bin = kBins - 1 - 2 * tid;
+        s.above_bin = above0;
+      }
+      const uint32_t above1 = above0 + h0;
+      if (above1 < r && r <= above1 + h1) {
+        s.sel_bin = kBins - 2 - 2 * tid;
+        s.above_bin = above1;
+      }
+    }
+    __syncthreads();
+    const int sel = static_cast<int>(s.sel_bin);
+    const uint32_t above_bin = s.above_bin;
+    const uint32_t bin_count = s.hist[sel];
+    const bool use_cand = bin_count <= kCandCap;
+    if (use_cand) {
+      for (int i = tid; i < L; i += kThreads) {
+        const uint32_t k = row_key<IN_LDS>(s, src, i);
+        if (bin_of(key_float(k), vmin, inv) == sel) {
+          const uint32_t slot = atomicAdd(&s.ncand, 1u);
+          if (slot < kCandCap) s.cand[slot] = k;
+        }
+      }
+    }
+    __syncthreads();
+    // ---- 4. exact radix select of rank r among the set
+    uint32_t r = use_cand ? static_cast<uint32_t>(topk) - above_bin
+                          : static_cast<uint32_t>(topk);
+    const int n_set = use_cand ? min(static_cast<int>(s.ncand), kCandCap) : L;
+    uint32_t prefix = 0, mask = 0, gt_extra = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kThreads) s.hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n_set; i += kThreads) {
+        const uint32_t k = use_cand ? s.cand[i] : row_key<IN_LDS>(s, src, i);
+        if ((k & mask) == prefix) atomicAdd(&s.hist[(k >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      find_digit(s, r);
+      __syncthreads();
+      const uint32_t d = s.digit;
+      const uint32_t da = s.digit_above;
+      r -= da;
+      gt_extra += da;
+      prefix |= d << shift;
+      mask |= 255u << shift;
+      __syncthreads();
+    }
+    T = prefix;
+    c_gt = (use_cand ? above_bin : 0u) + gt_extra;
+  }
+
+  // ---- 5. ordered compaction
+  const uint32_t need = static_cast<uint32_t>(topk) - c_gt;   // >= 1
+  const int span = ((L + kWaves - 1) / kWaves + 63) & ~63;
+  const int beg = wave * span;
+  const int end = min(L, beg + span);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    const uint32_t k = i < end ? row_key<IN_LDS>(s, src, i) : 0u;
+    const bool gt = i < end && k > T;
+    const bool eq = i < end && k == T;
+    n_gt += __popcll(__ballot(gt));
+    n_eq += __popcll(__ballot(eq));
+  }
+  if (lane == 0) {
+    s.wave_a[wave] = n_gt;
+    s.wave_b[wave] = n_eq;
+  }
+  __syncthreads();
+  uint32_t gt_run = 0, eq_run = 0;
+  for (int wv = 0; wv < wave; ++wv) {
+    gt_run += s.wave_a[wv];
+    eq_run += s.wave_b[wv];
+  }
+  const uint64_t below = lanes_below();
+  for (int base = beg; base < end; base += 64) {
+    const int i = base + lane;
+    const uint32_t k = i < end ? row_key<IN_LDS>(s, src, i) : 0u;
+    const bool gt = i < end && k > T;
+    const bool eq = i < end && k == T;
+    const uint64_t gm = __ballot(gt);
+    const uint64_t em = __ballot(eq);
+    const uint32_t eq_rank = eq_run + __popcll(em & below);
+    const bool take = gt || (eq && eq_rank < need);
+    const uint64_t tm = __ballot(take);
+    const uint32_t o = gt_run + min(eq_run, need) + __popcll(tm & below);
+    if (take && o < static_cast<uint32_t>(topk)) out[o] = i;
+    gt_run += __popcll(gm);
+    eq_run += __popcll(em);
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_topk(
+    const float* __restrict__ scores, int64_t row_stride,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
+    int32_t B, int32_t max_seq_len, int32_t topk, int32_t* __restrict__ out) {
+  __shared__ Shared s;
+  const int t = blockIdx.x;
+  const int b = request_of(cu_q, B, t);
+  const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
+  const int L = pos + 1;
+  int32_t* orow = out + static_cast<int64_t>(t) * topk;
+  if (L <= topk) {
+    for (int j = threadIdx.x; j < topk; j += kThreads) orow[j] = j < L ? j : -1;
+    return;
+  }
+  const float* src = scores + static_cast<int64_t>(t) * row_stride;
+  if (L <= kRowCap)
+    select_row<true>(s, src, L, topk, orow);
+  else
+    select_row<false>(s, src, L, topk, orow);
+}
+
+}  // namespace
+
+hipError_t launch_topk(const IndexerArgs& a, hipStream_t stream) {
+  if (a.b.num_q_tokens == 0) return hipSuccess;
+  k_topk<<<a.b.num_q_tokens, kThreads, 0, stream>>>(
+      a.scores, a.row_stride, a.b.seq_lens, a.b.cu_q, a.b.num_reqs,
+      a.b.max_seq_len, a.topk, a.topk_idx);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

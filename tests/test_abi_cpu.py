@@ -1,0 +1,162 @@
+"""The C-ABI library loads on a host without a GPU, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from _util import ROOT, ensure_library
+
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(?:int|size_t|const char\s*\*)\s+(\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    dsa = ensure_library()
+    lib = dsa.load_library()
+    declared = _declared()
+    assert len(declared) >= 10
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(dsa.exported_symbols()) == declared
+
+
+def test_resolve_sources_matches_the_oracle():
+    from oracle import indexshare as ix
+    dsa = ensure_library()
+    F, S = dsa.DSA_LAYER_FULL, dsa.DSA_LAYER_SHARED
+    names = {F: ix.FULL, S: ix.SHARED}
+    cases = [([F, S, S, S, F, S, S, S], 8), ([F], 1), ([F, F, S], 3),
+             ([F, S, F, S, S], 5), ([F, S, S, F, S, S, S, S], 4)]
+    for types, n in cases:
+        assert dsa.dsa_resolve_indexer_sources(types, n) == \
+            ix.resolve_sources([names[t] for t in types], n)
+    for types, n in ([S, F], 2), ([F, S], 3), ([F, 7], 2), ([F, S, -1], 2):
+        with pytest.raises(ValueError):
+            dsa.dsa_resolve_indexer_sources(types, n)
+        with pytest.raises(ValueError):
+            ix.resolve_sources([names.get(t, "bogus") for t in types], n)
+
+
+# Fake device addresses: every call below must fail host validation before
+# anything touches them.
+_FAKE = 1 << 40
+
+
+def _batch(lib_mod, **kw):
+    b = dict(num_reqs=2, num_q_tokens=4, max_q_len=2, max_seq_len=128,
+             max_blocks=2, block_size=64, num_slots=256, seq_lens=_FAKE,
+             cu_q=_FAKE, block_table=_FAKE)
+    b.update(kw)
+    return lib_mod._binding._CBatch(**b)
+
+
+def _topk(lib, cb, **kw):
+    a = dict(q=_FAKE, q_dtype=1, w=_FAKE, n_heads=32, d_idx=128,
+             k_cache=_FAKE, k_scale=None, cache_dtype=1, topk=16,
+             topk_idx=_FAKE, ws=_FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.dsa_indexer_topk(ctypes.byref(cb), a["q"], a["q_dtype"], a["w"],
+                                a["n_heads"], a["d_idx"], a["k_cache"],
+                                a["k_scale"], a["cache_dtype"], a["topk"],
+                                a["topk_idx"], a["ws"], a["ws_bytes"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1),
+    (dict(topk_idx=None), -1),
+    (dict(q_dtype=9), -1),
+    (dict(q_dtype=2, cache_dtype=2), -2),
+    (dict(cache_dtype=2), -1),            # FP8 cache without k_scale
+    (dict(q_dtype=0, cache_dtype=1), -2),
+    (dict(n_heads=65), -2),
+    (dict(d_idx=300), -2),
+    (dict(topk=0), -2),
+    (dict(topk=5000), -2),
+    (dict(ws=None), -5),
+    (dict(ws_bytes=10), -5),
+    (dict(ws=_FAKE + 8), -1),             # misaligned workspace
+])
+def test_indexer_topk_rejects_on_host(kw, code):
+    dsa = ensure_library()
+    lib = dsa.load_library()
+    assert _topk(lib, _batch(dsa), **kw) == code
+    assert dsa.dsa_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(num_reqs=0), -1),
+    (dict(block_size=48), -2),
+    (dict(max_blocks=1), -1),             # 1 * 64 < max_seq_len 128
+    (dict(max_q_len=200), -1),
+    (dict(seq_lens=None), -1),
+    (dict(num_slots=0), -1),
+])
+def test_batch_geometry_is_validated(kw, code):
+    dsa = ensure_library()
+    lib = dsa.load_library()
+    assert _topk(lib, _batch(dsa, **kw)) == code
+
+
+def test_workspace_size_formula():
+    dsa = ensure_library()
+    lib = dsa.load_library()
+    cb = _batch(dsa)
+    assert lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb), 16) == 4 * 128 * 4 + 256 - (4 * 128 * 4) % 256 if (4 * 128 * 4) % 256 else 4 * 128 * 4
+    # no split for the vector path, so no MLA workspace
+    assert lib.sparse_mla_attn_workspace_size(ctypes.byref(cb), 4, 64, 16, 16, 0) == 0
+    # the matrix-core path with few workgroups needs split partials
+    assert lib.sparse_mla_attn_workspace_size(ctypes.byref(cb), 64, 512, 64, 2048, 1) > 0
+
+
+def test_mla_and_cache_write_reject_on_host():
+    dsa = ensure_library()
+    lib = dsa.load_library()
+    cb = _batch(dsa)
+    P = _FAKE
+    # bad dtype
+    assert lib.sparse_mla_attn(ctypes.byref(cb), P, P, 2, 4, 64, 16, P, 16,
+                               ctypes.c_float(0.1), P, None, None, 0, None) == -2
+    # missing workspace for the split path
+    assert lib.sparse_mla_attn(ctypes.byref(cb), P, P, 1, 64, 512, 64, P, 2048,
+                               ctypes.c_float(0.1), P, None, None, 0, None) == -5
+    assert lib.sparse_mla_attn(ctypes.byref(cb), None, P, 1, 4, 64, 16, P, 16,
+                               ctypes.c_float(0.1), P, None, None, 0, None) == -1
+    # cache write: bf16 keys into an f32 cache, fp8 without scale, bad d
+    assert lib.dsa_indexer_cache_write(P, 1, 4, 128, P, 256, P, None, 0, None) == -2
+    assert lib.dsa_indexer_cache_write(P, 1, 4, 128, P, 256, P, None, 2, None) == -1
+    assert lib.dsa_indexer_cache_write(P, 1, 4, 0, P, 256, P, None, 1, None) == -1
+    assert lib.dsa_indexer_cache_write(P, 2, 4, 128, P, 256, P, P, 2, None) == -2
+    # n_new == 0 is a no-op that succeeds without touching the GPU
+    assert lib.dsa_indexer_cache_write(None, 1, 0, 128, None, 256, None, None, 1, None) == 0
+
+
+def test_indexshare_rejects_on_host():
+    dsa = ensure_library()
+    b = dsa.Batch(seq_lens=torch.zeros(2, dtype=torch.int32),
+                  cu_q=torch.zeros(3, dtype=torch.int32),
+                  block_table=torch.zeros((2, 2), dtype=torch.int32),
+                  num_q_tokens=2, max_q_len=1, max_seq_len=128, block_size=64,
+                  num_slots=256)
+    dims = dsa.StackDims(32, 128, dsa.DSA_BF16, dsa.DSA_BF16, 16, 64, 512, 64,
+                         dsa.DSA_BF16, 0.04)
+    t = torch.zeros(8, dtype=torch.bfloat16)
+    L = dsa.Layer(q_mla=t, kv_cache=t, out=t, q_idx=t, w=t.float(), k_cache=t,
+                  topk_idx=None)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    # shared first layer -> ValueError; full layer without top-k buffer too
+    with pytest.raises(ValueError, match="no preceding full"):
+        dsa.indexshare_forward(b, [dsa.DSA_LAYER_SHARED, dsa.DSA_LAYER_FULL], [L, L], dims, workspace=ws)
+    with pytest.raises(ValueError, match="no topk_idx"):
+        dsa.indexshare_forward(b, [dsa.DSA_LAYER_FULL, dsa.DSA_LAYER_SHARED], [L, L], dims, workspace=ws)
+    with pytest.raises(ValueError, match="entries"):
+        dsa.indexshare_forward(b, [dsa.DSA_LAYER_FULL], [L, L], dims, workspace=ws)

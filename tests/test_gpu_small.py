@@ -1,0 +1,347 @@
+"""GPU parity on small, ragged and degenerate inputs (through the C ABI)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from _util import (attn_close, check_row_invariants, ensure_library, np_bits,
+                   np_f64, recall)
+from oracle import codecs, indexer as OI, indexshare as OX, mla as OM
+from synth import get_config, make_batch, make_layer, make_random_indices
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    return ensure_library()
+
+
+def _dsa_batch(dsa, b):
+    return dsa.Batch.from_synth(b)
+
+
+# ---------------------------------------------------------------- fp8 decode
+def test_fp8_decode_matches_format_table(dsa):
+    codes = torch.arange(256, dtype=torch.uint8, device=DEV)
+    got = dsa.dsa_fp8_decode_check(codes).cpu().numpy().astype(np.float64)
+    ref = codecs.E4M3_TABLE
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    assert np.all(np.isnan(got[~fin]))
+
+
+# ---------------------------------------------------------------- cache write
+@pytest.mark.parametrize("kdt,cdt", [("bf16", "bf16"), ("f32", "f32"),
+                                     ("bf16", "fp8"), ("f32", "fp8")])
+def test_cache_write_bit_exact(dsa, kdt, cdt):
+    g = torch.Generator(device="cpu").manual_seed(11)
+    n, d, slots = 45, 128, 160
+    k = torch.randn(n, d, generator=g) * torch.exp(torch.randn(n, 1, generator=g) * 3)
+    k[3] = 0.0                               # zero key -> scale 1
+    k[4, :] = 1e-3
+    k[4, 7] = -200.0                         # one dominant element
+    k[5] = torch.linspace(-448, 448, d)      # scale 1, exact e4m3 grid points
+    k[6] = torch.tensor([1.0625, 1.1875, -1.0625, 2.0 ** -10] * 32)
+    k[6, 0] = 448.0                          # scale exactly 1: midpoints hit RNE
+    tdt = torch.bfloat16 if kdt == "bf16" else torch.float32
+    k = k.to(tdt).to(DEV)
+    perm = torch.randperm(slots, generator=g)[:n]
+    slot_map = perm.clone().to(torch.int64)
+    slot_map[[2, 9, 30]] = -1               # padding tokens
+    slot_map = slot_map.to(DEV)
+    if cdt == "fp8":
+        cache = torch.full((slots, d), 0x5A, dtype=torch.uint8, device=DEV)
+        scale = torch.full((slots,), 3.25, dtype=torch.float32, device=DEV)
+    else:
+        cache = torch.full((slots, d), -7.5, dtype=tdt, device=DEV)
+        scale = None
+    c0 = np_bits(cache)
+    s0 = None if scale is None else scale.cpu().numpy()
+    dsa.dsa_indexer_cache_write(k, slot_map, cache, scale)
+    torch.cuda.synchronize()
+    k32 = np_f64(k).astype(np.float32)
+    ref_c, ref_s = OI.cache_write(k32, slot_map.cpu().numpy(), c0, s0,
+                                  {"bf16": OI.BF16, "f32": OI.F32, "fp8": OI.FP8}[cdt])
+    got_c = np_bits(cache)
+    if cdt == "f32":
+        assert np.array_equal(got_c.view(np.uint32), ref_c.view(np.uint32))
+    else:
+        assert np.array_equal(got_c, ref_c)
+    if cdt == "fp8":
+        assert np.array_equal(scale.cpu().numpy().view(np.uint32), ref_s.view(np.uint32))
+
+
+# ---------------------------------------------------------------- indexer
+def _oracle_topk(b, lay, cfg, cache_np, scale_np, cdt, topk, tokens=None):
+    return OI.indexer_topk(b.seq_lens, b.cu_q_host, b.block_table_host,
+                           b.block_size, np_f64(lay.q_idx), np_f64(lay.w),
+                           cache_np, scale_np, cdt, topk, tokens=tokens)
+
+
+def test_tiny_prefill_indices_bit_exact(dsa):
+    cfg = get_config("tiny_prefill")
+    b = make_batch(cfg, DEV)
+    lay = make_layer(cfg, b, DEV)
+    # populate the cache through the cache write, token by token in order
+    cache = torch.zeros((b.num_slots, cfg.d_idx), dtype=torch.float32, device=DEV)
+    slots = torch.tensor(OI.physical_slots(b.block_table_host[0], b.block_size, 256),
+                         dtype=torch.int64, device=DEV)
+    k_logical = lay.k_src[slots].contiguous()
+    dsa.dsa_indexer_cache_write(k_logical, slots, cache)
+    idx = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), lay.q_idx, lay.w, cache, None, cfg.topk)
+    torch.cuda.synchronize()
+    ref = _oracle_topk(b, lay, cfg, np_bits(lay.k_src), None, OI.F32, cfg.topk)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def _small_cfg(**kw):
+    base = get_config("decode_32k_mtp")
+    return base.scaled(name="small", cid=60, **kw)
+
+
+@pytest.mark.parametrize("topk", [64, 300, 2048])
+def test_bf16_ragged_matrix_core_path(dsa, topk):
+    cfg = _small_cfg(num_reqs=6, topk=topk)
+    b = make_batch(cfg, DEV, seq_lens=[1, 37, 200, 1000, 3000, 5003],
+                   q_lens=[1, 2, 3, 1, 2, 4])
+    lay = make_layer(cfg, b, DEV)
+    idx = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), lay.q_idx, lay.w, lay.k_src, None, topk)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    ref = _oracle_topk(b, lay, cfg, np_bits(lay.k_src), None, OI.BF16, topk)
+    t = 0
+    for bi in range(b.num_reqs):
+        for i in range(b.q_lens[bi]):
+            pos = b.seq_lens[bi] - b.q_lens[bi] + i
+            check_row_invariants(got[t], pos, topk)
+            if pos + 1 <= topk:
+                assert np.array_equal(got[t], ref[t])
+            t += 1
+    r, worst = recall(got, ref)
+    assert r >= 0.999, (r, worst)
+
+
+def test_vector_path_odd_shapes(dsa):
+    cfg = _small_cfg(num_reqs=3, n_idx_heads=5, d_idx=24, topk=40)
+    b = make_batch(cfg, DEV, seq_lens=[50, 129, 700], q_lens=[2, 1, 3])
+    lay = make_layer(cfg, b, DEV)
+    idx = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), lay.q_idx, lay.w, lay.k_src, None, 40)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    ref = _oracle_topk(b, lay, cfg, np_bits(lay.k_src), None, OI.BF16, 40)
+    r, _ = recall(got, ref)
+    assert r >= 0.999
+
+
+def test_fp8_cache_including_row_longer_than_lds(dsa):
+    cfg = _small_cfg(num_reqs=3, q_len=1, idx_cache_dtype="fp8", topk=2048)
+    b = make_batch(cfg, DEV, seq_lens=[100, 2500, 40000], q_lens=[1, 1, 1])
+    lay = make_layer(cfg, b, DEV)
+    cache = torch.zeros((b.num_slots, 128), dtype=torch.uint8, device=DEV)
+    scale = torch.zeros((b.num_slots,), dtype=torch.float32, device=DEV)
+    all_slots = torch.arange(b.num_slots, dtype=torch.int64, device=DEV)
+    dsa.dsa_indexer_cache_write(lay.k_src, all_slots, cache, scale)
+    idx = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), lay.q_idx, lay.w, cache, scale, 2048)
+    torch.cuda.synchronize()
+    codes, scales = OI.fp8_quantize_rows(np_f64(lay.k_src).astype(np.float32))
+    assert np.array_equal(np_bits(cache), codes)
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), scales.view(np.uint32))
+    ref = _oracle_topk(b, lay, cfg, codes, scales, OI.FP8, 2048)
+    got = idx.cpu().numpy()
+    for t in range(3):
+        check_row_invariants(got[t], b.seq_lens[t] - 1, 2048)
+    r, _ = recall(got, ref)
+    assert r >= 0.999
+
+
+def _crafted(dsa, L, topk, kind):
+    """One request, one query, crafted so the scores are degenerate."""
+    cfg = _small_cfg(num_reqs=1, q_len=1, topk=topk)
+    b = make_batch(cfg, DEV, seq_lens=[L], q_lens=[1])
+    g = torch.Generator(device="cpu").manual_seed(5)
+    q = torch.zeros(1, 32, 128)
+    q[0, :, 0] = 1.0
+    k = -torch.ones(b.num_slots, 128)              # logit -1 -> ReLU 0
+    w = torch.ones(1, 32)
+    if kind == "all_zero":
+        pass
+    elif kind == "neg_zero":
+        w = -torch.ones(1, 32)                     # -1 * 0 = -0.0 everywhere
+        hot = torch.randperm(b.num_slots, generator=g)[:50]
+        k[hot, 0] = 1.0                            # a few scores -32
+    elif kind == "few_positive":
+        hot = torch.randperm(b.num_slots, generator=g)[:37]
+        k[hot, 0] = torch.arange(1, 38, dtype=torch.float32)
+    elif kind == "two_levels":
+        hot = torch.randperm(b.num_slots, generator=g)[: b.num_slots // 2]
+        k[hot, 0] = 2.0
+    lay_q = q.to(torch.bfloat16).to(DEV)
+    lay_k = k.to(torch.bfloat16).to(DEV)
+    lay_w = w.to(DEV)
+    idx = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), lay_q, lay_w, lay_k, None, topk)
+    torch.cuda.synchronize()
+    ref = OI.indexer_topk(b.seq_lens, b.cu_q_host, b.block_table_host, b.block_size,
+                          np_f64(lay_q), np_f64(lay_w), np_bits(lay_k), None,
+                          OI.BF16, topk)
+    return idx.cpu().numpy(), ref
+
+
+@pytest.mark.parametrize("kind", ["all_zero", "neg_zero", "few_positive", "two_levels"])
+@pytest.mark.parametrize("L", [3000, 32768, 50000])
+def test_degenerate_score_rows_exact(dsa, kind, L):
+    """Exactly representable scores with massive ties: indices must match the
+    oracle exactly (ties to the lower position)."""
+    got, ref = _crafted(dsa, L, 2048, kind)
+    assert np.array_equal(got, ref)
+
+
+def test_indices_deterministic_across_runs(dsa):
+    cfg = _small_cfg(num_reqs=4, topk=512)
+    b = make_batch(cfg, DEV, seq_lens=[4000, 9000, 33000, 600], q_lens=[2, 2, 1, 2])
+    lay = make_layer(cfg, b, DEV)
+    bb = _dsa_batch(dsa, b)
+    a1 = dsa.dsa_indexer_topk(bb, lay.q_idx, lay.w, lay.k_src, None, 512)
+    a2 = dsa.dsa_indexer_topk(bb, lay.q_idx, lay.w, lay.k_src, None, 512)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2)
+
+
+# ---------------------------------------------------------------- sparse MLA
+def _oracle_mla(b, lay, idx_np, R, scale, tokens=None):
+    kv = lay.kv_cache
+
+    def kv_values(slots):
+        s = torch.as_tensor(np.asarray(slots, dtype=np.int64), device=kv.device)
+        return np_f64(kv[s])
+
+    return OM.sparse_mla(b.seq_lens, b.cu_q_host, b.block_table_host,
+                         b.block_size, np_f64(lay.q_mla), kv_values, idx_np, R,
+                         scale, tokens=tokens)
+
+
+def test_tiny_prefill_attention_f32(dsa):
+    cfg = get_config("tiny_prefill")
+    b = make_batch(cfg, DEV)
+    lay = make_layer(cfg, b, DEV, with_indexer=False)
+    idx = make_random_indices(b, cfg.topk, 901, DEV)
+    out, lse = dsa.sparse_mla_attn(_dsa_batch(dsa, b), lay.q_mla, lay.kv_cache, idx,
+                                   cfg.kv_lora_rank, cfg.softmax_scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_mla(b, lay, idx.cpu().numpy(), cfg.kv_lora_rank, cfg.softmax_scale)
+    assert attn_close(out.cpu().numpy(), ro, 1e-4, 1e-4) <= 0
+    assert attn_close(lse.cpu().numpy(), rl, 1e-4, 1e-4) <= 0
+
+
+@pytest.mark.parametrize("n_req,q_len,topk", [(1, 1, 2048), (3, 2, 2048),
+                                              (4, 1, 100), (65, 2, 256)])
+def test_bf16_attention_matrix_core(dsa, n_req, q_len, topk):
+    cfg = _small_cfg(num_reqs=n_req, q_len=q_len, topk=topk)
+    lens = [max(q_len, 2600 - 37 * i) for i in range(n_req)]
+    lens[0] = 1500 if n_req > 1 else lens[0]
+    b = make_batch(cfg, DEV, seq_lens=lens, q_lens=[q_len] * n_req)
+    lay = make_layer(cfg, b, DEV, with_indexer=False)
+    idx = make_random_indices(b, topk, 77 + n_req, DEV)
+    out, lse = dsa.sparse_mla_attn(_dsa_batch(dsa, b), lay.q_mla, lay.kv_cache, idx,
+                                   cfg.kv_lora_rank, cfg.softmax_scale)
+    torch.cuda.synchronize()
+    toks = list(range(min(b.num_q_tokens, 6))) + [b.num_q_tokens - 1]
+    ro, rl = _oracle_mla(b, lay, idx.cpu().numpy(), cfg.kv_lora_rank,
+                         cfg.softmax_scale, tokens=toks)
+    go = np_f64(out)
+    gl = lse.cpu().numpy()
+    for t in toks:
+        assert attn_close(go[t], ro[t]) <= 0, t
+        assert attn_close(gl[t], rl[t], 1e-3, 1e-4) <= 0, t
+
+
+def test_attention_first_position_and_empty_rows(dsa):
+    cfg = _small_cfg(num_reqs=2, q_len=1, topk=64)
+    b = make_batch(cfg, DEV, seq_lens=[1, 300], q_lens=[1, 1])
+    lay = make_layer(cfg, b, DEV, with_indexer=False)
+    idx = torch.full((2, 64), -1, dtype=torch.int32, device=DEV)
+    idx[0, 0] = 0                     # the only key of request 0
+    out, lse = dsa.sparse_mla_attn(_dsa_batch(dsa, b), lay.q_mla, lay.kv_cache, idx,
+                                   cfg.kv_lora_rank, cfg.softmax_scale)
+    torch.cuda.synchronize()
+    slot0 = int(b.block_table_host[0, 0]) * b.block_size
+    v0 = lay.kv_cache[slot0, :512].float().cpu()
+    for h in range(64):
+        assert torch.equal(out[0, h].float().cpu(), v0)
+    assert torch.all(out[1] == 0)
+    assert torch.all(torch.isneginf(lse[1]))
+
+
+def test_sparse_equals_dense_when_topk_covers_context(dsa):
+    cfg = _small_cfg(num_reqs=1, q_len=40, topk=256, causal_prefill=True)
+    b = make_batch(cfg, DEV, seq_lens=[200], q_lens=[200])
+    lay = make_layer(cfg, b, DEV, with_indexer=False)
+    idx = torch.full((200, 256), -1, dtype=torch.int32)
+    for t in range(200):
+        idx[t, :t + 1] = torch.arange(t + 1)
+    idx = idx.to(DEV)
+    out, lse = dsa.sparse_mla_attn(_dsa_batch(dsa, b), lay.q_mla, lay.kv_cache, idx,
+                                   cfg.kv_lora_rank, cfg.softmax_scale)
+    torch.cuda.synchronize()
+    slots = torch.as_tensor(OI.physical_slots(b.block_table_host[0], 64, 200), device=DEV)
+    kv_logical = np_f64(lay.kv_cache[slots])
+    ro, rl = OM.dense_causal_mla(np_f64(lay.q_mla), kv_logical, np.arange(200), 512,
+                                 cfg.softmax_scale)
+    assert attn_close(np_f64(out), ro) <= 0
+    assert attn_close(lse.cpu().numpy(), rl, 1e-3, 1e-4) <= 0
+
+
+# ---------------------------------------------------------------- IndexShare
+def test_indexshare_stack_small(dsa):
+    types = ["full", "shared", "shared", "shared", "full", "shared", "shared", "shared"]
+    cfg = get_config("indexshare_8layer").scaled(num_reqs=5, cid=61, topk=256)
+    b = make_batch(cfg, DEV, seq_lens=[3000, 1200, 257, 4100, 2048], q_lens=[1] * 5)
+    src = OX.resolve_sources(types, 8)
+    lays = [make_layer(cfg, b, DEV, layer=i, with_indexer=(src[i] == i)) for i in range(8)]
+    bb = _dsa_batch(dsa, b)
+    N = b.num_q_tokens
+    L = []
+    for i, lay in enumerate(lays):
+        full = src[i] == i
+        L.append(dsa.Layer(
+            q_mla=lay.q_mla, kv_cache=lay.kv_cache,
+            out=torch.empty((N, 64, 512), dtype=torch.bfloat16, device=DEV),
+            lse=torch.empty((N, 64), dtype=torch.float32, device=DEV),
+            q_idx=lay.q_idx if full else None, w=lay.w if full else None,
+            k_cache=lay.k_src if full else None,
+            topk_idx=torch.full((N, 256), -7, dtype=torch.int32, device=DEV) if full else None))
+    dims = dsa.StackDims(32, 128, dsa.DSA_BF16, dsa.DSA_BF16, 256, 64, 512, 64,
+                         dsa.DSA_BF16, cfg.softmax_scale)
+    tcodes = [dsa.DSA_LAYER_FULL if t == "full" else dsa.DSA_LAYER_SHARED for t in types]
+    active = dsa.indexshare_forward(bb, tcodes, L, dims)
+    torch.cuda.synchronize()
+    for i in range(8):
+        assert active[i] == L[src[i]].topk_idx.data_ptr()
+    # full layers equal standalone calls; every layer's attention equals a
+    # standalone call with its source layer's indices (bit-identical)
+    for i in range(8):
+        if src[i] == i:
+            alone = dsa.dsa_indexer_topk(bb, lays[i].q_idx, lays[i].w, lays[i].k_src, None, 256)
+            assert torch.equal(alone, L[i].topk_idx)
+        o, l = dsa.sparse_mla_attn(bb, lays[i].q_mla, lays[i].kv_cache, L[src[i]].topk_idx,
+                                   512, cfg.softmax_scale)
+        assert torch.equal(o, L[i].out) and torch.equal(l, L[i].lse)
+    # against the oracle stack
+    def run_idx(i):
+        lay = lays[i]
+        return OI.indexer_topk(b.seq_lens, b.cu_q_host, b.block_table_host, 64,
+                               np_f64(lay.q_idx), np_f64(lay.w), np_bits(lay.k_src),
+                               None, OI.BF16, 256)
+
+    def run_att(i, tk):
+        return _oracle_mla(b, lays[i], tk, 512, cfg.softmax_scale)
+
+    res, acts, calls = OX.forward(types, list(range(8)), run_idx, run_att)
+    assert calls == 2
+    for i in range(8):
+        r, _ = recall(L[src[i]].topk_idx.cpu().numpy(), acts[i])
+        assert r >= 0.999
+        assert attn_close(np_f64(L[i].out), res[i][0]) <= 0

@@ -39,6 +39,15 @@ __device__ __forceinline__ float fp8_to_f32(uint8_t code) {
   return static_cast<float>(v[0]);
 }
 
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() also waits
+// for every outstanding global load of the wave, which would serialise a
+// register prefetch with the barrier; this one leaves them in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Physical cache row of logical position s of a request, or -1 when the
 // block id or slot falls outside the cache (treated as "no key").
 __device__ __forceinline__ int64_t slot_of(const int32_t* bt_row, int32_t s,
@@ -60,6 +69,22 @@ __device__ __forceinline__ int request_of(const int32_t* cu_q, int32_t B,
     if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Same as request_of, computed by the whole workgroup at once: one parallel
+// load of cu_q instead of a chain of dependent loads.  `counter` is an LDS
+// word; every thread of the workgroup must call this.
+__device__ __forceinline__ int request_of_block(const int32_t* cu_q, int32_t B,
+                                                int32_t t, uint32_t* counter) {
+  if (threadIdx.x == 0) *counter = 0;
+  lds_barrier();
+  uint32_t n = 0;
+  for (int b = threadIdx.x; b < B; b += blockDim.x) n += cu_q[b] <= t;
+  for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
+  if ((threadIdx.x & 63) == 0 && n) atomicAdd(counter, n);
+  lds_barrier();
+  const int r = static_cast<int>(*counter) - 1;
+  return r < 0 ? 0 : (r >= B ? B - 1 : r);
 }
 
 // Position of query token t of request b, clamped into [-1, max_seq_len-1].

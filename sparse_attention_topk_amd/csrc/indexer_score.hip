@@ -50,23 +50,21 @@ struct KeyTile {
   bf16x8 v[8];
 };
 
+// Loads one lane's operand of a 32-key tile.  A lane without a key (slot
+// < 0) reads row 0 instead, so the loads are unconditional; its score is
+// masked afterwards.
 template <bool FP8>
 __device__ __forceinline__ void load_key_tile(KeyTile<FP8>& kt,
                                               const uint8_t* __restrict__ kc,
                                               int64_t slot, int hf) {
-  if (slot < 0) {
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      kt.v[s] = bf16x8{};
-    return;
-  }
+  const int64_t row_id = slot < 0 ? 0 : slot;
   if constexpr (!FP8) {
-    const uint8_t* row = kc + slot * 256;
+    const uint8_t* row = kc + row_id * 256;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       kt.v[s] = *reinterpret_cast<const bf16x8*>(row + 2 * dim_of<false>(hf, s));
   } else {
-    const u32x4* row = reinterpret_cast<const u32x4*>(kc + slot * 128 + 64 * hf);
+    const u32x4* row = reinterpret_cast<const u32x4*>(kc + row_id * 128 + 64 * hf);
     u32x4 raw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) raw[j] = row[j];
@@ -137,23 +135,49 @@ __global__ __launch_bounds__(256, (TQ * MT > 2) ? 1 : 2) void k_score_mfma(
     }
   }
 
-  const int first_tile = key_beg / kTile + wave;
+  // The wave's tiles are first_tile + kWaves * i, i < kChunkTiles.  A 32-key
+  // tile never spans two cache blocks (block_size is a multiple of 32), so
+  // one block-table entry per tile gives every slot.  Those entries are read
+  // up front with wave-uniform scalar loads: the key loads inside the loop
+  // then depend on no memory access, and waiting for one tile's keys never
+  // waits behind a block-table load issued after a prefetch.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int first_tile = key_beg / kTile + wave_u;
   const int end_tile = (key_end + kTile - 1) / kTile;
-
-  KeyTile<FP8> cur, nxt;
-  int64_t slot_cur = -1;
-  if (first_tile < end_tile) {
-    const int32_t s = first_tile * kTile + col;
-    slot_cur = s < key_end ? slot_of(bt_row, s, block_size, max_blocks, num_slots) : -1;
-    load_key_tile<FP8>(cur, kc, slot_cur, hf);
+  int64_t row0[kChunkTiles];          // slot of the tile's first key, or -1
+#pragma unroll
+  for (int i = 0; i < kChunkTiles; ++i) {
+    const int tile = first_tile + kWaves * i;
+    row0[i] = -1;
+    if (tile < end_tile) {
+      const int32_t s0 = tile * kTile;
+      const int32_t blk = s0 / block_size;
+      if (blk < max_blocks) {
+        const int64_t slot0 = static_cast<int64_t>(bt_row[blk]) * block_size + s0 % block_size;
+        if (slot0 >= 0 && slot0 + kTile <= num_slots) row0[i] = slot0;
+      }
+    }
   }
-  for (int tile = first_tile; tile < end_tile; tile += kWaves) {
-    const int nxt_tile = tile + kWaves;
-    int64_t slot_nxt = -1;
-    if (nxt_tile < end_tile) {
-      const int32_t s = nxt_tile * kTile + col;
-      slot_nxt = s < key_end ? slot_of(bt_row, s, block_size, max_blocks, num_slots) : -1;
-      load_key_tile<FP8>(nxt, kc, slot_nxt, hf);
+  auto lane_slot = [&](int i) -> int64_t {
+    const int32_t s = (first_tile + kWaves * i) * kTile + col;
+    return (row0[i] >= 0 && s < key_end) ? row0[i] + col : -1;
+  };
+
+  // Three tiles per wave are live: the one being multiplied and the next
+  // two, whose loads are in flight.
+  KeyTile<FP8> cur, n1, n2;
+  int64_t slot_cur = lane_slot(0);
+  int64_t slot_n1 = lane_slot(1);
+  load_key_tile<FP8>(cur, kc, slot_cur, hf);
+  load_key_tile<FP8>(n1, kc, slot_n1, hf);
+#pragma unroll
+  for (int i = 0; i < kChunkTiles; ++i) {
+    const int tile = first_tile + kWaves * i;
+    if (tile >= end_tile) break;
+    int64_t slot_n2 = -1;
+    if (i + 2 < kChunkTiles) {
+      slot_n2 = lane_slot(i + 2);
+      load_key_tile<FP8>(n2, kc, slot_n2, hf);
     }
     float part[TQ];
 #pragma unroll
@@ -173,8 +197,8 @@ __global__ __launch_bounds__(256, (TQ * MT > 2) ? 1 : 2) void k_score_mfma(
       part[tt] += __shfl_xor(part[tt], 32);
     }
     const int32_t s = tile * kTile + col;
-    float ks = 1.0f;
-    if constexpr (FP8) ks = slot_cur >= 0 ? kscale[slot_cur] : 0.0f;
+    float ks = slot_cur >= 0 ? 1.0f : 0.0f;
+    if constexpr (FP8) ks *= kscale[slot_cur >= 0 ? slot_cur : 0];
     // lane half hf stores token hf's score for key s
     if (hf < nt) {
       const int32_t pos = pos0 + hf;
@@ -183,10 +207,10 @@ __global__ __launch_bounds__(256, (TQ * MT > 2) ? 1 : 2) void k_score_mfma(
       if (s <= pos && s < key_end)
         scores[(tbeg + t0 + hf) * row_stride + s] = v * ks;
     }
-    if (nxt_tile < end_tile) {
-      cur = nxt;
-      slot_cur = slot_nxt;
-    }
+    cur = n1;
+    slot_cur = slot_n1;
+    n1 = n2;
+    slot_n1 = slot_n2;
   }
 }
 

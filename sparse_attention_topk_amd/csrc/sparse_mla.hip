@@ -16,7 +16,7 @@
 // 32-key tile of selected rows is gathered from HBM as 16-byte pieces of the
 // 1152-byte rows (one row is 72 pieces; the 256 threads issue them
 // back-to-back, so every row is fetched as whole 128-byte lines), and the
-// next tile's pieces are in flight while the current one is multiplied.
+// next two tiles are in flight while the current one is multiplied.
 // The tile is staged in LDS twice: row-major (the key operand of the logits,
 // 8 consecutive dims per lane) and transposed for the first R dims (the
 // value operand of P.V needs 8 consecutive keys per lane).
@@ -50,7 +50,8 @@ struct MlaShared {
   uint16_t vt[kR * kVS];                // 40960 B
   float s[kHG][kT + 1];                 // logits exchange
   uint16_t p[4][kHG * kPS];             // per-wave probabilities (bf16)
-  int32_t valid[kT];
+  int64_t slots[DSA_MAX_TOPK];          // physical row of each index, or -1
+  uint32_t counter;
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -75,8 +76,8 @@ __device__ __forceinline__ int64_t sel_slot(const int32_t* __restrict__ idx_row,
 
 __global__ __launch_bounds__(256, 1) void k_mla_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
-    const int32_t* __restrict__ topk_idx, int32_t topk, int32_t n_heads,
-    int32_t n_split, int32_t split_len, float scale_log2,
+    const int32_t* __restrict__ topk_idx, int32_t topk, int32_t n_tokens,
+    int32_t n_heads, int32_t n_split, int32_t split_len, float scale_log2,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
     int32_t B, const int32_t* __restrict__ block_table, int32_t max_blocks,
     int32_t block_size, int64_t num_slots, int32_t max_seq_len,
@@ -91,17 +92,56 @@ __global__ __launch_bounds__(256, 1) void k_mla_mfma(
   const int mh = wave & 1;
   const int nk = wave >> 1;
 
+  // Workgroup order: consecutive ids go round-robin over the 8 XCDs, so the
+  // head groups of one (token, split) unit are given ids 8 apart; they land
+  // on the same XCD and the second read of each gathered row hits its L2.
   const int n_hg = n_heads / kHG;
-  const int split = blockIdx.x % n_split;
-  const int hg = (blockIdx.x / n_split) % n_hg;
-  const int t = blockIdx.x / (n_split * n_hg);
+  const int lo8 = blockIdx.x & 7;
+  const int hi = blockIdx.x >> 3;
+  const int hg = hi % n_hg;
+  const int unit = (hi / n_hg) * 8 + lo8;
+  if (unit >= n_tokens * n_split) return;
+  const int t = unit / n_split;
+  const int split = unit % n_split;
 
-  const int b = request_of(cu_q, B, t);
+  const int b = request_of_block(cu_q, B, t, &sh.counter);
   const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
   const int32_t* idx_row = topk_idx + static_cast<int64_t>(t) * topk;
   const int jbeg = split * split_len;
   const int jend = min(topk, jbeg + split_len);
+
+  // Resolve the physical row of every index of this split once, into LDS:
+  // index loads first, then block-table loads, each batch issued together.
+  // The gathers below then wait on no dependent global load.
+  for (int j0 = jbeg; j0 < jend; j0 += 8 * 256) {
+    int32_t p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = j0 + 256 * i + tid;
+      p[i] = j < jend ? idx_row[j] : -1;
+    }
+    int32_t bid[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = p[i] >= 0 && p[i] <= pos && p[i] / block_size < max_blocks;
+      bid[i] = ok ? bt_row[p[i] / block_size] : -1;
+      if (!ok) p[i] = -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = j0 + 256 * i + tid;
+      if (j < jend) {
+        int64_t slot = -1;
+        if (p[i] >= 0) {
+          slot = static_cast<int64_t>(bid[i]) * block_size + p[i] % block_size;
+          if (slot < 0 || slot >= num_slots) slot = -1;
+        }
+        sh.slots[j - jbeg] = slot;
+      }
+    }
+  }
+  lds_barrier();
 
   // query rows of this wave's 16 heads (logit A operand): head 16 mh + l16,
   // dims 32 s + 8 g16 .. +8
@@ -119,45 +159,56 @@ __global__ __launch_bounds__(256, 1) void k_mla_mfma(
   float m_run = -INFINITY, l_run = 0.0f;   // for head (lane & 31)
 
   // gather registers: piece c = tid + 256 i of the tile -> key c / 72,
-  // 16-byte piece c % 72 of that key's row
-  u32x4 g[kPerThread];
-  auto gather = [&](int tile_beg) {
+  // 16-byte piece c % 72 of that key's row; consecutive threads read
+  // consecutive pieces, so each row arrives as whole 128-byte lines
+  auto gather = [&](u32x4 (&g)[kPerThread], int tile_beg) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int c = tid + 256 * i;
       const int key = c / kPieces;
       const int pc = c % kPieces;
-      const int64_t slot = sel_slot(idx_row, tile_beg + key, jend, pos, bt_row,
-                                    block_size, max_blocks, num_slots);
+      const int j = tile_beg + key;
+      const int64_t slot = j < jend ? sh.slots[j - jbeg] : -1;
       g[i] = slot >= 0 ? *reinterpret_cast<const u32x4*>(kv + slot * kD + pc * 8)
                        : u32x4{0, 0, 0, 0};
     }
   };
-  auto stage = [&](int tile_beg) {
+  // registers -> row-major LDS copy of the tile
+  auto stage = [&](const u32x4 (&g)[kPerThread], int tile_beg) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
       const int c = tid + 256 * i;
       const int key = c / kPieces;
       const int pc = c % kPieces;
       *reinterpret_cast<u32x4*>(&sh.k[key * kKS + pc * 8]) = g[i];
-      if (pc < kR / 8) {
+    }
+  };
+  // row-major latent dims -> transposed value tile: unit u = (dim chunk
+  // u / 16, key pair u % 16) reads 8 dims of two keys and writes 8 dwords,
+  // each holding one dim of both keys
+  auto transpose = [&]() {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sh.vt[(pc * 8 + 2 * e) * kVS + key] = static_cast<uint16_t>(g[i][e]);
-          sh.vt[(pc * 8 + 2 * e + 1) * kVS + key] = static_cast<uint16_t>(g[i][e] >> 16);
-        }
+    for (int i = 0; i < (kR / 8) * (kT / 2) / 256; ++i) {
+      const int u = tid + 256 * i;
+      const int kp = u & 15;
+      const int dc = u >> 4;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(&sh.k[(2 * kp) * kKS + dc * 8]);
+      const u32x4 c = *reinterpret_cast<const u32x4*>(&sh.k[(2 * kp + 1) * kKS + dc * 8]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t even = (a[m] & 0xFFFFu) | (c[m] << 16);
+        const uint32_t odd = (a[m] >> 16) | (c[m] & 0xFFFF0000u);
+        *reinterpret_cast<uint32_t*>(&sh.vt[(dc * 8 + 2 * m) * kVS + 2 * kp]) = even;
+        *reinterpret_cast<uint32_t*>(&sh.vt[(dc * 8 + 2 * m + 1) * kVS + 2 * kp]) = odd;
       }
     }
-    if (tid < kT)
-      sh.valid[tid] = sel_slot(idx_row, tile_beg + tid, jend, pos, bt_row,
-                               block_size, max_blocks, num_slots) >= 0;
   };
 
-  if (jbeg < jend) gather(jbeg);
-  for (int tb = jbeg; tb < jend; tb += kT) {
-    stage(tb);
-    if (tb + kT < jend) gather(tb + kT);
-    __syncthreads();
+  auto tile_step = [&](u32x4 (&g)[kPerThread], int tb) {
+    stage(g, tb);
+    if (tb + 2 * kT < jend) gather(g, tb + 2 * kT);     // two tiles ahead
+    lds_barrier();
+    transpose();
 
     // ---- logits: 16 heads (mh) x 16 keys (nk)
     f32x4 acc = {0, 0, 0, 0};
@@ -168,12 +219,13 @@ __global__ __launch_bounds__(256, 1) void k_mla_mfma(
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kk, acc, 0, 0, 0);
     }
     {
-      const bool ok = sh.valid[16 * nk + l16] != 0;
+      const int j = tb + 16 * nk + l16;
+      const bool ok = j < jend && sh.slots[j - jbeg] >= 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         sh.s[16 * mh + 4 * g16 + i][16 * nk + l16] = ok ? acc[i] * scale_log2 : -INFINITY;
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- online softmax: lane handles head (lane & 31), keys 16*(lane>>5)..+16
     const int hh = lane & 31;
@@ -203,6 +255,10 @@ __global__ __launch_bounds__(256, 1) void k_mla_mfma(
     ps += __shfl_xor(ps, 32);
     l_run = l_run * alpha + ps;
     m_run = m_new;
+    // the P tile is wave-private: order its LDS writes before the reads below
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 
     // ---- O = alpha * O + P V for this wave's 128 dims
 #pragma unroll
@@ -227,7 +283,15 @@ __global__ __launch_bounds__(256, 1) void k_mla_mfma(
       for (int mt = 0; mt < 2; ++mt)
         o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], vb, o[mt][nt], 0, 0, 0);
     }
-    __syncthreads();
+    lds_barrier();
+  };
+
+  u32x4 ga[kPerThread], gb[kPerThread];
+  if (jbeg < jend) gather(ga, jbeg);
+  if (jbeg + kT < jend) gather(gb, jbeg + kT);
+  for (int tb = jbeg; tb < jend; tb += 2 * kT) {
+    tile_step(ga, tb);
+    if (tb + kT < jend) tile_step(gb, tb + kT);
   }
 
   // ---- epilogue
@@ -396,10 +460,12 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
     const int n_split = a.n_split;
     int split_len = (a.topk + n_split - 1) / n_split;
     split_len = (split_len + kT - 1) / kT * kT;
-    const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * (a.n_heads / kHG) * n_split;
+    const int64_t units = static_cast<int64_t>(b.num_q_tokens) * n_split;
+    const int64_t grid = (units + 7) / 8 * 8 * (a.n_heads / kHG);
     k_mla_mfma<<<static_cast<unsigned>(grid), 256, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv),
-        a.idx, a.topk, a.n_heads, n_split, split_len, a.scale * kLog2e,
+        a.idx, a.topk, b.num_q_tokens, a.n_heads, n_split, split_len,
+        a.scale * kLog2e,
         b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
         b.block_size, b.num_slots, b.max_seq_len,
         static_cast<uint16_t*>(a.out), a.lse, a.part_o, a.part_lse);

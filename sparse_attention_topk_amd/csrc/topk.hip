@@ -61,6 +61,7 @@ struct Shared {
   uint32_t above_bin;     // keys in bins above it
   uint32_t digit;         // radix step result
   uint32_t digit_above;
+  uint32_t counter;
 };
 
 __device__ __forceinline__ uint64_t lanes_below() {
@@ -108,6 +109,34 @@ __device__ __forceinline__ uint32_t row_key(const Shared& s,
   return float_key(src[i]);
 }
 
+// Visits every key of the row once, thread tid taking i = tid + 1024 j.
+// From global memory the loads are issued kBatch at a time before any is
+// used, so a thread keeps kBatch loads in flight instead of one.
+constexpr int kBatch = 16;
+template <bool IN_LDS, bool FROM_GLOBAL, typename F>
+__device__ __forceinline__ void for_each_key(const Shared& s,
+                                             const float* __restrict__ src,
+                                             int L, F&& f) {
+  const int tid = threadIdx.x;
+  if constexpr (IN_LDS && !FROM_GLOBAL) {
+    for (int i = tid; i < L; i += kThreads) f(i, s.row[i]);
+  } else {
+    for (int base = 0; base < L; base += kBatch * kThreads) {
+      float v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = base + j * kThreads + tid;
+        v[j] = i < L ? src[i] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int i = base + j * kThreads + tid;
+        if (i < L) f(i, float_key(v[j]));
+      }
+    }
+  }
+}
+
 __device__ __forceinline__ int bin_of(float v, float vmin, float inv) {
   float t = (v - vmin) * inv;
   // NaN (0 * inf when the range underflows) compares false -> bin 0;
@@ -123,15 +152,14 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // ---- 1. load + range
+  // ---- 1. load + range (loads issued in batches so many are in flight)
   float vmin = INFINITY, vmax = -INFINITY;
-  for (int i = tid; i < L; i += kThreads) {
-    const uint32_t k = float_key(src[i]);
+  for_each_key<IN_LDS, true>(s, src, L, [&](int i, uint32_t k) {
     if constexpr (IN_LDS) s.row[i] = k;
     const float f = key_float(k);
     vmin = fminf(vmin, f);
     vmax = fmaxf(vmax, f);
-  }
+  });
   for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -143,7 +171,7 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
     s.red_max[wave] = vmax;
   }
   if (tid == 0) s.ncand = 0;
-  __syncthreads();
+  lds_barrier();
   vmin = s.red_min[0];
   vmax = s.red_max[0];
 #pragma unroll
@@ -161,11 +189,10 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
   } else {
     // ---- 2. histogram
     const float inv = static_cast<float>(kBins) / (vmax - vmin);
-    for (int i = tid; i < L; i += kThreads) {
-      const float f = key_float(row_key<IN_LDS>(s, src, i));
-      atomicAdd(&s.hist[bin_of(f, vmin, inv)], 1u);
-    }
-    __syncthreads();
+    for_each_key<IN_LDS, false>(s, src, L, [&](int, uint32_t k) {
+      atomicAdd(&s.hist[bin_of(key_float(k), vmin, inv)], 1u);
+    });
+    lds_barrier();
     // ---- 3. threshold bin: thread tid owns bins 2047-2tid, 2046-2tid
     {
       const uint32_t h0 = s.hist[kBins - 1 - 2 * tid];
@@ -178,7 +205,7 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
         if (lane >= off) incl += v;
       }
       if (lane == 63) s.wave_a[wave] = incl;
-      __syncthreads();
+      lds_barrier();
       uint32_t base = 0;
       for (int wv = 0; wv < wave; ++wv) base += s.wave_a[wv];
       const uint32_t above0 = base + incl - tot;    // above bin 2047-2tid
@@ -193,21 +220,20 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
         s.above_bin = above1;
       }
     }
-    __syncthreads();
+    lds_barrier();
     const int sel = static_cast<int>(s.sel_bin);
     const uint32_t above_bin = s.above_bin;
     const uint32_t bin_count = s.hist[sel];
     const bool use_cand = bin_count <= kCandCap;
     if (use_cand) {
-      for (int i = tid; i < L; i += kThreads) {
-        const uint32_t k = row_key<IN_LDS>(s, src, i);
+      for_each_key<IN_LDS, false>(s, src, L, [&](int, uint32_t k) {
         if (bin_of(key_float(k), vmin, inv) == sel) {
           const uint32_t slot = atomicAdd(&s.ncand, 1u);
           if (slot < kCandCap) s.cand[slot] = k;
         }
-      }
+      });
     }
-    __syncthreads();
+    lds_barrier();
     // ---- 4. exact radix select of rank r among the set
     uint32_t r = use_cand ? static_cast<uint32_t>(topk) - above_bin
                           : static_cast<uint32_t>(topk);
@@ -215,21 +241,27 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
     uint32_t prefix = 0, mask = 0, gt_extra = 0;
     for (int shift = 24; shift >= 0; shift -= 8) {
       for (int i = tid; i < 256; i += kThreads) s.hist[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < n_set; i += kThreads) {
-        const uint32_t k = use_cand ? s.cand[i] : row_key<IN_LDS>(s, src, i);
-        if ((k & mask) == prefix) atomicAdd(&s.hist[(k >> shift) & 255u], 1u);
+      lds_barrier();
+      if (use_cand) {
+        for (int i = tid; i < n_set; i += kThreads) {
+          const uint32_t k = s.cand[i];
+          if ((k & mask) == prefix) atomicAdd(&s.hist[(k >> shift) & 255u], 1u);
+        }
+      } else {
+        for_each_key<IN_LDS, false>(s, src, L, [&](int, uint32_t k) {
+          if ((k & mask) == prefix) atomicAdd(&s.hist[(k >> shift) & 255u], 1u);
+        });
       }
-      __syncthreads();
+      lds_barrier();
       find_digit(s, r);
-      __syncthreads();
+      lds_barrier();
       const uint32_t d = s.digit;
       const uint32_t da = s.digit_above;
       r -= da;
       gt_extra += da;
       prefix |= d << shift;
       mask |= 255u << shift;
-      __syncthreads();
+      lds_barrier();
     }
     T = prefix;
     c_gt = (use_cand ? above_bin : 0u) + gt_extra;
@@ -241,28 +273,42 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
   const int beg = wave * span;
   const int end = min(L, beg + span);
   uint32_t n_gt = 0, n_eq = 0;
-  for (int base = beg; base < end; base += 64) {
-    const int i = base + lane;
-    const uint32_t k = i < end ? row_key<IN_LDS>(s, src, i) : 0u;
-    const bool gt = i < end && k > T;
-    const bool eq = i < end && k == T;
-    n_gt += __popcll(__ballot(gt));
-    n_eq += __popcll(__ballot(eq));
+  for (int base = beg; base < end; base += 64 * kBatch) {
+    uint32_t k[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + 64 * j + lane;
+      k[j] = i < end ? row_key<IN_LDS>(s, src, i) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + 64 * j + lane;
+      n_gt += __popcll(__ballot(i < end && k[j] > T));
+      n_eq += __popcll(__ballot(i < end && k[j] == T));
+    }
   }
   if (lane == 0) {
     s.wave_a[wave] = n_gt;
     s.wave_b[wave] = n_eq;
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t gt_run = 0, eq_run = 0;
   for (int wv = 0; wv < wave; ++wv) {
     gt_run += s.wave_a[wv];
     eq_run += s.wave_b[wv];
   }
   const uint64_t below = lanes_below();
-  for (int base = beg; base < end; base += 64) {
-    const int i = base + lane;
-    const uint32_t k = i < end ? row_key<IN_LDS>(s, src, i) : 0u;
+  for (int base = beg; base < end; base += 64 * kBatch) {
+    uint32_t kb[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + 64 * j + lane;
+      kb[j] = i < end ? row_key<IN_LDS>(s, src, i) : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+    const int i = base + 64 * j + lane;
+    const uint32_t k = kb[j];
     const bool gt = i < end && k > T;
     const bool eq = i < end && k == T;
     const uint64_t gm = __ballot(gt);
@@ -274,6 +320,7 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
     if (take && o < static_cast<uint32_t>(topk)) out[o] = i;
     gt_run += __popcll(gm);
     eq_run += __popcll(em);
+    }
   }
 }
 
@@ -283,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
     int32_t B, int32_t max_seq_len, int32_t topk, int32_t* __restrict__ out) {
   __shared__ Shared s;
   const int t = blockIdx.x;
-  const int b = request_of(cu_q, B, t);
+  const int b = request_of_block(cu_q, B, t, &s.counter);
   const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
   const int L = pos + 1;
   int32_t* orow = out + static_cast<int64_t>(t) * topk;

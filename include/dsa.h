@@ -169,7 +169,7 @@ int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
  *   lse      [N, n_heads] fp32 log-sum-exp of the scaled logits, or NULL
  * A token with no valid index gets out = 0 and lse = -inf.
  * Supported: dtype DSA_F32 or DSA_BF16.  The matrix-core path takes BF16
- * with R = 512, P = 64 and n_heads % 16 == 0; other shapes (R + P <= 1024,
+ * with R = 512, P = 64 and n_heads == 64; other shapes (R + P <= 1024,
  * n_heads <= 128) take a vector path.
  * workspace: at least sparse_mla_attn_workspace_size() bytes (may be 0, in
  * which case workspace may be NULL).

@@ -35,21 +35,29 @@ namespace dsa {
 namespace {
 
 constexpr int kR = 512, kP = 64, kD = kR + kP;
-constexpr int kHG = 32;                 // heads per workgroup
+constexpr int kH = 64;                  // heads per workgroup (all of them)
 constexpr int kT = 32;                  // keys per tile
-constexpr int kKS = kD + 8;             // row-major key stride (elements)
-constexpr int kVS = kT + 8;             // transposed value stride (elements)
+constexpr int kThreads = 256;           // 4 waves, one per SIMD
 constexpr int kPS = kT + 8;             // P stride (elements)
 constexpr int kPieces = kD / 8;         // 16-byte pieces per latent row (72)
-constexpr int kPerThread = kT * kPieces / 256;   // 9
+constexpr int kTilePieces = kT * kPieces;             // 2304
+constexpr int kDmaPerWave = kTilePieces / 64 / 4;     // 9 loads per wave per tile
+constexpr int kBufs = 3;                // tiles resident: current + 2 in flight
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// The running max used for the exponentials only moves when a tile's max
+// exceeds it by more than this (in log2 units), so O is rarely rescaled;
+// p = 2^(z - m) then stays below 2^8.
+constexpr float kRescaleSlack = 8.0f;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 struct MlaShared {
-  uint16_t k[kT * kKS];                 // 37376 B
-  uint16_t vt[kR * kVS];                // 40960 B
-  float s[kHG][kT + 1];                 // logits exchange
-  uint16_t p[4][kHG * kPS];             // per-wave probabilities (bf16)
+  uint16_t k[kBufs][kT * kD];           // row-major tiles, 3 x 36864 B
+  uint16_t p[kH * kPS];                 // probabilities (bf16), 5120 B
+  float alpha[kH];                      // per-head O rescale of this tile
+  float fin_l[kH];
+  float fin_m[kH];
   int64_t slots[DSA_MAX_TOPK];          // physical row of each index, or -1
   uint32_t counter;
 };
@@ -74,10 +82,52 @@ __device__ __forceinline__ int64_t sel_slot(const int32_t* __restrict__ idx_row,
   return slot_of(bt_row, p, block_size, max_blocks, num_slots);
 }
 
-__global__ __launch_bounds__(256, 1) void k_mla_mfma(
+// 4 consecutive bf16 of LDS read with the gfx950 transpose load: within each
+// 16-lane group, lane j supplies 4 elements that become A[4j .. 4j+3] and
+// lane i receives A[i], A[16+i], A[32+i], A[48+i].
+__device__ __forceinline__ v4i16 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(p));
+}
+
+// A tile row is 72 16-byte pieces; piece c of row r is stored at piece
+// position c ^ swz(r) of that row.  Rows are 1152 bytes (a multiple of the
+// LDS bank width), so without the swizzle the 16 rows read by one MFMA
+// operand load would hit the same banks.  swz < 8 keeps every position
+// inside the row (0..63 and 64..71 map onto themselves).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int tile_elem(int row, int dim) {
+  return row * kD + 8 * ((dim >> 3) ^ swz(row)) + (dim & 7);
+}
+
+// Barrier for the tile loop: LDS operations of this wave complete, then all
+// waves meet.  Unlike an LDS release fence it does not wait for the tile DMA
+// in flight (a DMA write to LDS counts as an LDS write for the fence); the
+// loop waits for each tile's own DMA explicitly with s_waitcnt vmcnt before
+// its first use.  The memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One workgroup = (query token, key split), all 64 heads, 4 waves.
+//   logits:  wave w computes S^T = K . Q^T for its 16 heads (16 w .. +16)
+//            and the tile's 32 keys (two v_mfma_f32_16x16x32_bf16 tiles with
+//            keys on M); each lane then holds 8 keys of one head, so the
+//            online-softmax max / sum are in-lane plus two exchanges, and
+//            the wave owns its heads' running statistics;
+//   P.V:     wave w accumulates O[64 heads, dims 128 w .. +128] from the
+//            probabilities of all heads (LDS) and the value rows read
+//            straight from the row-major tile with transpose loads: a
+//            16-lane group reads a 4-key x 16-dim block and each lane gets
+//            4 keys of one dim, the MFMA operand layout.
+// Gathered tiles go straight from HBM into one of three LDS tile buffers
+// (global_load_lds_dwordx4: each wave instruction fills 1 KB of LDS), so two
+// tiles are in flight while the third is multiplied, with no register cost.
+__global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk_idx, int32_t topk, int32_t n_tokens,
-    int32_t n_heads, int32_t n_split, int32_t split_len, float scale_log2,
+    int32_t n_split, int32_t split_len, float scale_log2,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
     int32_t B, const int32_t* __restrict__ block_table, int32_t max_blocks,
     int32_t block_size, int64_t num_slots, int32_t max_seq_len,
@@ -89,21 +139,10 @@ __global__ __launch_bounds__(256, 1) void k_mla_mfma(
   const int wave = tid >> 6;
   const int l16 = lane & 15;
   const int g16 = lane >> 4;
-  const int mh = wave & 1;
-  const int nk = wave >> 1;
 
-  // Workgroup order: consecutive ids go round-robin over the 8 XCDs, so the
-  // head groups of one (token, split) unit are given ids 8 apart; they land
-  // on the same XCD and the second read of each gathered row hits its L2.
-  const int n_hg = n_heads / kHG;
-  const int lo8 = blockIdx.x & 7;
-  const int hi = blockIdx.x >> 3;
-  const int hg = hi % n_hg;
-  const int unit = (hi / n_hg) * 8 + lo8;
-  if (unit >= n_tokens * n_split) return;
-  const int t = unit / n_split;
-  const int split = unit % n_split;
-
+  const int t = blockIdx.x / n_split;
+  const int split = blockIdx.x % n_split;
+  if (t >= n_tokens) return;
   const int b = request_of_block(cu_q, B, t, &sh.counter);
   const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
@@ -114,11 +153,11 @@ __global__ __launch_bounds__(256, 1) void k_mla_mfma(
   // Resolve the physical row of every index of this split once, into LDS:
   // index loads first, then block-table loads, each batch issued together.
   // The gathers below then wait on no dependent global load.
-  for (int j0 = jbeg; j0 < jend; j0 += 8 * 256) {
+  for (int j0 = jbeg; j0 < jend; j0 += 8 * kThreads) {
     int32_t p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int j = j0 + 256 * i + tid;
+      const int j = j0 + kThreads * i + tid;
       p[i] = j < jend ? idx_row[j] : -1;
     }
     int32_t bid[8];
@@ -130,7 +169,7 @@ __global__ __launch_bounds__(256, 1) void k_mla_mfma(
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int j = j0 + 256 * i + tid;
+      const int j = j0 + kThreads * i + tid;
       if (j < jend) {
         int64_t slot = -1;
         if (p[i] >= 0) {
@@ -143,185 +182,178 @@ __global__ __launch_bounds__(256, 1) void k_mla_mfma(
   }
   lds_barrier();
 
-  // query rows of this wave's 16 heads (logit A operand): head 16 mh + l16,
+  // query rows of this wave's 16 heads (logit B operand): head 16 w + l16,
   // dims 32 s + 8 g16 .. +8
-  const int64_t qbase = (static_cast<int64_t>(t) * n_heads + hg * kHG + mh * 16 + l16) * kD;
-  bf16x8 qa[kD / 32];
+  const int64_t qbase = (static_cast<int64_t>(t) * kH + 16 * wave + l16) * kD;
+  bf16x8 qb[kD / 32];
 #pragma unroll
   for (int s = 0; s < kD / 32; ++s)
-    qa[s] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * s + 8 * g16);
+    qb[s] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * s + 8 * g16);
 
-  f32x4 o[2][8];
+  f32x4 o[4][8];                        // [head tile][dim tile]
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) o[mt][nt] = f32x4{0, 0, 0, 0};
-  float m_run = -INFINITY, l_run = 0.0f;   // for head (lane & 31)
+  float m_ref = -INFINITY, l_run = 0.0f;   // head 16 w + l16 (all g16 alike)
 
-  // gather registers: piece c = tid + 256 i of the tile -> key c / 72,
-  // 16-byte piece c % 72 of that key's row; consecutive threads read
-  // consecutive pieces, so each row arrives as whole 128-byte lines
-  auto gather = [&](u32x4 (&g)[kPerThread], int tile_beg) {
+  // DMA of one tile into LDS buffer `kt`: wave instruction q (q = wave + 4 i)
+  // fills LDS pieces 64 q .. 64 q + 63; lane l loads the global piece that
+  // belongs at LDS piece 64 q + l.  Keys without a row load row 0 (finite
+  // cache data) and are masked out of the softmax.
+  auto dma = [&](int tile_beg, uint16_t* kt) {
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / kPieces;
-      const int pc = c % kPieces;
-      const int j = tile_beg + key;
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int qi = wave + 4 * i;
+      const int pc = 64 * qi + lane;
+      const int row = pc / kPieces;
+      const int col = (pc % kPieces) ^ swz(row);
+      const int j = tile_beg + row;
       const int64_t slot = j < jend ? sh.slots[j - jbeg] : -1;
-      g[i] = slot >= 0 ? *reinterpret_cast<const u32x4*>(kv + slot * kD + pc * 8)
-                       : u32x4{0, 0, 0, 0};
-    }
-  };
-  // registers -> row-major LDS copy of the tile
-  auto stage = [&](const u32x4 (&g)[kPerThread], int tile_beg) {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = tid + 256 * i;
-      const int key = c / kPieces;
-      const int pc = c % kPieces;
-      *reinterpret_cast<u32x4*>(&sh.k[key * kKS + pc * 8]) = g[i];
-    }
-  };
-  // row-major latent dims -> transposed value tile: unit u = (dim chunk
-  // u / 16, key pair u % 16) reads 8 dims of two keys and writes 8 dwords,
-  // each holding one dim of both keys
-  auto transpose = [&]() {
-#pragma unroll
-    for (int i = 0; i < (kR / 8) * (kT / 2) / 256; ++i) {
-      const int u = tid + 256 * i;
-      const int kp = u & 15;
-      const int dc = u >> 4;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(&sh.k[(2 * kp) * kKS + dc * 8]);
-      const u32x4 c = *reinterpret_cast<const u32x4*>(&sh.k[(2 * kp + 1) * kKS + dc * 8]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t even = (a[m] & 0xFFFFu) | (c[m] << 16);
-        const uint32_t odd = (a[m] >> 16) | (c[m] & 0xFFFF0000u);
-        *reinterpret_cast<uint32_t*>(&sh.vt[(dc * 8 + 2 * m) * kVS + 2 * kp]) = even;
-        *reinterpret_cast<uint32_t*>(&sh.vt[(dc * 8 + 2 * m + 1) * kVS + 2 * kp]) = odd;
-      }
+      const uint16_t* src = kv + (slot < 0 ? 0 : slot) * kD + col * 8;
+      __builtin_amdgcn_global_load_lds(
+          src, (__attribute__((address_space(3))) void*)(kt + 512 * qi), 16, 0, 0);
     }
   };
 
-  auto tile_step = [&](u32x4 (&g)[kPerThread], int tb) {
-    stage(g, tb);
-    if (tb + 2 * kT < jend) gather(g, tb + 2 * kT);     // two tiles ahead
-    lds_barrier();
-    transpose();
+  const int ntiles = (jend - jbeg + kT - 1) / kT;
+  auto tile_step = [&](int it) {
+    const int tb = jbeg + it * kT;
+    uint16_t* kt = sh.k[it % kBufs];
+    // this tile's loads are done when at most the next tile's are pending
+    if (it + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerWave);   // vmcnt(9)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
+    tile_barrier();
+    // every wave is past step it-1, so buffer (it + 2) % 3 is free
+    if (it + 2 < ntiles) dma(jbeg + (it + 2) * kT, sh.k[(it + 2) % kBufs]);
 
-    // ---- logits: 16 heads (mh) x 16 keys (nk)
-    f32x4 acc = {0, 0, 0, 0};
-    const uint16_t* kb = &sh.k[(16 * nk + l16) * kKS + 8 * g16];
+    // ---- logits S^T: key 16 kh + 4 g16 + i, head 16 w + l16
+    f32x4 acc[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
     for (int s = 0; s < kD / 32; ++s) {
-      const bf16x8 kk = *reinterpret_cast<const bf16x8*>(kb + 32 * s);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kk, acc, 0, 0, 0);
-    }
-    {
-      const int j = tb + 16 * nk + l16;
-      const bool ok = j < jend && sh.slots[j - jbeg] >= 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        sh.s[16 * mh + 4 * g16 + i][16 * nk + l16] = ok ? acc[i] * scale_log2 : -INFINITY;
+      for (int kh = 0; kh < 2; ++kh) {
+        const bf16x8 kk = *reinterpret_cast<const bf16x8*>(
+            &kt[tile_elem(16 * kh + l16, 32 * s + 8 * g16)]);
+        acc[kh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qb[s], acc[kh], 0, 0, 0);
+      }
     }
-    lds_barrier();
-
-    // ---- online softmax: lane handles head (lane & 31), keys 16*(lane>>5)..+16
-    const int hh = lane & 31;
-    const int kh = (lane >> 5) * 16;
-    float z[16];
+    float z[8];
     float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      z[j] = sh.s[hh][kh + j];
-      mx = fmaxf(mx, z[j]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float alpha = exp2f(m_run - m_use);
-    float ps = 0.0f;
-    uint16_t* pw = &sh.p[wave][hh * kPS + kh];
+    for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-    for (int j = 0; j < 16; j += 2) {
-      const float p0 = exp2f(z[j] - m_use);
-      const float p1 = exp2f(z[j + 1] - m_use);
-      ps += p0 + p1;
-      *reinterpret_cast<uint32_t*>(pw + j) =
-          static_cast<uint32_t>(f32_to_bf16_rne(p0)) |
-          (static_cast<uint32_t>(f32_to_bf16_rne(p1)) << 16);
+      for (int i = 0; i < 4; ++i) {
+        const int j = tb + 16 * kh + 4 * g16 + i;
+        const bool ok = j < jend && sh.slots[j - jbeg] >= 0;
+        z[4 * kh + i] = ok ? acc[kh][i] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, z[4 * kh + i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool move = mx > m_ref + kRescaleSlack || (m_ref == -INFINITY && mx != -INFINITY);
+    const float m_new = move ? mx : m_ref;
+    const float alpha = move ? exp2f(m_ref - m_new) : 1.0f;   // 0 from -inf
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    float ps = 0.0f;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      uint32_t pk[2];
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const float p0 = exp2f(z[4 * kh + i] - m_use);
+        const float p1 = exp2f(z[4 * kh + i + 1] - m_use);
+        ps += p0 + p1;
+        pk[i / 2] = static_cast<uint32_t>(f32_to_bf16_rne(p0)) |
+                    (static_cast<uint32_t>(f32_to_bf16_rne(p1)) << 16);
+      }
+      *reinterpret_cast<u32x2*>(&sh.p[(16 * wave + l16) * kPS + 16 * kh + 4 * g16]) =
+          u32x2{pk[0], pk[1]};
     }
+    ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
     l_run = l_run * alpha + ps;
-    m_run = m_new;
-    // the P tile is wave-private: order its LDS writes before the reads below
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+    m_ref = m_new;
+    if (g16 == 0) sh.alpha[16 * wave + l16] = alpha;
+    tile_barrier();
 
     // ---- O = alpha * O + P V for this wave's 128 dims
+    float a16[4][4];
+    bool any = false;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      float a4[4];
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 16 * mt + 4 * g16 + i);
+      for (int i = 0; i < 4; ++i) {
+        a16[mt][i] = sh.alpha[16 * mt + 4 * g16 + i];
+        any |= a16[mt][i] != 1.0f;
+      }
+    if (__ballot(any)) {
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[mt][nt][i] *= a4[i];
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[mt][nt][i] *= a16[mt][i];
     }
-    bf16x8 pa[2];
+    bf16x8 pa[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      pa[mt] = *reinterpret_cast<const bf16x8*>(&sh.p[wave][(16 * mt + l16) * kPS + 8 * g16]);
+    for (int mt = 0; mt < 4; ++mt)
+      pa[mt] = *reinterpret_cast<const bf16x8*>(&sh.p[(16 * mt + l16) * kPS + 8 * g16]);
+    // transpose-load rows 8 g16 + l16 / 4 (and +4) at dims 4 (l16 % 4) .. +4
+    const int vr = 8 * g16 + (l16 >> 2);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const int dim = 128 * wave + 16 * nt + l16;
-      const bf16x8 vb = *reinterpret_cast<const bf16x8*>(&sh.vt[dim * kVS + 8 * g16]);
+      const int dim = 128 * wave + 16 * nt + 4 * (l16 & 3);
+      const v4i16 v0 = lds_read_tr(&kt[tile_elem(vr, dim)]);
+      const v4i16 v1 = lds_read_tr(&kt[tile_elem(vr + 4, dim)]);
+      // whole-vector shuffle + bit cast (element-wise __bf16 inserts of the
+      // transpose-load results were lowered into a broadcast of element 0)
+      typedef short v8i16 __attribute__((ext_vector_type(8)));
+      const v8i16 v01 = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, v01);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
         o[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[mt], vb, o[mt][nt], 0, 0, 0);
     }
-    lds_barrier();
   };
 
-  u32x4 ga[kPerThread], gb[kPerThread];
-  if (jbeg < jend) gather(ga, jbeg);
-  if (jbeg + kT < jend) gather(gb, jbeg + kT);
-  for (int tb = jbeg; tb < jend; tb += 2 * kT) {
-    tile_step(ga, tb);
-    if (tb + kT < jend) tile_step(gb, tb + kT);
-  }
+  if (ntiles > 0) dma(jbeg, sh.k[0]);
+  if (ntiles > 1) dma(jbeg + kT, sh.k[1]);
+  for (int it = 0; it < ntiles; ++it) tile_step(it);
 
-  // ---- epilogue
-  const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-  const float lse_h = l_run > 0.0f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
-  const int head0 = hg * kHG;
+  // ---- epilogue: every wave needs l / m of all 64 heads
+  if (g16 == 0) {
+    sh.fin_l[16 * wave + l16] = l_run;
+    sh.fin_m[16 * wave + l16] = m_ref;
+  }
+  lds_barrier();
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int hl = 16 * mt + 4 * g16 + i;
-      const float il = __shfl(inv_l, hl);
-      const int h = head0 + hl;
+      const int h = 16 * mt + 4 * g16 + i;
+      const float lh = sh.fin_l[h];
+      const float il = lh > 0.0f ? 1.0f / lh : 0.0f;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const int r = 128 * wave + 16 * nt + l16;
         const float v = o[mt][nt][i] * il;
         if (n_split == 1)
-          out[(static_cast<int64_t>(t) * n_heads + h) * kR + r] = f32_to_bf16_rne(v);
+          out[(static_cast<int64_t>(t) * kH + h) * kR + r] = f32_to_bf16_rne(v);
         else
-          part_o[((static_cast<int64_t>(t) * n_split + split) * n_heads + h) * kR + r] = v;
+          part_o[((static_cast<int64_t>(t) * n_split + split) * kH + h) * kR + r] = v;
       }
     }
   }
-  if (wave == 0 && lane < 32) {
-    const int h = head0 + lane;
+  if (wave == 0) {
+    const float lh = sh.fin_l[lane];
+    const float lse_h = lh > 0.0f ? (sh.fin_m[lane] + log2f(lh)) * kLn2 : -INFINITY;
     if (n_split == 1) {
-      if (lse) lse[static_cast<int64_t>(t) * n_heads + h] = lse_h;
+      if (lse) lse[static_cast<int64_t>(t) * kH + lane] = lse_h;
     } else {
-      part_lse[(static_cast<int64_t>(t) * n_split + split) * n_heads + h] = lse_h;
+      part_lse[(static_cast<int64_t>(t) * n_split + split) * kH + lane] = lse_h;
     }
   }
 }
@@ -439,17 +471,18 @@ __global__ __launch_bounds__(256) void k_mla_vector(
 }  // namespace
 
 bool mla_mfma_ok(int dtype, int n_heads, int R, int P) {
-  return dtype == DSA_BF16 && R == kR && P == kP && n_heads % kHG == 0 &&
-         n_heads > 0;
+  return dtype == DSA_BF16 && R == kR && P == kP && n_heads == kH;
 }
 
 int mla_choose_split(const dsa_batch* b, int dtype, int n_heads, int R, int P,
                      int topk) {
   if (!mla_mfma_ok(dtype, n_heads, R, P)) return 1;
-  const int64_t wgs = static_cast<int64_t>(b->num_q_tokens) * (n_heads / kHG);
+  // one workgroup per CU at least: split the keys of each token until there
+  // are >= 256 workgroups, keeping >= 4 tiles per split
+  const int64_t wgs = static_cast<int64_t>(b->num_q_tokens);
   if (wgs <= 0 || wgs >= 256) return 1;
   int split = static_cast<int>((256 + wgs - 1) / wgs);
-  const int max_split = max(1, topk / (4 * kT));    // >= 4 tiles per split
+  const int max_split = max(1, topk / (4 * kT));
   return min(split, max_split);
 }
 
@@ -460,12 +493,10 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
     const int n_split = a.n_split;
     int split_len = (a.topk + n_split - 1) / n_split;
     split_len = (split_len + kT - 1) / kT * kT;
-    const int64_t units = static_cast<int64_t>(b.num_q_tokens) * n_split;
-    const int64_t grid = (units + 7) / 8 * 8 * (a.n_heads / kHG);
-    k_mla_mfma<<<static_cast<unsigned>(grid), 256, 0, stream>>>(
+    const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * n_split;
+    k_mla_mfma<<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv),
-        a.idx, a.topk, b.num_q_tokens, a.n_heads, n_split, split_len,
-        a.scale * kLog2e,
+        a.idx, a.topk, b.num_q_tokens, n_split, split_len, a.scale * kLog2e,
         b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
         b.block_size, b.num_slots, b.max_seq_len,
         static_cast<uint16_t*>(a.out), a.lse, a.part_o, a.part_lse);

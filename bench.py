@@ -30,6 +30,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+SCORE_SRC = os.path.join(ROOT, "sparse_attention_topk_amd", "csrc", "indexer_score.hip")
+SCORE_KERNEL = "k_score_mfma"
+COPY_BYTES = 1 << 30           # calibration copy: reads and writes 1 GiB
 METRIC = "decode query-tokens/s (indexer+top-k+sparse MLA) and % HBM roofline, 32K ctx"
 
 
@@ -49,6 +52,13 @@ def parse():
     p.add_argument("--no-cpu", action="store_true",
                    help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--pmc-run", action="store_true",
+                   help="for rocprofv3 --pmc: one 1 GiB copy (calibration), "
+                        "then the timed steps; prints nothing else")
+    p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn two rocprofv3 counter_collection.csv files "
+                        "(FETCH_SIZE run, WRITE_SIZE run) into a traffic "
+                        "summary (JSON on stdout); no GPU needed")
     return p.parse_args()
 
 
@@ -84,6 +94,56 @@ def mla_bytes(b, cfg):
 def cache_write_bytes(b, cfg):
     per = cfg.d_idx * (1 if cfg.idx_cache_dtype == "fp8" else 2)
     return b.num_q_tokens * (cfg.d_idx * 2 + per + 8)
+
+
+# ------------------------------------------------------------------ traffic
+def source_sha(path):
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", "traffic_%s.json.txt" % workload)
+
+
+def pmc_summary(fetch_csv, write_csv):
+    """HBM bytes per launch of the score kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the counter reads for the plain
+    1 GiB copy kernel of the same run."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        score = [float(r["Counter_Value"]) for r in rows if SCORE_KERNEL in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows
+                if "copy" in r["Kernel_Name"].lower() and "dsa" not in r["Kernel_Name"]]
+        return score, copy
+
+    fs, fc = per_kernel(fetch_csv, "FETCH_SIZE")
+    ws, wc = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (max(fc) * 1024.0)      # true bytes per counted byte
+    w_scale = COPY_BYTES / (max(wc) * 1024.0)
+    fetch = sum(fs) / len(fs) * 1024.0 * f_scale
+    write = sum(ws) / len(ws) * 1024.0 * w_scale
+    return {"kernel": SCORE_KERNEL, "source_sha256": source_sha(SCORE_SRC),
+            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+            "traffic_bytes_per_launch": fetch + write,
+            "copy_fetch_scale": f_scale, "copy_write_scale": w_scale,
+            "launches": len(fs)}
+
+
+def load_traffic(workload):
+    """Measured HBM bytes per score-kernel launch, or None when no summary
+    exists or the kernel source changed since the counters were taken."""
+    path = traffic_file(workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != source_sha(SCORE_SRC):
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 # ------------------------------------------------------------------ cpu leg
@@ -135,6 +195,9 @@ def cpu_baseline(cfg, b, lay, k_cache, seconds):
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(*args.pmc_summary), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(requests shard independently across GPUs; see the design notes). "
@@ -157,6 +220,12 @@ def main():
 
     if cfg.name == "indexshare_8layer":
         return bench_indexshare(args, cfg, b, bb, dsa, torch)
+    if args.pmc_run:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)                     # the calibration copy kernel
+        torch.cuda.synchronize()
+        del src, dst
 
     lay = make_layer(cfg, b, dev)
     # the cache before this step: every slot populated through the cache write
@@ -231,7 +300,9 @@ def main():
                    "idx_cache": cfg.idx_cache_dtype, "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "kernel": "dsa_indexer_topk (score + top-k)",
                      "achieved": ix_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ix_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": ix_gbs / HBM_PEAK_GBS,
+                     "traffic": load_traffic(cfg.name),
+                     "traffic_kernel": SCORE_KERNEL,
                      "bytes_per_launch": ib, "mean_ms": mean(ix)},
         "calls": {
             "cache_write": {"mean_ms": mean(cw), "bytes": cb},
@@ -243,6 +314,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.pmc_run:
+        return
     if not args.no_cpu and cfg.idx_cache_dtype != "fp8":
         log("cpu oracle baseline (~%.0f s)" % args.cpu_seconds)
         res["cpu_baseline"] = cpu_baseline(cfg, b, lay, k_cache, args.cpu_seconds)

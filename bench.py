@@ -30,9 +30,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
-SCORE_SRC = os.path.join(ROOT, "sparse_attention_topk_amd", "csrc", "indexer_score.hip")
-SCORE_KERNEL = "k_score_mfma"
-COPY_BYTES = 1 << 30           # calibration copy: reads and writes 1 GiB
 METRIC = "decode query-tokens/s (indexer+top-k+sparse MLA) and % HBM roofline, 32K ctx"
 
 
@@ -53,7 +50,7 @@ def parse():
                    help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--pmc-run", action="store_true",
-                   help="for rocprofv3 --pmc: one 1 GiB copy (calibration), "
+                   help="for rocprofv3 --pmc: one conversion of known size (calibration), "
                         "then the timed steps; prints nothing else")
     p.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn two rocprofv3 counter_collection.csv files "
@@ -97,53 +94,92 @@ def cache_write_bytes(b, cfg):
 
 
 # ------------------------------------------------------------------ traffic
-def source_sha(path):
+CSRC = os.path.join(ROOT, "sparse_attention_topk_amd", "csrc")
+# the dominant call's kernels, and the sources they are built from
+INDEXER_KERNELS = ("k_score_mfma", "k_topk")
+INDEXER_SRCS = ("common.h", "indexer_score.hip", "topk.hip")
+CALIB_ELEMS = 1 << 28          # calibration: fp32 -> bf16 conversion of 1 GiB
+CALIB_READ, CALIB_WRITE = CALIB_ELEMS * 4, CALIB_ELEMS * 2
+
+
+def source_sha(names=INDEXER_SRCS):
     import hashlib
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def traffic_file(workload):
-    return os.path.join(ROOT, "profiles", "traffic_%s.json.txt" % workload)
+    return os.path.join(ROOT, "profiles", "traffic_indexer_%s.json" % workload)
 
 
 def pmc_summary(fetch_csv, write_csv):
-    """HBM bytes per launch of the score kernel from FETCH_SIZE / WRITE_SIZE
-    (KiB per dispatch), each scaled by what the counter reads for the plain
-    1 GiB copy kernel of the same run."""
+    """HBM bytes per launch of every library kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the counter reads for
+    a conversion kernel of known size (1 GiB read, 512 MiB written) run in the
+    same process."""
     import csv
 
-    def per_kernel(path, counter):
-        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
-        score = [float(r["Counter_Value"]) for r in rows if SCORE_KERNEL in r["Kernel_Name"]]
-        copy = [float(r["Counter_Value"]) for r in rows
-                if "copy" in r["Kernel_Name"].lower() and "dsa" not in r["Kernel_Name"]]
-        return score, copy
+    def read(path, counter):
+        per, calib = {}, []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v, name = float(r["Counter_Value"]) * 1024.0, r["Kernel_Name"]
+            if ("copy" in name and "dsa::" not in name
+                    and int(r["Grid_Size"]) >= CALIB_ELEMS // 8):
+                calib.append((v, name[:120]))
+            if "dsa::" in name:
+                key = name.split("::")[-1].split("(")[0]
+                per.setdefault(key, []).append(v)
+        return per, calib
 
-    fs, fc = per_kernel(fetch_csv, "FETCH_SIZE")
-    ws, wc = per_kernel(write_csv, "WRITE_SIZE")
-    f_scale = COPY_BYTES / (max(fc) * 1024.0)      # true bytes per counted byte
-    w_scale = COPY_BYTES / (max(wc) * 1024.0)
-    fetch = sum(fs) / len(fs) * 1024.0 * f_scale
-    write = sum(ws) / len(ws) * 1024.0 * w_scale
-    return {"kernel": SCORE_KERNEL, "source_sha256": source_sha(SCORE_SRC),
-            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
-            "traffic_bytes_per_launch": fetch + write,
-            "copy_fetch_scale": f_scale, "copy_write_scale": w_scale,
-            "launches": len(fs)}
+    fetch, fcal = read(fetch_csv, "FETCH_SIZE")
+    write, wcal = read(write_csv, "WRITE_SIZE")
+    if len(fcal) != 1 or len(wcal) != 1:
+        raise SystemExit("expected one calibration dispatch per run, found %d / %d"
+                         % (len(fcal), len(wcal)))
+    f_scale = CALIB_READ / fcal[0][0]
+    w_scale = CALIB_WRITE / wcal[0][0]
+    kernels = {}
+    for k in sorted(set(fetch) | set(write)):
+        fb = sum(fetch.get(k, [0])) / max(1, len(fetch.get(k, []))) * f_scale
+        wb = sum(write.get(k, [0])) / max(1, len(write.get(k, []))) * w_scale
+        kernels[k] = {"fetch_bytes": fb, "write_bytes": wb,
+                      "launches": len(fetch.get(k, []))}
+    call = sum(v["fetch_bytes"] + v["write_bytes"] for k, v in kernels.items()
+               if k.split("<")[0] in INDEXER_KERNELS)
+    return {"commands": [
+                "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc -o fetch --output-format csv"
+                " -- python3 -u bench.py --pmc-run --steps 3 --warmup 1 --no-cpu",
+                "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc -o write --output-format csv"
+                " -- python3 -u bench.py --pmc-run --steps 3 --warmup 1 --no-cpu",
+                "python3 bench.py --pmc-summary gpurun_out/pmc/fetch_counter_collection.csv"
+                " gpurun_out/pmc/write_counter_collection.csv"],
+            "note": "per-launch means; FETCH_SIZE and WRITE_SIZE scaled by the ratio of "
+                    "known to counted bytes of the calibration kernel",
+            "source_sha256": source_sha(), "sources": list(INDEXER_SRCS),
+            "calibration": {"kernel": fcal[0][1], "read_bytes": CALIB_READ,
+                            "write_bytes": CALIB_WRITE,
+                            "fetch_counted_bytes": fcal[0][0],
+                            "write_counted_bytes": wcal[0][0],
+                            "fetch_scale": f_scale, "write_scale": w_scale},
+            "indexer_call_traffic_bytes": call, "kernels": kernels}
 
 
 def load_traffic(workload):
-    """Measured HBM bytes per score-kernel launch, or None when no summary
-    exists or the kernel source changed since the counters were taken."""
+    """Measured HBM bytes per dsa_indexer_topk call, or None when no summary
+    exists or a kernel source changed since the counters were taken."""
     path = traffic_file(workload)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != source_sha(SCORE_SRC):
+    if rec.get("source_sha256") != source_sha():
         return None
-    return rec["traffic_bytes_per_launch"]
+    return rec["indexer_call_traffic_bytes"]
 
 
 # ------------------------------------------------------------------ cpu leg
@@ -158,38 +194,41 @@ def cpu_baseline(cfg, b, lay, k_cache, seconds):
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    spent = 0.0
-    tokens = 0
-    reqs = 0
     bs = b.block_size
-    for bi in range(b.num_reqs):
-        if spent >= seconds:
-            break
+
+    def host_inputs(bi):
+        """Host copies of one request's inputs (not timed)."""
         L, ql = b.seq_lens[bi], b.q_lens[bi]
-        # host copies of this request's inputs (not timed)
         slots = torch.as_tensor(OI.physical_slots(b.block_table_host[bi], bs, L),
                                 device=k_cache.device)
-        keys = k_cache[slots].cpu()
+        keys = k_cache[slots].cpu().view(torch.int16).numpy().view(np.uint16)
         kv = lay.kv_cache[slots].cpu().float().numpy()
         t0 = int(b.cu_q_host[bi])
         q = lay.q_idx[t0:t0 + ql].float().cpu().numpy().astype(np.float64)
         w = lay.w[t0:t0 + ql].cpu().numpy().astype(np.float64)
         qm = lay.q_mla[t0:t0 + ql].float().cpu().numpy().astype(np.float64)
-        cache_np = keys.view(torch.int16).numpy().view(np.uint16)
         ident = np.arange((L + bs - 1) // bs, dtype=np.int64)[None, :]
+        return L, ql, keys, kv, q, w, qm, ident
+
+    # cycle over the first few requests until about `seconds` have run
+    pool = [host_inputs(bi) for bi in range(min(b.num_reqs, 16))]
+    spent, tokens, runs = 0.0, 0, 0
+    while spent < seconds:
+        L, ql, keys, kv, q, w, qm, ident = pool[runs % len(pool)]
         start = time.perf_counter()
-        idx = OI.indexer_topk([L], [0, ql], ident, bs, q, w, cache_np, None,
+        idx = OI.indexer_topk([L], [0, ql], ident, bs, q, w, keys, None,
                               OI.BF16, cfg.topk)
         OM.sparse_mla([L], [0, ql], ident, bs, qm, lambda s: kv[s], idx,
                       cfg.kv_lora_rank, cfg.softmax_scale)
         spent += time.perf_counter() - start
         tokens += ql
-        reqs += 1
+        runs += 1
     return {"value": tokens / spent, "unit": "query-tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%d of %d requests (%d query tokens) of %s, float64 NumPy "
-                      "oracle, compute only (%.1f s)" % (reqs, b.num_reqs, tokens,
-                                                         cfg.name, spent)}
+            "sample": "%d request passes (cycling over %d requests of %d, %d query "
+                      "tokens) of %s: float64 NumPy oracle, indexer+top-k+sparse MLA, "
+                      "compute only, %.1f s" % (runs, len(pool), b.num_reqs, tokens,
+                                                cfg.name, spent)}
 
 
 # ------------------------------------------------------------------ main
@@ -221,9 +260,9 @@ def main():
     if cfg.name == "indexshare_8layer":
         return bench_indexshare(args, cfg, b, bb, dsa, torch)
     if args.pmc_run:
-        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)                     # the calibration copy kernel
+        src = torch.ones(CALIB_ELEMS, dtype=torch.float32, device=dev)
+        dst = torch.empty(CALIB_ELEMS, dtype=torch.bfloat16, device=dev)
+        dst.copy_(src)                     # the calibration kernel
         torch.cuda.synchronize()
         del src, dst
 
@@ -302,7 +341,7 @@ def main():
                      "achieved": ix_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ix_gbs / HBM_PEAK_GBS,
                      "traffic": load_traffic(cfg.name),
-                     "traffic_kernel": SCORE_KERNEL,
+                     "traffic_kernels": list(INDEXER_KERNELS),
                      "bytes_per_launch": ib, "mean_ms": mean(ix)},
         "calls": {
             "cache_write": {"mean_ms": mean(cw), "bytes": cb},

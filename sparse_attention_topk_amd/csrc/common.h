@@ -135,7 +135,7 @@ struct MlaArgs {
   float* part_lse;        // workspace [N, n_split, H]
   int n_split;
 };
-bool mla_mfma_ok(int dtype, int n_heads, int R, int P);
+bool mla_mfma_ok(const dsa_batch& b, int dtype, int n_heads, int R, int P);
 int mla_choose_split(const dsa_batch* b, int dtype, int n_heads, int R, int P,
                      int topk);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);

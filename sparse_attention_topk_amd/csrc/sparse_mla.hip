@@ -11,25 +11,30 @@
 //     out[t, h, :] = sum_j softmax_j(z[h, :]) * kv[j, 0:R]
 //     lse[t, h] = log sum_j exp z[h, j]
 //
-// Matrix-core path (bf16, R = 512, P = 64, heads in groups of 32):
-// a workgroup = (query token, group of 32 heads, key split), 4 waves.  Each
-// 32-key tile of selected rows is gathered from HBM as 16-byte pieces of the
-// 1152-byte rows (one row is 72 pieces; the 256 threads issue them
-// back-to-back, so every row is fetched as whole 128-byte lines), and the
-// next two tiles are in flight while the current one is multiplied.
-// The tile is staged in LDS twice: row-major (the key operand of the logits,
-// 8 consecutive dims per lane) and transposed for the first R dims (the
-// value operand of P.V needs 8 consecutive keys per lane).
-//   logits: v_mfma_f32_16x16x32_bf16, wave (mh, nk) computes 16 heads x 16
-//           keys over 576 dims; its 16 query rows stay in registers;
-//   softmax: online (running max / sum per head, base-2 exponentials);
-//   P.V:    wave w accumulates O[32 heads, dims 128w .. 128w+127] in fp32.
+// Matrix-core path (bf16, R = 512, P = 64, 64 heads): one workgroup per
+// (query token, key split) covers all 64 heads, so every selected latent row
+// crosses HBM once per token.  Rows are gathered in 32-row tiles straight
+// from HBM into LDS (global_load_lds_dwordx4) through a ring of four tile
+// buffers (whole 128-byte lines per DMA instruction): three tiles are in
+// flight while one is multiplied.  Each of the
+// four waves owns 32 heads (hh) and one half (kh) of the work:
+//   logits: the 16 keys 16 kh .. 16 kh + 15 of the tile against its 32
+//           heads over all 576 dims (v_mfma_f32_16x16x32_bf16, queries in
+//           registers), so each tile row is read from LDS by two waves;
+//   softmax: the two waves of a head group swap their per-head maxima and
+//           bf16 probabilities through LDS; the reference maximum moves
+//           rarely (only when a tile beats it by more than 2^8), so the
+//           common tile needs no rescale of the accumulators;
+//   P.V:    value dims 256 kh .. 256 kh + 255 of its 32 heads over all 32
+//           keys, the value operand read with the gfx950 LDS transpose load
+//           straight from the row-major tile.
 // With more than one key split, each split writes its normalised partial
 // output and log-sum-exp, and a combine kernel merges them by LSE weights.
 //
 // Vector path (fp32 or other shapes): one workgroup per (token, head),
 // fp32 arithmetic, logits in LDS.
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -40,27 +45,34 @@ constexpr int kR = 512, kP = 64, kD = kR + kP;
 constexpr int kH = 64;                  // heads per workgroup (all of them)
 constexpr int kT = 32;                  // keys per tile
 constexpr int kThreads = 256;           // 4 waves, one per SIMD
-constexpr int kPS = kT + 8;             // P stride (elements)
 constexpr int kPieces = kD / 8;         // 16-byte pieces per latent row (72)
 constexpr int kTilePieces = kT * kPieces;             // 2304
 constexpr int kDmaInstr = kTilePieces / 64;           // 36 wave loads per tile
 constexpr int kDmaPerWave = kDmaInstr / 4;            // 9
-constexpr int kBufs = 3;                // tiles resident: current + 2 in flight
+constexpr int kBufs = 4;                // tiles resident: current + 3 in flight
+constexpr int kMaxSplitLen = 2048;      // indices per workgroup
+constexpr int kQSteps = kD / 32;        // 18 K-steps of the logits
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// The running max used for the exponentials only moves when a tile's max
-// exceeds it by more than this (in log2 units), so O is rarely rescaled;
-// p = 2^(z - m) then stays below 2^8.
-constexpr float kRescaleSlack = 8.0f;
+// Probabilities are 2^(z - m) against a per-head reference m fixed by the
+// head's first key; a later key may exceed m by up to this much (in log2
+// units), so p <= 2^64 and the fp32 sums stay far from overflow.
+constexpr float kMoveSlack = 64.0f;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
 
 struct MlaShared {
-  uint16_t k[kBufs][kT * kD];           // row-major tiles, 3 x 36864 B
-  int64_t slots[DSA_MAX_TOPK];          // physical row of each index, or -1
-  uint32_t vbits[DSA_MAX_TOPK / kT];    // per tile: bit k = key k has a row
+  uint16_t k[kBufs][kT * kD];           // row-major tiles, 4 x 36864 B
+  int32_t slots[kMaxSplitLen];          // physical row of each index, or -1
+  uint32_t vbits[kMaxSplitLen / kT];    // per tile: bit k = key k has a row
+  u32x2 xp[4][2][64];                   // bf16 probabilities, per wave / head tile / lane
+  float xm[4][2][64];                   // per-head tile maxima (sums at the end)
+  alignas(16) uint32_t xf[4];           // per wave: a reference maximum moves
+  alignas(16) uint32_t xr[4];           // per wave: the split must restart
   uint32_t counter;
 };
+static_assert(sizeof(MlaShared) <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -82,41 +94,57 @@ __device__ __forceinline__ int64_t sel_slot(const int32_t* __restrict__ idx_row,
   return slot_of(bt_row, p, block_size, max_blocks, num_slots);
 }
 
+// LDS operand loads issued as inline asm: as builtins the compiler puts an
+// s_waitcnt vmcnt(0) in front of a transpose load (it assumes the load may
+// read LDS still being written by a tile DMA), which would wait for the
+// tiles in flight.  The caller waits for the results with lgkm_keep<N>(),
+// which takes the consumed register as an operand so the compiler cannot
+// read it earlier.  Every sequence starts with lgkm_drain(), so the
+// compiler's own LDS operations are retired before the counting starts.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) const void*)(p)));
+}
 // 4 consecutive bf16 of LDS read with the gfx950 transpose load: within each
 // 16-lane group, lane j supplies 4 elements that become A[4j .. 4j+3] and
 // lane i receives A[i], A[16+i], A[32+i], A[48+i].
-__device__ __forceinline__ v4i16 lds_read_tr(const uint16_t* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4i16*)(p));
-}
-
-// Transpose loads issued as inline asm: as a builtin the compiler puts an
-// s_waitcnt vmcnt(0) in front of each one (it assumes the load may read LDS
-// still being written by a tile DMA), which would wait for the prefetch of
-// the tile after next.  The caller waits for the results itself with
-// lds_wait*() below, which take the result registers as operands so the
-// compiler cannot use them earlier.  All LDS operations issued this way are
-// retired with lgkmcnt(0) before the compiler issues LDS operations of its
-// own again.
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) const uint16_t*)(p)));
-}
+template <int OFF>
 __device__ __forceinline__ v4i16 tr_load(uint32_t addr) {
   v4i16 r;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
+template <int OFF>
 __device__ __forceinline__ bf16x8 b128_load(uint32_t addr) {
   bf16x8 r;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
+}
+// f(integral_constant<int, I>) for I = 0 .. N-1, so that loop indices can
+// feed immediates
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 // Waits until at most N LDS operations are outstanding; `r` is the register
 // the next instruction consumes, tied so the compiler cannot read it earlier.
 template <int N, typename T>
 __device__ __forceinline__ void lgkm_keep(T& r) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "n"(N));
+}
+__device__ __forceinline__ void lgkm_drain() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+// s_waitcnt with only the vector-memory count (gfx9 encoding: low four bits
+// in [3:0], high two in [15:14]; lgkmcnt / expcnt fields at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 // cross-lane reductions over lanes l ^ 16 and l ^ 32 (gfx950 permlane swaps:
 // each returns the values of the two lanes of the pair)
@@ -132,20 +160,22 @@ __device__ __forceinline__ float sum_x16_x32(float x) {
   auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
-// retire every outstanding LDS / scalar-memory operation of the compiler
-// before an asm-counted sequence starts
-__device__ __forceinline__ void lgkm_drain() {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
 
-// A tile row is 72 16-byte pieces; piece c of row r is stored at piece
-// position c ^ swz(r) of that row.  Rows are 1152 bytes (a multiple of the
-// LDS bank width), so without the swizzle the 16 rows read by one MFMA
-// operand load would hit the same banks.  swz < 8 keeps every position
-// inside the row (0..63 and 64..71 map onto themselves).
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int tile_elem(int row, int dim) {
-  return row * kD + 8 * ((dim >> 3) ^ swz(row)) + (dim & 7);
+// LDS layout of a 32-row tile (36 KB): rows in four groups h of 8, the 72
+// 16-byte pieces of a row in nine groups g of 8.  Block (h, g) is 1 KB at
+// 9216 h + 1024 g and is filled by one DMA instruction: lane l lands at
+// 16 l and carries row 8 h + rho, piece 8 g + pi with
+//     l = 8 (pi ^ (h & 1)) + (rho ^ 4 (pi & 1)),
+// so every DMA instruction fetches whole 128-byte lines (8 rows x 128 B) and
+// a lane's nine instructions of a tile differ only in an immediate offset.
+// The lane map makes both LDS read patterns conflict-free for 32 and for 64
+// banks: the logit loads (16 consecutive rows, one piece, 16 bytes per lane)
+// and the value transpose loads (16 consecutive rows, two adjacent pieces,
+// 8 bytes per lane).
+__device__ __forceinline__ uint32_t tile_byte(int row, int piece) {
+  const int h = row >> 3, rho = row & 7, pi = piece & 7;
+  const int l = 8 * (pi ^ (h & 1)) + (rho ^ (4 * (pi & 1)));
+  return 9216u * h + 1024u * (piece >> 3) + 16u * l;
 }
 
 // Barrier for the tile loop: LDS operations of this wave complete, then all
@@ -158,24 +188,30 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+__device__ __forceinline__ u32x2 pack_bf16x4(const float* p) {
+  u32x2 r;
+  r[0] = static_cast<uint32_t>(f32_to_bf16_rne(p[0])) |
+         (static_cast<uint32_t>(f32_to_bf16_rne(p[1])) << 16);
+  r[1] = static_cast<uint32_t>(f32_to_bf16_rne(p[2])) |
+         (static_cast<uint32_t>(f32_to_bf16_rne(p[3])) << 16);
+  return r;
+}
+
 // One workgroup = (query token, key split), all 64 heads, 4 waves (one per
-// SIMD); wave w owns heads 16 w .. 16 w + 15 end to end.
-//   logits:  S^T = K . Q^T over the tile's 32 keys (two
-//            v_mfma_f32_16x16x32_bf16 tiles with keys on M): lane
-//            (l16, g16) holds head l16's logits for keys 4 g16 + i and
-//            16 + 4 g16 + i (i < 4), so the online-softmax max / sum are
-//            in-lane plus two permlane-swap reductions;
-//   P.V:     those 8 probabilities are, unchanged, the lane's A operand of
-//            O[16 heads, 16 dims] += P[16 heads, 32 keys] . V[32 keys, 16 dims]
-//            provided the value operand uses the same key order: the gfx950
-//            transpose load of rows 4 g16 + c and 16 + 4 g16 + c gives lane
-//            (l16, g16) exactly those keys for dim l16.  Probabilities never
-//            leave registers, and the wave covers all 512 value dims.
-// Tiles go straight from HBM into one of three LDS buffers
-// (global_load_lds_dwordx4, 1 KB of LDS per wave instruction), so two tiles
-// are in flight while the third is multiplied; LDS operand loads are
-// software-pipelined (8 key loads, 16 transpose loads in flight).  One
-// barrier per tile.
+// SIMD).  Wave w = 2 hh + kh: heads 32 hh .. 32 hh + 31 in two 16-head tiles
+// n = 0, 1 (head 32 hh + 16 n + lane % 16 in the query operand).
+//   logits:  S^T[16 keys, 16 heads] = K . Q^T per head tile over 18 K-steps,
+//            keys 16 kh + 4 g16 + i on the rows (lane group g16 = lane / 16),
+//            so lane (l16, g16) holds head l16's logits of 4 keys;
+//   softmax: max over the wave's 16 keys in-lane plus two permlane swaps,
+//            then the partner wave's (2 hh + 1 - kh) maxima through LDS;
+//   P.V:     O[16 heads, 16 dims] += P[16 heads, 32 keys] . V[32 keys, 16 dims]
+//            with K-index 8 g16 + e = own key 16 kh + 4 g16 + e (e < 4) or
+//            the partner's key 16 (1 - kh) + 4 g16 + e - 4: the lane's own 4
+//            probabilities are the first half of its P operand unchanged, the
+//            partner lane's 4 (same lane index) the second half, and two
+//            transpose loads of rows 16 kh + 4 g16 + c and 16 (1 - kh) + 4 g16
+//            + c give the value operand in the same key order.
 __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk_idx, int32_t topk, int32_t n_tokens,
@@ -188,253 +224,346 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   __shared__ MlaShared sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform values live in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int g16 = lane >> 4;
+  const int hh = wave >> 1;
+  const int kh = wave & 1;
+  const int partner = wave ^ 1;
 
   const int t = blockIdx.x / n_split;
   const int split = blockIdx.x % n_split;
   if (t >= n_tokens) return;
 
-  // query rows of this wave's 16 heads (logit B operand): head 16 w + l16,
-  // dims 32 s + 8 g16 .. +8; issued first, they only depend on t
-  constexpr int kQS = kD / 32;                       // 18
-  const int64_t qbase = (static_cast<int64_t>(t) * kH + 16 * wave + l16) * kD;
-  bf16x8 qb[kQS];
-#pragma unroll
-  for (int s = 0; s < kQS; ++s)
-    qb[s] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * s + 8 * g16);
-
-  const int b = request_of_block(cu_q, B, t, &sh.counter);
-  const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
-  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
   const int32_t* idx_row = topk_idx + static_cast<int64_t>(t) * topk;
   const int jbeg = split * split_len;
   const int jend = min(topk, jbeg + split_len);
   const int ntiles = jend > jbeg ? (jend - jbeg + kT - 1) / kT : 0;
   const int jpad = jbeg + ntiles * kT;           // tile-aligned end
 
-  // Resolve the physical row of every index of this split once, into LDS
-  // (padded with -1 to whole tiles), plus a 32-bit validity mask per tile:
-  // index loads first, then block-table loads, each batch issued together.
-  for (int j0 = jbeg; j0 < jpad; j0 += 8 * kThreads) {
-    int32_t p[8];
+  // Index loads first: they depend only on t.
+  constexpr int kIdxPer = kMaxSplitLen / kThreads;   // 8
+  int32_t p[kIdxPer];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = j0 + kThreads * i + tid;
-      p[i] = j < jend ? idx_row[j] : -1;
-    }
-    int32_t bid[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool ok = p[i] >= 0 && p[i] <= pos && p[i] / block_size < max_blocks;
-      bid[i] = ok ? bt_row[p[i] / block_size] : -1;
-      if (!ok) p[i] = -1;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = j0 + kThreads * i + tid;    // a wave covers 64 aligned j
-      int64_t slot = -1;
-      if (p[i] >= 0) {
-        slot = static_cast<int64_t>(bid[i]) * block_size + p[i] % block_size;
-        if (slot < 0 || slot >= num_slots) slot = -1;
-      }
-      if (j < jpad) sh.slots[j - jbeg] = slot;
-      const uint64_t m = __ballot(j < jpad && slot >= 0);
-      const int tw = (j0 + kThreads * i + 64 * wave - jbeg) / kT;
-      if (lane == 0 && tw < ntiles) sh.vbits[tw] = static_cast<uint32_t>(m);
-      if (lane == 0 && tw + 1 < ntiles) sh.vbits[tw + 1] = static_cast<uint32_t>(m >> 32);
-    }
+  for (int i = 0; i < kIdxPer; ++i) {
+    const int j = jbeg + kThreads * i + tid;
+    p[i] = j < jend ? idx_row[j] : -1;
   }
-  lds_barrier();
+  const int b = request_of_block(cu_q, B, t, &sh.counter);
+  const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
+  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
+  int32_t bid[kIdxPer];
+#pragma unroll
+  for (int i = 0; i < kIdxPer; ++i) {
+    const bool ok = p[i] >= 0 && p[i] <= pos && p[i] / block_size < max_blocks;
+    bid[i] = ok ? bt_row[p[i] / block_size] : -1;
+    if (!ok) p[i] = -1;
+  }
+  // The query rows (logit B operand: head 32 hh + 16 n + l16, dims
+  // 32 st + 8 g16 .. +8) are issued behind the block-table loads, so the
+  // slot table below only waits for the latter.
+  asm volatile("" ::: "memory");
+  bf16x8 qb[2][kQSteps];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int64_t qbase = (static_cast<int64_t>(t) * kH + 32 * hh + 16 * n + l16) * kD;
+#pragma unroll
+    for (int s = 0; s < kQSteps; ++s)
+      qb[n][s] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * s + 8 * g16);
+  }
 
-  f32x4 o[kR / 16];                     // dims 16 nt + l16, heads 4 g16 + i
+  // Physical row of every index of this split (padded with -1 to whole
+  // tiles) and a 32-bit validity mask per tile, in LDS.
 #pragma unroll
-  for (int nt = 0; nt < kR / 16; ++nt) o[nt] = f32x4{0, 0, 0, 0};
-  float m_ref = -INFINITY, l_run = 0.0f;   // head 16 w + l16 (all g16 alike)
-
-  // DMA of one tile into LDS buffer `kt`: wave instruction q (q = wave + 4 i)
-  // fills LDS pieces 64 q .. 64 q + 63; lane l loads the global piece that
-  // belongs at LDS piece 64 q + l.  Keys without a row load row 0 (finite
-  // cache data) and are masked out of the softmax.
-  auto dma = [&](int tile_beg, uint16_t* kt) {
-    int64_t sl[kDmaPerWave];
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i)
-      sl[i] = sh.slots[tile_beg - jbeg + (64 * (wave + 4 * i) + lane) / kPieces];
-#pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
-      const int qi = wave + 4 * i;
-      const int pc = 64 * qi + lane;
-      const int row = pc / kPieces;
-      const int col = (pc % kPieces) ^ swz(row);
-      const uint16_t* src = kv + (sl[i] < 0 ? 0 : sl[i]) * kD + col * 8;
-      __builtin_amdgcn_global_load_lds(
-          src, (__attribute__((address_space(3))) void*)(kt + 512 * qi), 16, 0, 0);
+  for (int i = 0; i < kIdxPer; ++i) {
+    const int j = jbeg + kThreads * i + tid;      // a wave covers 64 aligned j
+    int32_t slot = -1;
+    if (p[i] >= 0) {
+      const int64_t s = static_cast<int64_t>(bid[i]) * block_size + p[i] % block_size;
+      slot = (s >= 0 && s < num_slots) ? static_cast<int32_t>(s) : -1;
     }
+    if (j < jpad) sh.slots[j - jbeg] = slot;
+    const uint64_t m = __ballot(j < jpad && slot >= 0);
+    const int tw = (kThreads * i + 64 * wave) / kT;
+    if (lane == 0 && tw < ntiles) sh.vbits[tw] = static_cast<uint32_t>(m);
+    if (lane == 0 && tw + 1 < ntiles) sh.vbits[tw + 1] = static_cast<uint32_t>(m >> 32);
+  }
+  tile_barrier();
+
+  // DMA of local tile `tile` into buffer `buf`: wave w fills row group
+  // h = w, one instruction per piece group g.  Keys without a row load row 0
+  // (finite cache data) and are masked out of the softmax.
+  const int dpi = (lane >> 3) ^ (wave & 1);
+  const int drow = 8 * wave + ((lane & 7) ^ (4 * (dpi & 1)));
+  const uint32_t dcol = 16u * static_cast<uint32_t>(dpi);
+  auto dma = [&](int tile, uint16_t* buf) {
+    const int32_t sl = sh.slots[tile * kT + drow];
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(kv) +
+                         static_cast<uint64_t>(max(sl, 0)) * (2 * kD) + dcol;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(buf) + 9216 * wave;
+    static_for<kDmaPerWave>([&](auto g) {
+      constexpr int G = decltype(g)::value;
+      __builtin_amdgcn_global_load_lds(
+          src + 128 * G, (__attribute__((address_space(3))) void*)(dst + 1024 * G), 16, 0, 0);
+    });
   };
 
-  // operand rows: keys l16 and 16 + l16 (logits), transpose loads of keys
-  // 4 g16 + c and 16 + 4 g16 + c at dims 16 nt + vd (values)
-  const int ksw0 = swz(l16), ksw1 = swz(16 + l16);
-  const int vr0 = 4 * g16 + (l16 >> 2);
-  const int vd = 4 * (l16 & 3);
-  const int vsw0 = swz(vr0), vsw1 = swz(vr0 + 16);
+  // Per-lane LDS byte offsets inside a tile buffer.  Logits: the lane's key
+  // row 16 kh + l16, even / odd K-steps.  Values: transpose-load rows
+  // 16 kh + 4 g16 + l16 / 4 (own keys, a) and 16 (1 - kh) + 4 g16 + l16 / 4
+  // (the partner's keys, b) at dims 256 kh + 16 nt + 4 (l16 & 3), for
+  // nt & 3 = m.
+  const int krow = 16 * kh + l16;
+  const uint32_t kodd[2] = {tile_byte(krow, g16), tile_byte(krow, 4 + g16)};
+  const int vrow_a = 16 * kh + 4 * g16 + (l16 >> 2);
+  const int vrow_b = 16 * (kh ^ 1) + 4 * g16 + (l16 >> 2);
+  const int vb_lo = (l16 & 3) >> 1;
+  uint32_t voff_a[4], voff_b[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    // piece 32 kh + 2 m + vb_lo (+ 8 (nt >> 2) as an immediate), half l16 & 1
+    const uint32_t half = 8u * static_cast<uint32_t>(l16 & 1);
+    voff_a[m] = tile_byte(vrow_a, 32 * kh + 2 * m + vb_lo) + half;
+    voff_b[m] = tile_byte(vrow_b, 32 * kh + 2 * m + vb_lo) + half;
+  }
 
-  auto tile_step = [&](int it) {
-    uint16_t* kt = sh.k[it % kBufs];
-    // this tile's loads are done when at most the next tile's are pending
-    if (it + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerWave);   // vmcnt(9)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);                 // vmcnt(0)
-    tile_barrier();
-    // every wave is past step it-1, so buffer (it + 2) % 3 is free
-    if (it + 2 < ntiles) dma(jbeg + (it + 2) * kT, sh.k[(it + 2) % kBufs]);
+  f32x4 o[2][kR / 32];                  // heads 32 hh + 16 n + 4 g16 + i, dims 256 kh + 16 nt + l16
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int nt = 0; nt < kR / 32; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
+  float m_ref[2] = {-INFINITY, -INFINITY};   // head 32 hh + 16 n + l16
+  float l_part[2] = {0.0f, 0.0f};            // this lane's share of the sum
+
+#pragma unroll
+  for (int i = 0; i < kBufs - 1; ++i)
+    if (i < ntiles) dma(i, sh.k[i]);
+
+  for (int it = 0; it < ntiles; ++it) {
+    // this wave's part of tile `it` is in when at most the later tiles'
+    // loads are pending
+    const int later = min(ntiles - 1 - it, kBufs - 2);
+    if (later >= 2) wait_vm<2 * kDmaPerWave>();
+    else if (later == 1) wait_vm<kDmaPerWave>();
+    else wait_vm<0>();
+    tile_barrier();              // (A) tile `it` complete, tile it-1 released
+    if (it + kBufs - 1 < ntiles) dma(it + kBufs - 1, sh.k[(it + kBufs - 1) % kBufs]);
+    const uint16_t* kt = sh.k[it % kBufs];
     const uint32_t vb32 = sh.vbits[it];
 
-    // ---- logits S^T: part[c] holds keys 16 c + 4 g16 + i, head 16 w + l16.
-    // 36 operand loads (load ld: step ld / 2, key half ld % 2), 8 in flight
+    // ---- logits: part[n][i] = head 32 hh + 16 n + l16, key 16 kh + 4 g16 + i
+    // K-step st reads piece 4 st + g16 of the lane's row: group st >> 1 (an
+    // immediate 1024 (st >> 1)) and one of two per-lane offsets.
     f32x4 part[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
     {
-      const uint32_t kb0 = lds_addr(&kt[l16 * kD]), kb1 = lds_addr(&kt[(16 + l16) * kD]);
-      auto kaddr = [&](int ld) -> uint32_t {
-        const int c = ld & 1, st = ld >> 1;
-        return (c ? kb1 : kb0) + 16u * static_cast<uint32_t>((4 * st + g16) ^ (c ? ksw1 : ksw0));
-      };
-      constexpr int kLoads = 2 * kQS;
-      bf16x8 kr[8];
+      const uint32_t kb = lds_addr(kt);
+      const uint32_t kbase[2] = {kb + kodd[0], kb + kodd[1]};
+      constexpr int kAhead = 4;
+      bf16x8 kr[kAhead];
       lgkm_drain();
-#pragma unroll
-      for (int ld = 0; ld < 8; ++ld) kr[ld] = b128_load(kaddr(ld));
-#pragma unroll
-      for (int ld = 0; ld < kLoads; ++ld) {
-        bf16x8& cur = kr[ld & 7];
-        constexpr int kAhead = 7;
-        // loads issued after load ld: min(7, kLoads - 1 - ld)
-        if (ld + kAhead <= kLoads - 1) lgkm_keep<7>(cur);
-        else if (kLoads - 1 - ld == 6) lgkm_keep<6>(cur);
-        else if (kLoads - 1 - ld == 5) lgkm_keep<5>(cur);
-        else if (kLoads - 1 - ld == 4) lgkm_keep<4>(cur);
-        else if (kLoads - 1 - ld == 3) lgkm_keep<3>(cur);
-        else if (kLoads - 1 - ld == 2) lgkm_keep<2>(cur);
-        else if (kLoads - 1 - ld == 1) lgkm_keep<1>(cur);
-        else lgkm_keep<0>(cur);
-        part[ld & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qb[ld >> 1], part[ld & 1], 0, 0, 0);
-        if (ld + 8 < kLoads) kr[ld & 7] = b128_load(kaddr(ld + 8));
-      }
+      static_for<kAhead>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        kr[S] = b128_load<1024 * (S >> 1)>(kbase[S & 1]);
+      });
+      static_for<kQSteps>([&](auto st) {
+        constexpr int S = decltype(st)::value;
+        bf16x8& cur = kr[S % kAhead];
+        constexpr int kAfter = (kQSteps - 1 - S) < (kAhead - 1) ? (kQSteps - 1 - S) : (kAhead - 1);
+        lgkm_keep<kAfter>(cur);
+        part[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qb[0][S], part[0], 0, 0, 0);
+        part[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qb[1][S], part[1], 0, 0, 0);
+        if constexpr (S + kAhead < kQSteps)
+          cur = b128_load<1024 * ((S + kAhead) >> 1)>(kbase[(S + kAhead) & 1]);
+      });
     }
 
-    // ---- online softmax over the tile (lane = head l16, keys of its g16)
-    const uint32_t vbl = vb32 >> (4 * g16);
-    float z[8];
-    float mx = -INFINITY;
+    // ---- softmax
+    const uint32_t vbl = vb32 >> (16 * kh + 4 * g16);
+    float z[2][4], mx[2];
+    bool need = false;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int n = 0; n < 2; ++n) {
+      mx[n] = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        z[4 * c + i] = ((vbl >> (16 * c + i)) & 1u) ? part[c][i] * scale_log2 : -INFINITY;
-        mx = fmaxf(mx, z[4 * c + i]);
+        z[n][i] = ((vbl >> i) & 1u) ? part[n][i] * scale_log2 : -INFINITY;
+        mx[n] = fmaxf(mx[n], z[n][i]);
       }
-    mx = max_x16_x32(mx);
-    const bool move = mx > m_ref + kRescaleSlack || (m_ref == -INFINITY && mx != -INFINITY);
-    const float m_new = move ? mx : m_ref;
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    float p[8];
-    float ps = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(z[e] - m_use);     // 0 for masked keys
-      ps += p[e];
+      mx[n] = max_x16_x32(mx[n]);
+      need |= mx[n] > m_ref[n] + kMoveSlack;
     }
-    ps = sum_x16_x32(ps);
-    if (__ballot(move)) {
-      // rescale the rows of heads whose reference max moved (rare)
-      const float alpha = move ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
-      float a4[4];
+    // speculative probabilities against the current reference maxima
+    float pr[2][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, 4 * g16 + i);
+    for (int n = 0; n < 2; ++n) {
+      const float mu = m_ref[n] == -INFINITY ? 0.0f : m_ref[n];
 #pragma unroll
-      for (int nt = 0; nt < kR / 16; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[nt][i] *= a4[i];
-      l_run *= alpha;
+      for (int i = 0; i < 4; ++i) pr[n][i] = __builtin_amdgcn_exp2f(z[n][i] - mu);
     }
-    l_run += ps;
-    m_ref = m_new;
-    bf16x8 pa;
+    const bool wave_need = __ballot(need) != 0;
+    sh.xp[wave][0][lane] = pack_bf16x4(pr[0]);
+    sh.xp[wave][1][lane] = pack_bf16x4(pr[1]);
+    sh.xm[wave][0][lane] = mx[0];
+    sh.xm[wave][1][lane] = mx[1];
+    if (lane == 0) sh.xf[wave] = wave_need ? 1u : 0u;
+    tile_barrier();              // (B) maxima, flags and probabilities published
+    const u32x4 flags = *reinterpret_cast<const u32x4*>(sh.xf);
+    if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
+      // Some reference maximum of the workgroup moves; every wave takes this
+      // branch.  A head's first key sets its reference (its sums are still
+      // zero, nothing to rescale).  A head whose tile maximum beats its
+      // reference by more than kMoveSlack would overflow: then the new maxima
+      // become the references and the workgroup restarts its split from the
+      // first tile with zero sums (later restarts can only come from later
+      // tiles, so there are at most ntiles of them).  The accumulators are
+      // never rescaled in place.
+      bool restart = false;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pa[e] = static_cast<__bf16>(p[e]);
-
-    // ---- O[16 heads, 512 dims] += P . V: 64 transpose loads (load 2 nt + c:
-    // key half c of dim tile nt), 16 in flight
-    {
-      const uint32_t vb0 = lds_addr(&kt[vr0 * kD]), vb1 = lds_addr(&kt[(vr0 + 16) * kD]);
-      auto vaddr = [&](int ld) -> uint32_t {
-        const int c = ld & 1, nt = ld >> 1;
-        const int dim = 16 * nt + vd;
-        return (c ? vb1 : vb0) + 16u * static_cast<uint32_t>((dim >> 3) ^ (c ? vsw1 : vsw0)) +
-               2u * static_cast<uint32_t>(dim & 7);
-      };
-      constexpr int kLoads = 2 * (kR / 16);           // 64
-      v4i16 vr[16];
-      lgkm_drain();
+      for (int n = 0; n < 2; ++n) {
+        const float mfull = fmaxf(mx[n], sh.xm[partner][n][lane]);
+        const bool first = m_ref[n] == -INFINITY && mfull != -INFINITY;
+        const bool over = m_ref[n] != -INFINITY && mfull > m_ref[n] + kMoveSlack;
+        restart |= over;
+        if (first || over) m_ref[n] = mfull;
+        const float mu = m_ref[n] == -INFINITY ? 0.0f : m_ref[n];
 #pragma unroll
-      for (int ld = 0; ld < 16; ++ld) vr[ld] = tr_load(vaddr(ld));
+        for (int i = 0; i < 4; ++i) pr[n][i] = __builtin_amdgcn_exp2f(z[n][i] - mu);
+      }
+      sh.xp[wave][0][lane] = pack_bf16x4(pr[0]);
+      sh.xp[wave][1][lane] = pack_bf16x4(pr[1]);
+      if (lane == 0) sh.xr[wave] = __ballot(restart) != 0 ? 1u : 0u;
+      tile_barrier();            // (C) probabilities against the new maxima
+      const u32x4 rf = *reinterpret_cast<const u32x4*>(sh.xr);
+      if ((rf[0] | rf[1] | rf[2] | rf[3]) != 0) {
 #pragma unroll
-      for (int nt = 0; nt < kR / 16; ++nt) {
-        v4i16& a0 = vr[(2 * nt) & 15];
-        v4i16& a1 = vr[(2 * nt + 1) & 15];
-        // loads issued after load 2 nt + 1: min(14, kLoads - 2 - 2 nt)
-        if (2 * nt + 16 <= kLoads) { lgkm_keep<14>(a0); lgkm_keep<14>(a1); }
-        else if (kLoads - 2 - 2 * nt == 12) { lgkm_keep<12>(a0); lgkm_keep<12>(a1); }
-        else if (kLoads - 2 - 2 * nt == 10) { lgkm_keep<10>(a0); lgkm_keep<10>(a1); }
-        else if (kLoads - 2 - 2 * nt == 8) { lgkm_keep<8>(a0); lgkm_keep<8>(a1); }
-        else if (kLoads - 2 - 2 * nt == 6) { lgkm_keep<6>(a0); lgkm_keep<6>(a1); }
-        else if (kLoads - 2 - 2 * nt == 4) { lgkm_keep<4>(a0); lgkm_keep<4>(a1); }
-        else if (kLoads - 2 - 2 * nt == 2) { lgkm_keep<2>(a0); lgkm_keep<2>(a1); }
-        else { lgkm_keep<0>(a0); lgkm_keep<0>(a1); }
-        typedef short v8i16 __attribute__((ext_vector_type(8)));
-        const v8i16 v01 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, v01),
-                                                        o[nt], 0, 0, 0);
-        if (2 * nt + 16 < kLoads) {
-          vr[(2 * nt) & 15] = tr_load(vaddr(2 * nt + 16));
-          vr[(2 * nt + 1) & 15] = tr_load(vaddr(2 * nt + 17));
+        for (int n = 0; n < 2; ++n) {
+          l_part[n] = 0.0f;
+#pragma unroll
+          for (int nt = 0; nt < kR / 32; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
         }
+        wait_vm<0>();
+        tile_barrier();          // every wave is done with the ring
+#pragma unroll
+        for (int i = 0; i < kBufs - 1; ++i)
+          if (i < ntiles) dma(i, sh.k[i]);
+        it = -1;
+        continue;
       }
     }
-  };
-
-  if (ntiles > 0) dma(jbeg, sh.k[0]);
-  if (ntiles > 1) dma(jbeg + kT, sh.k[1]);
-  for (int it = 0; it < ntiles; ++it) tile_step(it);
-
-  // ---- epilogue: rows of o are heads 16 w + 4 g16 + i
-  const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
-  const float lse_h = l_run > 0.0f ? (m_ref + log2f(l_run)) * kLn2 : -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int hl = 4 * g16 + i;
-    const float il = __shfl(inv_l, hl);
-    const int h = 16 * wave + hl;
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int nt = 0; nt < kR / 16; ++nt) {
-      const int r = 16 * nt + l16;
-      const float v = o[nt][i] * il;
-      if (n_split == 1)
-        out[(static_cast<int64_t>(t) * kH + h) * kR + r] = f32_to_bf16_rne(v);
-      else
-        part_o[((static_cast<int64_t>(t) * n_split + split) * kH + h) * kR + r] = v;
+      for (int i = 0; i < 4; ++i) l_part[n] += pr[n][i];
+    bf16x8 pa[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const u32x2 own = pack_bf16x4(pr[n]);
+      const u32x2 oth = sh.xp[partner][n][lane];
+      const u32x4 v = {own[0], own[1], oth[0], oth[1]};
+      pa[n] = __builtin_bit_cast(bf16x8, v);
+    }
+
+    // ---- O += P . V: 16 dim tiles, two transpose loads each, 8 in flight.
+    // Dim tile nt reads piece 32 kh + 2 nt + b of its rows: group
+    // 4 kh + (nt >> 2) (an immediate 1024 (nt >> 2)) and one of four per-lane
+    // offsets per row set.
+    {
+      const uint32_t tb = lds_addr(kt);
+      uint32_t va[4], vb[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        va[m] = tb + voff_a[m];
+        vb[m] = tb + voff_b[m];
+      }
+      constexpr int kLoads = 2 * (kR / 32);           // 32
+      constexpr int kAhead = 8;
+      v4i16 vr[kAhead];
+      auto vload = [&](auto ld) -> v4i16 {
+        constexpr int L = decltype(ld)::value;
+        constexpr int NT = L >> 1;
+        return (L & 1) ? tr_load<1024 * (NT >> 2)>(vb[NT & 3])
+                       : tr_load<1024 * (NT >> 2)>(va[NT & 3]);
+      };
+      lgkm_drain();
+      static_for<kAhead>([&](auto ld) { vr[decltype(ld)::value] = vload(ld); });
+      static_for<kR / 32>([&](auto ntc) {
+        constexpr int NT = decltype(ntc)::value;
+        v4i16& a0 = vr[(2 * NT) % kAhead];
+        v4i16& a1 = vr[(2 * NT + 1) % kAhead];
+        // loads issued after load 2 NT + 1
+        constexpr int kAfter = (kLoads - 2 - 2 * NT) < (kAhead - 2) ? (kLoads - 2 - 2 * NT) : (kAhead - 2);
+        lgkm_keep<kAfter>(a0);
+        lgkm_keep<kAfter>(a1);
+        const v8i16 v01 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, v01);
+        o[0][NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vop, o[0][NT], 0, 0, 0);
+        o[1][NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vop, o[1][NT], 0, 0, 0);
+        if constexpr (2 * NT + kAhead < kLoads) {
+          a0 = vload(std::integral_constant<int, 2 * NT + kAhead>{});
+          a1 = vload(std::integral_constant<int, 2 * NT + kAhead + 1>{});
+        }
+      });
     }
   }
-  if (g16 == 0) {
-    const int h = 16 * wave + l16;
-    if (n_split == 1) {
-      if (lse) lse[static_cast<int64_t>(t) * kH + h] = lse_h;
-    } else {
-      part_lse[(static_cast<int64_t>(t) * n_split + split) * kH + h] = lse_h;
+
+  // ---- epilogue: per-head sums, normalisation, staged coalesced stores
+#pragma unroll
+  for (int n = 0; n < 2; ++n) l_part[n] = sum_x16_x32(l_part[n]);
+  tile_barrier();                // every wave is done with the tiles and xm
+  sh.xm[wave][0][lane] = l_part[0];
+  sh.xm[wave][1][lane] = l_part[1];
+  tile_barrier();
+  float inv_l[2], lse_h[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const float l = l_part[n] + sh.xm[partner][n][lane];
+    inv_l[n] = l > 0.0f ? 1.0f / l : 0.0f;
+    lse_h[n] = l > 0.0f ? (m_ref[n] + log2f(l)) * kLn2 : -INFINITY;
+  }
+  const bool partial = n_split > 1;
+  // rows of the staged block: head h (0..63) at byte h * row_b of the tile
+  // buffers (free now); 16 bytes of padding per row spread the banks
+  const int row_b = partial ? kR * 4 + 16 : kR * 2 + 16;
+  uint8_t* stage = reinterpret_cast<uint8_t*>(&sh.k[0][0]);
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hl = 4 * g16 + i;
+      const float il = __shfl(inv_l[n], hl);
+      const int h = 32 * hh + 16 * n + hl;
+#pragma unroll
+      for (int nt = 0; nt < kR / 32; ++nt) {
+        const int d = 256 * kh + 16 * nt + l16;
+        const float v = o[n][nt][i] * il;
+        if (partial)
+          *reinterpret_cast<float*>(stage + h * row_b + 4 * d) = v;
+        else
+          *reinterpret_cast<uint16_t*>(stage + h * row_b + 2 * d) = f32_to_bf16_rne(v);
+      }
     }
+  }
+  if (kh == 0 && g16 == 0) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int h = 32 * hh + 16 * n + l16;
+      if (partial)
+        part_lse[(static_cast<int64_t>(t) * n_split + split) * kH + h] = lse_h[n];
+      else if (lse)
+        lse[static_cast<int64_t>(t) * kH + h] = lse_h[n];
+    }
+  }
+  tile_barrier();
+  // copy the staged block out in 16-byte pieces (a contiguous region)
+  const int row_pieces = partial ? kR * 4 / 16 : kR * 2 / 16;
+  const int total = kH * row_pieces;
+  u32x4* dst = partial
+      ? reinterpret_cast<u32x4*>(part_o + (static_cast<int64_t>(t) * n_split + split) * kH * kR)
+      : reinterpret_cast<u32x4*>(out + static_cast<int64_t>(t) * kH * kR);
+  for (int c = tid; c < total; c += kThreads) {
+    const int h = c / row_pieces, pc = c % row_pieces;
+    dst[c] = *reinterpret_cast<const u32x4*>(stage + h * row_b + 16 * pc);
   }
 }
 
@@ -559,29 +688,34 @@ __global__ __launch_bounds__(256) void k_mla_vector(
 
 }  // namespace
 
-bool mla_mfma_ok(int dtype, int n_heads, int R, int P) {
-  return dtype == DSA_BF16 && R == kR && P == kP && n_heads == kH;
+bool mla_mfma_ok(const dsa_batch& b, int dtype, int n_heads, int R, int P) {
+  // slots are kept as 32-bit row numbers on this path
+  return dtype == DSA_BF16 && R == kR && P == kP && n_heads == kH &&
+         b.num_slots <= INT32_MAX;
 }
 
 int mla_choose_split(const dsa_batch* b, int dtype, int n_heads, int R, int P,
                      int topk) {
-  if (!mla_mfma_ok(dtype, n_heads, R, P)) return 1;
-  // one workgroup per CU at least: split the keys of each token until there
-  // are >= 256 workgroups, keeping >= 4 tiles per split
+  if (!mla_mfma_ok(*b, dtype, n_heads, R, P)) return 1;
+  // at most kMaxSplitLen indices per workgroup; beyond that, one workgroup
+  // per CU at least: split the keys of each token until there are >= 256
+  // workgroups, keeping >= 4 tiles per split
+  const int min_split = max(1, (topk + kMaxSplitLen - 1) / kMaxSplitLen);
   const int64_t wgs = static_cast<int64_t>(b->num_q_tokens);
-  if (wgs <= 0 || wgs >= 256) return 1;
+  if (wgs <= 0 || wgs >= 256) return min_split;
   int split = static_cast<int>((256 + wgs - 1) / wgs);
   const int max_split = max(1, topk / (4 * kT));
-  return min(split, max_split);
+  return max(min_split, min(split, max_split));
 }
 
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
   const dsa_batch& b = a.b;
   if (b.num_q_tokens == 0) return hipSuccess;
-  if (mla_mfma_ok(a.dtype, a.n_heads, a.R, a.P)) {
+  if (mla_mfma_ok(b, a.dtype, a.n_heads, a.R, a.P)) {
     const int n_split = a.n_split;
     int split_len = (a.topk + n_split - 1) / n_split;
     split_len = (split_len + kT - 1) / kT * kT;
+    if (split_len > kMaxSplitLen) return hipErrorInvalidValue;
     const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * n_split;
     k_mla_mfma<<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv),

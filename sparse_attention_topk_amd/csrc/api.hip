@@ -72,9 +72,14 @@ bool known_dtype(int d) {
   return d == DSA_F32 || d == DSA_BF16 || d == DSA_FP8_E4M3;
 }
 
+// score rows are padded to 64 floats so that every row starts 256-byte aligned
+int64_t score_row_stride(const dsa_batch* b) {
+  return (static_cast<int64_t>(b->max_seq_len) + 63) / 64 * 64;
+}
+
 size_t topk_ws(const dsa_batch* b) {
   return round_up(static_cast<size_t>(b->num_q_tokens) *
-                  static_cast<size_t>(b->max_seq_len) * sizeof(float));
+                  static_cast<size_t>(score_row_stride(b)) * sizeof(float));
 }
 
 size_t mla_ws(const dsa_batch* b, int n_heads, int R, int P, int topk, int dtype) {
@@ -159,7 +164,7 @@ int run_indexer(const dsa_batch* b, const void* q, int q_dtype, const float* w,
   a.topk = topk;
   a.topk_idx = topk_idx;
   a.scores = static_cast<float*>(ws);
-  a.row_stride = b->max_seq_len;
+  a.row_stride = score_row_stride(b);
   hipError_t e = dsa::launch_indexer_score(a, stream);
   if (e != hipSuccess) return hip_fail(e, "indexer score launch");
   e = dsa::launch_topk(a, stream);

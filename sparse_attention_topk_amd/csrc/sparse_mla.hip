@@ -432,7 +432,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
       }
       sh.xp[wave][0][lane] = pack_bf16x4(pr[0]);
       sh.xp[wave][1][lane] = pack_bf16x4(pr[1]);
-      if (lane == 0) sh.xr[wave] = __ballot(restart) != 0 ? 1u : 0u;
+      const bool wave_restart = __ballot(restart) != 0;   // all lanes vote
+      if (lane == 0) sh.xr[wave] = wave_restart ? 1u : 0u;
       tile_barrier();            // (C) probabilities against the new maxima
       const u32x4 rf = *reinterpret_cast<const u32x4*>(sh.xr);
       if ((rf[0] | rf[1] | rf[2] | rf[3]) != 0) {

@@ -15,19 +15,19 @@
 // then every position with key > T plus the first topk - c_gt positions with
 // key == T, in position order.
 //
-//  1. load: the row is read once from HBM, into LDS when it fits
-//     (<= 32768 keys), tracking the value range [vmin, vmax];
+// Rows of up to 32768 keys stay in registers (thread i holds positions
+// 32 i .. 32 i + 31):
+//  1. load, value range [vmin, vmax];
 //  2. histogram over 2048 value-linear bins of [vmin, vmax] (the bin map is
 //     monotone in the value, so every key in a higher bin is strictly
-//     larger), LDS atomics;
-//  3. the bin holding the threshold is found by a suffix scan; its keys are
-//     gathered into a candidate list;
-//  4. an exact 4 x 8-bit radix select over the candidates (or over the whole
-//     row when the bin is too large) gives T and c_gt;
-//  5. ordered compaction: each wave owns a contiguous span of the row,
-//     counts keys > T and == T with wave ballots, the per-wave counts are
-//     scanned across waves, then each wave emits its positions in order
-//     using ballot prefix counts.
+//     larger), LDS atomics; a suffix scan finds the bin holding rank topk;
+//  3. the keys of that bin are gathered; when there are few, each is ranked
+//     against all of them directly, otherwise an exact 4 x 8-bit radix
+//     select over the row runs;
+//  4. ordered compaction: per-thread counts of keys > T and == T, one
+//     workgroup-wide exclusive scan, then every thread writes its positions.
+// Longer rows stream from memory in every pass (same steps, radix select
+// over candidates or the row, compaction by waves over contiguous spans).
 #include "common.h"
 
 namespace dsa {
@@ -36,8 +36,10 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
-constexpr int kRowCap = 32768;    // keys kept in LDS
+constexpr int kKpt = 32;                       // keys per thread, register path
+constexpr int kRegCap = kThreads * kKpt;       // 32768
 constexpr int kCandCap = 4096;
+constexpr int kRankCap = 256;                  // candidates ranked directly
 
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t b = __float_as_uint(f);
@@ -49,7 +51,6 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 }
 
 struct Shared {
-  uint32_t row[kRowCap];
   uint32_t hist[kBins];
   uint32_t cand[kCandCap];
   uint32_t wave_a[kWaves];
@@ -61,6 +62,8 @@ struct Shared {
   uint32_t above_bin;     // keys in bins above it
   uint32_t digit;         // radix step result
   uint32_t digit_above;
+  uint32_t thr;           // threshold key
+  uint32_t thr_above;     // keys above it within the candidate set
   uint32_t counter;
 };
 
@@ -101,42 +104,6 @@ __device__ void find_digit(Shared& s, uint32_t r) {
   }
 }
 
-template <bool IN_LDS>
-__device__ __forceinline__ uint32_t row_key(const Shared& s,
-                                            const float* __restrict__ src,
-                                            int i) {
-  if constexpr (IN_LDS) return s.row[i];
-  return float_key(src[i]);
-}
-
-// Visits every key of the row once, thread tid taking i = tid + 1024 j.
-// From global memory the loads are issued kBatch at a time before any is
-// used, so a thread keeps kBatch loads in flight instead of one.
-constexpr int kBatch = 16;
-template <bool IN_LDS, bool FROM_GLOBAL, typename F>
-__device__ __forceinline__ void for_each_key(const Shared& s,
-                                             const float* __restrict__ src,
-                                             int L, F&& f) {
-  const int tid = threadIdx.x;
-  if constexpr (IN_LDS && !FROM_GLOBAL) {
-    for (int i = tid; i < L; i += kThreads) f(i, s.row[i]);
-  } else {
-    for (int base = 0; base < L; base += kBatch * kThreads) {
-      float v[kBatch];
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = base + j * kThreads + tid;
-        v[j] = i < L ? src[i] : 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int i = base + j * kThreads + tid;
-        if (i < L) f(i, float_key(v[j]));
-      }
-    }
-  }
-}
-
 __device__ __forceinline__ int bin_of(float v, float vmin, float inv) {
   float t = (v - vmin) * inv;
   // NaN (0 * inf when the range underflows) compares false -> bin 0;
@@ -145,22 +112,10 @@ __device__ __forceinline__ int bin_of(float v, float vmin, float inv) {
   return b;
 }
 
-template <bool IN_LDS>
-__device__ void select_row(Shared& s, const float* __restrict__ src, int L,
-                           int topk, int32_t* __restrict__ out) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-
-  // ---- 1. load + range (loads issued in batches so many are in flight)
-  float vmin = INFINITY, vmax = -INFINITY;
-  for_each_key<IN_LDS, true>(s, src, L, [&](int i, uint32_t k) {
-    if constexpr (IN_LDS) s.row[i] = k;
-    const float f = key_float(k);
-    vmin = fminf(vmin, f);
-    vmax = fmaxf(vmax, f);
-  });
-  for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
+// Workgroup-wide min / max of per-thread values (every thread gets both).
+__device__ __forceinline__ void range_reduce(Shared& s, float& vmin, float& vmax) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     vmin = fminf(vmin, __shfl_xor(vmin, off));
@@ -170,7 +125,6 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
     s.red_min[wave] = vmin;
     s.red_max[wave] = vmax;
   }
-  if (tid == 0) s.ncand = 0;
   lds_barrier();
   vmin = s.red_min[0];
   vmax = s.red_max[0];
@@ -179,54 +133,255 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
     vmin = fminf(vmin, s.red_min[wv]);
     vmax = fmaxf(vmax, s.red_max[wv]);
   }
+}
 
-  uint32_t T;
-  uint32_t c_gt;
+// Thread tid owns bins 2047 - 2 tid and 2046 - 2 tid; the bin holding rank r
+// (counted from the top) and the number of keys above it go to s.sel_bin /
+// s.above_bin.  Ends with a barrier.
+__device__ __forceinline__ void find_threshold_bin(Shared& s, uint32_t r) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint32_t h0 = s.hist[kBins - 1 - 2 * tid];
+  const uint32_t h1 = s.hist[kBins - 2 - 2 * tid];
+  const uint32_t tot = h0 + h1;
+  uint32_t incl = tot;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s.wave_a[wave] = incl;
+  lds_barrier();
+  uint32_t base = 0;
+  for (int wv = 0; wv < wave; ++wv) base += s.wave_a[wv];
+  const uint32_t above0 = base + incl - tot;    // above bin 2047 - 2 tid
+  if (above0 < r && r <= above0 + h0) {
+    s.sel_bin = kBins - 1 - 2 * tid;
+    s.above_bin = above0;
+  }
+  const uint32_t above1 = above0 + h0;
+  if (above1 < r && r <= above1 + h1) {
+    s.sel_bin = kBins - 2 - 2 * tid;
+    s.above_bin = above1;
+  }
+  lds_barrier();
+}
+
+// Exact rank-r (from the top) key among the n <= kRankCap candidates in
+// s.cand: thread i < n counts the candidates above and at-or-above its own;
+// the thread(s) with above < r <= at-or-above hold the answer (equal keys
+// write equal values).  Result in s.thr / s.thr_above; ends with a barrier.
+__device__ __forceinline__ void rank_candidates(Shared& s, int n, uint32_t r) {
+  const int tid = threadIdx.x;
+  if (tid < n) {
+    const uint32_t mine = s.cand[tid];
+    uint32_t gt = 0, ge = 0;
+    for (int j = 0; j < n; ++j) {
+      const uint32_t o = s.cand[j];
+      gt += o > mine;
+      ge += o >= mine;
+    }
+    if (gt < r && r <= ge) {
+      s.thr = mine;
+      s.thr_above = gt;
+    }
+  }
+  lds_barrier();
+}
+
+// ------------------------------------------------------------ register path
+__device__ void select_row_regs(Shared& s, const float* __restrict__ src, int L,
+                                int topk, int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int p0 = kKpt * tid;
+
+  // ---- 1. load: 32 consecutive positions per thread (absent ones -> key 0,
+  // below every real key, and excluded from the range and the histogram).
+  // Rows start 16-byte aligned (the score rows are padded to 64 floats).
+  uint32_t k[kKpt];
+  if (p0 + kKpt <= L) {
+    const float4* v4 = reinterpret_cast<const float4*>(src + p0);
+    float4 v[kKpt / 4];
+#pragma unroll
+    for (int j = 0; j < kKpt / 4; ++j) v[j] = v4[j];
+#pragma unroll
+    for (int j = 0; j < kKpt / 4; ++j) {
+      k[4 * j + 0] = float_key(v[j].x);
+      k[4 * j + 1] = float_key(v[j].y);
+      k[4 * j + 2] = float_key(v[j].z);
+      k[4 * j + 3] = float_key(v[j].w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kKpt; ++j) k[j] = p0 + j < L ? float_key(src[p0 + j]) : 0u;
+  }
+  const int nmine = max(0, min(kKpt, L - p0));
+  float vmin = INFINITY, vmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kKpt; ++j) {
+    if (j < nmine) {
+      const float f = key_float(k[j]);
+      vmin = fminf(vmin, f);
+      vmax = fmaxf(vmax, f);
+    }
+  }
+  for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
+  if (tid == 0) s.ncand = 0;
+  range_reduce(s, vmin, vmax);
+
+  uint32_t T, c_gt;
   if (!(vmax > vmin)) {
     // every key is equal: positions decide
     T = float_key(vmax);
     c_gt = 0;
   } else {
-    // ---- 2. histogram
+    // ---- 2. histogram and threshold bin
     const float inv = static_cast<float>(kBins) / (vmax - vmin);
-    for_each_key<IN_LDS, false>(s, src, L, [&](int, uint32_t k) {
+#pragma unroll
+    for (int j = 0; j < kKpt; ++j)
+      if (j < nmine) atomicAdd(&s.hist[bin_of(key_float(k[j]), vmin, inv)], 1u);
+    lds_barrier();
+    find_threshold_bin(s, static_cast<uint32_t>(topk));
+    const int sel = static_cast<int>(s.sel_bin);
+    const uint32_t above_bin = s.above_bin;
+    const uint32_t bin_count = s.hist[sel];
+    const uint32_t r = static_cast<uint32_t>(topk) - above_bin;
+
+    if (bin_count <= static_cast<uint32_t>(kRankCap)) {
+      // ---- 3a. gather the bin's keys, rank them directly
+#pragma unroll
+      for (int j = 0; j < kKpt; ++j) {
+        if (j < nmine && bin_of(key_float(k[j]), vmin, inv) == sel) {
+          const uint32_t slot = atomicAdd(&s.ncand, 1u);
+          s.cand[slot] = k[j];
+        }
+      }
+      lds_barrier();
+      rank_candidates(s, static_cast<int>(bin_count), r);
+      T = s.thr;
+      c_gt = above_bin + s.thr_above;
+    } else {
+      // ---- 3b. exact radix select of rank topk over the row
+      uint32_t rr = static_cast<uint32_t>(topk);
+      uint32_t prefix = 0, mask = 0, gt_extra = 0;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        lds_barrier();
+        for (int i = tid; i < 256; i += kThreads) s.hist[i] = 0;
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < kKpt; ++j)
+          if (j < nmine && (k[j] & mask) == prefix)
+            atomicAdd(&s.hist[(k[j] >> shift) & 255u], 1u);
+        lds_barrier();
+        find_digit(s, rr);
+        lds_barrier();
+        const uint32_t d = s.digit;
+        const uint32_t da = s.digit_above;
+        rr -= da;
+        gt_extra += da;
+        prefix |= d << shift;
+        mask |= 255u << shift;
+      }
+      T = prefix;
+      c_gt = gt_extra;
+    }
+  }
+
+  // ---- 4. ordered compaction: (gt, eq) counts packed 16:16 (each <= 32768)
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int j = 0; j < kKpt; ++j) {
+    n_gt += k[j] > T;
+    n_eq += k[j] == T;          // absent keys are 0 < T
+  }
+  const uint32_t packed = (n_gt << 16) | n_eq;
+  uint32_t incl = packed;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) s.wave_b[wave] = incl;
+  lds_barrier();
+  uint32_t base = 0;
+  for (int wv = 0; wv < wave; ++wv) base += s.wave_b[wv];
+  const uint32_t excl = base + incl - packed;
+  const uint32_t need = static_cast<uint32_t>(topk) - c_gt;   // >= 1
+  uint32_t eq_before = excl & 0xFFFFu;
+  uint32_t o = (excl >> 16) + min(eq_before, need);
+#pragma unroll
+  for (int j = 0; j < kKpt; ++j) {
+    const bool gt = k[j] > T;
+    const bool eq = k[j] == T;
+    const bool take = gt || (eq && eq_before < need);
+    if (take) out[o++] = p0 + j;
+    eq_before += eq;
+  }
+}
+
+// ------------------------------------------------------------ streaming path
+// Visits every key of the row once, thread tid taking i = tid + 1024 j.
+// The loads are issued kBatch at a time before any is used, so a thread
+// keeps kBatch loads in flight instead of one.
+constexpr int kBatch = 16;
+template <typename F>
+__device__ __forceinline__ void for_each_key(const float* __restrict__ src,
+                                             int L, F&& f) {
+  const int tid = threadIdx.x;
+  for (int base = 0; base < L; base += kBatch * kThreads) {
+    float v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + j * kThreads + tid;
+      v[j] = i < L ? src[i] : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int i = base + j * kThreads + tid;
+      if (i < L) f(i, float_key(v[j]));
+    }
+  }
+}
+
+__device__ void select_row_stream(Shared& s, const float* __restrict__ src, int L,
+                                  int topk, int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // ---- 1. range
+  float vmin = INFINITY, vmax = -INFINITY;
+  for_each_key(src, L, [&](int, uint32_t k) {
+    const float f = key_float(k);
+    vmin = fminf(vmin, f);
+    vmax = fmaxf(vmax, f);
+  });
+  for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
+  if (tid == 0) s.ncand = 0;
+  range_reduce(s, vmin, vmax);
+
+  uint32_t T;
+  uint32_t c_gt;
+  if (!(vmax > vmin)) {
+    T = float_key(vmax);
+    c_gt = 0;
+  } else {
+    // ---- 2. histogram and threshold bin
+    const float inv = static_cast<float>(kBins) / (vmax - vmin);
+    for_each_key(src, L, [&](int, uint32_t k) {
       atomicAdd(&s.hist[bin_of(key_float(k), vmin, inv)], 1u);
     });
     lds_barrier();
-    // ---- 3. threshold bin: thread tid owns bins 2047-2tid, 2046-2tid
-    {
-      const uint32_t h0 = s.hist[kBins - 1 - 2 * tid];
-      const uint32_t h1 = s.hist[kBins - 2 - 2 * tid];
-      const uint32_t tot = h0 + h1;
-      uint32_t incl = tot;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        uint32_t v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-      }
-      if (lane == 63) s.wave_a[wave] = incl;
-      lds_barrier();
-      uint32_t base = 0;
-      for (int wv = 0; wv < wave; ++wv) base += s.wave_a[wv];
-      const uint32_t above0 = base + incl - tot;    // above bin 2047-2tid
-      const uint32_t r = static_cast<uint32_t>(topk);
-      if (above0 < r && r <= above0 + h0) {
-        s.sel_bin = kBins - 1 - 2 * tid;
-        s.above_bin = above0;
-      }
-      const uint32_t above1 = above0 + h0;
-      if (above1 < r && r <= above1 + h1) {
-        s.sel_bin = kBins - 2 - 2 * tid;
-        s.above_bin = above1;
-      }
-    }
-    lds_barrier();
+    find_threshold_bin(s, static_cast<uint32_t>(topk));
     const int sel = static_cast<int>(s.sel_bin);
     const uint32_t above_bin = s.above_bin;
     const uint32_t bin_count = s.hist[sel];
     const bool use_cand = bin_count <= kCandCap;
     if (use_cand) {
-      for_each_key<IN_LDS, false>(s, src, L, [&](int, uint32_t k) {
+      for_each_key(src, L, [&](int, uint32_t k) {
         if (bin_of(key_float(k), vmin, inv) == sel) {
           const uint32_t slot = atomicAdd(&s.ncand, 1u);
           if (slot < kCandCap) s.cand[slot] = k;
@@ -234,7 +389,7 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
       });
     }
     lds_barrier();
-    // ---- 4. exact radix select of rank r among the set
+    // ---- 3. exact radix select of rank r among the set
     uint32_t r = use_cand ? static_cast<uint32_t>(topk) - above_bin
                           : static_cast<uint32_t>(topk);
     const int n_set = use_cand ? min(static_cast<int>(s.ncand), kCandCap) : L;
@@ -248,7 +403,7 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
           if ((k & mask) == prefix) atomicAdd(&s.hist[(k >> shift) & 255u], 1u);
         }
       } else {
-        for_each_key<IN_LDS, false>(s, src, L, [&](int, uint32_t k) {
+        for_each_key(src, L, [&](int, uint32_t k) {
           if ((k & mask) == prefix) atomicAdd(&s.hist[(k >> shift) & 255u], 1u);
         });
       }
@@ -267,7 +422,7 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
     c_gt = (use_cand ? above_bin : 0u) + gt_extra;
   }
 
-  // ---- 5. ordered compaction
+  // ---- 4. ordered compaction over contiguous spans per wave
   const uint32_t need = static_cast<uint32_t>(topk) - c_gt;   // >= 1
   const int span = ((L + kWaves - 1) / kWaves + 63) & ~63;
   const int beg = wave * span;
@@ -278,7 +433,7 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int i = base + 64 * j + lane;
-      k[j] = i < end ? row_key<IN_LDS>(s, src, i) : 0u;
+      k[j] = i < end ? float_key(src[i]) : 0u;
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
@@ -303,23 +458,23 @@ __device__ void select_row(Shared& s, const float* __restrict__ src, int L,
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       const int i = base + 64 * j + lane;
-      kb[j] = i < end ? row_key<IN_LDS>(s, src, i) : 0u;
+      kb[j] = i < end ? float_key(src[i]) : 0u;
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-    const int i = base + 64 * j + lane;
-    const uint32_t k = kb[j];
-    const bool gt = i < end && k > T;
-    const bool eq = i < end && k == T;
-    const uint64_t gm = __ballot(gt);
-    const uint64_t em = __ballot(eq);
-    const uint32_t eq_rank = eq_run + __popcll(em & below);
-    const bool take = gt || (eq && eq_rank < need);
-    const uint64_t tm = __ballot(take);
-    const uint32_t o = gt_run + min(eq_run, need) + __popcll(tm & below);
-    if (take && o < static_cast<uint32_t>(topk)) out[o] = i;
-    gt_run += __popcll(gm);
-    eq_run += __popcll(em);
+      const int i = base + 64 * j + lane;
+      const uint32_t k = kb[j];
+      const bool gt = i < end && k > T;
+      const bool eq = i < end && k == T;
+      const uint64_t gm = __ballot(gt);
+      const uint64_t em = __ballot(eq);
+      const uint32_t eq_rank = eq_run + __popcll(em & below);
+      const bool take = gt || (eq && eq_rank < need);
+      const uint64_t tm = __ballot(take);
+      const uint32_t o = gt_run + min(eq_run, need) + __popcll(tm & below);
+      if (take && o < static_cast<uint32_t>(topk)) out[o] = i;
+      gt_run += __popcll(gm);
+      eq_run += __popcll(em);
     }
   }
 }
@@ -339,10 +494,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
     return;
   }
   const float* src = scores + static_cast<int64_t>(t) * row_stride;
-  if (L <= kRowCap)
-    select_row<true>(s, src, L, topk, orow);
+  if (L <= kRegCap)
+    select_row_regs(s, src, L, topk, orow);
   else
-    select_row<false>(s, src, L, topk, orow);
+    select_row_stream(s, src, L, topk, orow);
 }
 
 }  // namespace

@@ -111,7 +111,10 @@ def test_workspace_size_formula():
     dsa = ensure_library()
     lib = dsa.load_library()
     cb = _batch(dsa)
-    assert lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb), 16) == 4 * 128 * 4 + 256 - (4 * 128 * 4) % 256 if (4 * 128 * 4) % 256 else 4 * 128 * 4
+    # fp32 score rows padded to a multiple of 64 positions
+    assert lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb), 16) == 4 * 128 * 4
+    cb100 = _batch(dsa, max_seq_len=100)
+    assert lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb100), 16) == 4 * 128 * 4
     # no split for the vector path, so no MLA workspace
     assert lib.sparse_mla_attn_workspace_size(ctypes.byref(cb), 4, 64, 16, 16, 0) == 0
     # the matrix-core path with few workgroups needs split partials

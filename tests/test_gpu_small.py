@@ -258,6 +258,45 @@ def test_bf16_attention_matrix_core(dsa, n_req, q_len, topk):
         assert attn_close(gl[t], rl[t], 1e-3, 1e-4) <= 0, t
 
 
+def test_attention_with_late_dominant_keys(dsa):
+    """Keys late in a split whose logits beat everything before them by
+    hundreds (in natural-log units), twice in the same split for one head:
+    the probabilities must follow the new maxima exactly.  Each spike row is
+    orthogonal to the queries of every other head of its token, so only the
+    targeted head sees an extreme logit and the comparison stays well
+    conditioned."""
+    cfg = _small_cfg(num_reqs=6, q_len=1, topk=2048)
+    b = make_batch(cfg, DEV, seq_lens=[4000, 3000, 2600, 2100, 5000, 3500],
+                   q_lens=[1] * 6)
+    lay = make_layer(cfg, b, DEV, with_indexer=False)
+    idx = make_random_indices(b, 2048, 4242, DEV)
+    idx_h = idx.cpu().numpy()
+    qm = np_f64(lay.q_mla)                              # [N, 64, 576]
+    # (index-list position, head, natural-log logit): two spikes in the
+    # first split's third and fourth tiles (the second beats the first), one
+    # in a later split
+    spikes = ((70, 5, 300.0), (100, 5, 600.0), (1500, 40, 400.0))
+    for t in range(b.num_q_tokens):
+        phys = OI.physical_slots(b.block_table_host[t], b.block_size, b.seq_lens[t])
+        for j, h, target in spikes:
+            others = np.delete(qm[t], h, axis=0)          # [63, 576]
+            coef, *_ = np.linalg.lstsq(others.T, qm[t, h], rcond=None)
+            perp = qm[t, h] - others.T @ coef             # orthogonal to the others
+            row = perp * (target / cfg.softmax_scale / float(qm[t, h] @ perp))
+            lay.kv_cache[int(phys[int(idx_h[t, j])])] = torch.as_tensor(
+                row, dtype=torch.float32, device=DEV).to(lay.kv_cache.dtype)
+    out, lse = dsa.sparse_mla_attn(_dsa_batch(dsa, b), lay.q_mla, lay.kv_cache, idx,
+                                   cfg.kv_lora_rank, cfg.softmax_scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_mla(b, lay, idx_h, cfg.kv_lora_rank, cfg.softmax_scale)
+    assert np.all(np.isfinite(np_f64(out)))
+    assert attn_close(np_f64(out), ro) <= 0
+    assert attn_close(lse.cpu().numpy(), rl, 1e-3, 1e-4) <= 0
+    # the targeted heads are dominated by their last spike
+    assert np.all(rl[:, 5] > 550) and np.all(rl[:, 40] > 350)
+    assert np.all(np.abs(rl[:, 0]) < 50)
+
+
 def test_attention_first_position_and_empty_rows(dsa):
     cfg = _small_cfg(num_reqs=2, q_len=1, topk=64)
     b = make_batch(cfg, DEV, seq_lens=[1, 300], q_lens=[1, 1])

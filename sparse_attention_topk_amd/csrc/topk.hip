@@ -15,17 +15,18 @@
 // then every position with key > T plus the first topk - c_gt positions with
 // key == T, in position order.
 //
-// Rows of up to 32768 keys stay in registers (thread i holds positions
-// 32 i .. 32 i + 31):
+// Rows of up to 32768 keys stay in registers (each wave holds 2048
+// consecutive positions, loaded 1 KB per instruction):
 //  1. load, value range [vmin, vmax];
 //  2. histogram over 2048 value-linear bins of [vmin, vmax] (the bin map is
 //     monotone in the value, so every key in a higher bin is strictly
 //     larger), LDS atomics; a suffix scan finds the bin holding rank topk;
-//  3. the keys of that bin are gathered; when there are few, each is ranked
-//     against all of them directly, otherwise an exact 4 x 8-bit radix
-//     select over the row runs;
-//  4. ordered compaction: per-thread counts of keys > T and == T, one
-//     workgroup-wide exclusive scan, then every thread writes its positions.
+//  3. one pass marks the positions of every higher bin in an LDS bitmap and
+//     collects the threshold bin's (score, position) pairs; when there are
+//     few they are ranked directly and the top ones marked too, otherwise an
+//     exact 4 x 8-bit radix select over the row finds the threshold score;
+//  4. the bitmap is emitted in position order after one workgroup-wide
+//     scan of its popcounts.
 // Longer rows stream from memory in every pass (same steps, radix select
 // over candidates or the row, compaction by waves over contiguous spans).
 #include "common.h"
@@ -39,7 +40,7 @@ constexpr int kBins = 2048;
 constexpr int kKpt = 32;                       // keys per thread, register path
 constexpr int kRegCap = kThreads * kKpt;       // 32768
 constexpr int kCandCap = 4096;
-constexpr int kRankCap = 256;                  // candidates ranked directly
+constexpr int kRankCap = 256;                  // threshold-bin keys ranked directly
 
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t b = __float_as_uint(f);
@@ -53,6 +54,8 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 struct Shared {
   uint32_t hist[kBins];
   uint32_t cand[kCandCap];
+  uint32_t bm_sel[kRegCap / 32];   // register path: selected positions
+  uint32_t bm_eq[kRegCap / 32];    // register path: positions scoring == T
   uint32_t wave_a[kWaves];
   uint32_t wave_b[kWaves];
   float red_min[kWaves];
@@ -62,8 +65,6 @@ struct Shared {
   uint32_t above_bin;     // keys in bins above it
   uint32_t digit;         // radix step result
   uint32_t digit_above;
-  uint32_t thr;           // threshold key
-  uint32_t thr_above;     // keys above it within the candidate set
   uint32_t counter;
 };
 
@@ -75,7 +76,7 @@ __device__ __forceinline__ uint64_t lanes_below() {
 // Suffix scan helper: for a 256-bin histogram find digit d with
 // above(d) < r <= above(d) + h[d] (above = sum of higher bins).  Wave 0
 // scans; results land in s.digit / s.digit_above.
-__device__ void find_digit(Shared& s, uint32_t r) {
+__device__ __forceinline__ void find_digit(Shared& s, uint32_t r) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     // lane owns digits 255 - 4*lane - i, i = 0..3 (top-down)
@@ -168,81 +169,95 @@ __device__ __forceinline__ void find_threshold_bin(Shared& s, uint32_t r) {
   lds_barrier();
 }
 
-// Exact rank-r (from the top) key among the n <= kRankCap candidates in
-// s.cand: thread i < n counts the candidates above and at-or-above its own;
-// the thread(s) with above < r <= at-or-above hold the answer (equal keys
-// write equal values).  Result in s.thr / s.thr_above; ends with a barrier.
-__device__ __forceinline__ void rank_candidates(Shared& s, int n, uint32_t r) {
-  const int tid = threadIdx.x;
-  if (tid < n) {
-    const uint32_t mine = s.cand[tid];
-    uint32_t gt = 0, ge = 0;
-    for (int j = 0; j < n; ++j) {
-      const uint32_t o = s.cand[j];
-      gt += o > mine;
-      ge += o >= mine;
-    }
-    if (gt < r && r <= ge) {
-      s.thr = mine;
-      s.thr_above = gt;
-    }
-  }
-  lds_barrier();
+// ------------------------------------------------------------ register path
+// Position of register key (j, e) of a lane: wave w covers positions
+// 2048 w .. 2048 w + 2047, its load j (0..7) the 256 positions from
+// 2048 w + 256 j, lane l the 4 positions from there + 4 l.  Every load
+// instruction reads 1 KB contiguous.
+__device__ __forceinline__ int reg_pos(int wave, int lane, int j, int e) {
+  return 2048 * wave + 256 * j + 4 * lane + e;
 }
 
-// ------------------------------------------------------------ register path
-__device__ void select_row_regs(Shared& s, const float* __restrict__ src, int L,
-                                int topk, int32_t* __restrict__ out) {
+// Loads the first min(row_stride, 32768) scores of the row (the positions
+// any register-path row can hold); issued before the row's length is known.
+// Rows are padded to a multiple of 64 floats, so a float4 never straddles
+// the end of the allocation.
+__device__ __forceinline__ void load_row_regs(const float* __restrict__ src,
+                                              int64_t row_stride, float (&f)[kKpt]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < kKpt / 4; ++j) {
+    const int p = reg_pos(wave, lane, j, 0);
+    const float4 v = p < row_stride ? *reinterpret_cast<const float4*>(src + p)
+                                    : float4{0.f, 0.f, 0.f, 0.f};
+    f[4 * j + 0] = v.x;
+    f[4 * j + 1] = v.y;
+    f[4 * j + 2] = v.z;
+    f[4 * j + 3] = v.w;
+  }
+}
+
+// Register path.  Scores are compared as floats: -0.0 == +0.0 as the tie
+// rule needs, and the float order is the key order for the finite scores
+// this path handles.  Absent positions (>= L) hold NaN, which min / max
+// skip, every comparison rejects and the bin map sends to bin 0; the bin
+// counts below correct for them.  The selection is recorded in a bitmap of
+// positions (bit p & 31 of word p >> 5), emitted in position order at the
+// end.
+__device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int L,
+                                                int topk, int32_t* __restrict__ out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int p0 = kKpt * tid;
+  // register key (j, e) is position 2048 wave + 256 j + 4 lane + e: word
+  // 64 wave + 8 j + lane / 8, bit 4 (lane % 8) + e
+  auto word_of = [&](int j) { return 64 * wave + 8 * j + (lane >> 3); };
+  auto bit_of = [&](int e) { return 1u << (4 * (lane & 7) + e); };
 
-  // ---- 1. load: 32 consecutive positions per thread (absent ones -> key 0,
-  // below every real key, and excluded from the range and the histogram).
-  // Rows start 16-byte aligned (the score rows are padded to 64 floats).
-  uint32_t k[kKpt];
-  if (p0 + kKpt <= L) {
-    const float4* v4 = reinterpret_cast<const float4*>(src + p0);
-    float4 v[kKpt / 4];
+  // ---- 1. range
+  if (reg_pos(wave, lane, kKpt / 4 - 1, 3) >= L) {
 #pragma unroll
-    for (int j = 0; j < kKpt / 4; ++j) v[j] = v4[j];
+    for (int j = 0; j < kKpt / 4; ++j)
 #pragma unroll
-    for (int j = 0; j < kKpt / 4; ++j) {
-      k[4 * j + 0] = float_key(v[j].x);
-      k[4 * j + 1] = float_key(v[j].y);
-      k[4 * j + 2] = float_key(v[j].z);
-      k[4 * j + 3] = float_key(v[j].w);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kKpt; ++j) k[j] = p0 + j < L ? float_key(src[p0 + j]) : 0u;
+      for (int e = 0; e < 4; ++e)
+        if (reg_pos(wave, lane, j, e) >= L) f[4 * j + e] = __builtin_nanf("");
   }
-  const int nmine = max(0, min(kKpt, L - p0));
-  float vmin = INFINITY, vmax = -INFINITY;
+  const uint32_t absent = static_cast<uint32_t>(kRegCap - L);   // NaNs in bin 0
+  float vmin = f[0], vmax = f[0];
 #pragma unroll
-  for (int j = 0; j < kKpt; ++j) {
-    if (j < nmine) {
-      const float f = key_float(k[j]);
-      vmin = fminf(vmin, f);
-      vmax = fmaxf(vmax, f);
-    }
+  for (int j = 1; j < kKpt; ++j) {
+    vmin = fminf(vmin, f[j]);
+    vmax = fmaxf(vmax, f[j]);
   }
   for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
+  s.bm_sel[tid] = 0;
+  s.bm_eq[tid] = 0;
   if (tid == 0) s.ncand = 0;
   range_reduce(s, vmin, vmax);
 
-  uint32_t T, c_gt;
+  uint32_t need = 0;          // positions still to take among those == T
   if (!(vmax > vmin)) {
-    // every key is equal: positions decide
-    T = float_key(vmax);
-    c_gt = 0;
-  } else {
-    // ---- 2. histogram and threshold bin
-    const float inv = static_cast<float>(kBins) / (vmax - vmin);
+    // every score is equal: the first topk positions
+    need = static_cast<uint32_t>(topk);
 #pragma unroll
-    for (int j = 0; j < kKpt; ++j)
-      if (j < nmine) atomicAdd(&s.hist[bin_of(key_float(k[j]), vmin, inv)], 1u);
+    for (int j = 0; j < kKpt / 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (f[4 * j + e] == vmax) atomicOr(&s.bm_eq[word_of(j)], bit_of(e));
+  } else {
+    // ---- 2. histogram and threshold bin: bin = trunc(clamp(f * inv - vmin *
+    // inv, 0, 2047)), monotone in f; NaN lands in bin 0
+    const float inv = static_cast<float>(kBins) / (vmax - vmin);
+    const float off = -vmin * inv;
+    // fmaxf maps NaN to 0 (IEEE maxNum), so the conversion is always defined
+    auto bin = [&](float x) {
+      return static_cast<int>(fminf(fmaxf(fmaf(x, inv, off), 0.0f), kBins - 1.0f));
+    };
+#pragma unroll
+    for (int j = 0; j < kKpt; ++j) atomicAdd(&s.hist[bin(f[j])], 1u);
+    lds_barrier();
+    if (tid == kThreads - 1) s.hist[0] -= absent;
     lds_barrier();
     find_threshold_bin(s, static_cast<uint32_t>(topk));
     const int sel = static_cast<int>(s.sel_bin);
@@ -251,30 +266,81 @@ __device__ void select_row_regs(Shared& s, const float* __restrict__ src, int L,
     const uint32_t r = static_cast<uint32_t>(topk) - above_bin;
 
     if (bin_count <= static_cast<uint32_t>(kRankCap)) {
-      // ---- 3a. gather the bin's keys, rank them directly
+      // ---- 3a. one pass: keys of higher bins are taken, keys of the
+      // threshold bin become (score, position) candidates.  With t the same
+      // fma as in the bin map, bin > sel <=> t >= sel + 1 (sel < 2047) and
+      // bin >= sel <=> t >= sel (sel >= 1); for sel == 0 every non-NaN key
+      // has bin >= sel, which t >= -inf expresses.  NaN fails every test.
+      // Flags are collected branch-free; the rare candidates are appended
+      // after the pass.
+      const float thr_above = sel == kBins - 1 ? INFINITY : static_cast<float>(sel + 1);
+      const float thr_in = sel == 0 ? -INFINITY : static_cast<float>(sel);
+      // same values; the compiler is kept from holding the histogram pass's
+      // 32 products in registers until here
+      float inv2 = inv, off2 = off;
+      asm volatile("" : "+v"(inv2), "+v"(off2));
+      uint32_t cand_bits = 0;          // bit 4 j + e
 #pragma unroll
-      for (int j = 0; j < kKpt; ++j) {
-        if (j < nmine && bin_of(key_float(k[j]), vmin, inv) == sel) {
-          const uint32_t slot = atomicAdd(&s.ncand, 1u);
-          s.cand[slot] = k[j];
+      for (int j = 0; j < kKpt / 4; ++j) {
+        uint32_t take = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float t = fmaf(f[4 * j + e], inv2, off2);
+          take |= t >= thr_above ? bit_of(e) : 0u;
+          cand_bits |= (t >= thr_in && t < thr_above) ? (1u << (4 * j + e)) : 0u;
+        }
+        if (take) atomicOr(&s.bm_sel[word_of(j)], take);
+      }
+      float* cval = reinterpret_cast<float*>(s.cand);
+      int32_t* cpos = reinterpret_cast<int32_t*>(s.cand + kRankCap);
+      if (cand_bits) {
+#pragma unroll
+        for (int q = 0; q < kKpt; ++q) {
+          if ((cand_bits >> q) & 1u) {
+            const uint32_t slot = atomicAdd(&s.ncand, 1u);
+            cval[slot] = f[q];
+            cpos[slot] = reg_pos(wave, lane, q >> 2, q & 3);
+          }
         }
       }
       lds_barrier();
-      rank_candidates(s, static_cast<int>(bin_count), r);
-      T = s.thr;
-      c_gt = above_bin + s.thr_above;
+      // ---- rank the candidates by (score descending, position ascending);
+      // the top r join the selection
+      const int n = static_cast<int>(bin_count);
+      if (tid < n) {
+        const float mv = cval[tid];
+        const int32_t mp = cpos[tid];
+        uint32_t rank = 0;
+        for (int j0 = 0; j0 < n; j0 += 8) {
+          float ov[8];
+          int32_t op[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            ov[u] = cval[j0 + u];
+            op[u] = cpos[j0 + u];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            rank += (j0 + u < n) && (ov[u] > mv || (ov[u] == mv && op[u] < mp));
+        }
+        if (rank < r) atomicOr(&s.bm_sel[mp >> 5], 1u << (mp & 31));
+      }
     } else {
-      // ---- 3b. exact radix select of rank topk over the row
+      // ---- 3b. exact radix select of rank topk over the row's keys gives
+      // the threshold score T and the count above it
+      const int tid2 = tid;
       uint32_t rr = static_cast<uint32_t>(topk);
       uint32_t prefix = 0, mask = 0, gt_extra = 0;
       for (int shift = 24; shift >= 0; shift -= 8) {
         lds_barrier();
-        for (int i = tid; i < 256; i += kThreads) s.hist[i] = 0;
+        for (int i = tid2; i < 256; i += kThreads) s.hist[i] = 0;
         lds_barrier();
 #pragma unroll
-        for (int j = 0; j < kKpt; ++j)
-          if (j < nmine && (k[j] & mask) == prefix)
-            atomicAdd(&s.hist[(k[j] >> shift) & 255u], 1u);
+        for (int j = 0; j < kKpt; ++j) {
+          const uint32_t kk = float_key(f[j]);
+          if (f[j] == f[j] && (kk & mask) == prefix)
+            atomicAdd(&s.hist[(kk >> shift) & 255u], 1u);
+        }
         lds_barrier();
         find_digit(s, rr);
         lds_barrier();
@@ -285,40 +351,57 @@ __device__ void select_row_regs(Shared& s, const float* __restrict__ src, int L,
         prefix |= d << shift;
         mask |= 255u << shift;
       }
-      T = prefix;
-      c_gt = gt_extra;
+      const float T = key_float(prefix);
+      need = static_cast<uint32_t>(topk) - gt_extra;   // >= 1
+#pragma unroll
+      for (int j = 0; j < kKpt / 4; ++j) {
+        uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (f[4 * j + e] > T) gtm |= bit_of(e);
+          if (f[4 * j + e] == T) eqm |= bit_of(e);
+        }
+        if (gtm) atomicOr(&s.bm_sel[word_of(j)], gtm);
+        if (eqm) atomicOr(&s.bm_eq[word_of(j)], eqm);
+      }
     }
   }
+  lds_barrier();
 
-  // ---- 4. ordered compaction: (gt, eq) counts packed 16:16 (each <= 32768)
-  uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int j = 0; j < kKpt; ++j) {
-    n_gt += k[j] > T;
-    n_eq += k[j] == T;          // absent keys are 0 < T
-  }
-  const uint32_t packed = (n_gt << 16) | n_eq;
+  // ---- 4. emission in position order: thread tid owns word tid (positions
+  // 32 tid .. 32 tid + 31).  Counts of taken bits and of == T bits (packed
+  // 16:16, totals <= 32768) are scanned across the workgroup; the first
+  // `need` positions scoring == T join the taken ones.
+  uint32_t w_sel = s.bm_sel[tid];
+  const uint32_t w_eq = s.bm_eq[tid];
+  const uint32_t packed = (static_cast<uint32_t>(__popc(w_sel)) << 16) |
+                          static_cast<uint32_t>(__popc(w_eq));
   uint32_t incl = packed;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
   }
   if (lane == 63) s.wave_b[wave] = incl;
   lds_barrier();
   uint32_t base = 0;
   for (int wv = 0; wv < wave; ++wv) base += s.wave_b[wv];
   const uint32_t excl = base + incl - packed;
-  const uint32_t need = static_cast<uint32_t>(topk) - c_gt;   // >= 1
-  uint32_t eq_before = excl & 0xFFFFu;
+  const uint32_t eq_before = excl & 0xFFFFu;
   uint32_t o = (excl >> 16) + min(eq_before, need);
-#pragma unroll
-  for (int j = 0; j < kKpt; ++j) {
-    const bool gt = k[j] > T;
-    const bool eq = k[j] == T;
-    const bool take = gt || (eq && eq_before < need);
-    if (take) out[o++] = p0 + j;
-    eq_before += eq;
+  if (w_eq && eq_before < need) {
+    // the lowest (need - eq_before) bits of w_eq
+    uint32_t m = w_eq;
+    for (uint32_t c = need - eq_before; m && c; --c) {
+      const uint32_t low = m & (0u - m);
+      w_sel |= low;
+      m ^= low;
+    }
+  }
+  while (w_sel) {
+    const int b = __builtin_ctz(w_sel);
+    out[o++] = 32 * tid + b;
+    w_sel &= w_sel - 1;
   }
 }
 
@@ -346,7 +429,7 @@ __device__ __forceinline__ void for_each_key(const float* __restrict__ src,
   }
 }
 
-__device__ void select_row_stream(Shared& s, const float* __restrict__ src, int L,
+__device__ __forceinline__ void select_row_stream(Shared& s, const float* __restrict__ src, int L,
                                   int topk, int32_t* __restrict__ out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -485,6 +568,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
     int32_t B, int32_t max_seq_len, int32_t topk, int32_t* __restrict__ out) {
   __shared__ Shared s;
   const int t = blockIdx.x;
+  const float* src = scores + static_cast<int64_t>(t) * row_stride;
+  // the row's first 32768 scores are requested before its length is known
+  float f[kKpt];
+  load_row_regs(src, row_stride, f);
   const int b = request_of_block(cu_q, B, t, &s.counter);
   const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
   const int L = pos + 1;
@@ -493,9 +580,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
     for (int j = threadIdx.x; j < topk; j += kThreads) orow[j] = j < L ? j : -1;
     return;
   }
-  const float* src = scores + static_cast<int64_t>(t) * row_stride;
   if (L <= kRegCap)
-    select_row_regs(s, src, L, topk, orow);
+    select_row_regs(s, f, L, topk, orow);
   else
     select_row_stream(s, src, L, topk, orow);
 }

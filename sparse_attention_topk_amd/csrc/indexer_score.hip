@@ -24,6 +24,8 @@
 //
 // Vector path: any dtype / shape within the documented limits, one thread
 // per (query token, key), fp32 arithmetic.
+#include <utility>
+
 #include "common.h"
 
 namespace dsa {
@@ -214,6 +216,254 @@ __global__ __launch_bounds__(256, (TQ * MT > 2) ? 1 : 2) void k_score_mfma(
   }
 }
 
+// ------------------------------------------------- bf16 keys through LDS
+// Same contraction, but the keys reach LDS by DMA (global_load_lds_dwordx4)
+// in whole 1 KB lines: one wave instruction carries 4 consecutive 256-byte
+// rows.  Each wave streams its own tiles through a private ring of kRing
+// 8 KB buffers (kRing - 1 tiles in flight), so no barrier is ever needed;
+// the MFMA key operand is read back with ds_read_b128.  Lane l of DMA
+// instruction m lands at byte 16 l of block m and carries row
+// 4 m + l / 16, piece (l % 16) ^ (row % 16): piece p of row r sits at
+// 16-byte slot p ^ (r % 16) of the row, which spreads the 32 rows of one
+// operand load over distinct banks (32 and 64 banks alike).
+constexpr int kRing = 4;
+constexpr int kTileBytes = kTile * 256;          // 32 keys x 128 bf16
+
+// f(integral_constant<int, I>) for I = 0 .. N-1 (indices usable as
+// constants, e.g. for register arrays)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_b128(uint32_t addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int N, typename T>
+__device__ __forceinline__ void lgkm_keep(T& r) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "n"(N));
+}
+// s_waitcnt on the vector-memory count only (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int TQ, int MT>
+__global__ __launch_bounds__(256, 1) void k_score_dma(
+    const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint8_t* __restrict__ kc, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ block_table,
+    int32_t max_blocks, int32_t block_size, int64_t num_slots,
+    int32_t max_seq_len, int32_t qblocks_per_req, int32_t nchunks,
+    int32_t tiles_per_wave, float* __restrict__ scores, int64_t row_stride) {
+  constexpr int H = 32 * MT;
+  __shared__ __align__(16) uint8_t ring[kWaves][kRing][kTileBytes];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hf = lane >> 5;
+  const int col = lane & 31;
+
+  const int chunk = blockIdx.x % nchunks;
+  const int qbg = blockIdx.x / nchunks;
+  const int b = qbg / qblocks_per_req;
+  const int qb = qbg % qblocks_per_req;
+
+  const int32_t L = min(seq_lens[b], max_seq_len);
+  const int32_t tbeg = cu_q[b];
+  const int32_t qlen = min(cu_q[b + 1] - tbeg, L);
+  const int32_t t0 = qb * TQ;
+  if (t0 >= qlen) return;
+  const int nt = min(TQ, qlen - t0);
+  const int32_t pos0 = L - qlen + t0;
+  const int32_t chunk_keys = kTile * kWaves * tiles_per_wave;
+  const int32_t key_end = min(pos0 + nt, (chunk + 1) * chunk_keys);
+  const int32_t key_beg = chunk * chunk_keys;
+  if (key_beg >= key_end) return;
+  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
+
+  // query operand (head 32 mt + col, dims 16 s + 8 hf) and head weights
+  // (accumulator register r of a 32x32 tile holds head 8 (r / 4) + 4 hf +
+  // r % 4 of column col: four runs of 4 consecutive heads); issued before
+  // any tile DMA, so waiting for them never waits for a tile
+  bf16x8 qa[TQ][MT][8];
+  float wr[TQ][MT][16];
+#pragma unroll
+  for (int tt = 0; tt < TQ; ++tt) {
+    const bool live = tt < nt;
+    const int64_t tok = tbeg + t0 + (live ? tt : 0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint16_t* qrow = q + (tok * H + mt * 32 + col) * 128;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        qa[tt][mt][s] = live ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hf)
+                             : bf16x8{};
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 w4 = live ? *reinterpret_cast<const float4*>(
+                                     w + tok * H + mt * 32 + 8 * g + 4 * hf)
+                               : float4{0.f, 0.f, 0.f, 0.f};
+        wr[tt][mt][4 * g + 0] = w4.x;
+        wr[tt][mt][4 * g + 1] = w4.y;
+        wr[tt][mt][4 * g + 2] = w4.z;
+        wr[tt][mt][4 * g + 3] = w4.w;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+
+  // The wave's tiles are first_tile + kWaves i, i < ntiles.  A 32-key tile
+  // never spans two cache blocks, so one block-table entry (a wave-uniform
+  // scalar load, issued a tile ahead of its use) gives the whole tile.
+  const int first_tile = key_beg / kTile + wave;
+  const int end_tile = (key_end + kTile - 1) / kTile;
+  const int ntiles = end_tile > first_tile
+                         ? min(tiles_per_wave, (end_tile - first_tile + kWaves - 1) / kWaves)
+                         : 0;
+  auto tile_row0 = [&](int i) -> int64_t {     // slot of the tile's first key, or -1
+    const int32_t s0 = (first_tile + kWaves * i) * kTile;
+    const int32_t blk = s0 / block_size;
+    if (i >= ntiles || blk >= max_blocks) return -1;
+    const int64_t slot0 = static_cast<int64_t>(bt_row[blk]) * block_size + s0 % block_size;
+    return (slot0 >= 0 && slot0 + kTile <= num_slots) ? slot0 : -1;
+  };
+
+  // DMA geometry of this lane: row 4 m + lane / 16, slot lane % 16
+  const int drow = lane >> 4;
+  const int dslot = lane & 15;
+  auto dma = [&](int slot, int64_t row0) {
+    uint8_t* buf = &ring[wave][slot][0];
+    const int64_t base = row0 < 0 ? 0 : row0;
+#pragma unroll
+    for (int m = 0; m < kTile / 4; ++m) {
+      const int row = 4 * m + drow;
+      const int piece = dslot ^ (row & 15);
+      const uint8_t* src = kc + (base + row) * 256 + 16 * piece;
+      __builtin_amdgcn_global_load_lds(
+          src, (__attribute__((address_space(3))) void*)(buf + 1024 * m), 16, 0, 0);
+    }
+  };
+  // r0[m & 3] holds tile m's first slot from one tile before its DMA
+  int64_t r0[kRing];
+  static_for<kRing>([&](auto jc) { r0[decltype(jc)::value] = tile_row0(decltype(jc)::value); });
+  static_for<kRing - 1>([&](auto jc) {
+    constexpr int j = decltype(jc)::value;
+    if (j < ntiles) dma(j, r0[j]);
+  });
+
+  // The query and weight registers are re-defined by an empty asm once
+  // their loads are in: the compiler's wait tracking then no longer ties
+  // the MFMAs of every tile to outstanding vector-memory operations (it
+  // would otherwise wait for all tile DMAs in flight before each tile).
+#pragma unroll
+  for (int tt = 0; tt < TQ; ++tt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(qa[tt][mt][st]));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[tt][mt][r]));
+    }
+
+  // key operand of this lane: row col, piece 2 s + hf at 16-byte slot
+  // (2 s + hf) ^ (col % 16)
+  const uint32_t rbase = static_cast<uint32_t>(col) * 256u;
+  const int csw = col & 15;
+  for (int i0 = 0; i0 < ntiles; i0 += kRing) {
+    static_for<kRing>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;   // ring slot of tile i
+      const int i = i0 + j;
+      if (i >= ntiles) return;
+      if (i + kRing - 1 < ntiles) dma((j + kRing - 1) % kRing, r0[(j + kRing - 1) % kRing]);
+      const int64_t my_r0 = r0[j];
+      r0[j] = tile_row0(i + kRing);
+      // tile i landed when at most the later tiles' loads (and possibly
+      // one score store) are pending; counting the store too only waits
+      // longer
+      const int later = min(ntiles - 1 - i, kRing - 1);
+      if (later >= 3) wait_vm<24>();
+      else if (later == 2) wait_vm<16>();
+      else if (later == 1) wait_vm<8>();
+      else wait_vm<0>();
+      const uint32_t tb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+          (__attribute__((address_space(3))) uint8_t*)(&ring[wave][j][0]))) + rbase;
+      bf16x8 kv[8];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      static_for<8>([&](auto sc) {
+        constexpr int st = decltype(sc)::value;
+        kv[st] = lds_b128<0>(tb + 16u * static_cast<uint32_t>((2 * st + hf) ^ csw));
+      });
+      float part[TQ];
+#pragma unroll
+      for (int tt = 0; tt < TQ; ++tt) part[tt] = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x16 acc[TQ];
+#pragma unroll
+        for (int tt = 0; tt < TQ; ++tt) acc[tt] = f32x16{};
+        static_for<8>([&](auto sc) {
+          constexpr int st = decltype(sc)::value;
+          if (mt == 0) lgkm_keep<7 - st>(kv[st]);
+#pragma unroll
+          for (int tt = 0; tt < TQ; ++tt)
+            acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[tt][mt][st], kv[st],
+                                                              acc[tt], 0, 0, 0);
+        });
+#pragma unroll
+        for (int tt = 0; tt < TQ; ++tt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            part[tt] = fmaf(wr[tt][mt][r], fmaxf(acc[tt][r], 0.0f), part[tt]);
+      }
+#pragma unroll
+      for (int tt = 0; tt < TQ; ++tt) part[tt] += __shfl_xor(part[tt], 32);
+      const int32_t s = (first_tile + kWaves * i) * kTile + col;
+      // lane half hf stores token hf's score for key s (0 when the tile
+      // has no cache row)
+      if (hf < nt) {
+        const int32_t pos = pos0 + hf;
+        float v = part[0];
+        if constexpr (TQ > 1) v = hf ? part[1] : part[0];
+        if (my_r0 < 0) v = 0.0f;
+        if (s <= pos && s < key_end)
+          scores[(tbeg + t0 + hf) * row_stride + s] = v;
+      }
+    });
+  }
+}
+
+template <int TQ, int MT>
+hipError_t launch_dma(const IndexerArgs& a, hipStream_t stream) {
+  const dsa_batch& b = a.b;
+  const int qbpr = (b.max_q_len + TQ - 1) / TQ;
+  // one round of workgroups: about 256 of them (one per CU) share the
+  // longest request, each wave taking a multiple of kRing tiles
+  const int64_t groups = static_cast<int64_t>(b.num_reqs) * qbpr;
+  const int64_t tiles_total = (b.max_seq_len + kTile - 1) / kTile;
+  int64_t want = groups >= 256 ? 1 : (256 + groups - 1) / groups;     // chunks per request
+  int64_t tpw = (tiles_total + want * kWaves - 1) / (want * kWaves);  // tiles per wave
+  tpw = (tpw + kRing - 1) / kRing * kRing;
+  if (tpw < kRing) tpw = kRing;
+  const int nchunks = static_cast<int>((tiles_total + tpw * kWaves - 1) / (tpw * kWaves));
+  const int64_t grid = groups * nchunks;
+  if (grid == 0) return hipSuccess;
+  k_score_dma<TQ, MT><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
+      static_cast<const uint16_t*>(a.q), a.w,
+      static_cast<const uint8_t*>(a.k_cache), b.seq_lens, b.cu_q,
+      b.block_table, b.max_blocks, b.block_size, b.num_slots, b.max_seq_len,
+      qbpr, nchunks, static_cast<int32_t>(tpw), a.scores, a.row_stride);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- vector path
 __device__ __forceinline__ float ld(const void* p, int64_t i, int dt) {
   if (dt == DSA_F32) return static_cast<const float*>(p)[i];
@@ -289,12 +539,12 @@ hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t stream) {
     const bool fp8 = a.cache_dtype == DSA_FP8_E4M3;
     const bool one = b.max_q_len == 1;
     const bool mt2 = a.n_heads == 64;
-    if (one) {
-      if (mt2) return fp8 ? launch_mfma<1, 2, true>(a, stream) : launch_mfma<1, 2, false>(a, stream);
-      return fp8 ? launch_mfma<1, 1, true>(a, stream) : launch_mfma<1, 1, false>(a, stream);
+    if (!fp8) {
+      if (one) return mt2 ? launch_dma<1, 2>(a, stream) : launch_dma<1, 1>(a, stream);
+      return mt2 ? launch_dma<2, 2>(a, stream) : launch_dma<2, 1>(a, stream);
     }
-    if (mt2) return fp8 ? launch_mfma<2, 2, true>(a, stream) : launch_mfma<2, 2, false>(a, stream);
-    return fp8 ? launch_mfma<2, 1, true>(a, stream) : launch_mfma<2, 1, false>(a, stream);
+    if (one) return mt2 ? launch_mfma<1, 2, true>(a, stream) : launch_mfma<1, 1, true>(a, stream);
+    return mt2 ? launch_mfma<2, 2, true>(a, stream) : launch_mfma<2, 1, true>(a, stream);
   }
   const int key_blocks = (b.max_seq_len + 255) / 256;
   const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * key_blocks;

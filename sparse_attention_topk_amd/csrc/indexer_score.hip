@@ -226,7 +226,9 @@ __global__ __launch_bounds__(256, (TQ * MT > 2) ? 1 : 2) void k_score_mfma(
 // 4 m + l / 16, piece (l % 16) ^ (row % 16): piece p of row r sits at
 // 16-byte slot p ^ (r % 16) of the row, which spreads the 32 rows of one
 // operand load over distinct banks (32 and 64 banks alike).
-constexpr int kRing = 4;
+constexpr int kRing = 3;
+static_assert(kRing >= 2 && kRing <= 4, "tile waits cover rings of 2 to 4 tiles");
+constexpr int kMaxTpw = 64;                      // tiles per wave (one block id per lane)
 constexpr int kTileBytes = kTile * 256;          // 32 keys x 128 bf16
 
 // f(integral_constant<int, I>) for I = 0 .. N-1 (indices usable as
@@ -256,6 +258,16 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
+// s_waitcnt vmcnt(8 later): a tile is 8 DMA instructions, so the tile
+// issued `later` tiles before the newest one has landed
+__device__ __forceinline__ void wait_tile(int later) {
+  switch (later) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<8>(); break;
+    case 2: wait_vm<16>(); break;
+    default: wait_vm<24>(); break;
+  }
+}
 
 template <int TQ, int MT>
 __global__ __launch_bounds__(256, 1) void k_score_dma(
@@ -267,6 +279,9 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
     int32_t tiles_per_wave, float* __restrict__ scores, int64_t row_stride) {
   constexpr int H = 32 * MT;
   __shared__ __align__(16) uint8_t ring[kWaves][kRing][kTileBytes];
+  // the workgroup's scores, [token][key within chunk], written out at the
+  // end: score stores interleaved with the key stream slow the reads down
+  __shared__ __align__(16) float sc[TQ][kWaves * kMaxTpw * kTile];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5;
@@ -321,20 +336,28 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
   }
   asm volatile("" ::: "memory");
 
-  // The wave's tiles are first_tile + kWaves i, i < ntiles.  A 32-key tile
-  // never spans two cache blocks, so one block-table entry (a wave-uniform
-  // scalar load, issued a tile ahead of its use) gives the whole tile.
+  // The wave's tiles are first_tile + kWaves i, i < ntiles (<= 64).  A
+  // 32-key tile never spans two cache blocks, so one block-table entry
+  // gives the whole tile.  Lane i fetches tile i's entry once, with a vector
+  // load; each tile then takes it with v_readlane, so the tile loop issues
+  // no scalar memory loads (a scalar load could only be waited for together
+  // with every outstanding LDS read).
   const int first_tile = key_beg / kTile + wave;
   const int end_tile = (key_end + kTile - 1) / kTile;
   const int ntiles = end_tile > first_tile
                          ? min(tiles_per_wave, (end_tile - first_tile + kWaves - 1) / kWaves)
                          : 0;
+  int32_t bid_lane = -1;
+  {
+    const int32_t blk = (first_tile + kWaves * lane) * kTile / block_size;
+    if (lane < ntiles && blk < max_blocks) bid_lane = bt_row[blk];
+  }
   auto tile_row0 = [&](int i) -> int64_t {     // slot of the tile's first key, or -1
+    if (i >= ntiles) return -1;
     const int32_t s0 = (first_tile + kWaves * i) * kTile;
-    const int32_t blk = s0 / block_size;
-    if (i >= ntiles || blk >= max_blocks) return -1;
-    const int64_t slot0 = static_cast<int64_t>(bt_row[blk]) * block_size + s0 % block_size;
-    return (slot0 >= 0 && slot0 + kTile <= num_slots) ? slot0 : -1;
+    const int32_t bid = __builtin_amdgcn_readlane(bid_lane, i);
+    const int64_t slot0 = static_cast<int64_t>(bid) * block_size + s0 % block_size;
+    return (bid >= 0 && s0 / block_size < max_blocks && slot0 + kTile <= num_slots) ? slot0 : -1;
   };
 
   // DMA geometry of this lane: row 4 m + lane / 16, slot lane % 16
@@ -373,6 +396,7 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
 #pragma unroll
       for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[tt][mt][r]));
     }
+  asm volatile("" : "+v"(bid_lane));
 
   // key operand of this lane: row col, piece 2 s + hf at 16-byte slot
   // (2 s + hf) ^ (col % 16)
@@ -386,14 +410,9 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
       if (i + kRing - 1 < ntiles) dma((j + kRing - 1) % kRing, r0[(j + kRing - 1) % kRing]);
       const int64_t my_r0 = r0[j];
       r0[j] = tile_row0(i + kRing);
-      // tile i landed when at most the later tiles' loads (and possibly
-      // one score store) are pending; counting the store too only waits
-      // longer
+      // tile i landed when at most the later tiles' DMAs are pending
       const int later = min(ntiles - 1 - i, kRing - 1);
-      if (later >= 3) wait_vm<24>();
-      else if (later == 2) wait_vm<16>();
-      else if (later == 1) wait_vm<8>();
-      else wait_vm<0>();
+      wait_tile(later);
       const uint32_t tb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
           (__attribute__((address_space(3))) uint8_t*)(&ring[wave][j][0]))) + rbase;
       bf16x8 kv[8];
@@ -426,18 +445,26 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
       }
 #pragma unroll
       for (int tt = 0; tt < TQ; ++tt) part[tt] += __shfl_xor(part[tt], 32);
-      const int32_t s = (first_tile + kWaves * i) * kTile + col;
-      // lane half hf stores token hf's score for key s (0 when the tile
-      // has no cache row)
-      if (hf < nt) {
-        const int32_t pos = pos0 + hf;
-        float v = part[0];
-        if constexpr (TQ > 1) v = hf ? part[1] : part[0];
-        if (my_r0 < 0) v = 0.0f;
-        if (s <= pos && s < key_end)
-          scores[(tbeg + t0 + hf) * row_stride + s] = v;
-      }
+      // lane half hf keeps token hf's score for key
+      // (first_tile + kWaves i) * kTile + col (0 when the tile has no row)
+      float v = part[0];
+      if constexpr (TQ > 1) v = hf ? part[1] : part[0];
+      if (my_r0 < 0) v = 0.0f;
+      if (hf < TQ) sc[hf < TQ ? hf : 0][(kWaves * i + wave) * kTile + col] = v;
     });
+  }
+
+  // ---- write the chunk's scores: token tt, keys key_beg .. key_end - 1
+  // (up to the next multiple of 4, inside the padded row), 16 bytes per
+  // thread and instruction
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const int n4 = (key_end - key_beg + 3) / 4;
+#pragma unroll
+  for (int tt = 0; tt < TQ; ++tt) {
+    if (tt >= nt) break;
+    float* row = scores + (tbeg + t0 + tt) * row_stride + key_beg;
+    for (int c = threadIdx.x; c < n4; c += 256)
+      reinterpret_cast<float4*>(row)[c] = reinterpret_cast<const float4*>(&sc[tt][0])[c];
   }
 }
 
@@ -446,13 +473,13 @@ hipError_t launch_dma(const IndexerArgs& a, hipStream_t stream) {
   const dsa_batch& b = a.b;
   const int qbpr = (b.max_q_len + TQ - 1) / TQ;
   // one round of workgroups: about 256 of them (one per CU) share the
-  // longest request, each wave taking a multiple of kRing tiles
+  // longest request
   const int64_t groups = static_cast<int64_t>(b.num_reqs) * qbpr;
   const int64_t tiles_total = (b.max_seq_len + kTile - 1) / kTile;
   int64_t want = groups >= 256 ? 1 : (256 + groups - 1) / groups;     // chunks per request
   int64_t tpw = (tiles_total + want * kWaves - 1) / (want * kWaves);  // tiles per wave
-  tpw = (tpw + kRing - 1) / kRing * kRing;
-  if (tpw < kRing) tpw = kRing;
+  if (tpw < 1) tpw = 1;
+  if (tpw > kMaxTpw) tpw = kMaxTpw;        // one block id per lane
   const int nchunks = static_cast<int>((tiles_total + tpw * kWaves - 1) / (tpw * kWaves));
   const int64_t grid = groups * nchunks;
   if (grid == 0) return hipSuccess;

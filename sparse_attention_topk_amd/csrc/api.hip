@@ -2,6 +2,10 @@
 // workspace sizing, kernel dispatch, the IndexShare layer driver and the
 // thread-local error text.  Every host-checkable condition is checked before
 // anything is enqueued.
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -86,7 +90,22 @@ size_t mla_ws(const dsa_batch* b, int n_heads, int R, int P, int topk, int dtype
   const int split = dsa::mla_choose_split(b, dtype, n_heads, R, P, topk);
   if (split <= 1) return 0;
   const size_t th = static_cast<size_t>(b->num_q_tokens) * split * n_heads;
-  return round_up(th * R * sizeof(float)) + round_up(th * sizeof(float));
+  return round_up(th * R * sizeof(float)) + round_up(th * sizeof(float)) +
+         round_up(static_cast<size_t>(b->num_q_tokens) * sizeof(unsigned long long));
+}
+
+// 48-bit tag of a sparse MLA call: split arrivals counted under another tag
+// (an earlier call, or whatever the workspace held) do not count.  Starts
+// from a clock- and process-dependent value and never returns 0.
+unsigned long long next_call_tag() {
+  static std::atomic<unsigned long long> next{
+      (static_cast<unsigned long long>(
+           std::chrono::steady_clock::now().time_since_epoch().count()) ^
+       (static_cast<unsigned long long>(getpid()) << 24)) * 0x9E3779B97F4A7C15ull};
+  for (;;) {
+    const unsigned long long tag = next.fetch_add(1) & ((1ull << 48) - 1);
+    if (tag) return tag;
+  }
 }
 
 int check_indexer(const dsa_batch* b, const void* q, int q_dtype,
@@ -191,11 +210,17 @@ int run_mla(const dsa_batch* b, const void* q, const void* kv, int dtype,
   a.n_split = dsa::mla_choose_split(b, dtype, n_heads, R, P, topk);
   a.part_o = nullptr;
   a.part_lse = nullptr;
+  a.arrivals = nullptr;
+  a.call_tag = 0;
   if (a.n_split > 1) {
     const size_t th = static_cast<size_t>(b->num_q_tokens) * a.n_split * n_heads;
     a.part_o = static_cast<float*>(ws);
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                           round_up(th * R * sizeof(float)));
+    a.arrivals = reinterpret_cast<unsigned long long*>(
+        static_cast<char*>(ws) + round_up(th * R * sizeof(float)) +
+        round_up(th * sizeof(float)));
+    a.call_tag = next_call_tag();
   }
   hipError_t e = dsa::launch_sparse_mla(a, stream);
   if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");

@@ -133,6 +133,8 @@ struct MlaArgs {
   float* lse;
   float* part_o;          // workspace [N, n_split, H, R] when n_split > 1
   float* part_lse;        // workspace [N, n_split, H]
+  unsigned long long* arrivals;   // workspace [N]: splits of the token done
+  unsigned long long call_tag;    // 48-bit tag of this call, never 0
   int n_split;
 };
 bool mla_mfma_ok(const dsa_batch& b, int dtype, int n_heads, int R, int P);

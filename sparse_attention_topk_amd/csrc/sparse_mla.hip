@@ -29,7 +29,9 @@
 //           keys, the value operand read with the gfx950 LDS transpose load
 //           straight from the row-major tile.
 // With more than one key split, each split writes its normalised partial
-// output and log-sum-exp, and a combine kernel merges them by LSE weights.
+// output and log-sum-exp, and the split that finishes last merges them by
+// LSE weights (splits of a token are placed on one XCD, so the partials it
+// reads back are still in that XCD's L2).
 //
 // Vector path (fp32 or other shapes): one workgroup per (token, head),
 // fp32 arithmetic, logits in LDS.
@@ -51,6 +53,7 @@ constexpr int kDmaInstr = kTilePieces / 64;           // 36 wave loads per tile
 constexpr int kDmaPerWave = kDmaInstr / 4;            // 9
 constexpr int kBufs = 4;                // tiles resident: current + 3 in flight
 constexpr int kMaxSplitLen = 2048;      // indices per workgroup
+constexpr int kMaxSplits = 32;          // merge weights fit behind the staged block
 constexpr int kQSteps = kD / 32;        // 18 K-steps of the logits
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -73,6 +76,8 @@ struct MlaShared {
   uint32_t counter;
 };
 static_assert(sizeof(MlaShared) <= 160 * 1024, "LDS budget");
+static_assert(kH * (kR * 4 + 16) + (kMaxSplits + 1) * kH * 4 <= sizeof(MlaShared::k),
+              "staged partials and merge weights fit in the tile buffers");
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -161,6 +166,30 @@ __device__ __forceinline__ float sum_x16_x32(float x) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// Arrival count of a split at its token's word.  The word holds the tag of
+// the call that last counted there (upper 48 bits) and that call's
+// arrivals (lower 16): a word with another tag, whatever the workspace held
+// before, counts as no arrival.  A compare-and-swap fails only when another
+// split of the token changed the word after it was read, which each of them
+// does once, so the loop ends within n_split rounds.
+__device__ __forceinline__ float lo_f(unsigned long long u) {
+  return __uint_as_float(static_cast<uint32_t>(u));
+}
+__device__ __forceinline__ float hi_f(unsigned long long u) {
+  return __uint_as_float(static_cast<uint32_t>(u >> 32));
+}
+
+__device__ uint32_t arrive(unsigned long long* word, unsigned long long tag, int n_split) {
+  unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int round = 0; round <= n_split; ++round) {
+    const unsigned long long next = (cur >> 16) == tag ? cur + 1 : (tag << 16) | 1ull;
+    const unsigned long long prev = atomicCAS(word, cur, next);
+    if (prev == cur) return static_cast<uint32_t>(next & 0xFFFFull);
+    cur = prev;
+  }
+  return 0;
+}
+
 // LDS layout of a 32-row tile (36 KB): rows in four groups h of 8, the 72
 // 16-byte pieces of a row in nine groups g of 8.  Block (h, g) is 1 KB at
 // 9216 h + 1024 g and is filled by one DMA instruction: lane l lands at
@@ -220,7 +249,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     int32_t B, const int32_t* __restrict__ block_table, int32_t max_blocks,
     int32_t block_size, int64_t num_slots, int32_t max_seq_len,
     uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ part_o, float* __restrict__ part_lse,
+    unsigned long long* __restrict__ arrivals, unsigned long long call_tag) {
   __shared__ MlaShared sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -232,8 +262,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   const int kh = wave & 1;
   const int partner = wave ^ 1;
 
-  const int t = blockIdx.x / n_split;
-  const int split = blockIdx.x % n_split;
+  // Workgroups are dealt to the eight XCDs in turn (workgroup i to XCD
+  // i % 8); with a grid that divides by 8, the splits of a token take
+  // consecutive places in one XCD's share.
+  int vb = blockIdx.x;
+  if (n_split > 1 && (gridDim.x & 7) == 0)
+    vb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int t = vb / n_split;
+  const int split = vb % n_split;
   if (t >= n_tokens) return;
 
   const int32_t* idx_row = topk_idx + static_cast<int64_t>(t) * topk;
@@ -550,64 +586,135 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     for (int n = 0; n < 2; ++n) {
       const int h = 32 * hh + 16 * n + l16;
       if (partial)
-        part_lse[(static_cast<int64_t>(t) * n_split + split) * kH + h] = lse_h[n];
+        __hip_atomic_store(part_lse + (static_cast<int64_t>(t) * n_split + split) * kH + h,
+                           lse_h[n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       else if (lse)
         lse[static_cast<int64_t>(t) * kH + h] = lse_h[n];
     }
   }
   tile_barrier();
-  // copy the staged block out in 16-byte pieces (a contiguous region)
-  const int row_pieces = partial ? kR * 4 / 16 : kR * 2 / 16;
-  const int total = kH * row_pieces;
-  u32x4* dst = partial
-      ? reinterpret_cast<u32x4*>(part_o + (static_cast<int64_t>(t) * n_split + split) * kH * kR)
-      : reinterpret_cast<u32x4*>(out + static_cast<int64_t>(t) * kH * kR);
-  for (int c = tid; c < total; c += kThreads) {
-    const int h = c / row_pieces, pc = c % row_pieces;
-    dst[c] = *reinterpret_cast<const u32x4*>(stage + h * row_b + 16 * pc);
+  // Copy the staged block out.  The output: 16-byte pieces of a contiguous
+  // region.
+  if (!partial) {
+    constexpr int row_pieces = kR * 2 / 16;
+    constexpr int total = kH * row_pieces;
+    u32x4* dst = reinterpret_cast<u32x4*>(out + static_cast<int64_t>(t) * kH * kR);
+    for (int c = tid; c < total; c += kThreads) {
+      const int h = c / row_pieces, pc = c % row_pieces;
+      dst[c] = *reinterpret_cast<const u32x4*>(stage + h * row_b + 16 * pc);
+    }
+    return;
   }
-}
+  // Partials are read back by another workgroup of this launch, maybe on
+  // another XCD: they are stored as relaxed device-scope atomics, which the
+  // hardware keeps coherent across XCDs by themselves, so no cache-wide
+  // write-back or invalidation is needed to hand them over.  8-byte words,
+  // consecutive lanes on consecutive words, so every store instruction
+  // writes four whole 128-byte lines: thread tid takes word tid (dims
+  // 2 tid, 2 tid + 1) of every head row.
+  unsigned long long* dst = reinterpret_cast<unsigned long long*>(
+      part_o + (static_cast<int64_t>(t) * n_split + split) * kH * kR);
+#pragma unroll 8
+  for (int h = 0; h < kH; ++h) {
+    const unsigned long long v =
+        *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * tid);
+    __hip_atomic_store(dst + h * (kR / 2) + tid, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
-// merge split partials: one thread per (token, head, 8 dims); the split
-// weights exp(lse_s - lse) are computed once per thread
-__global__ __launch_bounds__(256) void k_mla_combine(
-    const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    int32_t N, int32_t n_heads, int32_t R, int32_t n_split,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
-  const int chunks = R / 8;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= static_cast<int64_t>(N) * n_heads * chunks) return;
-  const int c = static_cast<int>(i % chunks);
-  const int64_t th = i / chunks;                 // t * n_heads + h
-  const int h = static_cast<int>(th % n_heads);
-  const int64_t t = th / n_heads;
-  float mx = -INFINITY;
-  for (int s = 0; s < n_split; ++s)
-    mx = fmaxf(mx, part_lse[(t * n_split + s) * n_heads + h]);
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  float wsum = 0.0f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float wgt = expf(part_lse[(t * n_split + s) * n_heads + h] - mx);
-      wsum += wgt;
-      const f32x4* src = reinterpret_cast<const f32x4*>(
-          part_o + ((t * n_split + s) * n_heads + h) * R + 8 * c);
-      const f32x4 a = src[0], b = src[1];
+  // ---- the split that arrives last merges the token's partials.  Every
+  // thread waits until its partial stores have completed (reached the
+  // device-coherent level) before the workgroup counts its arrival; the
+  // merging workgroup loads the others' partials only after its own count
+  // came back, with device-scope atomic loads.
+  wait_vm<0>();
+  __syncthreads();
+  if (tid == 0) sh.counter = arrive(arrivals + t, call_tag, n_split) == static_cast<uint32_t>(n_split);
+  __syncthreads();
+  if (!sh.counter) return;
+  asm volatile("" ::: "memory");
+  // Thread tid merges dims 2 tid and 2 tid + 1 of every head (as the
+  // partials were written: whole lines per instruction).  Splits are
+  // summed in split order (0, 1, ...) whichever finished last, so the
+  // result does not depend on the arrival order.
+  const unsigned long long* po = reinterpret_cast<const unsigned long long*>(
+      part_o + static_cast<int64_t>(t) * n_split * kH * kR) + tid;
+  auto word = [&](int s, int h) -> unsigned long long {
+    return __hip_atomic_load(const_cast<unsigned long long*>(po + (s * kH + h) * (kR / 2)),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto own = [&](int h) -> float2 {
+    return *reinterpret_cast<const float2*>(stage + h * row_b + 8 * tid);
+  };
+  uint32_t* ob = reinterpret_cast<uint32_t*>(out + static_cast<int64_t>(t) * kH * kR) + tid;
+  auto put = [&](int h, float x, float y, float inv) {
+    ob[h * (kR / 2)] = static_cast<uint32_t>(f32_to_bf16_rne(x * inv)) |
+                       (static_cast<uint32_t>(f32_to_bf16_rne(y * inv)) << 16);
+  };
+  // with two splits, the other split's rows are in flight while the
+  // weights are made
+  unsigned long long u[kH];
+  if (n_split == 2) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += wgt * a[e];
-        acc[4 + e] += wgt * b[e];
+    for (int h = 0; h < kH; ++h) u[h] = word(1 - split, h);
+  }
+  // split weights exp(lse_s - max) per head in place of the log-sum-exps,
+  // then 1 / their sum, behind the staged block
+  float* wt = reinterpret_cast<float*>(stage + kH * row_b);
+  for (int c = tid; c < n_split * kH; c += kThreads)
+    wt[c] = __hip_atomic_load(part_lse + static_cast<int64_t>(t) * n_split * kH + c,
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (tid < kH) {
+    float mx = -INFINITY;
+    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, wt[s * kH + tid]);
+    float sum = 0.0f;
+    for (int s = 0; s < n_split; ++s) {
+      const float wgt = mx == -INFINITY ? 0.0f : expf(wt[s * kH + tid] - mx);
+      wt[s * kH + tid] = wgt;
+      sum += wgt;
+    }
+    wt[n_split * kH + tid] = sum > 0.0f ? 1.0f / sum : 0.0f;
+    if (lse) lse[static_cast<int64_t>(t) * kH + tid] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
+  }
+  __syncthreads();
+  if (n_split == 2) {
+#pragma unroll
+    for (int h = 0; h < kH; ++h) {
+      const float2 m = own(h);
+      const float2 o = make_float2(lo_f(u[h]), hi_f(u[h]));
+      const float2 p0 = split == 0 ? m : o;
+      const float2 p1 = split == 0 ? o : m;
+      const float w0 = wt[h], w1 = wt[kH + h];
+      put(h, fmaf(w1, p1.x, w0 * p0.x), fmaf(w1, p1.y, w0 * p0.y), wt[2 * kH + h]);
+    }
+  } else {
+    // 16 heads at a time
+    for (int h0 = 0; h0 < kH; h0 += 16) {
+      float ax[16], ay[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ax[i] = ay[i] = 0.0f;
+      for (int s = 0; s < n_split; ++s) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float2 p;
+          if (s == split) {
+            p = own(h0 + i);
+          } else {
+            const unsigned long long v = word(s, h0 + i);
+            p = make_float2(lo_f(v), hi_f(v));
+          }
+          const float wgt = wt[s * kH + h0 + i];
+          ax[i] = fmaf(wgt, p.x, ax[i]);
+          ay[i] = fmaf(wgt, p.y, ay[i]);
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) put(h0 + i, ax[i], ay[i], wt[n_split * kH + h0 + i]);
     }
   }
-  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
-  u32x4 packed;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    packed[e] = static_cast<uint32_t>(f32_to_bf16_rne(acc[2 * e] * inv)) |
-                (static_cast<uint32_t>(f32_to_bf16_rne(acc[2 * e + 1] * inv)) << 16);
-  *reinterpret_cast<u32x4*>(out + th * R + 8 * c) = packed;
-  if (c == 0 && lse) lse[th] = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
+  // every split of this call has arrived: clear the word, so that a replay
+  // of the same launch (same tag) counts from zero again
+  if (tid == 0) __hip_atomic_store(arrivals + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- vector path
@@ -705,7 +812,7 @@ int mla_choose_split(const dsa_batch* b, int dtype, int n_heads, int R, int P,
   const int64_t wgs = static_cast<int64_t>(b->num_q_tokens);
   if (wgs <= 0 || wgs >= 256) return min_split;
   int split = static_cast<int>((256 + wgs - 1) / wgs);
-  const int max_split = max(1, topk / (4 * kT));
+  const int max_split = min(kMaxSplits, max(1, topk / (4 * kT)));
   return max(min_split, min(split, max_split));
 }
 
@@ -716,20 +823,17 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
     const int n_split = a.n_split;
     int split_len = (a.topk + n_split - 1) / n_split;
     split_len = (split_len + kT - 1) / kT * kT;
-    if (split_len > kMaxSplitLen) return hipErrorInvalidValue;
+    if (split_len > kMaxSplitLen || n_split > kMaxSplits) return hipErrorInvalidValue;
+    if (n_split > 1 && (!a.part_o || !a.part_lse || !a.arrivals || !a.call_tag))
+      return hipErrorInvalidValue;
     const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * n_split;
     k_mla_mfma<<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv),
         a.idx, a.topk, b.num_q_tokens, n_split, split_len, a.scale * kLog2e,
         b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
         b.block_size, b.num_slots, b.max_seq_len,
-        static_cast<uint16_t*>(a.out), a.lse, a.part_o, a.part_lse);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || n_split == 1) return e;
-    const int64_t total = static_cast<int64_t>(b.num_q_tokens) * a.n_heads * (kR / 8);
-    k_mla_combine<<<static_cast<unsigned>((total + 255) / 256), 256, 0, stream>>>(
-        a.part_o, a.part_lse, b.num_q_tokens, a.n_heads, kR, n_split,
-        static_cast<uint16_t*>(a.out), a.lse);
+        static_cast<uint16_t*>(a.out), a.lse, a.part_o, a.part_lse, a.arrivals,
+        a.call_tag);
     return hipGetLastError();
   }
   const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * a.n_heads;

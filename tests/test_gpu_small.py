@@ -258,6 +258,49 @@ def test_bf16_attention_matrix_core(dsa, n_req, q_len, topk):
         assert attn_close(gl[t], rl[t], 1e-3, 1e-4) <= 0, t
 
 
+@pytest.mark.parametrize("fill", ["random", "ones", "zeros"])
+def test_split_merge_whatever_the_workspace_held(dsa, fill):
+    """With several key splits per token, the split that finishes last merges
+    the partials; arrivals are counted in a per-token word of the workspace.
+    Whatever the workspace held before the first call, and over consecutive
+    calls on the same workspace (the second with other queries), each result
+    matches the oracle, and a repeated call repeats its result bit for bit."""
+    cfg = _small_cfg(num_reqs=3, q_len=1, topk=2048)
+    b = make_batch(cfg, DEV, seq_lens=[3000, 2500, 2049], q_lens=[1] * 3)
+    lay = make_layer(cfg, b, DEV, with_indexer=False)
+    idx = make_random_indices(b, 2048, 5150, DEV)
+    bb = _dsa_batch(dsa, b)
+    nbytes = dsa.sparse_mla_attn_workspace_size(bb, 64, cfg.kv_lora_rank,
+                                                lay.q_mla.shape[2] - cfg.kv_lora_rank,
+                                                2048, 1)
+    assert nbytes > 0
+    g = torch.Generator(device="cpu").manual_seed(17)
+    if fill == "random":
+        ws = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).to(DEV)
+    else:
+        ws = torch.full((nbytes,), 255 if fill == "ones" else 0, dtype=torch.uint8,
+                        device=DEV)
+    ro, rl = _oracle_mla(b, lay, idx.cpu().numpy(), cfg.kv_lora_rank, cfg.softmax_scale)
+    o1, l1 = dsa.sparse_mla_attn(bb, lay.q_mla, lay.kv_cache, idx, cfg.kv_lora_rank,
+                                 cfg.softmax_scale, workspace=ws)
+    o1, l1 = o1.clone(), l1.clone()
+    o2, l2 = dsa.sparse_mla_attn(bb, lay.q_mla, lay.kv_cache, idx, cfg.kv_lora_rank,
+                                 cfg.softmax_scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert attn_close(np_f64(o1), ro) <= 0
+    assert attn_close(l1.cpu().numpy(), rl, 1e-3, 1e-4) <= 0
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # other queries on the same workspace
+    q2 = torch.flip(lay.q_mla, dims=[0]).contiguous()
+    lay.q_mla = q2
+    ro2, rl2 = _oracle_mla(b, lay, idx.cpu().numpy(), cfg.kv_lora_rank, cfg.softmax_scale)
+    o3, l3 = dsa.sparse_mla_attn(bb, q2, lay.kv_cache, idx, cfg.kv_lora_rank,
+                                 cfg.softmax_scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert attn_close(np_f64(o3), ro2) <= 0
+    assert attn_close(l3.cpu().numpy(), rl2, 1e-3, 1e-4) <= 0
+
+
 def test_attention_with_late_dominant_keys(dsa):
     """Keys late in a split whose logits beat everything before them by
     hundreds (in natural-log units), twice in the same split for one head:

@@ -364,7 +364,6 @@ def main():
 def bench_indexshare(args, cfg, b, bb, dsa, torch):
     """IndexShare stack: 8 layers, amortised time per layer."""
     from synth import make_layer
-    from oracle import indexshare as OX  # noqa: F401  (type names only)
     dev = "cuda"
     types = cfg.indexer_types
     src = []

@@ -41,8 +41,8 @@ def log(msg):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="decode_32k_mtp",
                    choices=["decode_32k_mtp", "fp8_decode_varlen",
                             "indexshare_8layer", "prefill_16k"])

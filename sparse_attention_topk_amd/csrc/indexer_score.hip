@@ -305,37 +305,6 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
   if (key_beg >= key_end) return;
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
 
-  // query operand (head 32 mt + col, dims 16 s + 8 hf) and head weights
-  // (accumulator register r of a 32x32 tile holds head 8 (r / 4) + 4 hf +
-  // r % 4 of column col: four runs of 4 consecutive heads); issued before
-  // any tile DMA, so waiting for them never waits for a tile
-  bf16x8 qa[TQ][MT][8];
-  float wr[TQ][MT][16];
-#pragma unroll
-  for (int tt = 0; tt < TQ; ++tt) {
-    const bool live = tt < nt;
-    const int64_t tok = tbeg + t0 + (live ? tt : 0);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const uint16_t* qrow = q + (tok * H + mt * 32 + col) * 128;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        qa[tt][mt][s] = live ? *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hf)
-                             : bf16x8{};
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 w4 = live ? *reinterpret_cast<const float4*>(
-                                     w + tok * H + mt * 32 + 8 * g + 4 * hf)
-                               : float4{0.f, 0.f, 0.f, 0.f};
-        wr[tt][mt][4 * g + 0] = w4.x;
-        wr[tt][mt][4 * g + 1] = w4.y;
-        wr[tt][mt][4 * g + 2] = w4.z;
-        wr[tt][mt][4 * g + 3] = w4.w;
-      }
-    }
-  }
-  asm volatile("" ::: "memory");
-
   // The wave's tiles are first_tile + kWaves i, i < ntiles (<= 64).  A
   // 32-key tile never spans two cache blocks, so one block-table entry
   // gives the whole tile.  Lane i fetches tile i's entry once, with a vector
@@ -352,6 +321,38 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
     const int32_t blk = (first_tile + kWaves * lane) * kTile / block_size;
     if (lane < ntiles && blk < max_blocks) bid_lane = bt_row[blk];
   }
+  // query operand (head 32 mt + col, dims 16 s + 8 hf) and head weights
+  // (accumulator register r of a 32x32 tile holds head 8 (r / 4) + 4 hf +
+  // r % 4 of column col: four runs of 4 consecutive heads).  Issued after
+  // the block-id load, so the first tile's address waits only for that,
+  // and before any tile DMA, so waiting for them never waits for a tile.
+  // The loads are unconditional (a block with one token loads that token
+  // twice): the second token's scores are then never written out, and
+  // branch-free loads leave the compiler's wait counting exact.
+  bf16x8 qa[TQ][MT][8];
+  float wr[TQ][MT][16];
+#pragma unroll
+  for (int tt = 0; tt < TQ; ++tt) {
+    const int64_t tok = tbeg + t0 + (tt < nt ? tt : 0);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const uint16_t* qrow = q + (tok * H + mt * 32 + col) * 128;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        qa[tt][mt][s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hf);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 w4 =
+            *reinterpret_cast<const float4*>(w + tok * H + mt * 32 + 8 * g + 4 * hf);
+        wr[tt][mt][4 * g + 0] = w4.x;
+        wr[tt][mt][4 * g + 1] = w4.y;
+        wr[tt][mt][4 * g + 2] = w4.z;
+        wr[tt][mt][4 * g + 3] = w4.w;
+      }
+    }
+  }
+  asm volatile("" ::: "memory");
+
   auto tile_row0 = [&](int i) -> int64_t {     // slot of the tile's first key, or -1
     if (i >= ntiles) return -1;
     const int32_t s0 = (first_tile + kWaves * i) * kTile;

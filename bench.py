@@ -323,6 +323,18 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     breakdown_ms_step = (time.perf_counter() - tb) * 1e3 / args.steps
+    # Cold caches: before each step, outside its events, a 1 GiB read evicts
+    # L2 and the last-level cache (a read leaves no dirty lines behind), as
+    # when other layers run between two steps of this one.
+    junk = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            for _ in range(min(args.steps, 50))]
+    log("cold-cache pass over %d steps" % len(cold))
+    for ev in cold:
+        junk.sum()
+        step(ev)
+    torch.cuda.synchronize()
+    del junk
     cw = [e[0].elapsed_time(e[1]) for e in evs]
     ix = [e[1].elapsed_time(e[2]) for e in evs]
     ml = [e[2].elapsed_time(e[3]) for e in evs]
@@ -363,6 +375,14 @@ def main():
             "note": "per-call means from a second pass of the same steps with an "
                     "event between calls (not the pass ms_per_step is taken from)",
             "breakdown_pass_ms_per_step": breakdown_ms_step,
+        },
+        "calls_cold_cache": {
+            "note": "per-call means with L2 and the last-level cache evicted (1 GiB "
+                    "read) before each step",
+            "indexer_topk_ms": mean([e[1].elapsed_time(e[2]) for e in cold]),
+            "sparse_mla_attn_ms": mean([e[2].elapsed_time(e[3]) for e in cold]),
+            "indexer_frac_hbm": ib / (mean([e[1].elapsed_time(e[2]) for e in cold]) * 1e-3)
+                                / 1e9 / HBM_PEAK_GBS,
         },
         "cpu_baseline": None,
     }

@@ -173,8 +173,8 @@ int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
  * n_heads <= 128) take a vector path.
  * workspace: at least sparse_mla_attn_workspace_size() bytes (may be 0, in
  * which case workspace may be NULL), 256-byte aligned.  When the keys of a
- * token are split over several workgroups it holds their fp32 partial
- * outputs [N, n_split, n_heads, R], partial log-sum-exps [N, n_split,
+ * token are split over several workgroups it holds their normalised bf16
+ * partial outputs [N, n_split, n_heads, R], fp32 log-sum-exps [N, n_split,
  * n_heads] and one 8-byte arrival word per token; its prior contents do
  * not matter (arrivals are counted under a tag unique to the call, and each
  * call leaves its words cleared).  Calls that may run at the same time must

@@ -90,7 +90,7 @@ size_t mla_ws(const dsa_batch* b, int n_heads, int R, int P, int topk, int dtype
   const int split = dsa::mla_choose_split(b, dtype, n_heads, R, P, topk);
   if (split <= 1) return 0;
   const size_t th = static_cast<size_t>(b->num_q_tokens) * split * n_heads;
-  return round_up(th * R * sizeof(float)) + round_up(th * sizeof(float)) +
+  return round_up(th * R * sizeof(uint16_t)) + round_up(th * sizeof(float)) +
          round_up(static_cast<size_t>(b->num_q_tokens) * sizeof(unsigned long long));
 }
 
@@ -214,11 +214,11 @@ int run_mla(const dsa_batch* b, const void* q, const void* kv, int dtype,
   a.call_tag = 0;
   if (a.n_split > 1) {
     const size_t th = static_cast<size_t>(b->num_q_tokens) * a.n_split * n_heads;
-    a.part_o = static_cast<float*>(ws);
+    a.part_o = static_cast<uint16_t*>(ws);
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                          round_up(th * R * sizeof(float)));
+                                          round_up(th * R * sizeof(uint16_t)));
     a.arrivals = reinterpret_cast<unsigned long long*>(
-        static_cast<char*>(ws) + round_up(th * R * sizeof(float)) +
+        static_cast<char*>(ws) + round_up(th * R * sizeof(uint16_t)) +
         round_up(th * sizeof(float)));
     a.call_tag = next_call_tag();
   }

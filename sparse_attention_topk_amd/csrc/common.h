@@ -131,7 +131,7 @@ struct MlaArgs {
   float scale;
   void* out;
   float* lse;
-  float* part_o;          // workspace [N, n_split, H, R] when n_split > 1
+  uint16_t* part_o;       // workspace [N, n_split, H, R] bf16 when n_split > 1
   float* part_lse;        // workspace [N, n_split, H]
   unsigned long long* arrivals;   // workspace [N]: splits of the token done
   unsigned long long call_tag;    // 48-bit tag of this call, never 0

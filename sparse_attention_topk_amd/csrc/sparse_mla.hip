@@ -76,7 +76,7 @@ struct MlaShared {
   uint32_t counter;
 };
 static_assert(sizeof(MlaShared) <= 160 * 1024, "LDS budget");
-static_assert(kH * (kR * 4 + 16) + (kMaxSplits + 1) * kH * 4 <= sizeof(MlaShared::k),
+static_assert(kH * (kR * 2 + 16) + (kMaxSplits + 1) * kH * 4 <= sizeof(MlaShared::k),
               "staged partials and merge weights fit in the tile buffers");
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     int32_t B, const int32_t* __restrict__ block_table, int32_t max_blocks,
     int32_t block_size, int64_t num_slots, int32_t max_seq_len,
     uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
     unsigned long long* __restrict__ arrivals, unsigned long long call_tag) {
   __shared__ MlaShared sh;
   const int tid = threadIdx.x;
@@ -559,9 +559,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     lse_h[n] = l > 0.0f ? (m_ref[n] + log2f(l)) * kLn2 : -INFINITY;
   }
   const bool partial = n_split > 1;
-  // rows of the staged block: head h (0..63) at byte h * row_b of the tile
-  // buffers (free now); 16 bytes of padding per row spread the banks
-  const int row_b = partial ? kR * 4 + 16 : kR * 2 + 16;
+  // rows of the staged block (bf16, the output's or the partial's values):
+  // head h (0..63) at byte h * row_b of the tile buffers (free now); 16
+  // bytes of padding per row spread the banks
+  constexpr int row_b = kR * 2 + 16;
   uint8_t* stage = reinterpret_cast<uint8_t*>(&sh.k[0][0]);
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
@@ -573,11 +574,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
 #pragma unroll
       for (int nt = 0; nt < kR / 32; ++nt) {
         const int d = 256 * kh + 16 * nt + l16;
-        const float v = o[n][nt][i] * il;
-        if (partial)
-          *reinterpret_cast<float*>(stage + h * row_b + 4 * d) = v;
-        else
-          *reinterpret_cast<uint16_t*>(stage + h * row_b + 2 * d) = f32_to_bf16_rne(v);
+        *reinterpret_cast<uint16_t*>(stage + h * row_b + 2 * d) =
+            f32_to_bf16_rne(o[n][nt][i] * il);
       }
     }
   }
@@ -605,20 +603,24 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     }
     return;
   }
-  // Partials are read back by another workgroup of this launch, maybe on
-  // another XCD: they are stored as relaxed device-scope atomics, which the
-  // hardware keeps coherent across XCDs by themselves, so no cache-wide
-  // write-back or invalidation is needed to hand them over.  8-byte words,
-  // consecutive lanes on consecutive words, so every store instruction
-  // writes four whole 128-byte lines: thread tid takes word tid (dims
-  // 2 tid, 2 tid + 1) of every head row.
+  // Partials (bf16, normalised) are read back by another workgroup of this
+  // launch, maybe on another XCD: they are stored as relaxed device-scope
+  // atomics, which the hardware keeps coherent across XCDs by themselves,
+  // so no cache-wide write-back or invalidation is needed to hand them
+  // over.  8-byte words (4 dims), consecutive lanes on consecutive words,
+  // so every store instruction writes four whole 128-byte lines: thread tid
+  // takes word tid % 128 of head rows tid / 128 + 2 i.
+  constexpr int kWords = kR / 4;                   // 8-byte words per head row
+  const int wq = tid % kWords;
+  const int h0 = tid / kWords;
   unsigned long long* dst = reinterpret_cast<unsigned long long*>(
       part_o + (static_cast<int64_t>(t) * n_split + split) * kH * kR);
 #pragma unroll 8
-  for (int h = 0; h < kH; ++h) {
+  for (int i = 0; i < kH / 2; ++i) {
+    const int h = h0 + 2 * i;
     const unsigned long long v =
-        *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * tid);
-    __hip_atomic_store(dst + h * (kR / 2) + tid, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq);
+    __hip_atomic_store(dst + h * kWords + wq, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- the split that arrives last merges the token's partials.  Every
@@ -632,30 +634,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   __syncthreads();
   if (!sh.counter) return;
   asm volatile("" ::: "memory");
-  // Thread tid merges dims 2 tid and 2 tid + 1 of every head (as the
+  // Thread tid merges dims 4 wq .. 4 wq + 3 of heads h0 + 2 i (as the
   // partials were written: whole lines per instruction).  Splits are
   // summed in split order (0, 1, ...) whichever finished last, so the
-  // result does not depend on the arrival order.
+  // result does not depend on the arrival order; this split's own partial
+  // comes from the staged block, rounded exactly as the others read theirs.
   const unsigned long long* po = reinterpret_cast<const unsigned long long*>(
-      part_o + static_cast<int64_t>(t) * n_split * kH * kR) + tid;
+      part_o + static_cast<int64_t>(t) * n_split * kH * kR) + wq;
   auto word = [&](int s, int h) -> unsigned long long {
-    return __hip_atomic_load(const_cast<unsigned long long*>(po + (s * kH + h) * (kR / 2)),
+    return __hip_atomic_load(const_cast<unsigned long long*>(po + (s * kH + h) * kWords),
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  auto own = [&](int h) -> float2 {
-    return *reinterpret_cast<const float2*>(stage + h * row_b + 8 * tid);
+  auto own = [&](int h) -> unsigned long long {
+    return *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq);
   };
-  uint32_t* ob = reinterpret_cast<uint32_t*>(out + static_cast<int64_t>(t) * kH * kR) + tid;
-  auto put = [&](int h, float x, float y, float inv) {
-    ob[h * (kR / 2)] = static_cast<uint32_t>(f32_to_bf16_rne(x * inv)) |
-                       (static_cast<uint32_t>(f32_to_bf16_rne(y * inv)) << 16);
+  auto unpack = [](unsigned long long v, float (&x)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      x[e] = __uint_as_float(static_cast<uint32_t>((v >> (16 * e)) & 0xFFFFu) << 16);
+  };
+  unsigned long long* ob = reinterpret_cast<unsigned long long*>(
+      out + static_cast<int64_t>(t) * kH * kR) + wq;
+  auto put = [&](int h, const float (&x)[4], float inv) {
+    unsigned long long v = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v |= static_cast<unsigned long long>(f32_to_bf16_rne(x[e] * inv)) << (16 * e);
+    ob[h * kWords] = v;
   };
   // with two splits, the other split's rows are in flight while the
   // weights are made
-  unsigned long long u[kH];
+  unsigned long long u[kH / 2];
   if (n_split == 2) {
 #pragma unroll
-    for (int h = 0; h < kH; ++h) u[h] = word(1 - split, h);
+    for (int i = 0; i < kH / 2; ++i) u[i] = word(1 - split, h0 + 2 * i);
   }
   // split weights exp(lse_s - max) per head in place of the log-sum-exps,
   // then 1 / their sum, behind the staged block
@@ -679,37 +691,44 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   __syncthreads();
   if (n_split == 2) {
 #pragma unroll
-    for (int h = 0; h < kH; ++h) {
-      const float2 m = own(h);
-      const float2 o = make_float2(lo_f(u[h]), hi_f(u[h]));
-      const float2 p0 = split == 0 ? m : o;
-      const float2 p1 = split == 0 ? o : m;
+    for (int i = 0; i < kH / 2; ++i) {
+      const int h = h0 + 2 * i;
+      float m[4], o4[4], x[4];
+      unpack(own(h), m);
+      unpack(u[i], o4);
       const float w0 = wt[h], w1 = wt[kH + h];
-      put(h, fmaf(w1, p1.x, w0 * p0.x), fmaf(w1, p1.y, w0 * p0.y), wt[2 * kH + h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = split == 0 ? m[e] : o4[e];
+        const float p1 = split == 0 ? o4[e] : m[e];
+        x[e] = fmaf(w1, p1, w0 * p0);
+      }
+      put(h, x, wt[2 * kH + h]);
     }
   } else {
-    // 16 heads at a time
-    for (int h0 = 0; h0 < kH; h0 += 16) {
-      float ax[16], ay[16];
+    // 8 heads at a time
+    for (int i0 = 0; i0 < kH / 2; i0 += 8) {
+      float acc[8][4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ax[i] = ay[i] = 0.0f;
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] = 0.0f;
       for (int s = 0; s < n_split; ++s) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float2 p;
-          if (s == split) {
-            p = own(h0 + i);
-          } else {
-            const unsigned long long v = word(s, h0 + i);
-            p = make_float2(lo_f(v), hi_f(v));
-          }
-          const float wgt = wt[s * kH + h0 + i];
-          ax[i] = fmaf(wgt, p.x, ax[i]);
-          ay[i] = fmaf(wgt, p.y, ay[i]);
+        for (int i = 0; i < 8; ++i) {
+          const int h = h0 + 2 * (i0 + i);
+          float p[4];
+          unpack(s == split ? own(h) : word(s, h), p);
+          const float wgt = wt[s * kH + h];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wgt, p[e], acc[i][e]);
         }
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) put(h0 + i, ax[i], ay[i], wt[n_split * kH + h0 + i]);
+      for (int i = 0; i < 8; ++i) {
+        const int h = h0 + 2 * (i0 + i);
+        put(h, acc[i], wt[n_split * kH + h]);
+      }
     }
   }
   // every split of this call has arrived: clear the word, so that a replay

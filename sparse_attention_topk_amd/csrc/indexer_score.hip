@@ -216,20 +216,30 @@ __global__ __launch_bounds__(256, (TQ * MT > 2) ? 1 : 2) void k_score_mfma(
   }
 }
 
-// ------------------------------------------------- bf16 keys through LDS
+// ------------------------------------------------- keys through LDS
 // Same contraction, but the keys reach LDS by DMA (global_load_lds_dwordx4)
 // in whole 1 KB lines: one wave instruction carries 4 consecutive 256-byte
-// rows.  Each wave streams its own tiles through a private ring of kRing
-// 8 KB buffers (kRing - 1 tiles in flight), so no barrier is ever needed;
-// the MFMA key operand is read back with ds_read_b128.  Lane l of DMA
-// instruction m lands at byte 16 l of block m and carries row
-// 4 m + l / 16, piece (l % 16) ^ (row % 16): piece p of row r sits at
-// 16-byte slot p ^ (r % 16) of the row, which spreads the 32 rows of one
-// operand load over distinct banks (32 and 64 banks alike).
+// bf16 rows (or 8 128-byte e4m3 rows).  Each wave streams its own tiles
+// through a private ring of kRing buffers (kRing - 1 tiles in flight), so
+// no barrier is ever needed; the MFMA key operand is read back with
+// ds_read_b128 (e4m3 bytes widened to bf16 in registers).  Lane l of DMA
+// instruction m lands at byte 16 l of block m; piece p (16 bytes) of row r
+// sits at slot p ^ (r % P) of the row (P pieces per row), which spreads
+// the 32 rows of one operand load over distinct banks.  An e4m3 tile's 32
+// scales follow its rows (one 4-byte DMA per lane, two copies).
 constexpr int kRing = 3;
 static_assert(kRing >= 2 && kRing <= 4, "tile waits cover rings of 2 to 4 tiles");
 constexpr int kMaxTpw = 64;                      // tiles per wave (one block id per lane)
-constexpr int kTileBytes = kTile * 256;          // 32 keys x 128 bf16
+template <bool F8>
+struct DmaTile {
+  static constexpr int kRowBytes = F8 ? 128 : 256;
+  static constexpr int kPieces = kRowBytes / 16;            // 16-byte pieces per row
+  static constexpr int kRowsPerInstr = 1024 / kRowBytes;
+  static constexpr int kKeyInstr = kTile / kRowsPerInstr;   // 4 or 8
+  static constexpr int kInstr = kKeyInstr + (F8 ? 1 : 0);   // + the scales
+  static constexpr int kScaleOff = kTile * kRowBytes;       // scales after the rows
+  static constexpr int kBytes = kScaleOff + (F8 ? 256 : 0);
+};
 
 // f(integral_constant<int, I>) for I = 0 .. N-1 (indices usable as
 // constants, e.g. for register arrays)
@@ -258,30 +268,36 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
-// s_waitcnt vmcnt(8 later): a tile is 8 DMA instructions, so the tile
+// s_waitcnt vmcnt(I later): a tile is I DMA instructions, so the tile
 // issued `later` tiles before the newest one has landed
+template <int I>
 __device__ __forceinline__ void wait_tile(int later) {
   switch (later) {
     case 0: wait_vm<0>(); break;
-    case 1: wait_vm<8>(); break;
-    case 2: wait_vm<16>(); break;
-    default: wait_vm<24>(); break;
+    case 1: wait_vm<I>(); break;
+    case 2: wait_vm<2 * I>(); break;
+    default: wait_vm<3 * I>(); break;
   }
 }
 
-template <int TQ, int MT>
-__global__ __launch_bounds__(256, 1) void k_score_dma(
+// MAXT: tiles per wave the LDS score buffer holds.  With 16 (launches of
+// several rounds) two workgroups share a CU, so one's start overlaps the
+// other's stream.
+template <int TQ, int MT, bool F8, int MAXT>
+__global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
     const uint16_t* __restrict__ q, const float* __restrict__ w,
-    const uint8_t* __restrict__ kc, const int32_t* __restrict__ seq_lens,
+    const uint8_t* __restrict__ kc, const float* __restrict__ kscale,
+    const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ block_table,
     int32_t max_blocks, int32_t block_size, int64_t num_slots,
     int32_t max_seq_len, int32_t qblocks_per_req, int32_t nchunks,
     int32_t tiles_per_wave, float* __restrict__ scores, int64_t row_stride) {
   constexpr int H = 32 * MT;
-  __shared__ __align__(16) uint8_t ring[kWaves][kRing][kTileBytes];
+  using DT = DmaTile<F8>;
+  __shared__ __align__(16) uint8_t ring[kWaves][kRing][DT::kBytes];
   // the workgroup's scores, [token][key within chunk], written out at the
   // end: score stores interleaved with the key stream slow the reads down
-  __shared__ __align__(16) float sc[TQ][kWaves * kMaxTpw * kTile];
+  __shared__ __align__(16) float sc[TQ][kWaves * MAXT * kTile];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5;
@@ -339,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
       const uint16_t* qrow = q + (tok * H + mt * 32 + col) * 128;
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        qa[tt][mt][s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hf);
+        qa[tt][mt][s] = *reinterpret_cast<const bf16x8*>(qrow + dim_of<F8>(hf, s));
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const float4 w4 =
@@ -361,19 +377,26 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
     return (bid >= 0 && s0 / block_size < max_blocks && slot0 + kTile <= num_slots) ? slot0 : -1;
   };
 
-  // DMA geometry of this lane: row 4 m + lane / 16, slot lane % 16
-  const int drow = lane >> 4;
-  const int dslot = lane & 15;
+  // DMA geometry of this lane: row R m + lane / P, slot lane % P (R rows
+  // per instruction, P pieces per row)
+  const int drow = lane / DT::kPieces;
+  const int dslot = lane % DT::kPieces;
   auto dma = [&](int slot, int64_t row0) {
     uint8_t* buf = &ring[wave][slot][0];
     const int64_t base = row0 < 0 ? 0 : row0;
 #pragma unroll
-    for (int m = 0; m < kTile / 4; ++m) {
-      const int row = 4 * m + drow;
-      const int piece = dslot ^ (row & 15);
-      const uint8_t* src = kc + (base + row) * 256 + 16 * piece;
+    for (int m = 0; m < DT::kKeyInstr; ++m) {
+      const int row = DT::kRowsPerInstr * m + drow;
+      const int piece = dslot ^ (row % DT::kPieces);
+      const uint8_t* src = kc + (base + row) * DT::kRowBytes + 16 * piece;
       __builtin_amdgcn_global_load_lds(
           src, (__attribute__((address_space(3))) void*)(buf + 1024 * m), 16, 0, 0);
+    }
+    if constexpr (F8) {
+      // the tile's 32 scales, lanes 32 .. 63 a second copy
+      __builtin_amdgcn_global_load_lds(
+          kscale + base + (lane & 31),
+          (__attribute__((address_space(3))) void*)(buf + DT::kScaleOff), 4, 0, 0);
     }
   };
   // r0[m & 3] holds tile m's first slot from one tile before its DMA
@@ -399,10 +422,11 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
     }
   asm volatile("" : "+v"(bid_lane));
 
-  // key operand of this lane: row col, piece 2 s + hf at 16-byte slot
-  // (2 s + hf) ^ (col % 16)
-  const uint32_t rbase = static_cast<uint32_t>(col) * 256u;
-  const int csw = col & 15;
+  // key operand of this lane: row col; bf16: piece 2 s + hf at slot
+  // (2 s + hf) ^ (col % 16); e4m3: pieces 4 hf + j (dims 64 hf + 16 j ..)
+  // at slot (4 hf + j) ^ (col % 8)
+  const uint32_t rbase = static_cast<uint32_t>(col) * DT::kRowBytes;
+  const int csw = col % DT::kPieces;
   for (int i0 = 0; i0 < ntiles; i0 += kRing) {
     static_for<kRing>([&](auto jc) {
       constexpr int j = decltype(jc)::value;   // ring slot of tile i
@@ -413,15 +437,32 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
       r0[j] = tile_row0(i + kRing);
       // tile i landed when at most the later tiles' DMAs are pending
       const int later = min(ntiles - 1 - i, kRing - 1);
-      wait_tile(later);
+      wait_tile<DT::kInstr>(later);
       const uint32_t tb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
           (__attribute__((address_space(3))) uint8_t*)(&ring[wave][j][0]))) + rbase;
       bf16x8 kv[8];
+      float kscl = 1.0f;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      static_for<8>([&](auto sc) {
-        constexpr int st = decltype(sc)::value;
-        kv[st] = lds_b128<0>(tb + 16u * static_cast<uint32_t>((2 * st + hf) ^ csw));
-      });
+      if constexpr (!F8) {
+        static_for<8>([&](auto sc) {
+          constexpr int st = decltype(sc)::value;
+          kv[st] = lds_b128<0>(tb + 16u * static_cast<uint32_t>((2 * st + hf) ^ csw));
+        });
+      } else {
+        u32x4 raw[4];
+        static_for<4>([&](auto jc2) {
+          constexpr int jj = decltype(jc2)::value;
+          raw[jj] = __builtin_bit_cast(
+              u32x4, lds_b128<0>(tb + 16u * static_cast<uint32_t>((4 * hf + jj) ^ csw)));
+        });
+        static_for<4>([&](auto jc2) {
+          constexpr int jj = decltype(jc2)::value;
+          lgkm_keep<3 - jj>(raw[jj]);
+          kv[2 * jj] = fp8x8_to_bf16x8(raw[jj][0], raw[jj][1]);
+          kv[2 * jj + 1] = fp8x8_to_bf16x8(raw[jj][2], raw[jj][3]);
+        });
+        kscl = *reinterpret_cast<const float*>(&ring[wave][j][DT::kScaleOff + 4 * col]);
+      }
       float part[TQ];
 #pragma unroll
       for (int tt = 0; tt < TQ; ++tt) part[tt] = 0.0f;
@@ -432,7 +473,9 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
         for (int tt = 0; tt < TQ; ++tt) acc[tt] = f32x16{};
         static_for<8>([&](auto sc) {
           constexpr int st = decltype(sc)::value;
-          if (mt == 0) lgkm_keep<7 - st>(kv[st]);
+          if constexpr (!F8) {
+            if (mt == 0) lgkm_keep<7 - st>(kv[st]);
+          }
 #pragma unroll
           for (int tt = 0; tt < TQ; ++tt)
             acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[tt][mt][st], kv[st],
@@ -450,6 +493,7 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
       // (first_tile + kWaves i) * kTile + col (0 when the tile has no row)
       float v = part[0];
       if constexpr (TQ > 1) v = hf ? part[1] : part[0];
+      v *= kscl;
       if (my_r0 < 0) v = 0.0f;
       if (hf < TQ) sc[hf < TQ ? hf : 0][(kWaves * i + wave) * kTile + col] = v;
     });
@@ -469,7 +513,21 @@ __global__ __launch_bounds__(256, 1) void k_score_dma(
   }
 }
 
-template <int TQ, int MT>
+template <int TQ, int MT, bool F8, int MAXT>
+hipError_t launch_dma_t(const IndexerArgs& a, int qbpr, int nchunks, int64_t tpw,
+                        hipStream_t stream) {
+  const dsa_batch& b = a.b;
+  const int64_t grid = static_cast<int64_t>(b.num_reqs) * qbpr * nchunks;
+  if (grid == 0) return hipSuccess;
+  k_score_dma<TQ, MT, F8, MAXT><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
+      static_cast<const uint16_t*>(a.q), a.w,
+      static_cast<const uint8_t*>(a.k_cache), a.k_scale, b.seq_lens, b.cu_q,
+      b.block_table, b.max_blocks, b.block_size, b.num_slots, b.max_seq_len,
+      qbpr, nchunks, static_cast<int32_t>(tpw), a.scores, a.row_stride);
+  return hipGetLastError();
+}
+
+template <int TQ, int MT, bool F8>
 hipError_t launch_dma(const IndexerArgs& a, hipStream_t stream) {
   const dsa_batch& b = a.b;
   const int qbpr = (b.max_q_len + TQ - 1) / TQ;
@@ -481,15 +539,17 @@ hipError_t launch_dma(const IndexerArgs& a, hipStream_t stream) {
   int64_t tpw = (tiles_total + want * kWaves - 1) / (want * kWaves);  // tiles per wave
   if (tpw < 1) tpw = 1;
   if (tpw > kMaxTpw) tpw = kMaxTpw;        // one block id per lane
-  const int nchunks = static_cast<int>((tiles_total + tpw * kWaves - 1) / (tpw * kWaves));
-  const int64_t grid = groups * nchunks;
-  if (grid == 0) return hipSuccess;
-  k_score_dma<TQ, MT><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
-      static_cast<const uint16_t*>(a.q), a.w,
-      static_cast<const uint8_t*>(a.k_cache), b.seq_lens, b.cu_q,
-      b.block_table, b.max_blocks, b.block_size, b.num_slots, b.max_seq_len,
-      qbpr, nchunks, static_cast<int32_t>(tpw), a.scores, a.row_stride);
-  return hipGetLastError();
+  int nchunks = static_cast<int>((tiles_total + tpw * kWaves - 1) / (tpw * kWaves));
+  // several rounds: smaller workgroups, two per CU, where the registers
+  // allow it (one query token, one head group, e4m3 keys)
+  if constexpr (TQ == 1 && MT == 1 && F8) {
+    if (groups * nchunks > 256 && tpw > 16) {
+      tpw = 16;
+      nchunks = static_cast<int>((tiles_total + tpw * kWaves - 1) / (tpw * kWaves));
+      return launch_dma_t<TQ, MT, F8, 16>(a, qbpr, nchunks, tpw, stream);
+    }
+  }
+  return launch_dma_t<TQ, MT, F8, kMaxTpw>(a, qbpr, nchunks, tpw, stream);
 }
 
 // ---------------------------------------------------------------- vector path
@@ -568,11 +628,11 @@ hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t stream) {
     const bool one = b.max_q_len == 1;
     const bool mt2 = a.n_heads == 64;
     if (!fp8) {
-      if (one) return mt2 ? launch_dma<1, 2>(a, stream) : launch_dma<1, 1>(a, stream);
-      return mt2 ? launch_dma<2, 2>(a, stream) : launch_dma<2, 1>(a, stream);
+      if (one) return mt2 ? launch_dma<1, 2, false>(a, stream) : launch_dma<1, 1, false>(a, stream);
+      return mt2 ? launch_dma<2, 2, false>(a, stream) : launch_dma<2, 1, false>(a, stream);
     }
-    if (one) return mt2 ? launch_mfma<1, 2, true>(a, stream) : launch_mfma<1, 1, true>(a, stream);
-    return mt2 ? launch_mfma<2, 2, true>(a, stream) : launch_mfma<2, 1, true>(a, stream);
+    if (one) return mt2 ? launch_dma<1, 2, true>(a, stream) : launch_dma<1, 1, true>(a, stream);
+    return mt2 ? launch_dma<2, 2, true>(a, stream) : launch_dma<2, 1, true>(a, stream);
   }
   const int key_blocks = (b.max_seq_len + 255) / 256;
   const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * key_blocks;

@@ -406,26 +406,72 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
 }
 
 // ------------------------------------------------------------ streaming path
-// Visits every key of the row once, thread tid taking i = tid + 1024 j.
-// The loads are issued kBatch at a time before any is used, so a thread
-// keeps kBatch loads in flight instead of one.
-constexpr int kBatch = 16;
+// Streams keys 0 .. L-1 of a score row through f(i, key): 16-byte loads,
+// kV per thread per round, the next round's loads in flight while a round
+// is processed (two register buffers, no copies between them).  Loads past
+// the row's end are clamped to its last 16 bytes (rows are padded to 64
+// floats) and the keys past L are skipped, so every round issues the same
+// loads and the compiler's wait counts stay exact.
+constexpr int kV = 4;
+constexpr int kRound = kV * 4 * kThreads;   // keys per round
+// Streams positions beg .. end - 1 of a row through one wave in blocks of
+// 256: f(block start, lane's float4) for each block in order, lane l
+// holding positions 4 l .. 4 l + 3.  kSub blocks per round, two register
+// buffers, loads clamped into the row like for_each_key's.
+constexpr int kSub = 4;
+template <typename F>
+__device__ __forceinline__ void wave_blocks(const float* __restrict__ src, int beg,
+                                            int end, int last4, F&& f) {
+  const int lane = threadIdx.x & 63;
+  auto load = [&](int base, float4 (&v)[kSub]) {
+#pragma unroll
+    for (int j = 0; j < kSub; ++j)
+      v[j] = *reinterpret_cast<const float4*>(src + min(base + 256 * j + 4 * lane, last4));
+  };
+  auto run = [&](int base, const float4 (&v)[kSub]) {
+#pragma unroll
+    for (int j = 0; j < kSub; ++j)
+      if (base + 256 * j < end) f(base + 256 * j, v[j]);
+  };
+  float4 A[kSub], B[kSub];
+  load(beg, A);
+  for (int base = beg; base < end; base += 2 * 256 * kSub) {
+    load(base + 256 * kSub, B);
+    run(base, A);
+    load(base + 2 * 256 * kSub, A);
+    run(base + 256 * kSub, B);
+  }
+}
+
 template <typename F>
 __device__ __forceinline__ void for_each_key(const float* __restrict__ src,
                                              int L, F&& f) {
   const int tid = threadIdx.x;
-  for (int base = 0; base < L; base += kBatch * kThreads) {
-    float v[kBatch];
+  const int last4 = ((L + 3) & ~3) - 4;
+  auto load = [&](int base, float4 (&v)[kV]) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int i = base + j * kThreads + tid;
-      v[j] = i < L ? src[i] : 0.0f;
+    for (int j = 0; j < kV; ++j) {
+      const int i = min(base + 4 * (j * kThreads + tid), last4);
+      v[j] = *reinterpret_cast<const float4*>(src + i);
     }
+  };
+  auto process = [&](int base, const float4 (&v)[kV]) {
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int i = base + j * kThreads + tid;
-      if (i < L) f(i, float_key(v[j]));
+    for (int j = 0; j < kV; ++j) {
+      const int i = base + 4 * (j * kThreads + tid);
+      const float e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (i + q < L) f(i + q, float_key(e[q]));
     }
+  };
+  float4 A[kV], B[kV];
+  load(0, A);
+  for (int base = 0; base < L; base += 2 * kRound) {
+    load(base + kRound, B);
+    process(base, A);
+    load(base + 2 * kRound, A);
+    process(base + kRound, B);
   }
 }
 
@@ -505,61 +551,84 @@ __device__ __forceinline__ void select_row_stream(Shared& s, const float* __rest
     c_gt = (use_cand ? above_bin : 0u) + gt_extra;
   }
 
-  // ---- 4. ordered compaction over contiguous spans per wave
+  // ---- 4. ordered compaction over contiguous spans per wave: a wave
+  // reads its span in blocks of 256 positions, lane l holding positions
+  // 4 l .. 4 l + 3 of a block (16-byte loads, kSub blocks per round, the
+  // next round in flight)
   const uint32_t need = static_cast<uint32_t>(topk) - c_gt;   // >= 1
-  const int span = ((L + kWaves - 1) / kWaves + 63) & ~63;
+  const int span = ((L + kWaves - 1) / kWaves + 255) & ~255;
   const int beg = wave * span;
   const int end = min(L, beg + span);
+  const int last4 = ((L + 3) & ~3) - 4;
+  // inclusive prefix sum over the wave's lanes
+  auto wave_incl = [&](uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    return v;
+  };
   uint32_t n_gt = 0, n_eq = 0;
-  for (int base = beg; base < end; base += 64 * kBatch) {
-    uint32_t k[kBatch];
+  wave_blocks(src, beg, end, last4, [&](int blk, const float4& v) {
+    const float e[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int i = base + 64 * j + lane;
-      k[j] = i < end ? float_key(src[i]) : 0u;
+    for (int q = 0; q < 4; ++q) {
+      const int i = blk + 4 * lane + q;
+      const uint32_t k = float_key(e[q]);
+      n_gt += (i < end && k > T) ? 1u : 0u;
+      n_eq += (i < end && k == T) ? 1u : 0u;
     }
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int i = base + 64 * j + lane;
-      n_gt += __popcll(__ballot(i < end && k[j] > T));
-      n_eq += __popcll(__ballot(i < end && k[j] == T));
-    }
+  });
+  for (int o = 32; o > 0; o >>= 1) {
+    n_gt += __shfl_xor(n_gt, o);
+    n_eq += __shfl_xor(n_eq, o);
   }
   if (lane == 0) {
     s.wave_a[wave] = n_gt;
     s.wave_b[wave] = n_eq;
   }
   lds_barrier();
-  uint32_t gt_run = 0, eq_run = 0;
+  uint32_t gt_before = 0, eq_run = 0;
   for (int wv = 0; wv < wave; ++wv) {
-    gt_run += s.wave_a[wv];
+    gt_before += s.wave_a[wv];
     eq_run += s.wave_b[wv];
   }
-  const uint64_t below = lanes_below();
-  for (int base = beg; base < end; base += 64 * kBatch) {
-    uint32_t kb[kBatch];
+  // positions taken before the next block, and == T positions seen
+  uint32_t out_run = gt_before + min(eq_run, need);
+  wave_blocks(src, beg, end, last4, [&](int blk, const float4& v) {
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    bool gt[4], eq[4];
+    uint32_t c_eq = 0;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int i = base + 64 * j + lane;
-      kb[j] = i < end ? float_key(src[i]) : 0u;
+    for (int q = 0; q < 4; ++q) {
+      const int i = blk + 4 * lane + q;
+      const uint32_t k = float_key(e[q]);
+      gt[q] = i < end && k > T;
+      eq[q] = i < end && k == T;
+      c_eq += eq[q] ? 1u : 0u;
     }
+    // == T positions before this lane's, in position order
+    const uint32_t eq_incl = wave_incl(c_eq);
+    uint32_t eq_rank = eq_run + eq_incl - c_eq;
+    bool take[4];
+    uint32_t c_take = 0;
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const int i = base + 64 * j + lane;
-      const uint32_t k = kb[j];
-      const bool gt = i < end && k > T;
-      const bool eq = i < end && k == T;
-      const uint64_t gm = __ballot(gt);
-      const uint64_t em = __ballot(eq);
-      const uint32_t eq_rank = eq_run + __popcll(em & below);
-      const bool take = gt || (eq && eq_rank < need);
-      const uint64_t tm = __ballot(take);
-      const uint32_t o = gt_run + min(eq_run, need) + __popcll(tm & below);
-      if (take && o < static_cast<uint32_t>(topk)) out[o] = i;
-      gt_run += __popcll(gm);
-      eq_run += __popcll(em);
+    for (int q = 0; q < 4; ++q) {
+      take[q] = gt[q] || (eq[q] && eq_rank < need);
+      eq_rank += eq[q] ? 1u : 0u;
+      c_take += take[q] ? 1u : 0u;
     }
-  }
+    const uint32_t take_incl = wave_incl(c_take);
+    uint32_t o = out_run + take_incl - c_take;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (take[q] && o < static_cast<uint32_t>(topk)) out[o] = blk + 4 * lane + q;
+      o += take[q] ? 1u : 0u;
+    }
+    out_run += __shfl(take_incl, 63);
+    eq_run += __shfl(eq_incl, 63);
+  });
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_topk(

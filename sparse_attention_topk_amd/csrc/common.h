@@ -71,19 +71,18 @@ __device__ __forceinline__ int request_of(const int32_t* cu_q, int32_t B,
   return lo;
 }
 
-// Same as request_of, computed by the whole workgroup at once: one parallel
-// load of cu_q instead of a chain of dependent loads.  `counter` is an LDS
-// word; every thread of the workgroup must call this.
-__device__ __forceinline__ int request_of_block(const int32_t* cu_q, int32_t B,
-                                                int32_t t, uint32_t* counter) {
-  if (threadIdx.x == 0) *counter = 0;
-  lds_barrier();
-  uint32_t n = 0;
-  for (int b = threadIdx.x; b < B; b += blockDim.x) n += cu_q[b] <= t;
-  for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
-  if ((threadIdx.x & 63) == 0 && n) atomicAdd(counter, n);
-  lds_barrier();
-  const int r = static_cast<int>(*counter) - 1;
+// Same as request_of, computed by one wave on its own: cu_q is read 64
+// entries per load and the entries <= t are counted with a ballot (no LDS,
+// no barrier; every wave of a workgroup gets the same, wave-uniform value).
+__device__ __forceinline__ int request_of_wave(const int32_t* cu_q, int32_t B, int32_t t) {
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const int32_t c = cu_q[b < B ? b : B];      // cu_q has B + 1 entries
+    n += __popcll(__ballot(b < B && c <= t));
+  }
+  const int r = n - 1;
   return r < 0 ? 0 : (r >= B ? B - 1 : r);
 }
 

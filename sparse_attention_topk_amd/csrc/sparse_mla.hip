@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     const int j = jbeg + kThreads * i + tid;
     p[i] = j < jend ? idx_row[j] : -1;
   }
-  const int b = request_of_block(cu_q, B, t, &sh.counter);
+  const int b = request_of_wave(cu_q, B, t);
   const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
   int32_t bid[kIdxPer];

@@ -65,7 +65,6 @@ struct Shared {
   uint32_t above_bin;     // keys in bins above it
   uint32_t digit;         // radix step result
   uint32_t digit_above;
-  uint32_t counter;
 };
 
 __device__ __forceinline__ uint64_t lanes_below() {
@@ -641,7 +640,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
   // the row's first 32768 scores are requested before its length is known
   float f[kKpt];
   load_row_regs(src, row_stride, f);
-  const int b = request_of_block(cu_q, B, t, &s.counter);
+  const int b = request_of_wave(cu_q, B, t);
   const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
   const int L = pos + 1;
   int32_t* orow = out + static_cast<int64_t>(t) * topk;

@@ -258,6 +258,12 @@ __device__ __forceinline__ bf16x8 lds_b128(uint32_t addr) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
+template <int OFF>
+__device__ __forceinline__ float lds_f32(uint32_t addr) {
+  float r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
 template <int N, typename T>
 __device__ __forceinline__ void lgkm_keep(T& r) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "n"(N));
@@ -381,6 +387,10 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   // per instruction, P pieces per row)
   const int drow = lane / DT::kPieces;
   const int dslot = lane % DT::kPieces;
+  // Each key is read once per call (all query tokens of a block share the
+  // workgroup), so the DMA carries the non-temporal cache policy: streaming
+  // reads then leave L2 and the last-level cache alone.
+  constexpr int kStream = 2;   // cache-policy bits: nt
   auto dma = [&](int slot, int64_t row0) {
     uint8_t* buf = &ring[wave][slot][0];
     const int64_t base = row0 < 0 ? 0 : row0;
@@ -390,19 +400,20 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
       const int piece = dslot ^ (row % DT::kPieces);
       const uint8_t* src = kc + (base + row) * DT::kRowBytes + 16 * piece;
       __builtin_amdgcn_global_load_lds(
-          src, (__attribute__((address_space(3))) void*)(buf + 1024 * m), 16, 0, 0);
+          src, (__attribute__((address_space(3))) void*)(buf + 1024 * m), 16, 0, kStream);
     }
     if constexpr (F8) {
       // the tile's 32 scales, lanes 32 .. 63 a second copy
       __builtin_amdgcn_global_load_lds(
           kscale + base + (lane & 31),
-          (__attribute__((address_space(3))) void*)(buf + DT::kScaleOff), 4, 0, 0);
+          (__attribute__((address_space(3))) void*)(buf + DT::kScaleOff), 4, 0, kStream);
     }
   };
-  // r0[m & 3] holds tile m's first slot from one tile before its DMA
+  // r0[j]: first slot of the tile that ring slot j holds or is loading
+  // (tile j, then j + kRing, ...)
   int64_t r0[kRing];
   static_for<kRing>([&](auto jc) { r0[decltype(jc)::value] = tile_row0(decltype(jc)::value); });
-  static_for<kRing - 1>([&](auto jc) {
+  static_for<kRing>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     if (j < ntiles) dma(j, r0[j]);
   });
@@ -432,14 +443,22 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
       constexpr int j = decltype(jc)::value;   // ring slot of tile i
       const int i = i0 + j;
       if (i >= ntiles) return;
-      if (i + kRing - 1 < ntiles) dma((j + kRing - 1) % kRing, r0[(j + kRing - 1) % kRing]);
       const int64_t my_r0 = r0[j];
       r0[j] = tile_row0(i + kRing);
-      // tile i landed when at most the later tiles' DMAs are pending
+      // tile i landed when at most the later tiles' DMAs are pending (tiles
+      // up to i + kRing - 1 are issued at this point)
       const int later = min(ntiles - 1 - i, kRing - 1);
       wait_tile<DT::kInstr>(later);
       const uint32_t tb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
           (__attribute__((address_space(3))) uint8_t*)(&ring[wave][j][0]))) + rbase;
+      // Slot j is refilled with tile i + kRing as soon as every LDS read of
+      // tile i has returned (the tile then lives in registers): kRing tiles
+      // are in flight while the wave multiplies.  The memory clobber keeps
+      // the DMA behind the reads' waits.
+      auto refill = [&]() {
+        asm volatile("" ::: "memory");
+        if (i + kRing < ntiles) dma(j, r0[j]);
+      };
       bf16x8 kv[8];
       float kscl = 1.0f;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -448,7 +467,16 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
           constexpr int st = decltype(sc)::value;
           kv[st] = lds_b128<0>(tb + 16u * static_cast<uint32_t>((2 * st + hf) ^ csw));
         });
+        static_for<8>([&](auto sc) {
+          constexpr int st = decltype(sc)::value;
+          lgkm_keep<7 - st>(kv[st]);
+        });
+        refill();
       } else {
+        // the key's scale first, then its four 16-byte pieces
+        kscl = lds_f32<0>(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+                   (__attribute__((address_space(3))) uint8_t*)(&ring[wave][j][0]))) +
+               DT::kScaleOff + 4u * static_cast<uint32_t>(col));
         u32x4 raw[4];
         static_for<4>([&](auto jc2) {
           constexpr int jj = decltype(jc2)::value;
@@ -458,10 +486,11 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
         static_for<4>([&](auto jc2) {
           constexpr int jj = decltype(jc2)::value;
           lgkm_keep<3 - jj>(raw[jj]);
+          if constexpr (jj == 0) asm volatile("" : "+v"(kscl));
           kv[2 * jj] = fp8x8_to_bf16x8(raw[jj][0], raw[jj][1]);
           kv[2 * jj + 1] = fp8x8_to_bf16x8(raw[jj][2], raw[jj][3]);
         });
-        kscl = *reinterpret_cast<const float*>(&ring[wave][j][DT::kScaleOff + 4 * col]);
+        refill();
       }
       float part[TQ];
 #pragma unroll
@@ -473,9 +502,6 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
         for (int tt = 0; tt < TQ; ++tt) acc[tt] = f32x16{};
         static_for<8>([&](auto sc) {
           constexpr int st = decltype(sc)::value;
-          if constexpr (!F8) {
-            if (mt == 0) lgkm_keep<7 - st>(kv[st]);
-          }
 #pragma unroll
           for (int tt = 0; tt < TQ; ++tt)
             acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[tt][mt][st], kv[st],

@@ -296,18 +296,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     bid[i] = ok ? bt_row[p[i] / block_size] : -1;
     if (!ok) p[i] = -1;
   }
-  // The query rows (logit B operand: head 32 hh + 16 n + l16, dims
-  // 32 st + 8 g16 .. +8) are issued behind the block-table loads, so the
-  // slot table below only waits for the latter.
-  asm volatile("" ::: "memory");
-  bf16x8 qb[2][kQSteps];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int64_t qbase = (static_cast<int64_t>(t) * kH + 32 * hh + 16 * n + l16) * kD;
-#pragma unroll
-    for (int s = 0; s < kQSteps; ++s)
-      qb[n][s] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * s + 8 * g16);
-  }
 
   // Physical row of every index of this split (padded with -1 to whole
   // tiles) and a 32-bit validity mask per tile, in LDS.
@@ -376,6 +364,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   for (int i = 0; i < kBufs - 1; ++i)
     if (i < ntiles) dma(i, sh.k[i]);
 
+  // The query rows (logit B operand: head 32 hh + 16 n + l16, dims
+  // 32 st + 8 g16 .. +8) are loaded behind the first tiles' DMAs, so their
+  // 72 KB overlap the tiles' latency instead of delaying the slot table and
+  // the first DMAs.  The wait for them also covers those tiles (the count
+  // is in issue order), which land at about the same time; the registers
+  // are then re-defined by an empty asm, so the compiler's wait tracking
+  // no longer ties the logits of every tile to outstanding loads.
+  bf16x8 qb[2][kQSteps];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int64_t qbase = (static_cast<int64_t>(t) * kH + 32 * hh + 16 * n + l16) * kD;
+#pragma unroll
+    for (int s = 0; s < kQSteps; ++s)
+      qb[n][s] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * s + 8 * g16);
+  }
+  wait_vm<0>();
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int s = 0; s < kQSteps; ++s) asm volatile("" : "+v"(qb[n][s]));
+
   for (int it = 0; it < ntiles; ++it) {
     // this wave's part of tile `it` is in when at most the later tiles'
     // loads are pending
@@ -384,9 +393,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     else if (later == 1) wait_vm<kDmaPerWave>();
     else wait_vm<0>();
     tile_barrier();              // (A) tile `it` complete, tile it-1 released
-    if (it + kBufs - 1 < ntiles) dma(it + kBufs - 1, sh.k[(it + kBufs - 1) % kBufs]);
     const uint16_t* kt = sh.k[it % kBufs];
     const uint32_t vb32 = sh.vbits[it];
+    // The ring's refill (tile it + kBufs - 1 into the buffer tile it - 1
+    // left) is issued one DMA instruction after every second logit K-step
+    // rather than all at once: with the memory queue full an issue waits
+    // for room, and spread out those waits overlap the MFMAs in flight.
+    // This lane's source row is read here, before the logits' LDS counting
+    // starts, and the value is tied so the read has returned by then.
+    const bool refill = it + kBufs - 1 < ntiles;
+    int32_t rsl = sh.slots[min(it + kBufs - 1, ntiles - 1) * kT + drow];
+    asm volatile("" : "+v"(rsl));
+    const uint8_t* rsrc = reinterpret_cast<const uint8_t*>(kv) +
+                          static_cast<uint64_t>(max(rsl, 0)) * (2 * kD) + dcol;
+    uint8_t* rdst = reinterpret_cast<uint8_t*>(sh.k[(it + kBufs - 1) % kBufs]) + 9216 * wave;
 
     // ---- logits: part[n][i] = head 32 hh + 16 n + l16, key 16 kh + 4 g16 + i
     // K-step st reads piece 4 st + g16 of the lane's row: group st >> 1 (an
@@ -411,7 +431,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
         part[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qb[1][S], part[1], 0, 0, 0);
         if constexpr (S + kAhead < kQSteps)
           cur = b128_load<1024 * ((S + kAhead) >> 1)>(kbase[(S + kAhead) & 1]);
+        if constexpr (S % 2 == 1 && S / 2 < kDmaPerWave) {
+          constexpr int G = S / 2;
+          if (refill) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_global_load_lds(
+                rsrc + 128 * G, (__attribute__((address_space(3))) void*)(rdst + 1024 * G), 16, 0, 0);
+          }
+        }
       });
+      static_assert(2 * kDmaPerWave <= kQSteps, "the refill fits in the logit K-steps");
     }
 
     // ---- softmax

@@ -315,6 +315,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   }
   tile_barrier();
 
+  static_assert(kQSteps / 4 == 4 && (kR / 32 + 1) / 3 == kDmaPerWave - 4,
+                "the refill pieces 0..3 follow logit K-steps, 4..8 P.V dim tiles");
   // DMA of local tile `tile` into buffer `buf`: wave w fills row group
   // h = w, one instruction per piece group g.  Keys without a row load row 0
   // (finite cache data) and are masked out of the softmax.
@@ -396,9 +398,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     const uint16_t* kt = sh.k[it % kBufs];
     const uint32_t vb32 = sh.vbits[it];
     // The ring's refill (tile it + kBufs - 1 into the buffer tile it - 1
-    // left) is issued one DMA instruction after every second logit K-step
-    // rather than all at once: with the memory queue full an issue waits
-    // for room, and spread out those waits overlap the MFMAs in flight.
+    // left) is issued one DMA instruction at a time, spread over the tile's
+    // MFMAs (after every fourth logit K-step: pieces 0..3; after every third
+    // P.V dim tile: pieces 4..8) rather than all at once: with the memory
+    // queue full an issue waits for room, and spread out those waits
+    // overlap the MFMAs in flight.
     // This lane's source row is read here, before the logits' LDS counting
     // starts, and the value is tied so the read has returned by then.
     const bool refill = it + kBufs - 1 < ntiles;
@@ -431,8 +435,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
         part[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qb[1][S], part[1], 0, 0, 0);
         if constexpr (S + kAhead < kQSteps)
           cur = b128_load<1024 * ((S + kAhead) >> 1)>(kbase[(S + kAhead) & 1]);
-        if constexpr (S % 2 == 1 && S / 2 < kDmaPerWave) {
-          constexpr int G = S / 2;
+        if constexpr (S % 4 == 3) {               // pieces 0 .. 3
+          constexpr int G = S / 4;
           if (refill) {
             asm volatile("" ::: "memory");
             __builtin_amdgcn_global_load_lds(
@@ -440,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
           }
         }
       });
-      static_assert(2 * kDmaPerWave <= kQSteps, "the refill fits in the logit K-steps");
+      
     }
 
     // ---- softmax
@@ -568,6 +572,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
         if constexpr (2 * NT + kAhead < kLoads) {
           a0 = vload(std::integral_constant<int, 2 * NT + kAhead>{});
           a1 = vload(std::integral_constant<int, 2 * NT + kAhead + 1>{});
+        }
+        if constexpr (NT % 3 == 1) {              // pieces 4 .. 8
+          constexpr int G = 4 + NT / 3;
+          if (refill) {
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_global_load_lds(
+                rsrc + 128 * G, (__attribute__((address_space(3))) void*)(rdst + 1024 * G), 16, 0, 0);
+          }
         }
       });
     }

@@ -96,7 +96,7 @@ def cache_write_bytes(b, cfg):
 # ------------------------------------------------------------------ traffic
 CSRC = os.path.join(ROOT, "sparse_attention_topk_amd", "csrc")
 # the dominant call's kernels, and the sources they are built from
-INDEXER_KERNELS = ("k_score_dma", "k_score_mfma", "k_topk")
+INDEXER_KERNELS = ("k_score_dma", "k_topk")
 INDEXER_SRCS = ("common.h", "indexer_score.hip", "topk.hip")
 CALIB_ELEMS = 1 << 28          # calibration: fp32 -> bf16 conversion of 1 GiB
 CALIB_READ, CALIB_WRITE = CALIB_ELEMS * 4, CALIB_ELEMS * 2

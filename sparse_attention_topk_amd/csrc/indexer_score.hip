@@ -18,9 +18,9 @@
 // summed in-lane and one cross-half exchange finishes the head reduction.
 // A workgroup is 4 waves sharing one query block (1 or 2 tokens of a
 // request) and one key chunk; each wave streams 32-key tiles of the paged
-// cache straight from HBM into MFMA operand registers, prefetching the next
-// tile while the current one is multiplied.  Keys of an e4m3 cache are
-// widened exactly to bf16 with the hardware conversion.
+// cache straight from HBM into a private LDS ring (DMA, non-temporal) and
+// reads them back as MFMA operands.  Keys of an e4m3 cache are widened
+// exactly to bf16 with the hardware conversion.
 //
 // Vector path: any dtype / shape within the documented limits, one thread
 // per (query token, key), fp32 arithmetic.
@@ -33,9 +33,6 @@ namespace {
 
 constexpr int kTile = 32;      // keys per MFMA tile
 constexpr int kWaves = 4;      // waves per workgroup
-constexpr int kChunkTiles = 8; // tiles per wave per workgroup
-constexpr int kChunk = kTile * kWaves * kChunkTiles;   // keys per workgroup
-
 // Dim mapping of the MFMA operands.  Lane half hf = lane / 32 and K-step s
 // (0..7) hold 8 consecutive dims starting at:
 //   bf16 keys: 16 s + 8 hf   (one 16-byte load per step, natural order)
@@ -47,187 +44,19 @@ __device__ __forceinline__ int dim_of(int hf, int s) {
   return FP8 ? (64 * hf + 8 * s) : (16 * s + 8 * hf);
 }
 
-template <bool FP8>
-struct KeyTile {
-  bf16x8 v[8];
-};
-
-// Loads one lane's operand of a 32-key tile.  A lane without a key (slot
-// < 0) reads row 0 instead, so the loads are unconditional; its score is
-// masked afterwards.
-template <bool FP8>
-__device__ __forceinline__ void load_key_tile(KeyTile<FP8>& kt,
-                                              const uint8_t* __restrict__ kc,
-                                              int64_t slot, int hf) {
-  const int64_t row_id = slot < 0 ? 0 : slot;
-  if constexpr (!FP8) {
-    const uint8_t* row = kc + row_id * 256;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      kt.v[s] = *reinterpret_cast<const bf16x8*>(row + 2 * dim_of<false>(hf, s));
-  } else {
-    const u32x4* row = reinterpret_cast<const u32x4*>(kc + row_id * 128 + 64 * hf);
-    u32x4 raw[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) raw[j] = row[j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      kt.v[2 * j] = fp8x8_to_bf16x8(raw[j][0], raw[j][1]);
-      kt.v[2 * j + 1] = fp8x8_to_bf16x8(raw[j][2], raw[j][3]);
-    }
-  }
-}
-
-// TQ: query tokens per workgroup (1 or 2).  MT: 32-head M-tiles (H / 32).
-template <int TQ, int MT, bool FP8>
-__global__ __launch_bounds__(256, (TQ * MT > 2) ? 1 : 2) void k_score_mfma(
-    const uint16_t* __restrict__ q, const float* __restrict__ w,
-    const uint8_t* __restrict__ kc, const float* __restrict__ kscale,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ block_table, int32_t max_blocks,
-    int32_t block_size, int64_t num_slots, int32_t max_seq_len,
-    int32_t qblocks_per_req, int32_t nchunks, float* __restrict__ scores,
-    int64_t row_stride) {
-  constexpr int H = 32 * MT;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int hf = lane >> 5;
-  const int col = lane & 31;
-
-  const int chunk = blockIdx.x % nchunks;
-  const int qbg = blockIdx.x / nchunks;
-  const int b = qbg / qblocks_per_req;
-  const int qb = qbg % qblocks_per_req;
-
-  const int32_t L = min(seq_lens[b], max_seq_len);
-  const int32_t tbeg = cu_q[b];
-  const int32_t qlen = min(cu_q[b + 1] - tbeg, L);
-  const int32_t t0 = qb * TQ;
-  if (t0 >= qlen) return;
-  const int nt = min(TQ, qlen - t0);
-  const int32_t pos0 = L - qlen + t0;            // position of the first token
-  const int32_t key_end = min(pos0 + nt, (chunk + 1) * kChunk);   // exclusive
-  const int32_t key_beg = chunk * kChunk;
-  if (key_beg >= key_end) return;
-  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
-
-  // query operand and head weights, per token and M-tile
-  bf16x8 qa[TQ][MT][8];
-  float wr[TQ][MT][16];
-#pragma unroll
-  for (int tt = 0; tt < TQ; ++tt) {
-    const bool live = tt < nt;
-    const int64_t tok = tbeg + t0 + (live ? tt : 0);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int head = mt * 32 + col;
-      const uint16_t* qrow = q + (tok * H + head) * 128;
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        qa[tt][mt][s] = live ? *reinterpret_cast<const bf16x8*>(
-                                   qrow + dim_of<FP8>(hf, s))
-                             : bf16x8{};
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // accumulator register r of a 32x32 tile holds row
-        // 8 * (r / 4) + 4 * hf + r % 4 of column `col`
-        const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
-        wr[tt][mt][r] = live ? w[tok * H + mt * 32 + row] : 0.0f;
-      }
-    }
-  }
-
-  // The wave's tiles are first_tile + kWaves * i, i < kChunkTiles.  A 32-key
-  // tile never spans two cache blocks (block_size is a multiple of 32), so
-  // one block-table entry per tile gives every slot.  Those entries are read
-  // up front with wave-uniform scalar loads: the key loads inside the loop
-  // then depend on no memory access, and waiting for one tile's keys never
-  // waits behind a block-table load issued after a prefetch.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int first_tile = key_beg / kTile + wave_u;
-  const int end_tile = (key_end + kTile - 1) / kTile;
-  int64_t row0[kChunkTiles];          // slot of the tile's first key, or -1
-#pragma unroll
-  for (int i = 0; i < kChunkTiles; ++i) {
-    const int tile = first_tile + kWaves * i;
-    row0[i] = -1;
-    if (tile < end_tile) {
-      const int32_t s0 = tile * kTile;
-      const int32_t blk = s0 / block_size;
-      if (blk < max_blocks) {
-        const int64_t slot0 = static_cast<int64_t>(bt_row[blk]) * block_size + s0 % block_size;
-        if (slot0 >= 0 && slot0 + kTile <= num_slots) row0[i] = slot0;
-      }
-    }
-  }
-  auto lane_slot = [&](int i) -> int64_t {
-    const int32_t s = (first_tile + kWaves * i) * kTile + col;
-    return (row0[i] >= 0 && s < key_end) ? row0[i] + col : -1;
-  };
-
-  // Three tiles per wave are live: the one being multiplied and the next
-  // two, whose loads are in flight.
-  KeyTile<FP8> cur, n1, n2;
-  int64_t slot_cur = lane_slot(0);
-  int64_t slot_n1 = lane_slot(1);
-  load_key_tile<FP8>(cur, kc, slot_cur, hf);
-  load_key_tile<FP8>(n1, kc, slot_n1, hf);
-#pragma unroll
-  for (int i = 0; i < kChunkTiles; ++i) {
-    const int tile = first_tile + kWaves * i;
-    if (tile >= end_tile) break;
-    int64_t slot_n2 = -1;
-    if (i + 2 < kChunkTiles) {
-      slot_n2 = lane_slot(i + 2);
-      load_key_tile<FP8>(n2, kc, slot_n2, hf);
-    }
-    float part[TQ];
-#pragma unroll
-    for (int tt = 0; tt < TQ; ++tt) {
-      part[tt] = 0.0f;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[tt][mt][s], cur.v[s],
-                                                        acc, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          part[tt] = fmaf(wr[tt][mt][r], fmaxf(acc[r], 0.0f), part[tt]);
-      }
-      part[tt] += __shfl_xor(part[tt], 32);
-    }
-    const int32_t s = tile * kTile + col;
-    float ks = slot_cur >= 0 ? 1.0f : 0.0f;
-    if constexpr (FP8) ks *= kscale[slot_cur >= 0 ? slot_cur : 0];
-    // lane half hf stores token hf's score for key s
-    if (hf < nt) {
-      const int32_t pos = pos0 + hf;
-      float v = part[0];
-      if constexpr (TQ > 1) v = hf ? part[1] : part[0];
-      if (s <= pos && s < key_end)
-        scores[(tbeg + t0 + hf) * row_stride + s] = v * ks;
-    }
-    cur = n1;
-    slot_cur = slot_n1;
-    n1 = n2;
-    slot_n1 = slot_n2;
-  }
-}
-
 // ------------------------------------------------- keys through LDS
 // Same contraction, but the keys reach LDS by DMA (global_load_lds_dwordx4)
 // in whole 1 KB lines: one wave instruction carries 4 consecutive 256-byte
 // bf16 rows (or 8 128-byte e4m3 rows).  Each wave streams its own tiles
-// through a private ring of kRing buffers (kRing - 1 tiles in flight), so
-// no barrier is ever needed; the MFMA key operand is read back with
+// through a private ring of kRing buffers, each refilled as soon as its
+// tile has been read into registers (kRing tiles in flight while the wave
+// multiplies), so no barrier is ever needed; the MFMA key operand is read back with
 // ds_read_b128 (e4m3 bytes widened to bf16 in registers).  Lane l of DMA
 // instruction m lands at byte 16 l of block m; piece p (16 bytes) of row r
 // sits at slot p ^ (r % P) of the row (P pieces per row), which spreads
 // the 32 rows of one operand load over distinct banks.  An e4m3 tile's 32
 // scales follow its rows (one 4-byte DMA per lane, two copies).
-constexpr int kRing = 3;
+constexpr int kRing = 2;
 static_assert(kRing >= 2 && kRing <= 4, "tile waits cover rings of 2 to 4 tiles");
 constexpr int kMaxTpw = 64;                      // tiles per wave (one block id per lane)
 template <bool F8>
@@ -620,21 +449,6 @@ __global__ __launch_bounds__(256) void k_score_vector(
     if (cache_dtype == DSA_FP8_E4M3) score *= kscale[slot];
   }
   scores[static_cast<int64_t>(t) * row_stride + s] = score;
-}
-
-template <int TQ, int MT, bool FP8>
-hipError_t launch_mfma(const IndexerArgs& a, hipStream_t stream) {
-  const dsa_batch& b = a.b;
-  const int qbpr = (b.max_q_len + TQ - 1) / TQ;
-  const int nchunks = (b.max_seq_len + kChunk - 1) / kChunk;
-  const int64_t grid = static_cast<int64_t>(b.num_reqs) * qbpr * nchunks;
-  if (grid == 0) return hipSuccess;
-  k_score_mfma<TQ, MT, FP8><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
-      static_cast<const uint16_t*>(a.q), a.w,
-      static_cast<const uint8_t*>(a.k_cache), a.k_scale, b.seq_lens, b.cu_q,
-      b.block_table, b.max_blocks, b.block_size, b.num_slots, b.max_seq_len,
-      qbpr, nchunks, a.scores, a.row_stride);
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -79,10 +79,17 @@ static_assert(sizeof(MlaShared) <= 160 * 1024, "LDS budget");
 static_assert(kH * (kR * 2 + 16) + (kMaxSplits + 1) * kH * 4 <= sizeof(MlaShared::k),
               "staged partials and merge weights fit in the tile buffers");
 
+// fp32 -> bf16, round to nearest even, with gfx950's conversion
+// instruction (v_cvt_pk_bf16_f32: two values per instruction)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// a -> bits 0..15, b -> bits 16..31
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // slot of index j of token t, or -1 when j is outside [jbeg, jend), the
@@ -219,10 +226,8 @@ __device__ __forceinline__ void tile_barrier() {
 
 __device__ __forceinline__ u32x2 pack_bf16x4(const float* p) {
   u32x2 r;
-  r[0] = static_cast<uint32_t>(f32_to_bf16_rne(p[0])) |
-         (static_cast<uint32_t>(f32_to_bf16_rne(p[1])) << 16);
-  r[1] = static_cast<uint32_t>(f32_to_bf16_rne(p[2])) |
-         (static_cast<uint32_t>(f32_to_bf16_rne(p[3])) << 16);
+  r[0] = pack2_bf16(p[0], p[1]);
+  r[1] = pack2_bf16(p[2], p[3]);
   return r;
 }
 
@@ -605,18 +610,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   // bytes of padding per row spread the banks
   constexpr int row_b = kR * 2 + 16;
   uint8_t* stage = reinterpret_cast<uint8_t*>(&sh.k[0][0]);
+  // heads i and i + 1 of a lane are converted together
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; i += 2) {
       const int hl = 4 * g16 + i;
-      const float il = __shfl(inv_l[n], hl);
+      const float il0 = __shfl(inv_l[n], hl);
+      const float il1 = __shfl(inv_l[n], hl + 1);
       const int h = 32 * hh + 16 * n + hl;
 #pragma unroll
       for (int nt = 0; nt < kR / 32; ++nt) {
         const int d = 256 * kh + 16 * nt + l16;
-        *reinterpret_cast<uint16_t*>(stage + h * row_b + 2 * d) =
-            f32_to_bf16_rne(o[n][nt][i] * il);
+        const uint32_t pk = pack2_bf16(o[n][nt][i] * il0, o[n][nt][i + 1] * il1);
+        *reinterpret_cast<uint16_t*>(stage + h * row_b + 2 * d) = static_cast<uint16_t>(pk);
+        *reinterpret_cast<uint16_t*>(stage + (h + 1) * row_b + 2 * d) =
+            static_cast<uint16_t>(pk >> 16);
       }
     }
   }
@@ -697,10 +706,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   unsigned long long* ob = reinterpret_cast<unsigned long long*>(
       out + static_cast<int64_t>(t) * kH * kR) + wq;
   auto put = [&](int h, const float (&x)[4], float inv) {
-    unsigned long long v = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v |= static_cast<unsigned long long>(f32_to_bf16_rne(x[e] * inv)) << (16 * e);
+    const unsigned long long v =
+        static_cast<unsigned long long>(pack2_bf16(x[0] * inv, x[1] * inv)) |
+        (static_cast<unsigned long long>(pack2_bf16(x[2] * inv, x[3] * inv)) << 32);
     ob[h * kWords] = v;
   };
   // with two splits, the other split's rows are in flight while the

@@ -167,6 +167,7 @@ int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
  *   out      [N, n_heads, R] (same dtype as q): for each head
  *            sum_j softmax_j(softmax_scale * q . kv_j) * kv_j[0:R]
  *   lse      [N, n_heads] fp32 log-sum-exp of the scaled logits, or NULL
+ *   softmax_scale  finite and > 0 (else DSA_ERR_INVALID_ARG)
  * A token with no valid index gets out = 0 and lse = -inf.
  * Supported: dtype DSA_F32 or DSA_BF16.  The matrix-core path takes BF16
  * with R = 512, P = 64 and n_heads == 64; other shapes (R + P <= 1024,

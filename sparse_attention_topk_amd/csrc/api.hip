@@ -3,6 +3,7 @@
 // thread-local error text.  Every host-checkable condition is checked before
 // anything is enqueued.
 #include <unistd.h>
+#include <cmath>
 
 #include <atomic>
 #include <chrono>
@@ -144,7 +145,7 @@ int check_indexer(const dsa_batch* b, const void* q, int q_dtype,
 }
 
 int check_mla(const dsa_batch* b, const void* q, const void* kv, int dtype,
-              int n_heads, int R, int P, const int32_t* idx, int topk,
+              int n_heads, int R, int P, const int32_t* idx, int topk, float scale,
               const void* out, const void* ws, size_t ws_bytes) {
   int st = check_batch(b);
   if (st) return st;
@@ -157,6 +158,8 @@ int check_mla(const dsa_batch* b, const void* q, const void* kv, int dtype,
                 n_heads, R, P);
   if (topk < 1 || topk > DSA_MAX_TOPK)
     return fail(DSA_ERR_UNSUPPORTED, "topk %d outside 1..%d", topk, DSA_MAX_TOPK);
+  if (!(scale > 0.0f) || !std::isfinite(scale))
+    return fail(DSA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   const size_t need = mla_ws(b, n_heads, R, P, topk, dtype);
   if (need && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
@@ -318,7 +321,7 @@ int sparse_mla_attn(const dsa_batch* batch, const void* q, const void* kv_cache,
                     float softmax_scale, void* out, float* lse, void* workspace,
                     size_t ws_bytes, void* stream) {
   int st = check_mla(batch, q, kv_cache, dtype, n_heads, kv_lora_rank, rope_dim,
-                     topk_idx, topk, out, workspace, ws_bytes);
+                     topk_idx, topk, softmax_scale, out, workspace, ws_bytes);
   if (st) return st;
   return run_mla(batch, q, kv_cache, dtype, n_heads, kv_lora_rank, rope_dim,
                  topk_idx, topk, softmax_scale, out, lse, workspace,
@@ -365,7 +368,7 @@ int indexshare_forward(const dsa_batch* batch, int32_t n_layers,
     }
     st = check_mla(batch, L.q_mla, L.kv_cache, d->mla_dtype, d->n_heads,
                    d->kv_lora_rank, d->rope_dim, layers[src_stack[i]].topk_idx,
-                   d->topk, L.out, workspace, ws_bytes);
+                   d->topk, d->softmax_scale, L.out, workspace, ws_bytes);
     if (st) return prefix_error(st, "layer %d attention", i);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -160,11 +160,24 @@ __device__ __forceinline__ void wait_vm() {
 }
 // cross-lane reductions over lanes l ^ 16 and l ^ 32 (gfx950 permlane swaps:
 // each returns the values of the two lanes of the pair)
+// max of values that are never NaN (logits or -inf), as plain v_max
+// instructions: through fmaxf the compiler first quiets possible signalling
+// NaNs of each input, an extra instruction per operand
+__device__ __forceinline__ float max_nn(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_nn(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float max_x16_x32(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max_nn(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  return max_nn(__uint_as_float(c[0]), __uint_as_float(c[1]));
 }
 __device__ __forceinline__ float sum_x16_x32(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -452,19 +465,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
       
     }
 
-    // ---- softmax
-    const uint32_t vbl = vb32 >> (16 * kh + 4 * g16);
-    float z[2][4], mx[2];
+    // ---- softmax.  The scale is positive, so the raw logits order as the
+    // scaled ones: maxima are taken raw and scaled once, and each
+    // probability is exp2(fma(raw, scale, -reference)).  Keys without a row
+    // take -inf (skipped when the whole tile has rows, the usual case).
+    float zr[2][4], mx[2];
+    if (__builtin_amdgcn_readfirstlane(vb32) == 0xFFFFFFFFu) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zr[n][i] = part[n][i];
+    } else {
+      const uint32_t vbl = vb32 >> (16 * kh + 4 * g16);
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zr[n][i] = ((vbl >> i) & 1u) ? part[n][i] : -INFINITY;
+    }
     bool need = false;
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
-      mx[n] = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        z[n][i] = ((vbl >> i) & 1u) ? part[n][i] * scale_log2 : -INFINITY;
-        mx[n] = fmaxf(mx[n], z[n][i]);
-      }
-      mx[n] = max_x16_x32(mx[n]);
+      const float r = max_nn(max3_nn(zr[n][0], zr[n][1], zr[n][2]), zr[n][3]);
+      mx[n] = max_x16_x32(r) * scale_log2;
       need |= mx[n] > m_ref[n] + kMoveSlack;
     }
     // speculative probabilities against the current reference maxima
@@ -473,7 +495,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     for (int n = 0; n < 2; ++n) {
       const float mu = m_ref[n] == -INFINITY ? 0.0f : m_ref[n];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pr[n][i] = __builtin_amdgcn_exp2f(z[n][i] - mu);
+      for (int i = 0; i < 4; ++i)
+        pr[n][i] = __builtin_amdgcn_exp2f(fmaf(zr[n][i], scale_log2, -mu));
     }
     const bool wave_need = __ballot(need) != 0;
     sh.xp[wave][0][lane] = pack_bf16x4(pr[0]);
@@ -502,7 +525,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
         if (first || over) m_ref[n] = mfull;
         const float mu = m_ref[n] == -INFINITY ? 0.0f : m_ref[n];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pr[n][i] = __builtin_amdgcn_exp2f(z[n][i] - mu);
+        for (int i = 0; i < 4; ++i)
+          pr[n][i] = __builtin_amdgcn_exp2f(fmaf(zr[n][i], scale_log2, -mu));
       }
       sh.xp[wave][0][lane] = pack_bf16x4(pr[0]);
       sh.xp[wave][1][lane] = pack_bf16x4(pr[1]);

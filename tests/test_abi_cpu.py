@@ -147,6 +147,10 @@ def test_mla_and_cache_write_reject_on_host():
                                ctypes.c_float(0.1), P, None, None, 0, None) == -5
     assert lib.sparse_mla_attn(ctypes.byref(cb), None, P, 1, 4, 64, 16, P, 16,
                                ctypes.c_float(0.1), P, None, None, 0, None) == -1
+    # the softmax scale must be finite and positive
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert lib.sparse_mla_attn(ctypes.byref(cb), P, P, 1, 4, 64, 16, P, 16,
+                                   ctypes.c_float(bad), P, None, None, 0, None) == -1
     # cache write: bf16 keys into an f32 cache, fp8 without scale, bad d
     assert lib.dsa_indexer_cache_write(P, 1, 4, 128, P, 256, P, None, 0, None) == -2
     assert lib.dsa_indexer_cache_write(P, 1, 4, 128, P, 256, P, None, 2, None) == -1

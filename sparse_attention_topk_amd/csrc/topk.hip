@@ -292,37 +292,44 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
       }
       float* cval = reinterpret_cast<float*>(s.cand);
       int32_t* cpos = reinterpret_cast<int32_t*>(s.cand + kRankCap);
-      if (cand_bits) {
+      // the threshold bin holds few keys: groups of 4 keys where no lane
+      // has one are skipped with one wave-uniform test
 #pragma unroll
-        for (int q = 0; q < kKpt; ++q) {
-          if ((cand_bits >> q) & 1u) {
+      for (int j = 0; j < kKpt / 4; ++j) {
+        const uint32_t cj = (cand_bits >> (4 * j)) & 0xFu;
+        if (__ballot(cj != 0u) == 0) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((cj >> e) & 1u) {
             const uint32_t slot = atomicAdd(&s.ncand, 1u);
-            cval[slot] = f[q];
-            cpos[slot] = reg_pos(wave, lane, q >> 2, q & 3);
+            cval[slot] = f[4 * j + e];
+            cpos[slot] = reg_pos(wave, lane, j, e);
           }
         }
       }
       lds_barrier();
       // ---- rank the candidates by (score descending, position ascending);
-      // the top r join the selection
+      // the top r join the selection.  Wave w ranks candidates 64 w + lane
+      // against every candidate, taken one at a time with v_readlane from a
+      // register copy (lane k of round k0 holds candidate k0 + k).
       const int n = static_cast<int>(bin_count);
-      if (tid < n) {
-        const float mv = cval[tid];
-        const int32_t mp = cpos[tid];
+      if (64 * wave < n) {
+        const int c = 64 * wave + lane;
+        const float mv = c < n ? cval[c] : 0.0f;
+        const int32_t mp = c < n ? cpos[c] : 0;
         uint32_t rank = 0;
-        for (int j0 = 0; j0 < n; j0 += 8) {
-          float ov[8];
-          int32_t op[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            ov[u] = cval[j0 + u];
-            op[u] = cpos[j0 + u];
+        for (int k0 = 0; k0 < n; k0 += 64) {
+          const float ov = k0 + lane < n ? cval[k0 + lane] : 0.0f;
+          const int32_t op = k0 + lane < n ? cpos[k0 + lane] : 0;
+          const int m = min(64, n - k0);
+          for (int k = 0; k < m; ++k) {
+            const float v = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ov), k));
+            const int32_t pk = __builtin_amdgcn_readlane(op, k);
+            rank += (v > mv || (v == mv && pk < mp)) ? 1u : 0u;
           }
-#pragma unroll
-          for (int u = 0; u < 8; ++u)
-            rank += (j0 + u < n) && (ov[u] > mv || (ov[u] == mv && op[u] < mp));
         }
-        if (rank < r) atomicOr(&s.bm_sel[mp >> 5], 1u << (mp & 31));
+        if (c < n && rank < r) atomicOr(&s.bm_sel[mp >> 5], 1u << (mp & 31));
       }
     } else {
       // ---- 3b. exact radix select of rank topk over the row's keys gives

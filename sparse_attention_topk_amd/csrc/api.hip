@@ -82,9 +82,16 @@ int64_t score_row_stride(const dsa_batch* b) {
   return (static_cast<int64_t>(b->max_seq_len) + 63) / 64 * 64;
 }
 
-size_t topk_ws(const dsa_batch* b) {
+// fp32 score rows, then the per-chunk score ranges
+size_t topk_scores_bytes(const dsa_batch* b) {
   return round_up(static_cast<size_t>(b->num_q_tokens) *
                   static_cast<size_t>(score_row_stride(b)) * sizeof(float));
+}
+size_t topk_ws(const dsa_batch* b) {
+  return topk_scores_bytes(b) +
+         round_up(static_cast<size_t>(b->num_q_tokens) *
+                  static_cast<size_t>(dsa::indexer_range_stride_max(b->max_seq_len)) *
+                  2 * sizeof(float));
 }
 
 size_t mla_ws(const dsa_batch* b, int n_heads, int R, int P, int topk, int dtype) {
@@ -187,6 +194,9 @@ int run_indexer(const dsa_batch* b, const void* q, int q_dtype, const float* w,
   a.topk_idx = topk_idx;
   a.scores = static_cast<float*>(ws);
   a.row_stride = score_row_stride(b);
+  a.chunk_range = reinterpret_cast<float2*>(static_cast<char*>(ws) + topk_scores_bytes(b));
+  a.range_stride = 0;
+  a.chunk_keys = 0;
   hipError_t e = dsa::launch_indexer_score(a, stream);
   if (e != hipSuccess) return hip_fail(e, "indexer score launch");
   e = dsa::launch_topk(a, stream);

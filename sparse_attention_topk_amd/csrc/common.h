@@ -114,9 +114,22 @@ struct IndexerArgs {
   int32_t* topk_idx;
   float* scores;          // workspace [N, max_seq_len]
   int64_t row_stride;
+  // Per-chunk score ranges (workspace [N, range_stride] of (min, max)): the
+  // matrix-core score pass writes, for each key chunk of kRangeParts waves,
+  // the range of each token's causal scores there, so the top-k needs no
+  // range pass.  Set by launch_indexer_score; null when that pass took the
+  // vector path (the top-k then finds the range itself).
+  float2* chunk_range;
+  int32_t range_stride;   // entries per token
+  int32_t chunk_keys;     // keys per chunk
 };
+constexpr int kRangeParts = 4;   // entries per chunk (one per score wave)
+// entries per token the chunk ranges can need (chunks of at least 128 keys)
+inline int64_t indexer_range_stride_max(int32_t max_seq_len) {
+  return (static_cast<int64_t>(max_seq_len) + 127) / 128 * kRangeParts;
+}
 bool indexer_mfma_ok(const IndexerArgs& a);
-hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t stream);
+hipError_t launch_indexer_score(IndexerArgs& a, hipStream_t stream);
 hipError_t launch_topk(const IndexerArgs& a, hipStream_t stream);
 
 struct MlaArgs {

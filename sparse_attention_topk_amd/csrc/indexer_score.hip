@@ -126,9 +126,11 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ block_table,
     int32_t max_blocks, int32_t block_size, int64_t num_slots,
     int32_t max_seq_len, int32_t qblocks_per_req, int32_t nchunks,
-    int32_t tiles_per_wave, float* __restrict__ scores, int64_t row_stride) {
+    int32_t tiles_per_wave, float* __restrict__ scores, int64_t row_stride,
+    float2* __restrict__ crange, int32_t range_stride) {
   constexpr int H = 32 * MT;
   using DT = DmaTile<F8>;
+  static_assert(kWaves == kRangeParts, "one range entry per wave and chunk");
   __shared__ __align__(16) uint8_t ring[kWaves][kRing][DT::kBytes];
   // the workgroup's scores, [token][key within chunk], written out at the
   // end: score stores interleaved with the key stream slow the reads down
@@ -267,6 +269,9 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   // at slot (4 hf + j) ^ (col % 8)
   const uint32_t rbase = static_cast<uint32_t>(col) * DT::kRowBytes;
   const int csw = col % DT::kPieces;
+  // range of token hf's causal scores among this wave's keys
+  float rmin = INFINITY, rmax = -INFINITY;
+  const int32_t my_pos = hf < nt ? pos0 + hf : -1;
   for (int i0 = 0; i0 < ntiles; i0 += kRing) {
     static_for<kRing>([&](auto jc) {
       constexpr int j = decltype(jc)::value;   // ring slot of tile i
@@ -350,9 +355,22 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
       if constexpr (TQ > 1) v = hf ? part[1] : part[0];
       v *= kscl;
       if (my_r0 < 0) v = 0.0f;
+      const bool causal = (first_tile + kWaves * i) * kTile + col <= my_pos;
+      rmin = fminf(rmin, causal ? v : INFINITY);
+      rmax = fmaxf(rmax, causal ? v : -INFINITY);
       if (hf < TQ) sc[hf < TQ ? hf : 0][(kWaves * i + wave) * kTile + col] = v;
     });
   }
+
+  // ---- the wave's range entries: one per token of the block
+#pragma unroll
+  for (int off = 1; off < 32; off <<= 1) {
+    rmin = fminf(rmin, __shfl_xor(rmin, off));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, off));
+  }
+  if (crange && col == 0 && hf < nt)
+    crange[(tbeg + t0 + hf) * static_cast<int64_t>(range_stride) + chunk * kRangeParts + wave] =
+        make_float2(rmin, rmax);
 
   // ---- write the chunk's scores: token tt, keys key_beg .. key_end - 1
   // (up to the next multiple of 4, inside the padded row), 16 bytes per
@@ -369,21 +387,25 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
 }
 
 template <int TQ, int MT, bool F8, int MAXT>
-hipError_t launch_dma_t(const IndexerArgs& a, int qbpr, int nchunks, int64_t tpw,
+hipError_t launch_dma_t(IndexerArgs& a, int qbpr, int nchunks, int64_t tpw,
                         hipStream_t stream) {
   const dsa_batch& b = a.b;
+  // the range layout the top-k reads: kRangeParts entries per chunk
+  a.chunk_keys = static_cast<int32_t>(kTile * kWaves * tpw);
+  a.range_stride = nchunks * kRangeParts;
   const int64_t grid = static_cast<int64_t>(b.num_reqs) * qbpr * nchunks;
   if (grid == 0) return hipSuccess;
   k_score_dma<TQ, MT, F8, MAXT><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
       static_cast<const uint16_t*>(a.q), a.w,
       static_cast<const uint8_t*>(a.k_cache), a.k_scale, b.seq_lens, b.cu_q,
       b.block_table, b.max_blocks, b.block_size, b.num_slots, b.max_seq_len,
-      qbpr, nchunks, static_cast<int32_t>(tpw), a.scores, a.row_stride);
+      qbpr, nchunks, static_cast<int32_t>(tpw), a.scores, a.row_stride, a.chunk_range,
+      a.range_stride);
   return hipGetLastError();
 }
 
 template <int TQ, int MT, bool F8>
-hipError_t launch_dma(const IndexerArgs& a, hipStream_t stream) {
+hipError_t launch_dma(IndexerArgs& a, hipStream_t stream) {
   const dsa_batch& b = a.b;
   const int qbpr = (b.max_q_len + TQ - 1) / TQ;
   // one round of workgroups: about 256 of them (one per CU) share the
@@ -460,7 +482,7 @@ bool indexer_mfma_ok(const IndexerArgs& a) {
          a.b.block_size % kTile == 0;
 }
 
-hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t stream) {
+hipError_t launch_indexer_score(IndexerArgs& a, hipStream_t stream) {
   const dsa_batch& b = a.b;
   if (b.num_q_tokens == 0) return hipSuccess;
   if (indexer_mfma_ok(a)) {
@@ -474,6 +496,7 @@ hipError_t launch_indexer_score(const IndexerArgs& a, hipStream_t stream) {
     if (one) return mt2 ? launch_dma<1, 2, true>(a, stream) : launch_dma<1, 1, true>(a, stream);
     return mt2 ? launch_dma<2, 2, true>(a, stream) : launch_dma<2, 1, true>(a, stream);
   }
+  a.chunk_range = nullptr;   // the top-k finds the range itself
   const int key_blocks = (b.max_seq_len + 255) / 256;
   const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * key_blocks;
   k_score_vector<<<static_cast<unsigned>(grid), 256, 0, stream>>>(

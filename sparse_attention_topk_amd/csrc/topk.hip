@@ -168,6 +168,28 @@ __device__ __forceinline__ void find_threshold_bin(Shared& s, uint32_t r) {
   lds_barrier();
 }
 
+// This thread's share of the row's score range (then reduced over the
+// workgroup).  With the score pass's per-chunk ranges (rng: the row's
+// entries, kRangeParts per chunk of chunk_keys keys) the chunks holding
+// positions 0 .. L - 1 are combined; without them own(lo, hi) scans the
+// keys.  Both give the exact min / max of the row's scores, NaN skipped.
+template <typename F>
+__device__ __forceinline__ void row_range(const float2* __restrict__ rng, int32_t chunk_keys,
+                                          int L, F&& own, float& vmin, float& vmax) {
+  if (rng) {
+    vmin = INFINITY;
+    vmax = -INFINITY;
+    const int nent = ((L - 1) / chunk_keys + 1) * kRangeParts;
+    for (int e = threadIdx.x; e < nent; e += kThreads) {
+      const float2 r = rng[e];
+      vmin = fminf(vmin, r.x);
+      vmax = fmaxf(vmax, r.y);
+    }
+  } else {
+    own(vmin, vmax);
+  }
+}
+
 // ------------------------------------------------------------ register path
 // Position of register key (j, e) of a lane: wave w covers positions
 // 2048 w .. 2048 w + 2047, its load j (0..7) the 256 positions from
@@ -205,7 +227,9 @@ __device__ __forceinline__ void load_row_regs(const float* __restrict__ src,
 // positions (bit p & 31 of word p >> 5), emitted in position order at the
 // end.
 __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int L,
-                                                int topk, int32_t* __restrict__ out) {
+                                                int topk, const float2* __restrict__ rng,
+                                                int32_t chunk_keys,
+                                                int32_t* __restrict__ out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -223,12 +247,16 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
         if (reg_pos(wave, lane, j, e) >= L) f[4 * j + e] = __builtin_nanf("");
   }
   const uint32_t absent = static_cast<uint32_t>(kRegCap - L);   // NaNs in bin 0
-  float vmin = f[0], vmax = f[0];
+  float vmin, vmax;
+  row_range(rng, chunk_keys, L, [&](float& lo, float& hi) {
+    lo = f[0];
+    hi = f[0];
 #pragma unroll
-  for (int j = 1; j < kKpt; ++j) {
-    vmin = fminf(vmin, f[j]);
-    vmax = fmaxf(vmax, f[j]);
-  }
+    for (int j = 1; j < kKpt; ++j) {
+      lo = fminf(lo, f[j]);
+      hi = fmaxf(hi, f[j]);
+    }
+  }, vmin, vmax);
   for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
   s.bm_sel[tid] = 0;
   s.bm_eq[tid] = 0;
@@ -482,18 +510,23 @@ __device__ __forceinline__ void for_each_key(const float* __restrict__ src,
 }
 
 __device__ __forceinline__ void select_row_stream(Shared& s, const float* __restrict__ src, int L,
-                                  int topk, int32_t* __restrict__ out) {
+                                  int topk, const float2* __restrict__ rng,
+                                  int32_t chunk_keys, int32_t* __restrict__ out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // ---- 1. range
-  float vmin = INFINITY, vmax = -INFINITY;
-  for_each_key(src, L, [&](int, uint32_t k) {
-    const float f = key_float(k);
-    vmin = fminf(vmin, f);
-    vmax = fmaxf(vmax, f);
-  });
+  // ---- 1. range (a pass over the row only without the score pass's)
+  float vmin, vmax;
+  row_range(rng, chunk_keys, L, [&](float& lo, float& hi) {
+    lo = INFINITY;
+    hi = -INFINITY;
+    for_each_key(src, L, [&](int, uint32_t k) {
+      const float f = key_float(k);
+      lo = fminf(lo, f);
+      hi = fmaxf(hi, f);
+    });
+  }, vmin, vmax);
   for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
   if (tid == 0) s.ncand = 0;
   range_reduce(s, vmin, vmax);
@@ -639,6 +672,7 @@ __device__ __forceinline__ void select_row_stream(Shared& s, const float* __rest
 
 __global__ __launch_bounds__(kThreads, 1) void k_topk(
     const float* __restrict__ scores, int64_t row_stride,
+    const float2* __restrict__ crange, int32_t range_stride, int32_t chunk_keys,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
     int32_t B, int32_t max_seq_len, int32_t topk, int32_t* __restrict__ out) {
   __shared__ Shared s;
@@ -655,10 +689,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
     for (int j = threadIdx.x; j < topk; j += kThreads) orow[j] = j < L ? j : -1;
     return;
   }
+  const float2* rng = crange ? crange + static_cast<int64_t>(t) * range_stride : nullptr;
   if (L <= kRegCap)
-    select_row_regs(s, f, L, topk, orow);
+    select_row_regs(s, f, L, topk, rng, chunk_keys, orow);
   else
-    select_row_stream(s, src, L, topk, orow);
+    select_row_stream(s, src, L, topk, rng, chunk_keys, orow);
 }
 
 }  // namespace
@@ -666,8 +701,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
 hipError_t launch_topk(const IndexerArgs& a, hipStream_t stream) {
   if (a.b.num_q_tokens == 0) return hipSuccess;
   k_topk<<<a.b.num_q_tokens, kThreads, 0, stream>>>(
-      a.scores, a.row_stride, a.b.seq_lens, a.b.cu_q, a.b.num_reqs,
-      a.b.max_seq_len, a.topk, a.topk_idx);
+      a.scores, a.row_stride, a.chunk_range, a.range_stride, a.chunk_keys, a.b.seq_lens,
+      a.b.cu_q, a.b.num_reqs, a.b.max_seq_len, a.topk, a.topk_idx);
   return hipGetLastError();
 }
 

@@ -111,10 +111,18 @@ def test_workspace_size_formula():
     dsa = ensure_library()
     lib = dsa.load_library()
     cb = _batch(dsa)
-    # fp32 score rows padded to a multiple of 64 positions
-    assert lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb), 16) == 4 * 128 * 4
+    def up(x):
+        return (x + 255) // 256 * 256
+    # fp32 score rows padded to a multiple of 64 positions, then per token
+    # 4 (min, max) float pairs for each possible chunk of 128 keys
+    assert lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb), 16) == (
+        up(4 * 128 * 4) + up(4 * 4 * 1 * 8))
     cb100 = _batch(dsa, max_seq_len=100)
-    assert lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb100), 16) == 4 * 128 * 4
+    assert lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb100), 16) == (
+        up(4 * 128 * 4) + up(4 * 4 * 1 * 8))
+    cb_long = _batch(dsa, max_seq_len=32768)
+    assert lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb_long), 16) == (
+        up(4 * 32768 * 4) + up(4 * 4 * 256 * 8))
     # no split for the vector path, so no MLA workspace
     assert lib.sparse_mla_attn_workspace_size(ctypes.byref(cb), 4, 64, 16, 16, 0) == 0
     # the matrix-core path with few workgroups splits the keys of a token:
@@ -122,8 +130,6 @@ def test_workspace_size_formula():
     # workgroups for 256 CUs); bf16 partials [N, split, H, R], their
     # log-sum-exps [N, split, H] and one 8-byte arrival word per token, each
     # region 256-byte aligned
-    def up(x):
-        return (x + 255) // 256 * 256
     th = 4 * 16 * 64
     assert lib.sparse_mla_attn_workspace_size(ctypes.byref(cb), 64, 512, 64, 2048, 1) == (
         up(th * 512 * 2) + up(th * 4) + up(4 * 8))

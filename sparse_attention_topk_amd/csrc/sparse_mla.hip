@@ -191,7 +191,8 @@ __device__ __forceinline__ float sum_x16_x32(float x) {
 // arrivals (lower 16): a word with another tag, whatever the workspace held
 // before, counts as no arrival.  A compare-and-swap fails only when another
 // split of the token changed the word after it was read, which each of them
-// does once, so the loop ends within n_split rounds.
+// does once, so the loop ends within n_split + 1 rounds (the first may
+// fail on the guess below).
 __device__ __forceinline__ float lo_f(unsigned long long u) {
   return __uint_as_float(static_cast<uint32_t>(u));
 }
@@ -199,9 +200,13 @@ __device__ __forceinline__ float hi_f(unsigned long long u) {
   return __uint_as_float(static_cast<uint32_t>(u >> 32));
 }
 
+// The first compare-and-swap guesses that every other split has already
+// counted, so the split that arrives last (the one that merges, on the
+// kernel's critical path) usually needs a single round trip; a wrong guess
+// costs the others one more.
 __device__ uint32_t arrive(unsigned long long* word, unsigned long long tag, int n_split) {
-  unsigned long long cur = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int round = 0; round <= n_split; ++round) {
+  unsigned long long cur = (tag << 16) | static_cast<unsigned long long>(n_split - 1);
+  for (int round = 0; round <= n_split + 1; ++round) {
     const unsigned long long next = (cur >> 16) == tag ? cur + 1 : (tag << 16) | 1ull;
     const unsigned long long prev = atomicCAS(word, cur, next);
     if (prev == cur) return static_cast<uint32_t>(next & 0xFFFFull);

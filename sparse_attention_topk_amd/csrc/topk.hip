@@ -173,14 +173,17 @@ __device__ __forceinline__ void find_threshold_bin(Shared& s, uint32_t r) {
 // entries, kRangeParts per chunk of chunk_keys keys) the chunks holding
 // positions 0 .. L - 1 are combined; without them own(lo, hi) scans the
 // keys.  Both give the exact min / max of the row's scores, NaN skipped.
+// pre: entry threadIdx.x of the row, loaded early (before L was known).
 template <typename F>
 __device__ __forceinline__ void row_range(const float2* __restrict__ rng, int32_t chunk_keys,
-                                          int L, F&& own, float& vmin, float& vmax) {
+                                          int L, float2 pre, F&& own, float& vmin,
+                                          float& vmax) {
   if (rng) {
-    vmin = INFINITY;
-    vmax = -INFINITY;
     const int nent = ((L - 1) / chunk_keys + 1) * kRangeParts;
-    for (int e = threadIdx.x; e < nent; e += kThreads) {
+    const bool mine = static_cast<int>(threadIdx.x) < nent;
+    vmin = mine ? pre.x : INFINITY;
+    vmax = mine ? pre.y : -INFINITY;
+    for (int e = threadIdx.x + kThreads; e < nent; e += kThreads) {
       const float2 r = rng[e];
       vmin = fminf(vmin, r.x);
       vmax = fmaxf(vmax, r.y);
@@ -228,7 +231,7 @@ __device__ __forceinline__ void load_row_regs(const float* __restrict__ src,
 // end.
 __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int L,
                                                 int topk, const float2* __restrict__ rng,
-                                                int32_t chunk_keys,
+                                                int32_t chunk_keys, float2 pre,
                                                 int32_t* __restrict__ out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -248,7 +251,7 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
   }
   const uint32_t absent = static_cast<uint32_t>(kRegCap - L);   // NaNs in bin 0
   float vmin, vmax;
-  row_range(rng, chunk_keys, L, [&](float& lo, float& hi) {
+  row_range(rng, chunk_keys, L, pre, [&](float& lo, float& hi) {
     lo = f[0];
     hi = f[0];
 #pragma unroll
@@ -511,14 +514,15 @@ __device__ __forceinline__ void for_each_key(const float* __restrict__ src,
 
 __device__ __forceinline__ void select_row_stream(Shared& s, const float* __restrict__ src, int L,
                                   int topk, const float2* __restrict__ rng,
-                                  int32_t chunk_keys, int32_t* __restrict__ out) {
+                                  int32_t chunk_keys, float2 pre,
+                                  int32_t* __restrict__ out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
   // ---- 1. range (a pass over the row only without the score pass's)
   float vmin, vmax;
-  row_range(rng, chunk_keys, L, [&](float& lo, float& hi) {
+  row_range(rng, chunk_keys, L, pre, [&](float& lo, float& hi) {
     lo = INFINITY;
     hi = -INFINITY;
     for_each_key(src, L, [&](int, uint32_t k) {
@@ -681,6 +685,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
   // the row's first 32768 scores are requested before its length is known
   float f[kKpt];
   load_row_regs(src, row_stride, f);
+  // and the first kThreads of its score-range entries
+  const float2* rng = crange ? crange + static_cast<int64_t>(t) * range_stride : nullptr;
+  float2 pre = make_float2(INFINITY, -INFINITY);
+  if (rng && static_cast<int>(threadIdx.x) < range_stride) pre = rng[threadIdx.x];
   const int b = request_of_wave(cu_q, B, t);
   const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
   const int L = pos + 1;
@@ -689,11 +697,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
     for (int j = threadIdx.x; j < topk; j += kThreads) orow[j] = j < L ? j : -1;
     return;
   }
-  const float2* rng = crange ? crange + static_cast<int64_t>(t) * range_stride : nullptr;
   if (L <= kRegCap)
-    select_row_regs(s, f, L, topk, rng, chunk_keys, orow);
+    select_row_regs(s, f, L, topk, rng, chunk_keys, pre, orow);
   else
-    select_row_stream(s, src, L, topk, rng, chunk_keys, orow);
+    select_row_stream(s, src, L, topk, rng, chunk_keys, pre, orow);
 }
 
 }  // namespace

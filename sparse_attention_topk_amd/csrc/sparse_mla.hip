@@ -16,16 +16,18 @@
 // crosses HBM once per token.  Rows are gathered in 32-row tiles straight
 // from HBM into LDS (global_load_lds_dwordx4) through a ring of four tile
 // buffers (whole 128-byte lines per DMA instruction): three tiles are in
-// flight while one is multiplied.  Each of the
-// four waves owns 32 heads (hh) and one half (kh) of the work:
-//   logits: the 16 keys 16 kh .. 16 kh + 15 of the tile against its 32
+// flight while one is multiplied.  Eight waves, two per SIMD: each owns 16
+// heads (head group hg) and one half (kh) of the work, and the first four
+// also issue the tile DMAs, so when one of them waits for room in the memory
+// queue the other wave on its SIMD keeps the matrix core busy:
+//   logits: the 16 keys 16 kh .. 16 kh + 15 of the tile against its 16
 //           heads over all 576 dims (v_mfma_f32_16x16x32_bf16, queries in
-//           registers), so each tile row is read from LDS by two waves;
+//           registers), so each tile row is read from LDS by four waves;
 //   softmax: the two waves of a head group swap their per-head maxima and
 //           bf16 probabilities through LDS; the reference maximum moves
 //           rarely (only when a tile beats it by more than 2^8), so the
 //           common tile needs no rescale of the accumulators;
-//   P.V:    value dims 256 kh .. 256 kh + 255 of its 32 heads over all 32
+//   P.V:    value dims 256 kh .. 256 kh + 255 of its 16 heads over all 32
 //           keys, the value operand read with the gfx950 LDS transpose load
 //           straight from the row-major tile.
 // With more than one key split, each split writes its normalised partial
@@ -46,11 +48,15 @@ namespace {
 constexpr int kR = 512, kP = 64, kD = kR + kP;
 constexpr int kH = 64;                  // heads per workgroup (all of them)
 constexpr int kT = 32;                  // keys per tile
-constexpr int kThreads = 256;           // 4 waves, one per SIMD
+constexpr int kHT = 1;                  // 16-head tiles per wave
+constexpr int kHG = kH / (16 * kHT);    // head groups (4)
+constexpr int kWavesM = 2 * kHG;        // waves: head group x key half (8, two per SIMD)
+constexpr int kThreads = 64 * kWavesM;  // 512
+constexpr int kDmaWaves = 4;            // waves that issue the tile DMAs
 constexpr int kPieces = kD / 8;         // 16-byte pieces per latent row (72)
 constexpr int kTilePieces = kT * kPieces;             // 2304
 constexpr int kDmaInstr = kTilePieces / 64;           // 36 wave loads per tile
-constexpr int kDmaPerWave = kDmaInstr / 4;            // 9
+constexpr int kDmaPerWave = kDmaInstr / kDmaWaves;    // 9
 constexpr int kBufs = 4;                // tiles resident: current + 3 in flight
 constexpr int kMaxSplitLen = 2048;      // indices per workgroup
 constexpr int kMaxSplits = 32;          // merge weights fit behind the staged block
@@ -69,10 +75,10 @@ struct MlaShared {
   uint16_t k[kBufs][kT * kD];           // row-major tiles, 4 x 36864 B
   int32_t slots[kMaxSplitLen];          // physical row of each index, or -1
   uint32_t vbits[kMaxSplitLen / kT];    // per tile: bit k = key k has a row
-  u32x2 xp[4][2][64];                   // bf16 probabilities, per wave / head tile / lane
-  float xm[4][2][64];                   // per-head tile maxima (sums at the end)
-  alignas(16) uint32_t xf[4];           // per wave: a reference maximum moves
-  alignas(16) uint32_t xr[4];           // per wave: the split must restart
+  u32x2 xp[kWavesM][kHT][64];           // bf16 probabilities, per wave / head tile / lane
+  float xm[kWavesM][kHT][64];           // per-head tile maxima (sums at the end)
+  alignas(16) uint32_t xf[kWavesM];     // per wave: a reference maximum moves
+  alignas(16) uint32_t xr[kWavesM];     // per wave: the split must restart
   uint32_t counter;
 };
 static_assert(sizeof(MlaShared) <= 160 * 1024, "LDS budget");
@@ -242,6 +248,18 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// whether any wave's flag word is set (kWavesM words, 16-byte aligned)
+__device__ __forceinline__ bool any_word(const uint32_t* w) {
+  static_assert(kWavesM % 4 == 0, "flag words are read four at a time");
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < kWavesM; i += 4) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(w + i);
+    o |= v[0] | v[1] | v[2] | v[3];
+  }
+  return o != 0;
+}
+
 __device__ __forceinline__ u32x2 pack_bf16x4(const float* p) {
   u32x2 r;
   r[0] = pack2_bf16(p[0], p[1]);
@@ -249,14 +267,14 @@ __device__ __forceinline__ u32x2 pack_bf16x4(const float* p) {
   return r;
 }
 
-// One workgroup = (query token, key split), all 64 heads, 4 waves (one per
-// SIMD).  Wave w = 2 hh + kh: heads 32 hh .. 32 hh + 31 in two 16-head tiles
-// n = 0, 1 (head 32 hh + 16 n + lane % 16 in the query operand).
+// One workgroup = (query token, key split), all 64 heads, kWavesM waves (two
+// per SIMD).  Wave w = 2 hg + kh: heads 16 kHT hg .. in kHT 16-head tiles n
+// (head 16 kHT hg + 16 n + lane % 16 in the query operand).
 //   logits:  S^T[16 keys, 16 heads] = K . Q^T per head tile over 18 K-steps,
 //            keys 16 kh + 4 g16 + i on the rows (lane group g16 = lane / 16),
 //            so lane (l16, g16) holds head l16's logits of 4 keys;
 //   softmax: max over the wave's 16 keys in-lane plus two permlane swaps,
-//            then the partner wave's (2 hh + 1 - kh) maxima through LDS;
+//            then the partner wave's (2 hg + 1 - kh) maxima through LDS;
 //   P.V:     O[16 heads, 16 dims] += P[16 heads, 32 keys] . V[32 keys, 16 dims]
 //            with K-index 8 g16 + e = own key 16 kh + 4 g16 + e (e < 4) or
 //            the partner's key 16 (1 - kh) + 4 g16 + e - 4: the lane's own 4
@@ -281,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;
   const int g16 = lane >> 4;
-  const int hh = wave >> 1;
+  const int hg = wave >> 1;             // heads 16 kHT hg .. 16 kHT hg + 16 kHT - 1
   const int kh = wave & 1;
   const int partner = wave ^ 1;
 
@@ -302,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   const int jpad = jbeg + ntiles * kT;           // tile-aligned end
 
   // Index loads first: they depend only on t.
-  constexpr int kIdxPer = kMaxSplitLen / kThreads;   // 8
+  constexpr int kIdxPer = kMaxSplitLen / kThreads;   // 4
   int32_t p[kIdxPer];
 #pragma unroll
   for (int i = 0; i < kIdxPer; ++i) {
@@ -340,13 +358,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
 
   static_assert(kQSteps / 4 == 4 && (kR / 32 + 1) / 3 == kDmaPerWave - 4,
                 "the refill pieces 0..3 follow logit K-steps, 4..8 P.V dim tiles");
-  // DMA of local tile `tile` into buffer `buf`: wave w fills row group
-  // h = w, one instruction per piece group g.  Keys without a row load row 0
-  // (finite cache data) and are masked out of the softmax.
+  // DMA of local tile `tile` into buffer `buf`: wave w < kDmaWaves fills
+  // row group h = w, one instruction per piece group g (the other waves
+  // issue none).  Keys without a row load row 0 (finite cache data) and are
+  // masked out of the softmax.
   const int dpi = (lane >> 3) ^ (wave & 1);
   const int drow = 8 * wave + ((lane & 7) ^ (4 * (dpi & 1)));
   const uint32_t dcol = 16u * static_cast<uint32_t>(dpi);
   auto dma = [&](int tile, uint16_t* buf) {
+    if (wave >= kDmaWaves) return;
     const int32_t sl = sh.slots[tile * kT + drow];
     const uint8_t* src = reinterpret_cast<const uint8_t*>(kv) +
                          static_cast<uint64_t>(max(sl, 0)) * (2 * kD) + dcol;
@@ -377,36 +397,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     voff_b[m] = tile_byte(vrow_b, 32 * kh + 2 * m + vb_lo) + half;
   }
 
-  f32x4 o[2][kR / 32];                  // heads 32 hh + 16 n + 4 g16 + i, dims 256 kh + 16 nt + l16
+  f32x4 o[kHT][kR / 32];                  // heads 16 kHT hg + 16 n + 4 g16 + i, dims 256 kh + 16 nt + l16
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
+  for (int n = 0; n < kHT; ++n)
 #pragma unroll
     for (int nt = 0; nt < kR / 32; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
-  float m_ref[2] = {-INFINITY, -INFINITY};   // head 32 hh + 16 n + l16
-  float l_part[2] = {0.0f, 0.0f};            // this lane's share of the sum
+  float m_ref[kHT], l_part[kHT];   // head 16 kHT hg + 16 n + l16: reference, this lane's sum
+#pragma unroll
+  for (int n = 0; n < kHT; ++n) {
+    m_ref[n] = -INFINITY;
+    l_part[n] = 0.0f;
+  }
 
 #pragma unroll
   for (int i = 0; i < kBufs - 1; ++i)
     if (i < ntiles) dma(i, sh.k[i]);
 
-  // The query rows (logit B operand: head 32 hh + 16 n + l16, dims
+  // The query rows (logit B operand: head 16 kHT hg + 16 n + l16, dims
   // 32 st + 8 g16 .. +8) are loaded behind the first tiles' DMAs, so their
   // 72 KB overlap the tiles' latency instead of delaying the slot table and
   // the first DMAs.  The wait for them also covers those tiles (the count
   // is in issue order), which land at about the same time; the registers
   // are then re-defined by an empty asm, so the compiler's wait tracking
   // no longer ties the logits of every tile to outstanding loads.
-  bf16x8 qb[2][kQSteps];
+  bf16x8 qb[kHT][kQSteps];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int64_t qbase = (static_cast<int64_t>(t) * kH + 32 * hh + 16 * n + l16) * kD;
+  for (int n = 0; n < kHT; ++n) {
+    const int64_t qbase = (static_cast<int64_t>(t) * kH + 16 * kHT * hg + 16 * n + l16) * kD;
 #pragma unroll
     for (int s = 0; s < kQSteps; ++s)
       qb[n][s] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * s + 8 * g16);
   }
   wait_vm<0>();
 #pragma unroll
-  for (int n = 0; n < 2; ++n)
+  for (int n = 0; n < kHT; ++n)
 #pragma unroll
     for (int s = 0; s < kQSteps; ++s) asm volatile("" : "+v"(qb[n][s]));
 
@@ -428,17 +452,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     // overlap the MFMAs in flight.
     // This lane's source row is read here, before the logits' LDS counting
     // starts, and the value is tied so the read has returned by then.
-    const bool refill = it + kBufs - 1 < ntiles;
-    int32_t rsl = sh.slots[min(it + kBufs - 1, ntiles - 1) * kT + drow];
+    const bool refill = wave < kDmaWaves && it + kBufs - 1 < ntiles;
+    int32_t rsl = wave < kDmaWaves ? sh.slots[min(it + kBufs - 1, ntiles - 1) * kT + drow] : 0;
     asm volatile("" : "+v"(rsl));
     const uint8_t* rsrc = reinterpret_cast<const uint8_t*>(kv) +
                           static_cast<uint64_t>(max(rsl, 0)) * (2 * kD) + dcol;
     uint8_t* rdst = reinterpret_cast<uint8_t*>(sh.k[(it + kBufs - 1) % kBufs]) + 9216 * wave;
 
-    // ---- logits: part[n][i] = head 32 hh + 16 n + l16, key 16 kh + 4 g16 + i
+    // ---- logits: part[n][i] = head 16 kHT hg + 16 n + l16, key 16 kh + 4 g16 + i
     // K-step st reads piece 4 st + g16 of the lane's row: group st >> 1 (an
     // immediate 1024 (st >> 1)) and one of two per-lane offsets.
-    f32x4 part[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    f32x4 part[kHT];
+#pragma unroll
+    for (int n = 0; n < kHT; ++n) part[n] = f32x4{0, 0, 0, 0};
     {
       const uint32_t kb = lds_addr(kt);
       const uint32_t kbase[2] = {kb + kodd[0], kb + kodd[1]};
@@ -454,8 +480,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
         bf16x8& cur = kr[S % kAhead];
         constexpr int kAfter = (kQSteps - 1 - S) < (kAhead - 1) ? (kQSteps - 1 - S) : (kAhead - 1);
         lgkm_keep<kAfter>(cur);
-        part[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qb[0][S], part[0], 0, 0, 0);
-        part[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qb[1][S], part[1], 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < kHT; ++n)
+          part[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qb[n][S], part[n], 0, 0, 0);
         if constexpr (S + kAhead < kQSteps)
           cur = b128_load<1024 * ((S + kAhead) >> 1)>(kbase[(S + kAhead) & 1]);
         if constexpr (S % 4 == 3) {               // pieces 0 .. 3
@@ -474,44 +501,44 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     // scaled ones: maxima are taken raw and scaled once, and each
     // probability is exp2(fma(raw, scale, -reference)).  Keys without a row
     // take -inf (skipped when the whole tile has rows, the usual case).
-    float zr[2][4], mx[2];
+    float zr[kHT][4], mx[kHT];
     if (__builtin_amdgcn_readfirstlane(vb32) == 0xFFFFFFFFu) {
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+      for (int n = 0; n < kHT; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) zr[n][i] = part[n][i];
     } else {
       const uint32_t vbl = vb32 >> (16 * kh + 4 * g16);
 #pragma unroll
-      for (int n = 0; n < 2; ++n)
+      for (int n = 0; n < kHT; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) zr[n][i] = ((vbl >> i) & 1u) ? part[n][i] : -INFINITY;
     }
     bool need = false;
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int n = 0; n < kHT; ++n) {
       const float r = max_nn(max3_nn(zr[n][0], zr[n][1], zr[n][2]), zr[n][3]);
       mx[n] = max_x16_x32(r) * scale_log2;
       need |= mx[n] > m_ref[n] + kMoveSlack;
     }
     // speculative probabilities against the current reference maxima
-    float pr[2][4];
+    float pr[kHT][4];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int n = 0; n < kHT; ++n) {
       const float mu = m_ref[n] == -INFINITY ? 0.0f : m_ref[n];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         pr[n][i] = __builtin_amdgcn_exp2f(fmaf(zr[n][i], scale_log2, -mu));
     }
     const bool wave_need = __ballot(need) != 0;
-    sh.xp[wave][0][lane] = pack_bf16x4(pr[0]);
-    sh.xp[wave][1][lane] = pack_bf16x4(pr[1]);
-    sh.xm[wave][0][lane] = mx[0];
-    sh.xm[wave][1][lane] = mx[1];
+#pragma unroll
+    for (int n = 0; n < kHT; ++n) {
+      sh.xp[wave][n][lane] = pack_bf16x4(pr[n]);
+      sh.xm[wave][n][lane] = mx[n];
+    }
     if (lane == 0) sh.xf[wave] = wave_need ? 1u : 0u;
     tile_barrier();              // (B) maxima, flags and probabilities published
-    const u32x4 flags = *reinterpret_cast<const u32x4*>(sh.xf);
-    if ((flags[0] | flags[1] | flags[2] | flags[3]) != 0) {
+    if (any_word(sh.xf)) {
       // Some reference maximum of the workgroup moves; every wave takes this
       // branch.  A head's first key sets its reference (its sums are still
       // zero, nothing to rescale).  A head whose tile maximum beats its
@@ -522,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
       // never rescaled in place.
       bool restart = false;
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      for (int n = 0; n < kHT; ++n) {
         const float mfull = fmaxf(mx[n], sh.xm[partner][n][lane]);
         const bool first = m_ref[n] == -INFINITY && mfull != -INFINITY;
         const bool over = m_ref[n] != -INFINITY && mfull > m_ref[n] + kMoveSlack;
@@ -533,15 +560,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
         for (int i = 0; i < 4; ++i)
           pr[n][i] = __builtin_amdgcn_exp2f(fmaf(zr[n][i], scale_log2, -mu));
       }
-      sh.xp[wave][0][lane] = pack_bf16x4(pr[0]);
-      sh.xp[wave][1][lane] = pack_bf16x4(pr[1]);
+#pragma unroll
+      for (int n = 0; n < kHT; ++n) sh.xp[wave][n][lane] = pack_bf16x4(pr[n]);
       const bool wave_restart = __ballot(restart) != 0;   // all lanes vote
       if (lane == 0) sh.xr[wave] = wave_restart ? 1u : 0u;
       tile_barrier();            // (C) probabilities against the new maxima
-      const u32x4 rf = *reinterpret_cast<const u32x4*>(sh.xr);
-      if ((rf[0] | rf[1] | rf[2] | rf[3]) != 0) {
+      if (any_word(sh.xr)) {
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
+        for (int n = 0; n < kHT; ++n) {
           l_part[n] = 0.0f;
 #pragma unroll
           for (int nt = 0; nt < kR / 32; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
@@ -556,12 +582,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
       }
     }
 #pragma unroll
-    for (int n = 0; n < 2; ++n)
+    for (int n = 0; n < kHT; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) l_part[n] += pr[n][i];
-    bf16x8 pa[2];
+    bf16x8 pa[kHT];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+    for (int n = 0; n < kHT; ++n) {
       const u32x2 own = pack_bf16x4(pr[n]);
       const u32x2 oth = sh.xp[partner][n][lane];
       const u32x4 v = {own[0], own[1], oth[0], oth[1]};
@@ -601,8 +627,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
         lgkm_keep<kAfter>(a1);
         const v8i16 v01 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8 vop = __builtin_bit_cast(bf16x8, v01);
-        o[0][NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[0], vop, o[0][NT], 0, 0, 0);
-        o[1][NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[1], vop, o[1][NT], 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < kHT; ++n)
+          o[n][NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[n], vop, o[n][NT], 0, 0, 0);
         if constexpr (2 * NT + kAhead < kLoads) {
           a0 = vload(std::integral_constant<int, 2 * NT + kAhead>{});
           a1 = vload(std::integral_constant<int, 2 * NT + kAhead + 1>{});
@@ -621,14 +648,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
 
   // ---- epilogue: per-head sums, normalisation, staged coalesced stores
 #pragma unroll
-  for (int n = 0; n < 2; ++n) l_part[n] = sum_x16_x32(l_part[n]);
+  for (int n = 0; n < kHT; ++n) l_part[n] = sum_x16_x32(l_part[n]);
   tile_barrier();                // every wave is done with the tiles and xm
-  sh.xm[wave][0][lane] = l_part[0];
-  sh.xm[wave][1][lane] = l_part[1];
-  tile_barrier();
-  float inv_l[2], lse_h[2];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
+  for (int n = 0; n < kHT; ++n) sh.xm[wave][n][lane] = l_part[n];
+  tile_barrier();
+  float inv_l[kHT], lse_h[kHT];
+#pragma unroll
+  for (int n = 0; n < kHT; ++n) {
     const float l = l_part[n] + sh.xm[partner][n][lane];
     inv_l[n] = l > 0.0f ? 1.0f / l : 0.0f;
     lse_h[n] = l > 0.0f ? (m_ref[n] + log2f(l)) * kLn2 : -INFINITY;
@@ -641,13 +668,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   uint8_t* stage = reinterpret_cast<uint8_t*>(&sh.k[0][0]);
   // heads i and i + 1 of a lane are converted together
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
+  for (int n = 0; n < kHT; ++n) {
 #pragma unroll
     for (int i = 0; i < 4; i += 2) {
       const int hl = 4 * g16 + i;
       const float il0 = __shfl(inv_l[n], hl);
       const float il1 = __shfl(inv_l[n], hl + 1);
-      const int h = 32 * hh + 16 * n + hl;
+      const int h = 16 * kHT * hg + 16 * n + hl;
 #pragma unroll
       for (int nt = 0; nt < kR / 32; ++nt) {
         const int d = 256 * kh + 16 * nt + l16;
@@ -660,8 +687,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   }
   if (kh == 0 && g16 == 0) {
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      const int h = 32 * hh + 16 * n + l16;
+    for (int n = 0; n < kHT; ++n) {
+      const int h = 16 * kHT * hg + 16 * n + l16;
       if (partial)
         __hip_atomic_store(part_lse + (static_cast<int64_t>(t) * n_split + split) * kH + h,
                            lse_h[n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -690,13 +717,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   // so every store instruction writes four whole 128-byte lines: thread tid
   // takes word tid % 128 of head rows tid / 128 + 2 i.
   constexpr int kWords = kR / 4;                   // 8-byte words per head row
+  constexpr int kRowsPer = kThreads / kWords;      // head rows per pass (4)
   const int wq = tid % kWords;
   const int h0 = tid / kWords;
   unsigned long long* dst = reinterpret_cast<unsigned long long*>(
       part_o + (static_cast<int64_t>(t) * n_split + split) * kH * kR);
 #pragma unroll 8
-  for (int i = 0; i < kH / 2; ++i) {
-    const int h = h0 + 2 * i;
+  for (int i = 0; i < kH / kRowsPer; ++i) {
+    const int h = h0 + kRowsPer * i;
     const unsigned long long v =
         *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq);
     __hip_atomic_store(dst + h * kWords + wq, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -742,10 +770,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   };
   // with two splits, the other split's rows are in flight while the
   // weights are made
-  unsigned long long u[kH / 2];
+  unsigned long long u[kH / kRowsPer];
   if (n_split == 2) {
 #pragma unroll
-    for (int i = 0; i < kH / 2; ++i) u[i] = word(1 - split, h0 + 2 * i);
+    for (int i = 0; i < kH / kRowsPer; ++i) u[i] = word(1 - split, h0 + kRowsPer * i);
   }
   // split weights exp(lse_s - max) per head in place of the log-sum-exps,
   // then 1 / their sum, behind the staged block
@@ -769,8 +797,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   __syncthreads();
   if (n_split == 2) {
 #pragma unroll
-    for (int i = 0; i < kH / 2; ++i) {
-      const int h = h0 + 2 * i;
+    for (int i = 0; i < kH / kRowsPer; ++i) {
+      const int h = h0 + kRowsPer * i;
       float m[4], o4[4], x[4];
       unpack(own(h), m);
       unpack(u[i], o4);
@@ -785,7 +813,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     }
   } else {
     // 8 heads at a time
-    for (int i0 = 0; i0 < kH / 2; i0 += 8) {
+    for (int i0 = 0; i0 < kH / kRowsPer; i0 += 8) {
       float acc[8][4];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
@@ -794,7 +822,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
       for (int s = 0; s < n_split; ++s) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const int h = h0 + 2 * (i0 + i);
+          const int h = h0 + kRowsPer * (i0 + i);
           float p[4];
           unpack(s == split ? own(h) : word(s, h), p);
           const float wgt = wt[s * kH + h];
@@ -804,7 +832,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int h = h0 + 2 * (i0 + i);
+        const int h = h0 + kRowsPer * (i0 + i);
         put(h, acc[i], wt[n_split * kH + h]);
       }
     }

@@ -147,8 +147,9 @@ int dsa_indexer_cache_write(const void* k_new, int32_t k_dtype, int32_t n_new,
  * workspace: at least dsa_indexer_topk_workspace_size() bytes, 256-byte
  * aligned; contents on entry are ignored.  It holds the fp32 score rows
  * [N, max_seq_len rounded up to 64] and, behind them, the range (min, max)
- * of each token's scores in each key chunk, written by the score pass so
- * that the selection needs no range pass of its own.
+ * of each token's scores in each key chunk, which the score pass writes
+ * when rows can exceed 32768 keys so that the selection, which then streams
+ * its rows from memory, needs no range pass of its own.
  */
 size_t dsa_indexer_topk_workspace_size(const dsa_batch* batch, int32_t topk);
 int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,

@@ -117,13 +117,18 @@ struct IndexerArgs {
   // Per-chunk score ranges (workspace [N, range_stride] of (min, max)): the
   // matrix-core score pass writes, for each key chunk of kRangeParts waves,
   // the range of each token's causal scores there, so the top-k needs no
-  // range pass.  Set by launch_indexer_score; null when that pass took the
-  // vector path (the top-k then finds the range itself).
+  // range pass.  Set by launch_indexer_score; null when rows are short
+  // enough for the top-k's register path (see kTopkRegCap) or that pass
+  // took the vector path (the top-k then finds the range itself).
   float2* chunk_range;
   int32_t range_stride;   // entries per token
   int32_t chunk_keys;     // keys per chunk
 };
 constexpr int kRangeParts = 4;   // entries per chunk (one per score wave)
+// Rows up to this many keys are selected from registers, where finding the
+// range costs next to nothing; the score pass records ranges only for
+// batches with longer rows (they are streamed in every pass).
+constexpr int kTopkRegCap = 32768;
 // entries per token the chunk ranges can need (chunks of at least 128 keys)
 inline int64_t indexer_range_stride_max(int32_t max_seq_len) {
   return (static_cast<int64_t>(max_seq_len) + 127) / 128 * kRangeParts;

@@ -355,18 +355,22 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
       if constexpr (TQ > 1) v = hf ? part[1] : part[0];
       v *= kscl;
       if (my_r0 < 0) v = 0.0f;
-      const bool causal = (first_tile + kWaves * i) * kTile + col <= my_pos;
-      rmin = fminf(rmin, causal ? v : INFINITY);
-      rmax = fmaxf(rmax, causal ? v : -INFINITY);
+      if (crange) {   // uniform: recorded only for batches of long rows
+        const bool causal = (first_tile + kWaves * i) * kTile + col <= my_pos;
+        rmin = fminf(rmin, causal ? v : INFINITY);
+        rmax = fmaxf(rmax, causal ? v : -INFINITY);
+      }
       if (hf < TQ) sc[hf < TQ ? hf : 0][(kWaves * i + wave) * kTile + col] = v;
     });
   }
 
   // ---- the wave's range entries: one per token of the block
+  if (crange) {
 #pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
-    rmin = fminf(rmin, __shfl_xor(rmin, off));
-    rmax = fmaxf(rmax, __shfl_xor(rmax, off));
+    for (int off = 1; off < 32; off <<= 1) {
+      rmin = fminf(rmin, __shfl_xor(rmin, off));
+      rmax = fmaxf(rmax, __shfl_xor(rmax, off));
+    }
   }
   if (crange && col == 0 && hf < nt)
     crange[(tbeg + t0 + hf) * static_cast<int64_t>(range_stride) + chunk * kRangeParts + wave] =
@@ -485,6 +489,7 @@ bool indexer_mfma_ok(const IndexerArgs& a) {
 hipError_t launch_indexer_score(IndexerArgs& a, hipStream_t stream) {
   const dsa_batch& b = a.b;
   if (b.num_q_tokens == 0) return hipSuccess;
+  if (b.max_seq_len <= kTopkRegCap) a.chunk_range = nullptr;   // see kTopkRegCap
   if (indexer_mfma_ok(a)) {
     const bool fp8 = a.cache_dtype == DSA_FP8_E4M3;
     const bool one = b.max_q_len == 1;
@@ -496,7 +501,7 @@ hipError_t launch_indexer_score(IndexerArgs& a, hipStream_t stream) {
     if (one) return mt2 ? launch_dma<1, 2, true>(a, stream) : launch_dma<1, 1, true>(a, stream);
     return mt2 ? launch_dma<2, 2, true>(a, stream) : launch_dma<2, 1, true>(a, stream);
   }
-  a.chunk_range = nullptr;   // the top-k finds the range itself
+  a.chunk_range = nullptr;   // the top-k finds the range itself (vector path)
   const int key_blocks = (b.max_seq_len + 255) / 256;
   const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * key_blocks;
   k_score_vector<<<static_cast<unsigned>(grid), 256, 0, stream>>>(

@@ -39,6 +39,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
 constexpr int kKpt = 32;                       // keys per thread, register path
 constexpr int kRegCap = kThreads * kKpt;       // 32768
+static_assert(kRegCap == kTopkRegCap, "the score pass knows the register path's reach");
 constexpr int kCandCap = 4096;
 constexpr int kRankCap = 256;                  // threshold-bin keys ranked directly
 

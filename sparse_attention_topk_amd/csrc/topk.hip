@@ -73,6 +73,20 @@ __device__ __forceinline__ uint64_t lanes_below() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts
+// within each 16-lane row, then the gfx9 row broadcasts (lane 15 of a row
+// into the next row, lane 31 into the upper half).  Lanes a move does not
+// reach keep 0, so each step adds only what lies below them.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xA, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xC, 0xF, false));
+  return v;
+}
+
 // Suffix scan helper: for a 256-bin histogram find digit d with
 // above(d) < r <= above(d) + h[d] (above = sum of higher bins).  Wave 0
 // scans; results land in s.digit / s.digit_above.
@@ -87,12 +101,7 @@ __device__ __forceinline__ void find_digit(Shared& s, uint32_t r) {
       c[i] = s.hist[255 - 4 * lane - i];
       tot += c[i];
     }
-    uint32_t incl = tot;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      uint32_t v = __shfl_up(incl, off);
-      if (lane >= off) incl += v;
-    }
+    uint32_t incl = wave_scan_incl(tot);
     uint32_t above = incl - tot;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -146,12 +155,7 @@ __device__ __forceinline__ void find_threshold_bin(Shared& s, uint32_t r) {
   const uint32_t h0 = s.hist[kBins - 1 - 2 * tid];
   const uint32_t h1 = s.hist[kBins - 2 - 2 * tid];
   const uint32_t tot = h0 + h1;
-  uint32_t incl = tot;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
+  uint32_t incl = wave_scan_incl(tot);
   if (lane == 63) s.wave_a[wave] = incl;
   lds_barrier();
   uint32_t base = 0;
@@ -414,12 +418,7 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
   const uint32_t w_eq = s.bm_eq[tid];
   const uint32_t packed = (static_cast<uint32_t>(__popc(w_sel)) << 16) |
                           static_cast<uint32_t>(__popc(w_eq));
-  uint32_t incl = packed;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
-  }
+  uint32_t incl = wave_scan_incl(packed);
   if (lane == 63) s.wave_b[wave] = incl;
   lds_barrier();
   uint32_t base = 0;
@@ -605,14 +604,7 @@ __device__ __forceinline__ void select_row_stream(Shared& s, const float* __rest
   const int end = min(L, beg + span);
   const int last4 = ((L + 3) & ~3) - 4;
   // inclusive prefix sum over the wave's lanes
-  auto wave_incl = [&](uint32_t v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t u = __shfl_up(v, o);
-      if (lane >= o) v += u;
-    }
-    return v;
-  };
+  auto wave_incl = [](uint32_t v) { return wave_scan_incl(v); };
   uint32_t n_gt = 0, n_eq = 0;
   wave_blocks(src, beg, end, last4, [&](int blk, const float4& v) {
     const float e[4] = {v.x, v.y, v.z, v.w};

@@ -166,18 +166,14 @@ __device__ __forceinline__ void wait_vm() {
 }
 // cross-lane reductions over lanes l ^ 16 and l ^ 32 (gfx950 permlane swaps:
 // each returns the values of the two lanes of the pair)
-// max of values that are never NaN (logits or -inf), as plain v_max
-// instructions: through fmaxf the compiler first quiets possible signalling
-// NaNs of each input, an extra instruction per operand
-__device__ __forceinline__ float max_nn(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
+// max of logits (never NaN; -inf for keys without a row).  These take the
+// compiler's own max instruction, never inline asm: the first inputs come
+// straight from MFMA accumulators, and the compiler inserts the wait states
+// that a VALU read of an MFMA result needs only for instructions it can see
+// (an asm max read the accumulators before the last MFMA had written them).
+__device__ __forceinline__ float max_nn(float a, float b) { return __builtin_fmaxf(a, b); }
 __device__ __forceinline__ float max3_nn(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 __device__ __forceinline__ float max_x16_x32(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);

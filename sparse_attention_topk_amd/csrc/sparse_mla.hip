@@ -16,20 +16,24 @@
 // crosses HBM once per token.  Rows are gathered in 32-row tiles straight
 // from HBM into LDS (global_load_lds_dwordx4) through a ring of four tile
 // buffers (whole 128-byte lines per DMA instruction): three tiles are in
-// flight while one is multiplied.  Eight waves, two per SIMD: each owns 16
-// heads (head group hg) and one half (kh) of the work, and the first four
-// also issue the tile DMAs, so when one of them waits for room in the memory
-// queue the other wave on its SIMD keeps the matrix core busy:
-//   logits: the 16 keys 16 kh .. 16 kh + 15 of the tile against its 16
-//           heads over all 576 dims (v_mfma_f32_16x16x32_bf16, queries in
-//           registers), so each tile row is read from LDS by four waves;
+// flight while one is multiplied.  Eight waves, two per SIMD; the first
+// four also issue the tile DMAs, so when one of them waits for room in the
+// memory queue the other wave on its SIMD keeps the matrix core busy:
+//   logits: wave w = 2 hg + kh: the 16 keys 16 kh .. 16 kh + 15 of the tile
+//           against the 16 heads of head group hg over all 576 dims
+//           (v_mfma_f32_16x16x32_bf16, queries in registers), so each tile
+//           row is read from LDS by four waves;
 //   softmax: the two waves of a head group swap their per-head maxima and
-//           bf16 probabilities through LDS; the reference maximum moves
-//           rarely (only when a tile beats it by more than 2^8), so the
-//           common tile needs no rescale of the accumulators;
-//   P.V:    value dims 256 kh .. 256 kh + 255 of its 16 heads over all 32
-//           keys, the value operand read with the gfx950 LDS transpose load
-//           straight from the row-major tile.
+//           publish their bf16 probabilities in LDS; the reference maximum
+//           moves rarely (only when a tile beats it by more than 64 in
+//           base-2 log units), so the common tile needs no rescale of the
+//           accumulators;
+//   P.V:    wave w = 4 php + pq: the 32 heads of head groups 2 php and
+//           2 php + 1 over value dims 128 pq .. 128 pq + 127 and all 32
+//           keys; each value fragment, read with the gfx950 LDS transpose
+//           load straight from the row-major tile, feeds two MFMAs (one per
+//           head group), so each value element is read by two waves instead
+//           of four.
 // With more than one key split, each split writes its normalised partial
 // output and log-sum-exp, and the split that finishes last merges them by
 // LSE weights (splits of a token are placed on one XCD, so the partials it
@@ -52,6 +56,8 @@ constexpr int kHT = 1;                  // 16-head tiles per wave
 constexpr int kHG = kH / (16 * kHT);    // head groups (4)
 constexpr int kWavesM = 2 * kHG;        // waves: head group x key half (8, two per SIMD)
 constexpr int kThreads = 64 * kWavesM;  // 512
+constexpr int kPvHT = 2;                // 16-head tiles per wave in P.V
+constexpr int kPvNT = kR / 4 / 16;      // 16-dim tiles per wave in P.V (128 dims)
 constexpr int kDmaWaves = 4;            // waves that issue the tile DMAs
 constexpr int kPieces = kD / 8;         // 16-byte pieces per latent row (72)
 constexpr int kTilePieces = kT * kPieces;             // 2304
@@ -264,20 +270,21 @@ __device__ __forceinline__ u32x2 pack_bf16x4(const float* p) {
 }
 
 // One workgroup = (query token, key split), all 64 heads, kWavesM waves (two
-// per SIMD).  Wave w = 2 hg + kh: heads 16 kHT hg .. in kHT 16-head tiles n
-// (head 16 kHT hg + 16 n + lane % 16 in the query operand).
+// per SIMD).  Logits and softmax: wave w = 2 hg + kh, heads 16 kHT hg .. in
+// kHT 16-head tiles n (head 16 kHT hg + 16 n + lane % 16 in the query
+// operand).  P.V: wave w = 4 php + pq, heads 32 php .. 32 php + 31.
 //   logits:  S^T[16 keys, 16 heads] = K . Q^T per head tile over 18 K-steps,
 //            keys 16 kh + 4 g16 + i on the rows (lane group g16 = lane / 16),
 //            so lane (l16, g16) holds head l16's logits of 4 keys;
 //   softmax: max over the wave's 16 keys in-lane plus two permlane swaps,
 //            then the partner wave's (2 hg + 1 - kh) maxima through LDS;
 //   P.V:     O[16 heads, 16 dims] += P[16 heads, 32 keys] . V[32 keys, 16 dims]
-//            with K-index 8 g16 + e = own key 16 kh + 4 g16 + e (e < 4) or
-//            the partner's key 16 (1 - kh) + 4 g16 + e - 4: the lane's own 4
-//            probabilities are the first half of its P operand unchanged, the
-//            partner lane's 4 (same lane index) the second half, and two
-//            transpose loads of rows 16 kh + 4 g16 + c and 16 (1 - kh) + 4 g16
-//            + c give the value operand in the same key order.
+//            for each of the wave's two head tiles, with K-index 8 g16 + e =
+//            key 4 g16 + e (e < 4) or key 16 + 4 g16 + e - 4: lane (l16, g16)
+//            of the P operand takes the 4 probabilities that lane holds in
+//            the head group's kh = 0 wave, then those of its kh = 1 wave
+//            (both from LDS), and two transpose loads of rows 4 g16 + c and
+//            16 + 4 g16 + c give the value operand in the same key order.
 __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const int32_t* __restrict__ topk_idx, int32_t topk, int32_t n_tokens,
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   }
   tile_barrier();
 
-  static_assert(kQSteps / 4 == 4 && (kR / 32 + 1) / 3 == kDmaPerWave - 4,
+  static_assert(kQSteps / 4 == 4 && kPvNT == 8 && kDmaPerWave == 9 && kHT == 1,
                 "the refill pieces 0..3 follow logit K-steps, 4..8 P.V dim tiles");
   // DMA of local tile `tile` into buffer `buf`: wave w < kDmaWaves fills
   // row group h = w, one instruction per piece group g (the other waves
@@ -376,28 +383,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
 
   // Per-lane LDS byte offsets inside a tile buffer.  Logits: the lane's key
   // row 16 kh + l16, even / odd K-steps.  Values: transpose-load rows
-  // 16 kh + 4 g16 + l16 / 4 (own keys, a) and 16 (1 - kh) + 4 g16 + l16 / 4
-  // (the partner's keys, b) at dims 256 kh + 16 nt + 4 (l16 & 3), for
-  // nt & 3 = m.
+  // 4 g16 + l16 / 4 (keys 0..15, a) and 16 + 4 g16 + l16 / 4 (keys 16..31,
+  // b) at dims 128 pq + 16 nt + 4 (l16 & 3), for nt & 3 = m.
   const int krow = 16 * kh + l16;
   const uint32_t kodd[2] = {tile_byte(krow, g16), tile_byte(krow, 4 + g16)};
-  const int vrow_a = 16 * kh + 4 * g16 + (l16 >> 2);
-  const int vrow_b = 16 * (kh ^ 1) + 4 * g16 + (l16 >> 2);
+  const int php = wave >> 2;            // P.V: head groups 2 php, 2 php + 1
+  const int pq = wave & 3;              // P.V: value dims 128 pq .. 128 pq + 127
+  const int vrow_a = 4 * g16 + (l16 >> 2);
+  const int vrow_b = 16 + vrow_a;
   const int vb_lo = (l16 & 3) >> 1;
   uint32_t voff_a[4], voff_b[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    // piece 32 kh + 2 m + vb_lo (+ 8 (nt >> 2) as an immediate), half l16 & 1
+    // piece 16 pq + 2 m + vb_lo (+ 8 (nt >> 2) as an immediate), half l16 & 1
     const uint32_t half = 8u * static_cast<uint32_t>(l16 & 1);
-    voff_a[m] = tile_byte(vrow_a, 32 * kh + 2 * m + vb_lo) + half;
-    voff_b[m] = tile_byte(vrow_b, 32 * kh + 2 * m + vb_lo) + half;
+    voff_a[m] = tile_byte(vrow_a, 16 * pq + 2 * m + vb_lo) + half;
+    voff_b[m] = tile_byte(vrow_b, 16 * pq + 2 * m + vb_lo) + half;
   }
 
-  f32x4 o[kHT][kR / 32];                  // heads 16 kHT hg + 16 n + 4 g16 + i, dims 256 kh + 16 nt + l16
+  f32x4 o[kPvHT][kPvNT];                  // heads 32 php + 16 n + 4 g16 + i, dims 128 pq + 16 nt + l16
 #pragma unroll
-  for (int n = 0; n < kHT; ++n)
+  for (int n = 0; n < kPvHT; ++n)
 #pragma unroll
-    for (int nt = 0; nt < kR / 32; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
+    for (int nt = 0; nt < kPvNT; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
   float m_ref[kHT], l_part[kHT];   // head 16 kHT hg + 16 n + l16: reference, this lane's sum
 #pragma unroll
   for (int n = 0; n < kHT; ++n) {
@@ -442,8 +450,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     const uint32_t vb32 = sh.vbits[it];
     // The ring's refill (tile it + kBufs - 1 into the buffer tile it - 1
     // left) is issued one DMA instruction at a time, spread over the tile's
-    // MFMAs (after every fourth logit K-step: pieces 0..3; after every third
-    // P.V dim tile: pieces 4..8) rather than all at once: with the memory
+    // MFMAs (after every fourth logit K-step: pieces 0..3; after P.V dim
+    // tiles 0, 2, 3, 5, 6: pieces 4..8) rather than all at once: with the memory
     // queue full an issue waits for room, and spread out those waits
     // overlap the MFMAs in flight.
     // This lane's source row is read here, before the logits' LDS counting
@@ -563,11 +571,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
       tile_barrier();            // (C) probabilities against the new maxima
       if (any_word(sh.xr)) {
 #pragma unroll
-        for (int n = 0; n < kHT; ++n) {
-          l_part[n] = 0.0f;
+        for (int n = 0; n < kHT; ++n) l_part[n] = 0.0f;
 #pragma unroll
-          for (int nt = 0; nt < kR / 32; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
-        }
+        for (int n = 0; n < kPvHT; ++n)
+#pragma unroll
+          for (int nt = 0; nt < kPvNT; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
         wait_vm<0>();
         tile_barrier();          // every wave is done with the ring
 #pragma unroll
@@ -581,19 +589,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
     for (int n = 0; n < kHT; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) l_part[n] += pr[n][i];
-    bf16x8 pa[kHT];
+    // P operands of head groups 2 php + n: keys 0..15 from wave 2 (2 php + n),
+    // keys 16..31 from wave 2 (2 php + n) + 1, as published in LDS
+    bf16x8 pa[kPvHT];
 #pragma unroll
-    for (int n = 0; n < kHT; ++n) {
-      const u32x2 own = pack_bf16x4(pr[n]);
-      const u32x2 oth = sh.xp[partner][n][lane];
-      const u32x4 v = {own[0], own[1], oth[0], oth[1]};
+    for (int n = 0; n < kPvHT; ++n) {
+      const u32x2 p0 = sh.xp[4 * php + 2 * n][0][lane];
+      const u32x2 p1 = sh.xp[4 * php + 2 * n + 1][0][lane];
+      const u32x4 v = {p0[0], p0[1], p1[0], p1[1]};
       pa[n] = __builtin_bit_cast(bf16x8, v);
     }
 
-    // ---- O += P . V: 16 dim tiles, two transpose loads each, 8 in flight.
-    // Dim tile nt reads piece 32 kh + 2 nt + b of its rows: group
-    // 4 kh + (nt >> 2) (an immediate 1024 (nt >> 2)) and one of four per-lane
-    // offsets per row set.
+    // ---- O += P . V: 8 dim tiles of both head tiles, two transpose loads
+    // per dim tile, 8 loads in flight.  Dim tile nt reads piece
+    // 16 pq + 2 nt + b of its rows: group 2 pq + (nt >> 2) (an immediate
+    // 1024 (nt >> 2)) and one of four per-lane offsets per row set.
     {
       const uint32_t tb = lds_addr(kt);
       uint32_t va[4], vb[4];
@@ -602,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
         va[m] = tb + voff_a[m];
         vb[m] = tb + voff_b[m];
       }
-      constexpr int kLoads = 2 * (kR / 32);           // 32
+      constexpr int kLoads = 2 * kPvNT;               // 16
       constexpr int kAhead = 8;
       v4i16 vr[kAhead];
       auto vload = [&](auto ld) -> v4i16 {
@@ -613,7 +623,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
       };
       lgkm_drain();
       static_for<kAhead>([&](auto ld) { vr[decltype(ld)::value] = vload(ld); });
-      static_for<kR / 32>([&](auto ntc) {
+      static_for<kPvNT>([&](auto ntc) {
         constexpr int NT = decltype(ntc)::value;
         v4i16& a0 = vr[(2 * NT) % kAhead];
         v4i16& a1 = vr[(2 * NT + 1) % kAhead];
@@ -624,14 +634,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
         const v8i16 v01 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
         const bf16x8 vop = __builtin_bit_cast(bf16x8, v01);
 #pragma unroll
-        for (int n = 0; n < kHT; ++n)
+        for (int n = 0; n < kPvHT; ++n)
           o[n][NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[n], vop, o[n][NT], 0, 0, 0);
         if constexpr (2 * NT + kAhead < kLoads) {
           a0 = vload(std::integral_constant<int, 2 * NT + kAhead>{});
           a1 = vload(std::integral_constant<int, 2 * NT + kAhead + 1>{});
         }
-        if constexpr (NT % 3 == 1) {              // pieces 4 .. 8
-          constexpr int G = 4 + NT / 3;
+        // pieces 4 .. 8 after dim tiles 0, 2, 3, 5, 6
+        constexpr int G = NT == 0 ? 4 : NT == 2 ? 5 : NT == 3 ? 6 : NT == 5 ? 7 : NT == 6 ? 8 : -1;
+        if constexpr (G >= 0) {
           if (refill) {
             asm volatile("" ::: "memory");
             __builtin_amdgcn_global_load_lds(
@@ -649,12 +660,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
 #pragma unroll
   for (int n = 0; n < kHT; ++n) sh.xm[wave][n][lane] = l_part[n];
   tile_barrier();
-  float inv_l[kHT], lse_h[kHT];
+  float lse_h[kHT];                // head 16 kHT hg + 16 n + l16
 #pragma unroll
   for (int n = 0; n < kHT; ++n) {
     const float l = l_part[n] + sh.xm[partner][n][lane];
-    inv_l[n] = l > 0.0f ? 1.0f / l : 0.0f;
     lse_h[n] = l > 0.0f ? (m_ref[n] + log2f(l)) * kLn2 : -INFINITY;
+  }
+  float inv_l[kPvHT];              // head 32 php + 16 n + l16
+#pragma unroll
+  for (int n = 0; n < kPvHT; ++n) {
+    const float l = sh.xm[4 * php + 2 * n][0][lane] + sh.xm[4 * php + 2 * n + 1][0][lane];
+    inv_l[n] = l > 0.0f ? 1.0f / l : 0.0f;
   }
   const bool partial = n_split > 1;
   // rows of the staged block (bf16, the output's or the partial's values):
@@ -664,16 +680,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
   uint8_t* stage = reinterpret_cast<uint8_t*>(&sh.k[0][0]);
   // heads i and i + 1 of a lane are converted together
 #pragma unroll
-  for (int n = 0; n < kHT; ++n) {
+  for (int n = 0; n < kPvHT; ++n) {
 #pragma unroll
     for (int i = 0; i < 4; i += 2) {
       const int hl = 4 * g16 + i;
       const float il0 = __shfl(inv_l[n], hl);
       const float il1 = __shfl(inv_l[n], hl + 1);
-      const int h = 16 * kHT * hg + 16 * n + hl;
+      const int h = 32 * php + 16 * n + hl;
 #pragma unroll
-      for (int nt = 0; nt < kR / 32; ++nt) {
-        const int d = 256 * kh + 16 * nt + l16;
+      for (int nt = 0; nt < kPvNT; ++nt) {
+        const int d = 128 * pq + 16 * nt + l16;
         const uint32_t pk = pack2_bf16(o[n][nt][i] * il0, o[n][nt][i + 1] * il1);
         *reinterpret_cast<uint16_t*>(stage + h * row_b + 2 * d) = static_cast<uint16_t>(pk);
         *reinterpret_cast<uint16_t*>(stage + (h + 1) * row_b + 2 * d) =

@@ -48,6 +48,44 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Cross-lane reductions inside a wave with VALU moves only (no LDS round
+// trip, unlike a shuffle): DPP permutations inside each 16-lane row (lane
+// l ^ 1, l ^ 2, then the half-row and row mirrors), then gfx950's permlane
+// swaps between rows (lanes l ^ 16, l ^ 32).
+template <int Ctrl>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
+}
+// x[l] + x[l ^ 32] in every lane (the same bits as in either order)
+__device__ __forceinline__ float lane_sum_x32(float x) {
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+// min and max over each 32-lane half of the wave (NaN skipped, as fminf /
+// fmaxf do), in every lane of the half
+__device__ __forceinline__ void half_minmax(float& lo, float& hi) {
+  lo = fminf(lo, dpp_move<0xB1>(lo));    // quad_perm [1, 0, 3, 2]: lane l ^ 1
+  hi = fmaxf(hi, dpp_move<0xB1>(hi));
+  lo = fminf(lo, dpp_move<0x4E>(lo));    // quad_perm [2, 3, 0, 1]: lane l ^ 2
+  hi = fmaxf(hi, dpp_move<0x4E>(hi));
+  lo = fminf(lo, dpp_move<0x141>(lo));   // row_half_mirror: the other quad of 8
+  hi = fmaxf(hi, dpp_move<0x141>(hi));
+  lo = fminf(lo, dpp_move<0x140>(lo));   // row_mirror: the other 8 of 16
+  hi = fmaxf(hi, dpp_move<0x140>(hi));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(lo), false, false);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(hi), __float_as_uint(hi), false, false);
+  lo = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  hi = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+// min and max over the whole wave, in every lane
+__device__ __forceinline__ void wave_minmax(float& lo, float& hi) {
+  half_minmax(lo, hi);
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(lo), false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(hi), __float_as_uint(hi), false, false);
+  lo = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  hi = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Physical cache row of logical position s of a request, or -1 when the
 // block id or slot falls outside the cache (treated as "no key").
 __device__ __forceinline__ int64_t slot_of(const int32_t* bt_row, int32_t s,

@@ -144,6 +144,25 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   const int qbg = blockIdx.x / nchunks;
   const int b = qbg / qblocks_per_req;
   const int qb = qbg % qblocks_per_req;
+  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
+
+  // The wave's tiles are first_tile + kWaves i, i < ntiles (<= 64).  A
+  // 32-key tile never spans two cache blocks, so one block-table entry
+  // gives the whole tile.  Lane i fetches tile i's entry once, with a vector
+  // load; each tile then takes it with v_readlane, so the tile loop issues
+  // no scalar memory loads (a scalar load could only be waited for together
+  // with every outstanding LDS read).  The tiles' places depend only on the
+  // chunk, so the load is issued first, beside the request's length and
+  // query range, rather than behind them: the first tile's address then
+  // waits for one memory round trip instead of two.
+  const int32_t chunk_keys = kTile * kWaves * tiles_per_wave;
+  const int32_t key_beg = chunk * chunk_keys;
+  const int first_tile = key_beg / kTile + wave;
+  int32_t bid_lane = -1;
+  {
+    const int32_t blk = (first_tile + kWaves * lane) * kTile / block_size;
+    if (lane < tiles_per_wave && blk < max_blocks) bid_lane = bt_row[blk];
+  }
 
   const int32_t L = min(seq_lens[b], max_seq_len);
   const int32_t tbeg = cu_q[b];
@@ -152,28 +171,12 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   if (t0 >= qlen) return;
   const int nt = min(TQ, qlen - t0);
   const int32_t pos0 = L - qlen + t0;
-  const int32_t chunk_keys = kTile * kWaves * tiles_per_wave;
   const int32_t key_end = min(pos0 + nt, (chunk + 1) * chunk_keys);
-  const int32_t key_beg = chunk * chunk_keys;
   if (key_beg >= key_end) return;
-  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
-
-  // The wave's tiles are first_tile + kWaves i, i < ntiles (<= 64).  A
-  // 32-key tile never spans two cache blocks, so one block-table entry
-  // gives the whole tile.  Lane i fetches tile i's entry once, with a vector
-  // load; each tile then takes it with v_readlane, so the tile loop issues
-  // no scalar memory loads (a scalar load could only be waited for together
-  // with every outstanding LDS read).
-  const int first_tile = key_beg / kTile + wave;
   const int end_tile = (key_end + kTile - 1) / kTile;
   const int ntiles = end_tile > first_tile
                          ? min(tiles_per_wave, (end_tile - first_tile + kWaves - 1) / kWaves)
                          : 0;
-  int32_t bid_lane = -1;
-  {
-    const int32_t blk = (first_tile + kWaves * lane) * kTile / block_size;
-    if (lane < ntiles && blk < max_blocks) bid_lane = bt_row[blk];
-  }
   // query operand (head 32 mt + col, dims 16 s + 8 hf) and head weights
   // (accumulator register r of a 32x32 tile holds head 8 (r / 4) + 4 hf +
   // r % 4 of column col: four runs of 4 consecutive heads).  Issued after
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
             part[tt] = fmaf(wr[tt][mt][r], fmaxf(acc[tt][r], 0.0f), part[tt]);
       }
 #pragma unroll
-      for (int tt = 0; tt < TQ; ++tt) part[tt] += __shfl_xor(part[tt], 32);
+      for (int tt = 0; tt < TQ; ++tt) part[tt] = lane_sum_x32(part[tt]);
       // lane half hf keeps token hf's score for key
       // (first_tile + kWaves i) * kTile + col (0 when the tile has no row)
       float v = part[0];
@@ -365,13 +368,7 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   }
 
   // ---- the wave's range entries: one per token of the block
-  if (crange) {
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) {
-      rmin = fminf(rmin, __shfl_xor(rmin, off));
-      rmax = fmaxf(rmax, __shfl_xor(rmax, off));
-    }
-  }
+  if (crange) half_minmax(rmin, rmax);
   if (crange && col == 0 && hf < nt)
     crange[(tbeg + t0 + hf) * static_cast<int64_t>(range_stride) + chunk * kRangeParts + wave] =
         make_float2(rmin, rmax);

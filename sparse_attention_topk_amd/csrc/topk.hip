@@ -126,11 +126,7 @@ __device__ __forceinline__ int bin_of(float v, float vmin, float inv) {
 __device__ __forceinline__ void range_reduce(Shared& s, float& vmin, float& vmax) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    vmin = fminf(vmin, __shfl_xor(vmin, off));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-  }
+  wave_minmax(vmin, vmax);
   if (lane == 0) {
     s.red_min[wave] = vmin;
     s.red_max[wave] = vmax;
@@ -616,10 +612,8 @@ __device__ __forceinline__ void select_row_stream(Shared& s, const float* __rest
       n_eq += (i < end && k == T) ? 1u : 0u;
     }
   });
-  for (int o = 32; o > 0; o >>= 1) {
-    n_gt += __shfl_xor(n_gt, o);
-    n_eq += __shfl_xor(n_eq, o);
-  }
+  n_gt = __builtin_amdgcn_readlane(wave_scan_incl(n_gt), 63);   // the wave's totals
+  n_eq = __builtin_amdgcn_readlane(wave_scan_incl(n_eq), 63);
   if (lane == 0) {
     s.wave_a[wave] = n_gt;
     s.wave_b[wave] = n_eq;
@@ -662,8 +656,8 @@ __device__ __forceinline__ void select_row_stream(Shared& s, const float* __rest
       if (take[q] && o < static_cast<uint32_t>(topk)) out[o] = blk + 4 * lane + q;
       o += take[q] ? 1u : 0u;
     }
-    out_run += __shfl(take_incl, 63);
-    eq_run += __shfl(eq_incl, 63);
+    out_run += __builtin_amdgcn_readlane(take_incl, 63);
+    eq_run += __builtin_amdgcn_readlane(eq_incl, 63);
   });
 }
 

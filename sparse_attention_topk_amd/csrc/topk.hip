@@ -206,7 +206,10 @@ __device__ __forceinline__ int reg_pos(int wave, int lane, int j, int e) {
 // Loads the first min(row_stride, 32768) scores of the row (the positions
 // any register-path row can hold); issued before the row's length is known.
 // Rows are padded to a multiple of 64 floats, so a float4 never straddles
-// the end of the allocation.
+// the end of the allocation.  Positions past the row's stride (>= its
+// length, so replaced by NaN before use) re-read the row's last float4:
+// every load is unconditional, and the eight go out back to back (loads
+// under a branch each were waited for before the next was issued).
 __device__ __forceinline__ void load_row_regs(const float* __restrict__ src,
                                               int64_t row_stride, float (&f)[kKpt]) {
   const int lane = threadIdx.x & 63;
@@ -214,8 +217,8 @@ __device__ __forceinline__ void load_row_regs(const float* __restrict__ src,
 #pragma unroll
   for (int j = 0; j < kKpt / 4; ++j) {
     const int p = reg_pos(wave, lane, j, 0);
-    const float4 v = p < row_stride ? *reinterpret_cast<const float4*>(src + p)
-                                    : float4{0.f, 0.f, 0.f, 0.f};
+    const int64_t pc = p < row_stride ? p : row_stride - 4;
+    const float4 v = *reinterpret_cast<const float4*>(src + pc);
     f[4 * j + 0] = v.x;
     f[4 * j + 1] = v.y;
     f[4 * j + 2] = v.z;
@@ -669,6 +672,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
   __shared__ Shared s;
   const int t = blockIdx.x;
   const float* src = scores + static_cast<int64_t>(t) * row_stride;
+  // The request lookup (the largest b with cu_q[b] <= t, counted with a
+  // ballot over 64 entries per load) reads its first entries before the
+  // row is requested: loads return in order, so behind the row's 128 KB it
+  // would wait for all of it before the length could even be asked for.
+  const int lane = threadIdx.x & 63;
+  const int32_t c0 = cu_q[lane < B ? lane : B];      // cu_q has B + 1 entries
+  asm volatile("" ::: "memory");
   // the row's first 32768 scores are requested before its length is known
   float f[kKpt];
   load_row_regs(src, row_stride, f);
@@ -676,7 +686,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
   const float2* rng = crange ? crange + static_cast<int64_t>(t) * range_stride : nullptr;
   float2 pre = make_float2(INFINITY, -INFINITY);
   if (rng && static_cast<int>(threadIdx.x) < range_stride) pre = rng[threadIdx.x];
-  const int b = request_of_wave(cu_q, B, t);
+  int n = __popcll(__ballot(lane < B && c0 <= t));
+  for (int b0 = 64; b0 < B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int32_t c = cu_q[bb < B ? bb : B];
+    n += __popcll(__ballot(bb < B && c <= t));
+  }
+  const int b = n - 1 < 0 ? 0 : (n - 1 >= B ? B - 1 : n - 1);
   const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
   const int L = pos + 1;
   int32_t* orow = out + static_cast<int64_t>(t) * topk;

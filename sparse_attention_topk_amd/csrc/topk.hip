@@ -346,7 +346,9 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
       // ---- rank the candidates by (score descending, position ascending);
       // the top r join the selection.  Wave w ranks candidates 64 w + lane
       // against every candidate, taken one at a time with v_readlane from a
-      // register copy (lane k of round k0 holds candidate k0 + k).
+      // register copy (lane k of round k0 holds candidate k0 + k), eight per
+      // step; lanes past the last candidate hold (-inf, INT_MAX), which
+      // outranks no candidate, so a step needs no bound test.
       const int n = static_cast<int>(bin_count);
       if (64 * wave < n) {
         const int c = 64 * wave + lane;
@@ -354,14 +356,17 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
         const int32_t mp = c < n ? cpos[c] : 0;
         uint32_t rank = 0;
         for (int k0 = 0; k0 < n; k0 += 64) {
-          const float ov = k0 + lane < n ? cval[k0 + lane] : 0.0f;
-          const int32_t op = k0 + lane < n ? cpos[k0 + lane] : 0;
+          const float ov = k0 + lane < n ? cval[k0 + lane] : -INFINITY;
+          const int32_t op = k0 + lane < n ? cpos[k0 + lane] : INT32_MAX;
           const int m = min(64, n - k0);
-          for (int k = 0; k < m; ++k) {
-            const float v = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ov), k));
-            const int32_t pk = __builtin_amdgcn_readlane(op, k);
-            rank += (v > mv || (v == mv && pk < mp)) ? 1u : 0u;
+          for (int k = 0; k < m; k += 8) {
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+              const float v = __builtin_bit_cast(
+                  float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ov), k + kk));
+              const int32_t pk = __builtin_amdgcn_readlane(op, k + kk);
+              rank += (v > mv || (v == mv && pk < mp)) ? 1u : 0u;
+            }
           }
         }
         if (c < n && rank < r) atomicOr(&s.bm_sel[mp >> 5], 1u << (mp & 31));

@@ -154,8 +154,10 @@ __device__ __forceinline__ void find_threshold_bin(Shared& s, uint32_t r) {
   uint32_t incl = wave_scan_incl(tot);
   if (lane == 63) s.wave_a[wave] = incl;
   lds_barrier();
-  uint32_t base = 0;
-  for (int wv = 0; wv < wave; ++wv) base += s.wave_a[wv];
+  // the totals of the waves before this one, one per lane, summed with the
+  // DPP scan (instead of a serial run of LDS reads)
+  const uint32_t base = __builtin_amdgcn_readlane(
+      wave_scan_incl(lane < wave ? s.wave_a[lane] : 0u), 63);
   const uint32_t above0 = base + incl - tot;    // above bin 2047 - 2 tid
   if (above0 < r && r <= above0 + h0) {
     s.sel_bin = kBins - 1 - 2 * tid;
@@ -425,8 +427,8 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
   uint32_t incl = wave_scan_incl(packed);
   if (lane == 63) s.wave_b[wave] = incl;
   lds_barrier();
-  uint32_t base = 0;
-  for (int wv = 0; wv < wave; ++wv) base += s.wave_b[wv];
+  const uint32_t base = __builtin_amdgcn_readlane(
+      wave_scan_incl(lane < wave ? s.wave_b[lane] : 0u), 63);
   const uint32_t excl = base + incl - packed;
   const uint32_t eq_before = excl & 0xFFFFu;
   uint32_t o = (excl >> 16) + min(eq_before, need);

@@ -125,6 +125,31 @@ def test_bf16_ragged_matrix_core_path(dsa, topk):
     assert r >= 0.999, (r, worst)
 
 
+@pytest.mark.parametrize("topk", [64, 2048])
+def test_bf16_prefill_like_ragged_query_blocks(dsa, topk):
+    """Requests with many query tokens (prefill-like): the score pass serves
+    two query tokens per workgroup, so odd counts (9, 13) leave a
+    one-token block at the end of a request, and several chunks of keys
+    per request run side by side."""
+    cfg = _small_cfg(num_reqs=3, topk=topk)
+    b = make_batch(cfg, DEV, seq_lens=[300, 5000, 2100], q_lens=[9, 13, 8])
+    lay = make_layer(cfg, b, DEV)
+    idx = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), lay.q_idx, lay.w, lay.k_src, None, topk)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    ref = _oracle_topk(b, lay, cfg, np_bits(lay.k_src), None, OI.BF16, topk)
+    t = 0
+    for bi in range(b.num_reqs):
+        for i in range(b.q_lens[bi]):
+            pos = b.seq_lens[bi] - b.q_lens[bi] + i
+            check_row_invariants(got[t], pos, topk)
+            if pos + 1 <= topk:
+                assert np.array_equal(got[t], ref[t])
+            t += 1
+    r, worst = recall(got, ref)
+    assert r >= 0.999, (r, worst)
+
+
 def test_vector_path_odd_shapes(dsa):
     cfg = _small_cfg(num_reqs=3, n_idx_heads=5, d_idx=24, topk=40)
     b = make_batch(cfg, DEV, seq_lens=[50, 129, 700], q_lens=[2, 1, 3])

@@ -824,22 +824,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
       put(h, x, wt[2 * kH + h]);
     }
   } else {
-    // 8 heads at a time
+    // Eight head rows at a time, splits in groups of four: the group's
+    // words (the eight rows of each of its splits) are requested before any
+    // is used, so a group costs one memory round trip rather than one per
+    // split.  The loads are unconditional (a split past the last re-reads
+    // the last, and this split's own words are read but taken from the
+    // staged block), so the compiler issues them back to back.  Splits are
+    // summed in split order.
     for (int i0 = 0; i0 < kH / kRowsPer; i0 += 8) {
       float acc[8][4];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[i][e] = 0.0f;
-      for (int s = 0; s < n_split; ++s) {
+      for (int s0 = 0; s0 < n_split; s0 += 4) {
+        unsigned long long wv[4][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int h = h0 + kRowsPer * (i0 + i);
-          float p[4];
-          unpack(s == split ? own(h) : word(s, h), p);
-          const float wgt = wt[s * kH + h];
+        for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wgt, p[e], acc[i][e]);
+          for (int i = 0; i < 8; ++i)
+            wv[g][i] = word(min(s0 + g, n_split - 1), h0 + kRowsPer * (i0 + i));
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int sg = s0 + g;
+          if (sg < n_split) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int h = h0 + kRowsPer * (i0 + i);
+              float p[4];
+              unpack(sg == split ? own(h) : wv[g][i], p);
+              const float wgt = wt[sg * kH + h];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wgt, p[e], acc[i][e]);
+            }
+          }
         }
       }
 #pragma unroll

@@ -204,6 +204,17 @@ def _crafted(dsa, L, topk, kind):
     elif kind == "two_levels":
         hot = torch.randperm(b.num_slots, generator=g)[: b.num_slots // 2]
         k[hot, 0] = 2.0
+    elif kind == "spread":
+        # keys (1 + m / 128) * 2^e over 240 binades, exact in bf16 and their
+        # scores (32 k) exact in fp32: 30720 distinct values, repeats beyond;
+        # a quarter negative (score 0: ties between them fall to position)
+        m = torch.arange(b.num_slots) % 128
+        e = (torch.arange(b.num_slots) // 128) % 240 - 120
+        vals = (1.0 + m.to(torch.float64) / 128.0) * torch.pow(2.0, e.to(torch.float64))
+        vals = vals[torch.randperm(b.num_slots, generator=g)].to(torch.float32)
+        neg = torch.randperm(b.num_slots, generator=g)[: b.num_slots // 4]
+        vals[neg] = -vals[neg]
+        k[:, 0] = vals
     lay_q = q.to(torch.bfloat16).to(DEV)
     lay_k = k.to(torch.bfloat16).to(DEV)
     lay_w = w.to(DEV)
@@ -215,11 +226,13 @@ def _crafted(dsa, L, topk, kind):
     return idx.cpu().numpy(), ref
 
 
-@pytest.mark.parametrize("kind", ["all_zero", "neg_zero", "few_positive", "two_levels"])
-@pytest.mark.parametrize("L", [3000, 32768, 50000])
+@pytest.mark.parametrize("kind", ["all_zero", "neg_zero", "few_positive", "two_levels",
+                                  "spread"])
+@pytest.mark.parametrize("L", [3000, 32767, 32768, 50000])
 def test_degenerate_score_rows_exact(dsa, kind, L):
-    """Exactly representable scores with massive ties: indices must match the
-    oracle exactly (ties to the lower position)."""
+    """Exactly representable scores, with massive ties or spread over many
+    binades:
+    indices must match the oracle exactly (ties to the lower position)."""
     got, ref = _crafted(dsa, L, 2048, kind)
     assert np.array_equal(got, ref)
 

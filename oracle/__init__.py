@@ -24,9 +24,17 @@ Pins (what each function is checked against, in tests/test_oracle_*.py):
               bf16 round-to-nearest-even examples
   indexer     brute-force full sort with Python integer/tuple comparison on
               tiny inputs, hand-computed worked example (tests/golden),
-              exact-integer scores, threshold certificate, invariants
+              exact-integer scores, threshold certificate, invariants; a
+              hand-worked batch of two requests with permuted block tables
+              and an FP8 cache with distinct per-slot scales (key values,
+              scores and top-k rows)
   mla         sparse == dense when k covers the context, pos == 0 row,
-              uniform-logit closed form, permutation invariance, convex hull
+              uniform-logit closed form, permutation invariance, convex hull;
+              the same two-request batch with hand-computed outputs
+Planted mistakes (a dropped ReLU, the tie rule flipped, the scale divided
+or taken from the wrong row, one request's block table used for all, an
+off-by-one request lookup, prefill positions for decode queries) each fail
+one of these pins.
   indexshare  hand-derived source maps and every rejection case
 No oracle function is "parity unpinned".
 """

@@ -173,17 +173,9 @@ def indexer_topk(seq_lens, cu_q, block_table, block_size, q, w, cache, scale,
             continue
         keys_all = key_values(cache, scale, cache_dtype,
                               physical_slots(block_table[b], block_size, L))
+        positions = positions_of_request(L, qlen)
         for t in todo:
-            pos = L - qlen + (t - t0)
+            pos = positions[t - t0]
             sc = indexer_scores(q[t], w[t], keys_all[:pos + 1])
             out[t] = select_topk(sc, topk)
     return out
-
-
-def token_scores(seq_len, q_len, i, block_table_row, block_size, q_t, w_t,
-                 cache, scale, cache_dtype):
-    """Scores of query i of one request over its causal keys (float64)."""
-    pos = seq_len - q_len + i
-    keys = key_values(cache, scale, cache_dtype,
-                      physical_slots(block_table_row, block_size, pos + 1))
-    return indexer_scores(q_t, w_t, keys)

@@ -58,14 +58,26 @@ def sparse_mla(seq_lens, cu_q, block_table, block_size, q, kv_values,
     lse = np.full((N, H), np.nan)
     want = range(N) if tokens is None else tokens
     for t in want:
-        b = int(np.searchsorted(np.asarray(cu_q), t, side="right") - 1)
+        b = request_of_token(cu_q, t)
         idx = np.asarray(topk_idx[t])
         idx = idx[idx >= 0]
-        slots = (np.asarray(block_table[b])[idx // block_size] * block_size
-                 + idx % block_size)
-        out[t], lse[t] = attend(q[t], kv_values(slots), kv_lora_rank,
-                                softmax_scale)
+        out[t], lse[t] = attend(q[t], kv_values(slots_of(block_table, b, idx, block_size)),
+                                kv_lora_rank, softmax_scale)
     return out, lse
+
+
+def request_of_token(cu_q, t):
+    """The request that owns query token t: the last b with cu_q[b] <= t."""
+    return int(np.searchsorted(np.asarray(cu_q), t, side="right") - 1)
+
+
+def slots_of(block_table, b, positions, block_size):
+    """Physical cache rows of logical positions of request b (its own
+    block-table row: block id of position s, times the block size, plus the
+    offset of s in its block)."""
+    positions = np.asarray(positions)
+    return (np.asarray(block_table[b])[positions // block_size] * block_size
+            + positions % block_size)
 
 
 def dense_causal_mla(q, kv, positions, kv_lora_rank, softmax_scale):

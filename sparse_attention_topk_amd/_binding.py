@@ -115,7 +115,17 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _torch_stream(stream):
+    """A torch stream object for `stream` (a torch.cuda.Stream or a raw
+    hipStream_t handle)."""
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
 def _stream(stream):
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
     if stream is not None:
         return ctypes.c_void_p(stream)
     if torch.cuda.is_available():
@@ -191,12 +201,18 @@ def dsa_indexer_topk_workspace_size(batch, topk):
     return load_library().dsa_indexer_topk_workspace_size(ctypes.byref(cb), topk)
 
 
-def _workspace(nbytes, device, workspace):
+def _workspace(nbytes, device, workspace, stream=None):
+    """The caller's workspace, or a fresh one.  A fresh one is allocated on
+    the stream the kernels run on, so the caching allocator does not hand its
+    memory to other work before those kernels are done with it."""
     if workspace is not None:
         return workspace
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(_torch_stream(stream)):
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
 def dsa_indexer_topk(batch, q, w, k_cache, k_scale, topk, topk_idx=None,
@@ -209,7 +225,7 @@ def dsa_indexer_topk(batch, q, w, k_cache, k_scale, topk, topk_idx=None,
         topk_idx = torch.empty((N, topk), dtype=torch.int32, device=q.device)
     cb = batch.c()
     ws = _workspace(lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb), topk),
-                    q.device, workspace)
+                    q.device, workspace, stream)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.dsa_indexer_topk(
         ctypes.byref(cb), _ptr(q), _dtype(q), _ptr(w), H, D, _ptr(k_cache),
@@ -241,7 +257,7 @@ def sparse_mla_attn(batch, q, kv_cache, topk_idx, kv_lora_rank, softmax_scale,
     cb = batch.c()
     dt = _dtype(q)
     ws = _workspace(lib.sparse_mla_attn_workspace_size(
-        ctypes.byref(cb), H, kv_lora_rank, rope, topk, dt), q.device, workspace)
+        ctypes.byref(cb), H, kv_lora_rank, rope, topk, dt), q.device, workspace, stream)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.sparse_mla_attn(
         ctypes.byref(cb), _ptr(q), _ptr(kv_cache), dt, H, kv_lora_rank, rope,
@@ -309,7 +325,7 @@ def indexshare_forward(batch, types: Sequence[int], layers: List[Layer],
     device = device or layers[0].q_mla.device
     ws = _workspace(lib.indexshare_forward_workspace_size(ctypes.byref(cb),
                                                           ctypes.byref(cd)),
-                    device, workspace)
+                    device, workspace, stream)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     act = (ctypes.c_void_p * len(layers))()
     _check(lib.indexshare_forward(ctypes.byref(cb), len(layers), arr, len(types),

@@ -283,99 +283,110 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
         if (f[4 * j + e] == vmax) atomicOr(&s.bm_eq[word_of(j)], bit_of(e));
   } else {
     // ---- 2. histogram and threshold bin: bin = trunc(clamp(f * inv - vmin *
-    // inv, 0, 2047)), monotone in f; NaN lands in bin 0
+    // inv, 0, 2047)), monotone in f; NaN lands in bin 0.  The map needs a
+    // finite, non-zero inv and a finite offset: a range narrower than about
+    // 6e-36 (scores all in the subnormal range) overflows inv, one wider than
+    // the largest float underflows it.  Such rows (workgroup-uniform) take
+    // the exact radix select instead.
     const float inv = static_cast<float>(kBins) / (vmax - vmin);
     const float off = -vmin * inv;
-    // fmaxf maps NaN to 0 (IEEE maxNum), so the conversion is always defined
-    auto bin = [&](float x) {
-      return static_cast<int>(fminf(fmaxf(fmaf(x, inv, off), 0.0f), kBins - 1.0f));
-    };
+    const bool linear = inv > 0.0f && inv < INFINITY && off > -INFINITY && off < INFINITY;
+    bool ranked = false;     // the selection is complete without the radix select
+    if (linear) {
+      // fmaxf maps NaN to 0 (IEEE maxNum), so the conversion is always defined
+      auto bin = [&](float x) {
+        return static_cast<int>(fminf(fmaxf(fmaf(x, inv, off), 0.0f), kBins - 1.0f));
+      };
 #pragma unroll
-    for (int j = 0; j < kKpt; ++j) atomicAdd(&s.hist[bin(f[j])], 1u);
-    lds_barrier();
-    if (tid == kThreads - 1) s.hist[0] -= absent;
-    lds_barrier();
-    find_threshold_bin(s, static_cast<uint32_t>(topk));
-    const int sel = static_cast<int>(s.sel_bin);
-    const uint32_t above_bin = s.above_bin;
-    const uint32_t bin_count = s.hist[sel];
-    const uint32_t r = static_cast<uint32_t>(topk) - above_bin;
-
-    if (bin_count <= static_cast<uint32_t>(kRankCap)) {
-      // ---- 3a. one pass: keys of higher bins are taken, keys of the
-      // threshold bin become (score, position) candidates.  With t the same
-      // fma as in the bin map, bin > sel <=> t >= sel + 1 (sel < 2047) and
-      // bin >= sel <=> t >= sel (sel >= 1); for sel == 0 every non-NaN key
-      // has bin >= sel, which t >= -inf expresses.  NaN fails every test.
-      // Flags are collected branch-free; the rare candidates are appended
-      // after the pass.
-      const float thr_above = sel == kBins - 1 ? INFINITY : static_cast<float>(sel + 1);
-      const float thr_in = sel == 0 ? -INFINITY : static_cast<float>(sel);
-      // same values; the compiler is kept from holding the histogram pass's
-      // 32 products in registers until here
-      float inv2 = inv, off2 = off;
-      asm volatile("" : "+v"(inv2), "+v"(off2));
-      uint32_t cand_bits = 0;          // bit 4 j + e
-#pragma unroll
-      for (int j = 0; j < kKpt / 4; ++j) {
-        uint32_t take = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float t = fmaf(f[4 * j + e], inv2, off2);
-          take |= t >= thr_above ? bit_of(e) : 0u;
-          cand_bits |= (t >= thr_in && t < thr_above) ? (1u << (4 * j + e)) : 0u;
-        }
-        if (take) atomicOr(&s.bm_sel[word_of(j)], take);
-      }
-      float* cval = reinterpret_cast<float*>(s.cand);
-      int32_t* cpos = reinterpret_cast<int32_t*>(s.cand + kRankCap);
-      // the threshold bin holds few keys: groups of 4 keys where no lane
-      // has one are skipped with one wave-uniform test
-#pragma unroll
-      for (int j = 0; j < kKpt / 4; ++j) {
-        const uint32_t cj = (cand_bits >> (4 * j)) & 0xFu;
-        if (__ballot(cj != 0u) == 0) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if ((cj >> e) & 1u) {
-            const uint32_t slot = atomicAdd(&s.ncand, 1u);
-            cval[slot] = f[4 * j + e];
-            cpos[slot] = reg_pos(wave, lane, j, e);
-          }
-        }
-      }
+      for (int j = 0; j < kKpt; ++j) atomicAdd(&s.hist[bin(f[j])], 1u);
       lds_barrier();
-      // ---- rank the candidates by (score descending, position ascending);
-      // the top r join the selection.  Wave w ranks candidates 64 w + lane
-      // against every candidate, taken one at a time with v_readlane from a
-      // register copy (lane k of round k0 holds candidate k0 + k), eight per
-      // step; lanes past the last candidate hold (-inf, INT_MAX), which
-      // outranks no candidate, so a step needs no bound test.
-      const int n = static_cast<int>(bin_count);
-      if (64 * wave < n) {
-        const int c = 64 * wave + lane;
-        const float mv = c < n ? cval[c] : 0.0f;
-        const int32_t mp = c < n ? cpos[c] : 0;
-        uint32_t rank = 0;
-        for (int k0 = 0; k0 < n; k0 += 64) {
-          const float ov = k0 + lane < n ? cval[k0 + lane] : -INFINITY;
-          const int32_t op = k0 + lane < n ? cpos[k0 + lane] : INT32_MAX;
-          const int m = min(64, n - k0);
-          for (int k = 0; k < m; k += 8) {
+      if (tid == kThreads - 1) s.hist[0] -= absent;
+      lds_barrier();
+      find_threshold_bin(s, static_cast<uint32_t>(topk));
+      const int sel = static_cast<int>(s.sel_bin);
+      const uint32_t above_bin = s.above_bin;
+      const uint32_t bin_count = s.hist[sel];
+      const uint32_t r = static_cast<uint32_t>(topk) - above_bin;
+
+      if (bin_count <= static_cast<uint32_t>(kRankCap)) {
+        // ---- 3a. one pass: keys of higher bins are taken, keys of the
+        // threshold bin become (score, position) candidates.  With t the same
+        // fma as in the bin map, bin > sel <=> t >= sel + 1 (sel < 2047) and
+        // bin >= sel <=> t >= sel (sel >= 1); for sel == 0 every non-NaN key
+        // has bin >= sel, which t >= -inf expresses.  NaN fails every test.
+        // Flags are collected branch-free; the rare candidates are appended
+        // after the pass.
+        const float thr_above = sel == kBins - 1 ? INFINITY : static_cast<float>(sel + 1);
+        const float thr_in = sel == 0 ? -INFINITY : static_cast<float>(sel);
+        // same values; the compiler is kept from holding the histogram pass's
+        // 32 products in registers until here
+        float inv2 = inv, off2 = off;
+        asm volatile("" : "+v"(inv2), "+v"(off2));
+        uint32_t cand_bits = 0;          // bit 4 j + e
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-              const float v = __builtin_bit_cast(
-                  float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ov), k + kk));
-              const int32_t pk = __builtin_amdgcn_readlane(op, k + kk);
-              rank += (v > mv || (v == mv && pk < mp)) ? 1u : 0u;
+        for (int j = 0; j < kKpt / 4; ++j) {
+          uint32_t take = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float t = fmaf(f[4 * j + e], inv2, off2);
+            take |= t >= thr_above ? bit_of(e) : 0u;
+            cand_bits |= (t >= thr_in && t < thr_above) ? (1u << (4 * j + e)) : 0u;
+          }
+          if (take) atomicOr(&s.bm_sel[word_of(j)], take);
+        }
+        float* cval = reinterpret_cast<float*>(s.cand);
+        int32_t* cpos = reinterpret_cast<int32_t*>(s.cand + kRankCap);
+        // the threshold bin holds few keys: groups of 4 keys where no lane
+        // has one are skipped with one wave-uniform test
+#pragma unroll
+        for (int j = 0; j < kKpt / 4; ++j) {
+          const uint32_t cj = (cand_bits >> (4 * j)) & 0xFu;
+          if (__ballot(cj != 0u) == 0) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if ((cj >> e) & 1u) {
+              const uint32_t slot = atomicAdd(&s.ncand, 1u);
+              cval[slot] = f[4 * j + e];
+              cpos[slot] = reg_pos(wave, lane, j, e);
             }
           }
         }
-        if (c < n && rank < r) atomicOr(&s.bm_sel[mp >> 5], 1u << (mp & 31));
+        lds_barrier();
+        // ---- rank the candidates by (score descending, position ascending);
+        // the top r join the selection.  Wave w ranks candidates 64 w + lane
+        // against every candidate, taken one at a time with v_readlane from a
+        // register copy (lane k of round k0 holds candidate k0 + k), eight per
+        // step; lanes past the last candidate hold (-inf, INT_MAX), which
+        // outranks no candidate, so a step needs no bound test.
+        const int n = static_cast<int>(bin_count);
+        if (64 * wave < n) {
+          const int c = 64 * wave + lane;
+          const float mv = c < n ? cval[c] : 0.0f;
+          const int32_t mp = c < n ? cpos[c] : 0;
+          uint32_t rank = 0;
+          for (int k0 = 0; k0 < n; k0 += 64) {
+            const float ov = k0 + lane < n ? cval[k0 + lane] : -INFINITY;
+            const int32_t op = k0 + lane < n ? cpos[k0 + lane] : INT32_MAX;
+            const int m = min(64, n - k0);
+            for (int k = 0; k < m; k += 8) {
+#pragma unroll
+              for (int kk = 0; kk < 8; ++kk) {
+                const float v = __builtin_bit_cast(
+                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ov), k + kk));
+                const int32_t pk = __builtin_amdgcn_readlane(op, k + kk);
+                rank += (v > mv || (v == mv && pk < mp)) ? 1u : 0u;
+              }
+            }
+          }
+          if (c < n && rank < r) atomicOr(&s.bm_sel[mp >> 5], 1u << (mp & 31));
+        }
+        ranked = true;
       }
-    } else {
+    }
+    if (!ranked) {
       // ---- 3b. exact radix select of rank topk over the row's keys gives
-      // the threshold score T and the count above it
+      // the threshold score T and the count above it (the bitmaps are still
+      // empty: a row comes here from step 2 before anything was marked)
       const int tid2 = tid;
       uint32_t rr = static_cast<uint32_t>(topk);
       uint32_t prefix = 0, mask = 0, gt_extra = 0;
@@ -441,7 +452,9 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
       m ^= low;
     }
   }
-  while (w_sel) {
+  // bounded by the row width: the bitmap holds exactly topk positions when
+  // the steps above agree, and a disagreement must not write past the row
+  while (w_sel && o < static_cast<uint32_t>(topk)) {
     const int b = __builtin_ctz(w_sel);
     out[o++] = 32 * tid + b;
     w_sel &= w_sel - 1;

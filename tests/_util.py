@@ -2,6 +2,7 @@
 
 No arithmetic of the method lives here."""
 import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -68,3 +69,17 @@ def attn_close(gpu, ref, atol=2e-2, rtol=1e-2):
     ref = np.asarray(ref, dtype=np.float64)
     excess = np.abs(gpu - ref) - (atol + rtol * np.abs(ref))
     return float(np.max(excess)) if excess.size else -1.0
+
+
+def pool_map(fn, items, workers=None):
+    """fn over items in a thread pool sized to the host's cores (NumPy and
+    BLAS release the GIL in the heavy parts).  Results in item order."""
+    items = list(items)
+    n = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    with ThreadPoolExecutor(n) as ex:
+        return list(ex.map(fn, items))
+
+
+def bf16_bits_to_f32(bits):
+    """uint16 bf16 bit patterns -> float32 values (exact)."""
+    return (np.asarray(bits).astype(np.uint32) << np.uint32(16)).view(np.float32)

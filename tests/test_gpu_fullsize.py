@@ -1,11 +1,14 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times.  The oracle computes sampled query tokens one by one; every
-row is checked for the invariants that hold at any size."""
+benchmark times.  The oracle recomputes every query token of the decode
+workloads (the FP8 cache's codes and scales for every key), and 72 query
+tokens spread over the 16384-token prefill; every row is also checked for the
+invariants that hold at any size."""
 import numpy as np
 import pytest
 import torch
 
-from _util import attn_close, check_row_invariants, ensure_library, np_bits, np_f64, recall
+from _util import (attn_close, bf16_bits_to_f32, check_row_invariants, ensure_library,
+                   np_bits, np_f64, pool_map, recall)
 from oracle import indexer as OI, indexshare as OX, mla as OM
 from synth import get_config, make_batch, make_layer
 
@@ -33,6 +36,24 @@ def _all_rows_valid(idx, b, topk):
     return got
 
 
+def _oracle_topk(b, q64, w64, cache_np, scale_np, cdt, topk, tokens):
+    """The oracle's rows for the given tokens, one request per pool task."""
+    req_of = np.searchsorted(b.cu_q_host, np.asarray(tokens), side="right") - 1
+    groups = {}
+    for t, r in zip(tokens, req_of):
+        groups.setdefault(int(r), []).append(int(t))
+
+    def one(ts):
+        return ts, OI.indexer_topk(b.seq_lens, b.cu_q_host, b.block_table_host,
+                                   b.block_size, q64, w64, cache_np, scale_np, cdt,
+                                   topk, tokens=ts)
+
+    ref = np.full((b.num_q_tokens, topk), -1, dtype=np.int32)
+    for ts, rows in pool_map(one, groups.values()):
+        ref[ts] = rows[ts]
+    return ref
+
+
 def _mla_oracle(b, lay, idx_np, cfg, tokens):
     kv = lay.kv_cache
 
@@ -45,18 +66,18 @@ def _mla_oracle(b, lay, idx_np, cfg, tokens):
                          cfg.softmax_scale, tokens=tokens)
 
 
-def _check_sampled(b, lay, cfg, got_idx, out, lse, cache_np, scale_np, cdt, tokens):
-    ref = OI.indexer_topk(b.seq_lens, b.cu_q_host, b.block_table_host, b.block_size,
-                          np_f64(lay.q_idx), np_f64(lay.w), cache_np, scale_np, cdt,
-                          cfg.topk, tokens=tokens)
+def _check(b, lay, cfg, got_idx, out, lse, cache_np, scale_np, cdt, tokens):
+    ref = _oracle_topk(b, np_f64(lay.q_idx), np_f64(lay.w), cache_np, scale_np, cdt,
+                       cfg.topk, tokens)
     r, worst = recall(got_idx[tokens], ref[tokens])
-    print("sampled recall %.6f (worst row %.6f)" % (r, worst), flush=True)
+    print("recall over %d rows %.6f (worst row %.6f)" % (len(tokens), r, worst), flush=True)
     assert r >= 0.999, (r, worst)
     ro, rl = _mla_oracle(b, lay, ref, cfg, tokens)
     go, gl = np_f64(out), lse.cpu().numpy()
     for t in tokens:
         assert attn_close(go[t], ro[t]) <= 0, t
         assert attn_close(gl[t], rl[t], 2e-2, 1e-3) <= 0, t
+    return ref
 
 
 def test_decode_32k_mtp_full(dsa):
@@ -83,8 +104,8 @@ def test_decode_32k_mtp_full(dsa):
                                          cfg.softmax_scale)
         torch.cuda.synchronize()
         assert torch.equal(out, out2) and torch.equal(lse, lse2)
-    _check_sampled(b, lay, cfg, got, out, lse, np_bits(cache), None, OI.BF16,
-                   [0, 1, 2, 63, 64, 126, 127])
+    _check(b, lay, cfg, got, out, lse, np_bits(cache), None, OI.BF16,
+           list(range(b.num_q_tokens)))
 
 
 def test_prefill_16k_full(dsa):
@@ -98,10 +119,29 @@ def test_prefill_16k_full(dsa):
     torch.cuda.synchronize()
     got = _all_rows_valid(idx, b, cfg.topk)
     # rows with t < topk take every position 0..t
-    for t in (0, 1, 777, 2047):
-        assert np.array_equal(got[t][:t + 1], np.arange(t + 1))
-    _check_sampled(b, lay, cfg, got, out, lse, np_bits(lay.k_src), None, OI.BF16,
-                   [0, 5, 2047, 2048, 2049, 9000, 16383])
+    for t in range(cfg.topk):
+        assert np.array_equal(got[t][:t + 1], np.arange(t + 1)), t
+    # 64 rows spread evenly over the sequence, plus the edges of the
+    # top-k width
+    tokens = sorted(set(np.linspace(0, 16383, 64).astype(int).tolist())
+                    | {0, 5, 2046, 2047, 2048, 2049, 4095, 16383})
+    _check(b, lay, cfg, got, out, lse, np_bits(lay.k_src), None, OI.BF16, tokens)
+
+
+def _oracle_fp8_cache(k_src, chunk=32768):
+    """The oracle's e4m3 codes and scales of every key (bf16 keys, quantised
+    on the host in chunks, one per pool task)."""
+    bits = np_bits(k_src)
+    n = bits.shape[0]
+    codes = np.empty(bits.shape, dtype=np.uint8)
+    scales = np.empty(n, dtype=np.float32)
+
+    def one(s):
+        e = min(n, s + chunk)
+        codes[s:e], scales[s:e] = OI.fp8_quantize_rows(bf16_bits_to_f32(bits[s:e]))
+
+    pool_map(one, range(0, n, chunk))
+    return codes, scales
 
 
 def test_fp8_decode_varlen_full(dsa):
@@ -118,20 +158,12 @@ def test_fp8_decode_varlen_full(dsa):
                                    cfg.softmax_scale)
     torch.cuda.synchronize()
     got = _all_rows_valid(idx, b, cfg.topk)
-    lens = np.array(b.seq_lens)
-    reqs = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 0, 77})
-    # oracle cache: quantise exactly the rows these requests use
-    codes = np.zeros((b.num_slots, cfg.d_idx), dtype=np.uint8)
-    scales = np.ones(b.num_slots, dtype=np.float32)
-    for r in reqs:
-        slots = OI.physical_slots(b.block_table_host[r], b.block_size, b.seq_lens[r])
-        k32 = np_f64(lay.k_src[torch.as_tensor(slots, device=DEV)]).astype(np.float32)
-        c, s = OI.fp8_quantize_rows(k32)
-        codes[slots], scales[slots] = c, s
-        gs = torch.as_tensor(slots, device=DEV)
-        assert np.array_equal(np_bits(cache[gs]), c), r
-        assert np.array_equal(scale[gs].cpu().numpy().view(np.uint32), s.view(np.uint32)), r
-    _check_sampled(b, lay, cfg, got, out, lse, codes, scales, OI.FP8, reqs)
+    # every key's codes and scale, bit for bit
+    codes, scales = _oracle_fp8_cache(lay.k_src)
+    print("fp8 cache: %d keys compared" % codes.shape[0], flush=True)
+    assert np.array_equal(np_bits(cache), codes)
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), scales.view(np.uint32))
+    _check(b, lay, cfg, got, out, lse, codes, scales, OI.FP8, list(range(b.num_q_tokens)))
 
 
 def test_indexshare_8layer_full(dsa):
@@ -171,16 +203,18 @@ def test_indexshare_8layer_full(dsa):
     torch.cuda.synchronize()
     for i in range(8):
         assert torch.equal(before[i], L[i].out), i
-    tokens = [0, 31, 63]
-    for i in (0, 1, 4, 7):
-        s = src[i]
+    tokens = list(range(N))
+    refs = {}
+    for s in sorted(set(src)):
         got = _all_rows_valid(L[s].topk_idx, b, cfg.topk)
-        ref = OI.indexer_topk(b.seq_lens, b.cu_q_host, b.block_table_host, 64,
-                              np_f64(lays[s].q_idx), np_f64(lays[s].w), np_bits(lays[s].k_src),
-                              None, OI.BF16, cfg.topk, tokens=tokens)
-        r, _ = recall(got[tokens], ref[tokens])
-        assert r >= 0.999
-        ro, _ = _mla_oracle(b, lays[i], ref, cfg, tokens)
-        go = np_f64(L[i].out)
+        refs[s] = _oracle_topk(b, np_f64(lays[s].q_idx), np_f64(lays[s].w),
+                               np_bits(lays[s].k_src), None, OI.BF16, cfg.topk, tokens)
+        r, worst = recall(got, refs[s])
+        print("layer %d recall %.6f (worst row %.6f)" % (s, r, worst), flush=True)
+        assert r >= 0.999, (s, r, worst)
+    for i in range(8):
+        ro, rl = _mla_oracle(b, lays[i], refs[src[i]], cfg, tokens)
+        go, gl = np_f64(L[i].out), L[i].lse.cpu().numpy()
         for t in tokens:
             assert attn_close(go[t], ro[t]) <= 0, (i, t)
+            assert attn_close(gl[t], rl[t], 2e-2, 1e-3) <= 0, (i, t)

@@ -237,6 +237,129 @@ def test_degenerate_score_rows_exact(dsa, kind, L):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("L,topk", [(200, 16), (256, 100), (97, 96), (3000, 64)])
+def test_subnormal_score_rows_exact(dsa, L, topk):
+    """Scores that are all subnormal (integers times 2^-141 .. 2^-139, exact in
+    fp32 on the vector path), a third of them zero: the row's range is far
+    below 1e-35, where a value-linear bin map over [min, max] overflows.  The
+    selection must still equal the oracle's exactly."""
+    cfg = _small_cfg(num_reqs=2, q_len=1, topk=topk, n_idx_heads=2, d_idx=4,
+                     idx_dtype="f32", idx_cache_dtype="f32")
+    b = make_batch(cfg, DEV, seq_lens=[L, L], q_lens=[1, 1])
+    g = torch.Generator(device="cpu").manual_seed(L + topk)
+    q = torch.zeros(2, 2, 4)
+    q[:, :, 0] = 2.0 ** -70
+    k = torch.zeros(b.num_slots, 4)
+    m = torch.randint(-200, 400, (b.num_slots,), generator=g).to(torch.float32)
+    k[:, 0] = m * 2.0 ** -70                       # logits m * 2^-140, ReLU -> 0 below 0
+    k[:, 1] = torch.randn(b.num_slots, generator=g)   # meets q = 0: no effect
+    w = torch.tensor([[1.0, 1.0], [1.0, 0.5]])     # scores relu(m) * 2^-139 / * 3 * 2^-141
+    lay_q, lay_k, lay_w = q.to(DEV), k.to(DEV), w.to(DEV)
+    idx = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), lay_q, lay_w, lay_k, None, topk)
+    torch.cuda.synchronize()
+    ref = OI.indexer_topk(b.seq_lens, b.cu_q_host, b.block_table_host, b.block_size,
+                          np_f64(lay_q), np_f64(lay_w), np_bits(lay_k), None, OI.F32, topk)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def test_topk_4096_through_both_calls(dsa):
+    """The largest top-k width: rows of 4096 positions from both selection
+    paths (a row of 5000 keys in registers, one of 40000 streamed), rows
+    shorter than 4096, and attention over them at two splits per token
+    (split length 2048) and at many splits (few tokens)."""
+    topk = 4096
+    cfg = _small_cfg(num_reqs=4, topk=topk)
+    b = make_batch(cfg, DEV, seq_lens=[5000, 40000, 3000, 4097], q_lens=[2, 1, 2, 1])
+    lay = make_layer(cfg, b, DEV)
+    bb = _dsa_batch(dsa, b)
+    idx = dsa.dsa_indexer_topk(bb, lay.q_idx, lay.w, lay.k_src, None, topk)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    ref = _oracle_topk(b, lay, cfg, np_bits(lay.k_src), None, OI.BF16, topk)
+    pos = [4998, 4999, 39999, 2998, 2999, 4096]
+    for t, p in enumerate(pos):
+        check_row_invariants(got[t], p, topk)
+    r, worst = recall(got, ref)
+    assert r >= 0.999, (r, worst)
+    # few tokens: many splits per token
+    out, lse = dsa.sparse_mla_attn(bb, lay.q_mla, lay.kv_cache, idx, cfg.kv_lora_rank,
+                                   cfg.softmax_scale)
+    torch.cuda.synchronize()
+    ro, rl = _oracle_mla(b, lay, got, cfg.kv_lora_rank, cfg.softmax_scale)
+    assert attn_close(np_f64(out), ro) <= 0
+    assert attn_close(lse.cpu().numpy(), rl, 1e-3, 1e-4) <= 0
+    # 256 tokens: two splits of 2048 per token
+    cfg2 = _small_cfg(num_reqs=128, q_len=2, topk=topk)
+    b2 = make_batch(cfg2, DEV, seq_lens=[4100 + 3 * i for i in range(128)], q_lens=[2] * 128)
+    lay2 = make_layer(cfg2, b2, DEV, with_indexer=False)
+    idx2 = make_random_indices(b2, topk, 4096, DEV)
+    bb2 = _dsa_batch(dsa, b2)
+    assert dsa.sparse_mla_attn_workspace_size(bb2, 64, 512, 64, topk, 1) > 0
+    out2, lse2 = dsa.sparse_mla_attn(bb2, lay2.q_mla, lay2.kv_cache, idx2, 512,
+                                     cfg2.softmax_scale)
+    torch.cuda.synchronize()
+    toks = [0, 1, 100, 200, 255]
+    ro2, rl2 = _oracle_mla(b2, lay2, idx2.cpu().numpy(), 512, cfg2.softmax_scale, tokens=toks)
+    go2, gl2 = np_f64(out2), lse2.cpu().numpy()
+    for t in toks:
+        assert attn_close(go2[t], ro2[t]) <= 0, t
+        assert attn_close(gl2[t], rl2[t], 1e-3, 1e-4) <= 0, t
+
+
+def test_ragged_batch_with_requests_without_queries(dsa):
+    """Requests with no query token this step (q_len = 0, one of them with
+    an empty cache) between others: both calls skip them and every other
+    token's row and attention still match the oracle."""
+    topk = 256
+    cfg = _small_cfg(num_reqs=5, topk=topk)
+    b = make_batch(cfg, DEV, seq_lens=[700, 1200, 0, 300, 2100], q_lens=[2, 0, 0, 3, 1])
+    lay = make_layer(cfg, b, DEV)
+    bb = _dsa_batch(dsa, b)
+    idx = dsa.dsa_indexer_topk(bb, lay.q_idx, lay.w, lay.k_src, None, topk)
+    out, lse = dsa.sparse_mla_attn(bb, lay.q_mla, lay.kv_cache, idx, cfg.kv_lora_rank,
+                                   cfg.softmax_scale)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert got.shape == (6, topk)
+    ref = _oracle_topk(b, lay, cfg, np_bits(lay.k_src), None, OI.BF16, topk)
+    for t, p in enumerate([698, 699, 297, 298, 299, 2099]):
+        check_row_invariants(got[t], p, topk)
+    r, worst = recall(got, ref)
+    assert r >= 0.999, (r, worst)
+    ro, rl = _oracle_mla(b, lay, got, cfg.kv_lora_rank, cfg.softmax_scale)
+    assert attn_close(np_f64(out), ro) <= 0
+    assert attn_close(lse.cpu().numpy(), rl, 1e-3, 1e-4) <= 0
+
+
+def test_calls_on_a_side_stream_match(dsa):
+    """Both calls enqueued on another stream (workspace allocated by the
+    binding for that stream) give the same results as on the current one,
+    while the current stream allocates and frees memory meanwhile."""
+    cfg = _small_cfg(num_reqs=3, topk=512)
+    b = make_batch(cfg, DEV, seq_lens=[3000, 5000, 700], q_lens=[2, 1, 2])
+    lay = make_layer(cfg, b, DEV)
+    bb = _dsa_batch(dsa, b)
+    idx0 = dsa.dsa_indexer_topk(bb, lay.q_idx, lay.w, lay.k_src, None, 512)
+    out0, lse0 = dsa.sparse_mla_attn(bb, lay.q_mla, lay.kv_cache, idx0, 512,
+                                     cfg.softmax_scale)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    idx1 = torch.empty_like(idx0)
+    out1, lse1 = torch.empty_like(out0), torch.empty_like(lse0)
+    for _ in range(3):
+        dsa.dsa_indexer_topk(bb, lay.q_idx, lay.w, lay.k_src, None, 512, topk_idx=idx1,
+                             stream=side)
+        dsa.sparse_mla_attn(bb, lay.q_mla, lay.kv_cache, idx1, 512, cfg.softmax_scale,
+                            out=out1, lse=lse1, stream=side)
+        junk = [torch.full((1 << 20,), 7, dtype=torch.int32, device=DEV) for _ in range(8)]
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(idx0, idx1)
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+
+
 def test_indices_deterministic_across_runs(dsa):
     cfg = _small_cfg(num_reqs=4, topk=512)
     b = make_batch(cfg, DEV, seq_lens=[4000, 9000, 33000, 600], q_lens=[2, 2, 1, 2])

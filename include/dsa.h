@@ -33,8 +33,10 @@
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked [host].  All device buffers
  *     belong to the caller; the library never allocates or frees device
- *     memory, never synchronises the device and keeps no state between calls
- *     except the thread-local error text.
+ *     memory and never synchronises the device.  State kept between calls:
+ *     the thread-local error text, a process-wide counter that tags each
+ *     sparse_mla_attn call, and, once dsa_indexer_topk_noalloc has run on a
+ *     device, that device's static scratch array and its address.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it; inputs must stay valid until that work completes.
  *   - Return value: DSA_OK (0) or a negative dsa_status.  Every condition
@@ -157,6 +159,32 @@ int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
                      const void* k_cache, const float* k_scale,
                      int32_t cache_dtype, int32_t topk, int32_t* topk_idx,
                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Allocation-free variant of dsa_indexer_topk, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results and errors as
+ * dsa_indexer_topk, minus the workspace: its scratch (the score rows and
+ * chunk ranges) lives in a static device array of
+ * DSA_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until
+ * the process ends.  Nothing is allocated or freed.
+ *   - A batch whose dsa_indexer_topk_workspace_size() exceeds
+ *     DSA_NOALLOC_SCRATCH_BYTES is rejected with DSA_ERR_WORKSPACE before
+ *     anything is enqueued (e.g. 128 query tokens of up to 64K keys fit).
+ *   - `stream` must belong to the current device (else
+ *     DSA_ERR_INVALID_ARG); the first call on a device looks up that
+ *     device's copy of the array.
+ *   - Calls share their device's array and need nothing cleared between
+ *     them (every entry a call reads was written earlier in the same call);
+ *     calls that may overlap on one GPU (other streams, other threads) race
+ *     on it and must not be issued.
+ */
+enum { DSA_NOALLOC_SCRATCH_BYTES = 32 << 20 };
+int dsa_indexer_topk_noalloc(const dsa_batch* batch, const void* q, int32_t q_dtype,
+                             const float* w, int32_t n_heads, int32_t d_idx,
+                             const void* k_cache, const float* k_scale,
+                             int32_t cache_dtype, int32_t topk, int32_t* topk_idx,
+                             void* stream);
 
 /*
  * Absorbed sparse MLA over the selected latent rows (section "DSA Indexer

@@ -18,7 +18,8 @@ DSA_LAYER_FULL, DSA_LAYER_SHARED = 0, 1
 
 EXPORTS = [
     "dsa_indexer_cache_write", "dsa_indexer_topk_workspace_size",
-    "dsa_indexer_topk", "sparse_mla_attn_workspace_size", "sparse_mla_attn",
+    "dsa_indexer_topk", "dsa_indexer_topk_noalloc", "sparse_mla_attn_workspace_size",
+    "sparse_mla_attn",
     "dsa_resolve_indexer_sources", "indexshare_forward_workspace_size",
     "indexshare_forward", "dsa_fp8_decode_check", "dsa_last_error",
 ]
@@ -77,6 +78,7 @@ def load_library():
         "dsa_indexer_cache_write": (ctypes.c_int, [P, I32, I32, I32, P, I64, P, P, I32, P]),
         "dsa_indexer_topk_workspace_size": (SZ, [P, I32]),
         "dsa_indexer_topk": (ctypes.c_int, [P, P, I32, P, I32, I32, P, P, I32, I32, P, P, SZ, P]),
+        "dsa_indexer_topk_noalloc": (ctypes.c_int, [P, P, I32, P, I32, I32, P, P, I32, I32, P, P]),
         "sparse_mla_attn_workspace_size": (SZ, [P, I32, I32, I32, I32, I32]),
         "sparse_mla_attn": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, P, I32, F, P, P, P, SZ, P]),
         "dsa_resolve_indexer_sources": (ctypes.c_int, [I32, P, I32, P]),
@@ -231,6 +233,23 @@ def dsa_indexer_topk(batch, q, w, k_cache, k_scale, topk, topk_idx=None,
         ctypes.byref(cb), _ptr(q), _dtype(q), _ptr(w), H, D, _ptr(k_cache),
         _ptr(k_scale), _dtype(k_cache) if cache_dtype is None else cache_dtype,
         topk, _ptr(topk_idx), _ptr(ws), ws_bytes, _stream(stream)))
+    return topk_idx
+
+
+def dsa_indexer_topk_noalloc(batch, q, w, k_cache, k_scale, topk, topk_idx,
+                             cache_dtype=None, stream=None):
+    """The allocation-free indexer call: the caller passes the output buffer;
+    the library's static per-device scratch replaces the workspace."""
+    lib = load_library()
+    for n, t in (("q", q), ("w", w), ("k_cache", k_cache), ("k_scale", k_scale),
+                 ("topk_idx", topk_idx)):
+        _contig(n, t)
+    N, H, D = q.shape
+    cb = batch.c()
+    _check(lib.dsa_indexer_topk_noalloc(
+        ctypes.byref(cb), _ptr(q), _dtype(q), _ptr(w), H, D, _ptr(k_cache),
+        _ptr(k_scale), _dtype(k_cache) if cache_dtype is None else cache_dtype,
+        topk, _ptr(topk_idx), _stream(stream)))
     return topk_idx
 
 

@@ -13,6 +13,14 @@
 
 #include "common.h"
 
+#include <mutex>
+
+// Scratch of the allocation-free indexer entry point: one copy per GPU, held
+// until the process ends.  In host code this name is only a stand-in for the
+// device array: its device address comes from hipGetSymbolAddress, once per
+// device (see scratch_on_current_device), and only that address is used.
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -119,7 +127,8 @@ unsigned long long next_call_tag() {
 int check_indexer(const dsa_batch* b, const void* q, int q_dtype,
                   const float* w, int n_heads, int d_idx, const void* k_cache,
                   const float* k_scale, int cache_dtype, int topk,
-                  const int32_t* topk_idx, const void* ws, size_t ws_bytes) {
+                  const int32_t* topk_idx, const void* ws, size_t ws_bytes,
+                  bool check_ws = true) {
   int st = check_batch(b);
   if (st) return st;
   if (!q || !w || !k_cache || !topk_idx)
@@ -143,6 +152,7 @@ int check_indexer(const dsa_batch* b, const void* q, int q_dtype,
     return fail(DSA_ERR_UNSUPPORTED, "n_heads * d_idx > 8192");
   if (topk < 1 || topk > DSA_MAX_TOPK)
     return fail(DSA_ERR_UNSUPPORTED, "topk %d outside 1..%d", topk, DSA_MAX_TOPK);
+  if (!check_ws) return DSA_OK;
   if (b->num_q_tokens > 0 && (!ws || ws_bytes < topk_ws(b)))
     return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", topk_ws(b),
                 ws ? ws_bytes : static_cast<size_t>(0));
@@ -267,6 +277,41 @@ int resolve_sources(int32_t n_layers, const int32_t* types, int32_t n_types,
   return DSA_OK;
 }
 
+// Device address of `scratch` on the current device, looked up on the first
+// call on that device and kept.  The stream (if any) must belong to the
+// current device.  Returns DSA_OK or an error code with the text set.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DSA_ERR_UNSUPPORTED, "device %d beyond the %d devices supported", dev,
+                kMaxDevices);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(DSA_ERR_INVALID_ARG,
+                  "the stream belongs to device %d but device %d is current", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || reinterpret_cast<uintptr_t>(p) % kAlign)
+      return fail(DSA_ERR_HIP, "scratch address %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -316,6 +361,28 @@ int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
   return run_indexer(batch, q, q_dtype, w, n_heads, d_idx, k_cache, k_scale,
                      cache_dtype, topk, topk_idx, workspace,
                      static_cast<hipStream_t>(stream));
+}
+
+int dsa_indexer_topk_noalloc(const dsa_batch* batch, const void* q, int32_t q_dtype,
+                             const float* w, int32_t n_heads, int32_t d_idx,
+                             const void* k_cache, const float* k_scale,
+                             int32_t cache_dtype, int32_t topk, int32_t* topk_idx,
+                             void* stream) {
+  // every host-side check first, the scratch's size included
+  if (batch && batch->num_q_tokens >= 0 && batch->max_seq_len >= 0 &&
+      topk_ws(batch) > static_cast<size_t>(DSA_NOALLOC_SCRATCH_BYTES))
+    return fail(DSA_ERR_WORKSPACE,
+                "this batch needs %zu bytes of scratch; the allocation-free entry point "
+                "holds %d (use dsa_indexer_topk with a workspace)",
+                topk_ws(batch), DSA_NOALLOC_SCRATCH_BYTES);
+  int st = check_indexer(batch, q, q_dtype, w, n_heads, d_idx, k_cache, k_scale,
+                         cache_dtype, topk, topk_idx, nullptr, 0, /*check_ws=*/false);
+  if (st) return st;
+  void* ws = nullptr;
+  st = scratch_on_current_device(static_cast<hipStream_t>(stream), &ws);
+  if (st) return st;
+  return run_indexer(batch, q, q_dtype, w, n_heads, d_idx, k_cache, k_scale,
+                     cache_dtype, topk, topk_idx, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t sparse_mla_attn_workspace_size(const dsa_batch* batch, int32_t n_heads,

@@ -186,3 +186,16 @@ def test_indexshare_rejects_on_host():
         dsa.indexshare_forward(b, [dsa.DSA_LAYER_FULL, dsa.DSA_LAYER_SHARED], [L, L], dims, workspace=ws)
     with pytest.raises(ValueError, match="entries"):
         dsa.indexshare_forward(b, [dsa.DSA_LAYER_FULL], [L, L], dims, workspace=ws)
+
+
+def test_noalloc_rejects_oversized_batches_on_the_host():
+    """The allocation-free indexer call refuses a batch whose scratch would
+    exceed its static array, before touching the device."""
+    dsa = ensure_library()
+    lib = dsa.load_library()
+    cb = _batch(dsa, num_q_tokens=128, max_q_len=1, max_seq_len=131072, max_blocks=2048,
+                num_slots=1 << 24)
+    rc = lib.dsa_indexer_topk_noalloc(ctypes.byref(cb), _FAKE, 1, _FAKE, 32, 128, _FAKE,
+                                      None, 1, 2048, _FAKE, None)
+    assert rc == -5
+    assert "allocation-free" in dsa.dsa_last_error()

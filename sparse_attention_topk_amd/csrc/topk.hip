@@ -196,6 +196,39 @@ __device__ __forceinline__ void row_range(const float2* __restrict__ rng, int32_
   }
 }
 
+// Ranks the n threshold-bin candidates (values cval, positions cpos, in
+// LDS) by (score descending, position ascending) and marks the r best in
+// bm_sel.  Wave w ranks candidates 64 w + lane against every candidate,
+// taken one at a time with v_readlane from a register copy (lane k of round
+// k0 holds candidate k0 + k), eight per step; lanes past the last candidate
+// hold (-inf, INT_MAX), which outranks no candidate, so a step needs no bound
+// test.  n <= 64 * kWaves.
+__device__ __forceinline__ void rank_direct(const float* cval, const int32_t* cpos, int n,
+                                            uint32_t r, uint32_t* bm_sel) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  if (64 * wave >= n) return;
+  const int c = 64 * wave + lane;
+  const float mv = c < n ? cval[c] : 0.0f;
+  const int32_t mp = c < n ? cpos[c] : 0;
+  uint32_t rank = 0;
+  for (int k0 = 0; k0 < n; k0 += 64) {
+    const float ov = k0 + lane < n ? cval[k0 + lane] : -INFINITY;
+    const int32_t op = k0 + lane < n ? cpos[k0 + lane] : INT32_MAX;
+    const int m = min(64, n - k0);
+    for (int k = 0; k < m; k += 8) {
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const float v = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ov), k + kk));
+        const int32_t pk = __builtin_amdgcn_readlane(op, k + kk);
+        rank += (v > mv || (v == mv && pk < mp)) ? 1u : 0u;
+      }
+    }
+  }
+  if (c < n && rank < r) atomicOr(&bm_sel[mp >> 5], 1u << (mp & 31));
+}
+
 // ------------------------------------------------------------ register path
 // Position of register key (j, e) of a lane: wave w covers positions
 // 2048 w .. 2048 w + 2047, its load j (0..7) the 256 positions from
@@ -352,34 +385,8 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
           }
         }
         lds_barrier();
-        // ---- rank the candidates by (score descending, position ascending);
-        // the top r join the selection.  Wave w ranks candidates 64 w + lane
-        // against every candidate, taken one at a time with v_readlane from a
-        // register copy (lane k of round k0 holds candidate k0 + k), eight per
-        // step; lanes past the last candidate hold (-inf, INT_MAX), which
-        // outranks no candidate, so a step needs no bound test.
-        const int n = static_cast<int>(bin_count);
-        if (64 * wave < n) {
-          const int c = 64 * wave + lane;
-          const float mv = c < n ? cval[c] : 0.0f;
-          const int32_t mp = c < n ? cpos[c] : 0;
-          uint32_t rank = 0;
-          for (int k0 = 0; k0 < n; k0 += 64) {
-            const float ov = k0 + lane < n ? cval[k0 + lane] : -INFINITY;
-            const int32_t op = k0 + lane < n ? cpos[k0 + lane] : INT32_MAX;
-            const int m = min(64, n - k0);
-            for (int k = 0; k < m; k += 8) {
-#pragma unroll
-              for (int kk = 0; kk < 8; ++kk) {
-                const float v = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ov), k + kk));
-                const int32_t pk = __builtin_amdgcn_readlane(op, k + kk);
-                rank += (v > mv || (v == mv && pk < mp)) ? 1u : 0u;
-              }
-            }
-          }
-          if (c < n && rank < r) atomicOr(&s.bm_sel[mp >> 5], 1u << (mp & 31));
-        }
+        // ---- rank the candidates; the top r join the selection
+        rank_direct(cval, cpos, static_cast<int>(bin_count), r, s.bm_sel);
         ranked = true;
       }
     }
@@ -684,12 +691,230 @@ __device__ __forceinline__ void select_row_stream(Shared& s, const float* __rest
   });
 }
 
+// ------------------------------------------------------------ long rows
+// Rows of kRegCap < L <= kLongCap keys take the register path's steps with
+// the keys streamed from memory, two passes over the row (the histogram,
+// then one classification pass that marks every key of a higher bin in a
+// position bitmap and collects the threshold bin's keys as candidates); the
+// bitmaps live in dynamic LDS.  A row whose range the bin map cannot express,
+// or whose threshold bin holds more than kCandCap keys, is left to the exact
+// multi-pass path above (returns false before writing anything).
+constexpr int kLongCap = 262144;
+
+// Positions i .. i + 3 of a row (i a multiple of 4, i < L) as a float4,
+// f(i, v), streamed kV float4 per thread per round with the next round in
+// flight; entries at positions >= L hold clamped data the caller ignores.
+template <typename F>
+__device__ __forceinline__ void for_each_quad(const float* __restrict__ src, int L, F&& f) {
+  const int tid = threadIdx.x;
+  const int last4 = ((L + 3) & ~3) - 4;
+  auto load = [&](int base, float4 (&v)[kV]) {
+#pragma unroll
+    for (int j = 0; j < kV; ++j)
+      v[j] = *reinterpret_cast<const float4*>(src + min(base + 4 * (j * kThreads + tid), last4));
+  };
+  auto process = [&](int base, const float4 (&v)[kV]) {
+#pragma unroll
+    for (int j = 0; j < kV; ++j) {
+      const int i = base + 4 * (j * kThreads + tid);
+      if (i < L) f(i, v[j]);
+    }
+  };
+  float4 A[kV], B[kV];
+  load(0, A);
+  for (int base = 0; base < L; base += 2 * kRound) {
+    load(base + kRound, B);
+    process(base, A);
+    load(base + 2 * kRound, A);
+    process(base + kRound, B);
+  }
+}
+
+// Emits, in position order, every position set in bm_sel plus the first
+// `need` positions set in bm_eq (nwords words each, at most topk outputs).
+// Thread tid owns the run of words wpt tid .. wpt tid + wpt - 1; the counts
+// before each thread's run come from workgroup-wide scans.
+__device__ __forceinline__ void emit_bitmaps(Shared& s, const uint32_t* bm_sel,
+                                             const uint32_t* bm_eq, int nwords,
+                                             uint32_t need, int topk,
+                                             int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wpt = (nwords + kThreads - 1) / kThreads;
+  const int w0 = min(nwords, wpt * tid);
+  const int w1 = min(nwords, w0 + wpt);
+  uint32_t c_sel = 0, c_eq = 0;
+  for (int w = w0; w < w1; ++w) {
+    c_sel += __popc(bm_sel[w]);
+    c_eq += __popc(bm_eq[w]);
+  }
+  const uint32_t is = wave_scan_incl(c_sel);
+  const uint32_t ie = wave_scan_incl(c_eq);
+  if (lane == 63) {
+    s.wave_a[wave] = is;
+    s.wave_b[wave] = ie;
+  }
+  lds_barrier();
+  const uint32_t bs = __builtin_amdgcn_readlane(
+      wave_scan_incl(lane < wave ? s.wave_a[lane] : 0u), 63);
+  const uint32_t be = __builtin_amdgcn_readlane(
+      wave_scan_incl(lane < wave ? s.wave_b[lane] : 0u), 63);
+  uint32_t eq_before = be + ie - c_eq;
+  uint32_t o = bs + is - c_sel + min(eq_before, need);
+  for (int w = w0; w < w1 && o < static_cast<uint32_t>(topk); ++w) {
+    uint32_t ws = bm_sel[w];
+    const uint32_t we = bm_eq[w];
+    if (we && eq_before < need) {
+      uint32_t m = we;              // its lowest (need - eq_before) bits join
+      for (uint32_t c = need - eq_before; m && c; --c) {
+        const uint32_t low = m & (0u - m);
+        ws |= low;
+        m ^= low;
+      }
+    }
+    eq_before += __popc(we);
+    while (ws && o < static_cast<uint32_t>(topk)) {
+      out[o++] = 32 * w + __builtin_ctz(ws);
+      ws &= ws - 1;
+    }
+  }
+}
+
+// dyn: [bm_sel: words_cap][bm_eq: words_cap][candidate positions: kCandCap]
+__device__ __noinline__ bool select_row_long(Shared& s, uint32_t* __restrict__ dyn,
+                                             int32_t words_cap, const float* __restrict__ src,
+                                             int L, int topk, const float2* __restrict__ rng,
+                                             int32_t chunk_keys, float2 pre,
+                                             int32_t* __restrict__ out) {
+  const int tid = threadIdx.x;
+  const int nwords = (L + 31) / 32;
+  uint32_t* bm_sel = dyn;
+  uint32_t* bm_eq = dyn + words_cap;
+  int32_t* cpos = reinterpret_cast<int32_t*>(dyn + 2 * words_cap);
+  float* cval = reinterpret_cast<float*>(s.cand);
+
+  // ---- 1. range
+  float vmin, vmax;
+  row_range(rng, chunk_keys, L, pre, [&](float& lo, float& hi) {
+    lo = INFINITY;
+    hi = -INFINITY;
+    for_each_quad(src, L, [&](int i, const float4& v) {
+      const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool in = i + q < L;
+        lo = fminf(lo, in ? e[q] : INFINITY);
+        hi = fmaxf(hi, in ? e[q] : -INFINITY);
+      }
+    });
+  }, vmin, vmax);
+  for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
+  for (int w = tid; w < nwords; w += kThreads) {
+    bm_sel[w] = 0;
+    bm_eq[w] = 0;
+  }
+  if (tid == 0) s.ncand = 0;
+  range_reduce(s, vmin, vmax);
+  if (!(vmax > vmin)) {
+    // every score is equal: the first topk positions (L > topk here)
+    for (int j = tid; j < topk; j += kThreads) out[j] = j;
+    return true;
+  }
+  const float inv = static_cast<float>(kBins) / (vmax - vmin);
+  const float off = -vmin * inv;
+  if (!(inv > 0.0f && inv < INFINITY && off > -INFINITY && off < INFINITY)) return false;
+  // bin = trunc(clamp(x inv + off, 0, 2047)), monotone in x (see the
+  // register path)
+  auto bin = [&](float x) {
+    return static_cast<int>(fminf(fmaxf(fmaf(x, inv, off), 0.0f), kBins - 1.0f));
+  };
+
+  // ---- 2. histogram pass and threshold bin
+  for_each_quad(src, L, [&](int i, const float4& v) {
+    const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (i + q < L) atomicAdd(&s.hist[bin(e[q])], 1u);
+  });
+  lds_barrier();
+  find_threshold_bin(s, static_cast<uint32_t>(topk));
+  const int sel = static_cast<int>(s.sel_bin);
+  const uint32_t above_bin = s.above_bin;
+  const uint32_t r = static_cast<uint32_t>(topk) - above_bin;
+  if (s.hist[sel] > static_cast<uint32_t>(kCandCap)) return false;
+
+  // ---- 3. classification pass: a higher bin marks the position, the
+  // threshold bin appends a candidate (same tests as the register path)
+  const float thr_above = sel == kBins - 1 ? INFINITY : static_cast<float>(sel + 1);
+  const float thr_in = sel == 0 ? -INFINITY : static_cast<float>(sel);
+  for_each_quad(src, L, [&](int i, const float4& v) {
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t take = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float t = fmaf(e[q], inv, off);
+      const bool in = i + q < L;
+      take |= (in && t >= thr_above) ? (1u << q) : 0u;
+      if (in && t >= thr_in && t < thr_above) {
+        const uint32_t slot = atomicAdd(&s.ncand, 1u);
+        if (slot < static_cast<uint32_t>(kCandCap)) {   // always: same test as the bins
+          cval[slot] = e[q];
+          cpos[slot] = i + q;
+        }
+      }
+    }
+    if (take) atomicOr(&bm_sel[i >> 5], take << (i & 31));
+  });
+  lds_barrier();
+
+  // ---- 4. the r best candidates (as many as the threshold bin counted)
+  const uint32_t n = min(s.ncand, static_cast<uint32_t>(kCandCap));
+  uint32_t need = 0;
+  if (n <= static_cast<uint32_t>(kRankCap)) {
+    rank_direct(cval, cpos, static_cast<int>(n), r, bm_sel);
+  } else {
+    // exact radix select of rank r among the candidates' keys
+    uint32_t rr = r, prefix = 0, mask = 0, gt_extra = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kThreads) s.hist[i] = 0;
+      lds_barrier();
+      for (int i = tid; i < static_cast<int>(n); i += kThreads) {
+        const uint32_t k = float_key(cval[i]);
+        if ((k & mask) == prefix) atomicAdd(&s.hist[(k >> shift) & 255u], 1u);
+      }
+      lds_barrier();
+      find_digit(s, rr);
+      lds_barrier();
+      rr -= s.digit_above;
+      gt_extra += s.digit_above;
+      prefix |= s.digit << shift;
+      mask |= 255u << shift;
+      lds_barrier();
+    }
+    need = r - gt_extra;
+    for (int i = tid; i < static_cast<int>(n); i += kThreads) {
+      const uint32_t k = float_key(cval[i]);
+      const int32_t p = cpos[i];
+      if (k > prefix) atomicOr(&bm_sel[p >> 5], 1u << (p & 31));
+      if (k == prefix) atomicOr(&bm_eq[p >> 5], 1u << (p & 31));
+    }
+  }
+  lds_barrier();
+
+  // ---- 5. emission in position order
+  emit_bitmaps(s, bm_sel, bm_eq, nwords, need, topk, out);
+  return true;
+}
+
 __global__ __launch_bounds__(kThreads, 1) void k_topk(
     const float* __restrict__ scores, int64_t row_stride,
     const float2* __restrict__ crange, int32_t range_stride, int32_t chunk_keys,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
-    int32_t B, int32_t max_seq_len, int32_t topk, int32_t* __restrict__ out) {
+    int32_t B, int32_t max_seq_len, int32_t topk, int32_t* __restrict__ out,
+    int32_t words_cap) {
   __shared__ Shared s;
+  extern __shared__ uint32_t dyn[];   // long rows: words_cap > 0
   const int t = blockIdx.x;
   const float* src = scores + static_cast<int64_t>(t) * row_stride;
   // The request lookup (the largest b with cu_q[b] <= t, counted with a
@@ -720,19 +945,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
     for (int j = threadIdx.x; j < topk; j += kThreads) orow[j] = j < L ? j : -1;
     return;
   }
-  if (L <= kRegCap)
+  if (L <= kRegCap) {
     select_row_regs(s, f, L, topk, rng, chunk_keys, pre, orow);
-  else
-    select_row_stream(s, src, L, topk, rng, chunk_keys, pre, orow);
+    return;
+  }
+  if (L <= 32 * words_cap &&
+      select_row_long(s, dyn, words_cap, src, L, topk, rng, chunk_keys, pre, orow))
+    return;
+  lds_barrier();
+  select_row_stream(s, src, L, topk, rng, chunk_keys, pre, orow);
 }
 
 }  // namespace
 
 hipError_t launch_topk(const IndexerArgs& a, hipStream_t stream) {
   if (a.b.num_q_tokens == 0) return hipSuccess;
-  k_topk<<<a.b.num_q_tokens, kThreads, 0, stream>>>(
+  // long rows' bitmaps and candidate positions in dynamic LDS, sized for the
+  // longest row this launch can hold (none when every row fits registers)
+  const int32_t words_cap = a.b.max_seq_len > kRegCap
+                                ? (min(a.b.max_seq_len, kLongCap) + 31) / 32 : 0;
+  const size_t dyn_bytes = words_cap > 0 ? (2 * static_cast<size_t>(words_cap) + kCandCap) * 4 : 0;
+  k_topk<<<a.b.num_q_tokens, kThreads, dyn_bytes, stream>>>(
       a.scores, a.row_stride, a.chunk_range, a.range_stride, a.chunk_keys, a.b.seq_lens,
-      a.b.cu_q, a.b.num_reqs, a.b.max_seq_len, a.topk, a.topk_idx);
+      a.b.cu_q, a.b.num_reqs, a.b.max_seq_len, a.topk, a.topk_idx, words_cap);
   return hipGetLastError();
 }
 

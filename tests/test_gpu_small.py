@@ -162,6 +162,24 @@ def test_vector_path_odd_shapes(dsa):
     assert r >= 0.999
 
 
+@pytest.mark.parametrize("topk", [2048, 4096])
+def test_long_rows_random_scores(dsa, topk):
+    """Rows past the register path's reach (32769 .. 131072 keys, one
+    query each, bf16 N(0,1) data): recall against the oracle and the row
+    invariants."""
+    cfg = _small_cfg(num_reqs=4, q_len=1, topk=topk)
+    b = make_batch(cfg, DEV, seq_lens=[32769, 65543, 100000, 131072], q_lens=[1] * 4)
+    lay = make_layer(cfg, b, DEV)
+    idx = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), lay.q_idx, lay.w, lay.k_src, None, topk)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    ref = _oracle_topk(b, lay, cfg, np_bits(lay.k_src), None, OI.BF16, topk)
+    for t in range(4):
+        check_row_invariants(got[t], b.seq_lens[t] - 1, topk)
+    r, worst = recall(got, ref)
+    assert r >= 0.999, (r, worst)
+
+
 def test_fp8_cache_including_row_longer_than_lds(dsa):
     cfg = _small_cfg(num_reqs=3, q_len=1, idx_cache_dtype="fp8", topk=2048)
     b = make_batch(cfg, DEV, seq_lens=[100, 2500, 40000], q_lens=[1, 1, 1])
@@ -204,6 +222,11 @@ def _crafted(dsa, L, topk, kind):
     elif kind == "two_levels":
         hot = torch.randperm(b.num_slots, generator=g)[: b.num_slots // 2]
         k[hot, 0] = 2.0
+    elif kind == "int_levels":
+        # a quarter of the keys score 32 v for v uniform in 1..64, the rest 0:
+        # the selection's last level holds a few hundred equal scores
+        hot = torch.randperm(b.num_slots, generator=g)[: b.num_slots // 4]
+        k[hot, 0] = torch.randint(1, 65, (hot.numel(),), generator=g).to(torch.float32)
     elif kind == "spread":
         # keys (1 + m / 128) * 2^e over 240 binades, exact in bf16 and their
         # scores (32 k) exact in fp32: 30720 distinct values, repeats beyond;
@@ -227,8 +250,8 @@ def _crafted(dsa, L, topk, kind):
 
 
 @pytest.mark.parametrize("kind", ["all_zero", "neg_zero", "few_positive", "two_levels",
-                                  "spread"])
-@pytest.mark.parametrize("L", [3000, 32767, 32768, 50000])
+                                  "int_levels", "spread"])
+@pytest.mark.parametrize("L", [3000, 32767, 32768, 50000, 131072])
 def test_degenerate_score_rows_exact(dsa, kind, L):
     """Exactly representable scores, with massive ties or spread over many
     binades:
@@ -237,7 +260,8 @@ def test_degenerate_score_rows_exact(dsa, kind, L):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("L,topk", [(200, 16), (256, 100), (97, 96), (3000, 64)])
+@pytest.mark.parametrize("L,topk", [(200, 16), (256, 100), (97, 96), (3000, 64),
+                                    (40000, 512)])
 def test_subnormal_score_rows_exact(dsa, L, topk):
     """Scores that are all subnormal (integers times 2^-141 .. 2^-139, exact in
     fp32 on the vector path), a third of them zero: the row's range is far

@@ -56,8 +56,10 @@ __device__ __forceinline__ int dim_of(int hf, int s) {
 // sits at slot p ^ (r % P) of the row (P pieces per row), which spreads
 // the 32 rows of one operand load over distinct banks.  An e4m3 tile's 32
 // scales follow its rows (one 4-byte DMA per lane, two copies).
-constexpr int kRing = 2;
-static_assert(kRing >= 2 && kRing <= 4, "tile waits cover rings of 2 to 4 tiles");
+constexpr int kRing = 2;       // bf16 tiles (8 KiB) in flight per wave
+constexpr int kRingF8 = 2;     // e4m3 tiles (4.25 KiB) in flight per wave (3 or 4 measured slower)
+static_assert(kRing >= 2 && kRing <= 4 && kRingF8 >= 2 && kRingF8 <= 4,
+              "tile waits cover rings of 2 to 4 tiles");
 constexpr int kMaxTpw = 64;                      // tiles per wave (one block id per lane)
 template <bool F8>
 struct DmaTile {
@@ -131,7 +133,8 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   constexpr int H = 32 * MT;
   using DT = DmaTile<F8>;
   static_assert(kWaves == kRangeParts, "one range entry per wave and chunk");
-  __shared__ __align__(16) uint8_t ring[kWaves][kRing][DT::kBytes];
+  constexpr int RING = F8 ? kRingF8 : kRing;
+  __shared__ __align__(16) uint8_t ring[kWaves][RING][DT::kBytes];
   // the workgroup's scores, [token][key within chunk], written out at the
   // end: score stores interleaved with the key stream slow the reads down
   __shared__ __align__(16) float sc[TQ][kWaves * MAXT * kTile];
@@ -244,10 +247,10 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
     }
   };
   // r0[j]: first slot of the tile that ring slot j holds or is loading
-  // (tile j, then j + kRing, ...)
-  int64_t r0[kRing];
-  static_for<kRing>([&](auto jc) { r0[decltype(jc)::value] = tile_row0(decltype(jc)::value); });
-  static_for<kRing>([&](auto jc) {
+  // (tile j, then j + RING, ...)
+  int64_t r0[RING];
+  static_for<RING>([&](auto jc) { r0[decltype(jc)::value] = tile_row0(decltype(jc)::value); });
+  static_for<RING>([&](auto jc) {
     constexpr int j = decltype(jc)::value;
     if (j < ntiles) dma(j, r0[j]);
   });
@@ -275,26 +278,26 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   // range of token hf's causal scores among this wave's keys
   float rmin = INFINITY, rmax = -INFINITY;
   const int32_t my_pos = hf < nt ? pos0 + hf : -1;
-  for (int i0 = 0; i0 < ntiles; i0 += kRing) {
-    static_for<kRing>([&](auto jc) {
+  for (int i0 = 0; i0 < ntiles; i0 += RING) {
+    static_for<RING>([&](auto jc) {
       constexpr int j = decltype(jc)::value;   // ring slot of tile i
       const int i = i0 + j;
       if (i >= ntiles) return;
       const int64_t my_r0 = r0[j];
-      r0[j] = tile_row0(i + kRing);
+      r0[j] = tile_row0(i + RING);
       // tile i landed when at most the later tiles' DMAs are pending (tiles
-      // up to i + kRing - 1 are issued at this point)
-      const int later = min(ntiles - 1 - i, kRing - 1);
+      // up to i + RING - 1 are issued at this point)
+      const int later = min(ntiles - 1 - i, RING - 1);
       wait_tile<DT::kInstr>(later);
       const uint32_t tb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
           (__attribute__((address_space(3))) uint8_t*)(&ring[wave][j][0]))) + rbase;
-      // Slot j is refilled with tile i + kRing as soon as every LDS read of
-      // tile i has returned (the tile then lives in registers): kRing tiles
+      // Slot j is refilled with tile i + RING as soon as every LDS read of
+      // tile i has returned (the tile then lives in registers): RING tiles
       // are in flight while the wave multiplies.  The memory clobber keeps
       // the DMA behind the reads' waits.
       auto refill = [&]() {
         asm volatile("" ::: "memory");
-        if (i + kRing < ntiles) dma(j, r0[j]);
+        if (i + RING < ntiles) dma(j, r0[j]);
       };
       bf16x8 kv[8];
       float kscl = 1.0f;

@@ -15,6 +15,8 @@ rounding explicitly.
 Modules
   codecs     bf16 and OCP e4m3fn value codecs
   indexer    key-cache write, indexer score, deterministic top-k
+  fp8_indexer  the FP8-query variant: Hadamard rotation, per-row activation
+             quantisation, score over e4m3 queries and keys
   mla        absorbed sparse MLA over selected latent rows, and a dense
              causal MLA used only for the sparse == dense invariant
   indexshare GLM-5.2 IndexShare source-layer resolution and layer stack
@@ -36,7 +38,11 @@ or taken from the wrong row, one request's block table used for all, an
 off-by-one request lookup, prefill positions for decode queries) each fail
 one of these pins.
   indexshare  hand-derived source maps and every rejection case
+  fp8_indexer Hadamard orders 2 and 4 by hand, orthogonality and involution,
+              dot products kept, the fp32 butterflies within their rounding
+              bound, a hand-worked rotation / quantisation / score example
+              (tests/golden), brute-force top-k over e4m3 codes
 No oracle function is "parity unpinned".
 """
 
-from . import codecs, indexer, mla, indexshare  # noqa: F401
+from . import codecs, indexer, mla, indexshare, fp8_indexer  # noqa: F401

@@ -41,7 +41,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak, vendor figure
 SIMD_COUNT = 1024              # 256 CUs x 4 SIMDs
 METRIC = "decode query-tokens/s (indexer+top-k+sparse MLA) and % HBM roofline, 32K ctx"
-WORKLOADS = ["decode_32k_mtp", "fp8_decode_varlen", "indexshare_8layer", "prefill_16k"]
+WORKLOADS = ["decode_32k_mtp", "fp8_decode_varlen", "indexshare_8layer", "prefill_16k",
+             "fp8q_decode_32k_mtp"]
 
 
 def log(msg):
@@ -103,7 +104,7 @@ def indexer_bytes(b, cfg):
     if cfg.idx_cache_dtype == "fp8":
         key_b += 4
     keys = sum(b.seq_lens) * key_b
-    q = b.num_q_tokens * cfg.n_idx_heads * cfg.d_idx * 2
+    q = b.num_q_tokens * cfg.n_idx_heads * cfg.d_idx * 2   # bf16 queries read once
     w = b.num_q_tokens * cfg.n_idx_heads * 4
     out = b.num_q_tokens * cfg.topk * 4
     bt = b.num_reqs * b.max_blocks * 4
@@ -389,7 +390,7 @@ def cpu_baseline(cfg, b, lay, seconds, units):
     mean context of the units used)."""
     import numpy as np
     import torch
-    from oracle import indexer as OI, mla as OM
+    from oracle import fp8_indexer as F8, indexer as OI, mla as OM
     bs = b.block_size
     fp8 = cfg.idx_cache_dtype == "fp8"
 
@@ -404,7 +405,8 @@ def cpu_baseline(cfg, b, lay, seconds, units):
         kbits = lay.k_src[slots].cpu().view(torch.int16).numpy().view(np.uint16)
         if fp8:
             k32 = (kbits.astype(np.uint32) << np.uint32(16)).view(np.float32)
-            keys, scale, kd = (*OI.fp8_quantize_rows(k32), OI.FP8)
+            quant = F8.rotate_quantize if cfg.idx_q_fp8 else OI.fp8_quantize_rows
+            keys, scale, kd = (*quant(k32), OI.FP8)
         else:
             keys, scale, kd = kbits, None, OI.BF16
         kv = lay.kv_cache[slots].cpu().float().numpy()
@@ -420,7 +422,11 @@ def cpu_baseline(cfg, b, lay, seconds, units):
             pool.append(host_inputs(units[len(pool)]))
         L, ql, keys, scale, kd, kv, q, w, qm, ident = pool[runs % len(pool)]
         start = time.perf_counter()
-        idx = OI.indexer_topk([L], [0, ql], ident, bs, q, w, keys, scale, kd, cfg.topk)
+        if cfg.idx_q_fp8:
+            qc, qs = F8.rotate_quantize(q.astype(np.float32))
+            idx = F8.indexer_topk([L], [0, ql], ident, bs, qc, qs, w, keys, scale, cfg.topk)
+        else:
+            idx = OI.indexer_topk([L], [0, ql], ident, bs, q, w, keys, scale, kd, cfg.topk)
         OM.sparse_mla([L], [0, ql], ident, bs, qm, lambda s: kv[s], idx,
                       cfg.kv_lora_rank, cfg.softmax_scale)
         spent += time.perf_counter() - start
@@ -497,7 +503,14 @@ def main():
 
     lay = make_layer(cfg, b, dev)
     # the cache before this step: every slot populated through the cache write
-    if cfg.idx_cache_dtype == "fp8":
+    if cfg.idx_q_fp8:
+        k_cache = torch.empty((b.num_slots, cfg.d_idx), dtype=torch.uint8, device=dev)
+        k_scale = torch.empty((b.num_slots,), dtype=torch.float32, device=dev)
+        all_slots = torch.arange(b.num_slots, dtype=torch.int64, device=dev)
+        dsa.dsa_rotate_quantize(lay.k_src, k_cache, k_scale, row_slots=all_slots)
+        q_codes = torch.empty(lay.q_idx.shape, dtype=torch.uint8, device=dev)
+        q_scale = torch.empty(lay.q_idx.shape[:2], dtype=torch.float32, device=dev)
+    elif cfg.idx_cache_dtype == "fp8":
         k_cache = torch.empty((b.num_slots, cfg.d_idx), dtype=torch.uint8, device=dev)
         k_scale = torch.empty((b.num_slots,), dtype=torch.float32, device=dev)
         all_slots = torch.arange(b.num_slots, dtype=torch.int64, device=dev)
@@ -515,11 +528,19 @@ def main():
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
     def cache_write():
-        dsa.dsa_indexer_cache_write(k_new, b.slot_mapping_t, k_cache, k_scale)
+        if cfg.idx_q_fp8:        # rotated, quantised keys into the FP8 cache
+            dsa.dsa_rotate_quantize(k_new, k_cache, k_scale, row_slots=b.slot_mapping_t)
+        else:
+            dsa.dsa_indexer_cache_write(k_new, b.slot_mapping_t, k_cache, k_scale)
 
     def indexer():
-        dsa.dsa_indexer_topk(bb, lay.q_idx, lay.w, k_cache, k_scale, cfg.topk,
-                             topk_idx=topk_idx, workspace=ws)
+        if cfg.idx_q_fp8:        # rotated, quantised queries, then the e4m3 score
+            dsa.dsa_rotate_quantize(lay.q_idx, q_codes, q_scale)
+            dsa.dsa_indexer_topk_fp8q(bb, q_codes, q_scale, lay.w, k_cache, k_scale,
+                                      cfg.topk, topk_idx=topk_idx, workspace=ws)
+        else:
+            dsa.dsa_indexer_topk(bb, lay.q_idx, lay.w, k_cache, k_scale, cfg.topk,
+                                 topk_idx=topk_idx, workspace=ws)
 
     def attention():
         dsa.sparse_mla_attn(bb, lay.q_mla, lay.kv_cache, topk_idx, cfg.kv_lora_rank,
@@ -569,6 +590,8 @@ def main():
         # latent rows and keys stay cache-resident: matrix-core bound
         roof = (mfma_roofline("sparse_mla_attn (k_mla_mfma)", mfl, ml_ms) if ml_ms >= ix_ms
                 else mfma_roofline("dsa_indexer_topk", ifl, ix_ms))
+    elif cfg.idx_q_fp8:
+        roof = hbm_roofline("dsa_rotate_quantize (queries) + dsa_indexer_topk_fp8q", ib, ix_ms)
     else:
         roof = hbm_roofline("dsa_indexer_topk (score + top-k)", ib, ix_ms,
                             load_traffic(cfg.name), INDEXER_KERNELS)
@@ -581,7 +604,9 @@ def main():
         "p10_ms": st["p10_ms"], "p90_ms": st["p90_ms"],
         "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.idx_cache_dtype != "fp8" else "bf16+fp8-cache",
+        "dtype": ("bf16" if cfg.idx_cache_dtype != "fp8" else
+                  "fp8 indexer (e4m3 q and k), bf16 MLA" if cfg.idx_q_fp8 else
+                  "bf16+fp8-cache"),
         "data": "synthetic",
         "config": {"workload": cfg.name, "requests": b.num_reqs,
                    "max_context": b.max_seq_len, "total_context": int(sum(b.seq_lens)),

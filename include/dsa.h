@@ -143,7 +143,8 @@ int dsa_indexer_cache_write(const void* k_new, int32_t k_dtype, int32_t n_new,
  *            Selection order is (score descending, position ascending), so
  *            the set is unique.
  * Scores use fp32 accumulation (bf16 / fp8 operands are widened exactly).
- * Supported: q_dtype == cache_dtype for F32/BF16, q BF16 with an FP8 cache;
+ * Supported: q_dtype == cache_dtype for F32/BF16, q BF16 with an FP8 cache
+ * (FP8 queries: dsa_indexer_topk_fp8q);
  * n_heads 1..64 and d_idx 1..256 (the matrix-core path needs n_heads % 32 == 0
  * and d_idx == 128; other shapes take a slower vector path); topk 1..4096.
  * workspace: at least dsa_indexer_topk_workspace_size() bytes, 256-byte
@@ -159,6 +160,50 @@ int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
                      const void* k_cache, const float* k_scale,
                      int32_t cache_dtype, int32_t topk, int32_t* topk_idx,
                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Activation rotation and quantisation of the FP8 indexer path (section
+ * "DSA Indexer fused semantic op": the DeepSeek-V3.2 FP8 path applies
+ * rotate_activation and activation quantisation before the FP8 key cache /
+ * scale cache write and the FP8 index score; section "Performance model
+ * design", bucket 5).  Each row of d elements is rotated by the orthonormal
+ * Hadamard transform (Sylvester order, scaled by d^-1/2: butterflies over
+ * strides 1, 2, ..., d/2 in fp32, then one multiply by fl32(d^-1/2)) and
+ * quantised like a key of an FP8 cache: scale = fl32(amax / 448) (1 if
+ * amax == 0), code = e4m3(fl32(v / scale)), round to nearest even,
+ * saturating.
+ *   x          [n_rows, d] F32 or BF16
+ *   row_slots  [n_rows] int64 output rows (-1 or >= num_out: skipped), or
+ *              NULL: row i goes to output row i (n_rows <= num_out)
+ *   codes      [num_out, d] e4m3 codes; scales [num_out] fp32
+ * Queries: rows are the heads of each token (n_rows = N * n_heads, one scale
+ * per token and head), row_slots NULL.  Keys: rows are tokens, row_slots the
+ * slot mapping, codes / scales the FP8 indexer cache and its scale cache.
+ * d: a power of two in 32..256.
+ */
+int dsa_rotate_quantize(const void* x, int32_t x_dtype, int64_t n_rows, int32_t d,
+                        const int64_t* row_slots, int64_t num_out, uint8_t* codes,
+                        float* scales, void* stream);
+
+/*
+ * Indexer score + top-k over e4m3 queries and an e4m3 cache (the FP8 path of
+ * section "DSA Indexer fused semantic op"; section "Performance model
+ * design", bucket 7: ReLU / q-scale / k-scale shaping):
+ *     score[t, s] = k_scale[s] * sum_h w[t, h] * q_scale[t, h] *
+ *                   ReLU(qv[t, h, :] . kv[s, :])
+ * with qv, kv the values of the e4m3 codes (both rotated by
+ * dsa_rotate_quantize, which keeps every dot product).  Selection, output
+ * rows, workspace and errors as dsa_indexer_topk.
+ *   q_codes  [N, n_heads, d_idx] e4m3;  q_scale [N, n_heads] fp32 (> 0)
+ *   k_cache  [num_slots, d_idx] e4m3;  k_scale [num_slots] fp32
+ * d_idx == 128 with n_heads 32 or 64 runs on the fp8 matrix cores; other
+ * shapes within dsa_indexer_topk's limits take the vector path.
+ */
+int dsa_indexer_topk_fp8q(const dsa_batch* batch, const uint8_t* q_codes,
+                          const float* q_scale, const float* w, int32_t n_heads,
+                          int32_t d_idx, const void* k_cache, const float* k_scale,
+                          int32_t topk, int32_t* topk_idx, void* workspace,
+                          size_t ws_bytes, void* stream);
 
 /*
  * Allocation-free variant of dsa_indexer_topk, for callers that cannot

@@ -18,7 +18,8 @@ DSA_LAYER_FULL, DSA_LAYER_SHARED = 0, 1
 
 EXPORTS = [
     "dsa_indexer_cache_write", "dsa_indexer_topk_workspace_size",
-    "dsa_indexer_topk", "dsa_indexer_topk_noalloc", "sparse_mla_attn_workspace_size",
+    "dsa_indexer_topk", "dsa_indexer_topk_noalloc", "dsa_rotate_quantize",
+    "dsa_indexer_topk_fp8q", "sparse_mla_attn_workspace_size",
     "sparse_mla_attn",
     "dsa_resolve_indexer_sources", "indexshare_forward_workspace_size",
     "indexshare_forward", "dsa_fp8_decode_check", "dsa_last_error",
@@ -79,6 +80,8 @@ def load_library():
         "dsa_indexer_topk_workspace_size": (SZ, [P, I32]),
         "dsa_indexer_topk": (ctypes.c_int, [P, P, I32, P, I32, I32, P, P, I32, I32, P, P, SZ, P]),
         "dsa_indexer_topk_noalloc": (ctypes.c_int, [P, P, I32, P, I32, I32, P, P, I32, I32, P, P]),
+        "dsa_rotate_quantize": (ctypes.c_int, [P, I32, I64, I32, P, I64, P, P, P]),
+        "dsa_indexer_topk_fp8q": (ctypes.c_int, [P, P, P, P, I32, I32, P, P, I32, P, P, SZ, P]),
         "sparse_mla_attn_workspace_size": (SZ, [P, I32, I32, I32, I32, I32]),
         "sparse_mla_attn": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, P, I32, F, P, P, P, SZ, P]),
         "dsa_resolve_indexer_sources": (ctypes.c_int, [I32, P, I32, P]),
@@ -250,6 +253,52 @@ def dsa_indexer_topk_noalloc(batch, q, w, k_cache, k_scale, topk, topk_idx,
         ctypes.byref(cb), _ptr(q), _dtype(q), _ptr(w), H, D, _ptr(k_cache),
         _ptr(k_scale), _dtype(k_cache) if cache_dtype is None else cache_dtype,
         topk, _ptr(topk_idx), _stream(stream)))
+    return topk_idx
+
+
+def dsa_rotate_quantize(x, codes=None, scales=None, row_slots=None, stream=None):
+    """Hadamard-rotate and e4m3-quantise the rows of x [..., d].  Without
+    row_slots the outputs have x's row shape (allocated when not given);
+    with row_slots (int64, one per row) codes / scales are the destination
+    cache [num_out, d] / [num_out] and row i goes to row row_slots[i]."""
+    lib = load_library()
+    _contig("x", x)
+    d = x.shape[-1]
+    n = x.numel() // d if d else 0
+    if row_slots is None:
+        if codes is None:
+            codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        if scales is None:
+            scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+        num_out = n
+    else:
+        if codes is None or scales is None:
+            raise ValueError("row_slots needs the destination codes and scales")
+        if row_slots.dtype != torch.int64 or row_slots.numel() != n:
+            raise ValueError("row_slots must be int64 with one entry per row")
+        num_out = codes.shape[0]
+    _contig("codes", codes), _contig("scales", scales)
+    _check(lib.dsa_rotate_quantize(_ptr(x), _dtype(x), n, d, _ptr(row_slots), num_out,
+                                   _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def dsa_indexer_topk_fp8q(batch, q_codes, q_scale, w, k_cache, k_scale, topk,
+                          topk_idx=None, workspace=None, stream=None):
+    lib = load_library()
+    for n, t in (("q_codes", q_codes), ("q_scale", q_scale), ("w", w),
+                 ("k_cache", k_cache), ("k_scale", k_scale)):
+        _contig(n, t)
+    N, H, D = q_codes.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((N, topk), dtype=torch.int32, device=q_codes.device)
+    cb = batch.c()
+    ws = _workspace(lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb), topk),
+                    q_codes.device, workspace, stream)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.dsa_indexer_topk_fp8q(
+        ctypes.byref(cb), _ptr(q_codes), _ptr(q_scale), _ptr(w), H, D, _ptr(k_cache),
+        _ptr(k_scale), topk, _ptr(topk_idx), _ptr(ws), ws_bytes, _stream(stream)))
     return topk_idx
 
 

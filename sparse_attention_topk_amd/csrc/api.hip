@@ -128,18 +128,22 @@ int check_indexer(const dsa_batch* b, const void* q, int q_dtype,
                   const float* w, int n_heads, int d_idx, const void* k_cache,
                   const float* k_scale, int cache_dtype, int topk,
                   const int32_t* topk_idx, const void* ws, size_t ws_bytes,
-                  bool check_ws = true) {
+                  bool check_ws = true, const float* q_scale = nullptr) {
   int st = check_batch(b);
   if (st) return st;
   if (!q || !w || !k_cache || !topk_idx)
     return fail(DSA_ERR_INVALID_ARG, "q, w, k_cache and topk_idx must be non-NULL");
   if (!known_dtype(q_dtype) || !known_dtype(cache_dtype))
     return fail(DSA_ERR_INVALID_ARG, "unknown dtype");
-  if (q_dtype == DSA_FP8_E4M3)
-    return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer queries are not supported");
+  if (q_dtype == DSA_FP8_E4M3) {
+    if (!q_scale)
+      return fail(DSA_ERR_UNSUPPORTED, "FP8 queries go through dsa_indexer_topk_fp8q");
+    if (cache_dtype != DSA_FP8_E4M3)
+      return fail(DSA_ERR_UNSUPPORTED, "FP8 queries need an FP8 cache");
+  }
   if (cache_dtype == DSA_FP8_E4M3) {
-    if (q_dtype != DSA_BF16)
-      return fail(DSA_ERR_UNSUPPORTED, "an FP8 cache needs bf16 queries");
+    if (q_dtype != DSA_BF16 && q_dtype != DSA_FP8_E4M3)
+      return fail(DSA_ERR_UNSUPPORTED, "an FP8 cache needs bf16 or FP8 queries");
     if (!k_scale) return fail(DSA_ERR_INVALID_ARG, "FP8 cache needs k_scale");
   } else if (cache_dtype != q_dtype) {
     return fail(DSA_ERR_UNSUPPORTED, "q dtype %d with cache dtype %d", q_dtype,
@@ -189,11 +193,12 @@ int check_mla(const dsa_batch* b, const void* q, const void* kv, int dtype,
 int run_indexer(const dsa_batch* b, const void* q, int q_dtype, const float* w,
                 int n_heads, int d_idx, const void* k_cache, const float* k_scale,
                 int cache_dtype, int topk, int32_t* topk_idx, void* ws,
-                hipStream_t stream) {
+                hipStream_t stream, const float* q_scale = nullptr) {
   dsa::IndexerArgs a;
   a.b = *b;
   a.q = q;
   a.q_dtype = q_dtype;
+  a.q_scale = q_scale;
   a.w = w;
   a.n_heads = n_heads;
   a.d_idx = d_idx;
@@ -361,6 +366,40 @@ int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
   return run_indexer(batch, q, q_dtype, w, n_heads, d_idx, k_cache, k_scale,
                      cache_dtype, topk, topk_idx, workspace,
                      static_cast<hipStream_t>(stream));
+}
+
+int dsa_rotate_quantize(const void* x, int32_t x_dtype, int64_t n_rows, int32_t d,
+                        const int64_t* row_slots, int64_t num_out, uint8_t* codes,
+                        float* scales, void* stream) {
+  if (n_rows < 0 || num_out < 1)
+    return fail(DSA_ERR_INVALID_ARG, "n_rows %lld / num_out %lld",
+                static_cast<long long>(n_rows), static_cast<long long>(num_out));
+  if (d < 32 || d > 256 || (d & (d - 1)))
+    return fail(DSA_ERR_UNSUPPORTED, "d %d is not a power of two in 32..256", d);
+  if (x_dtype != DSA_F32 && x_dtype != DSA_BF16)
+    return fail(DSA_ERR_UNSUPPORTED, "rows must be F32 or BF16");
+  if (n_rows > 0 && (!x || !codes || !scales))
+    return fail(DSA_ERR_INVALID_ARG, "x, codes and scales must be non-NULL");
+  if (!row_slots && n_rows > num_out)
+    return fail(DSA_ERR_INVALID_ARG, "n_rows exceeds num_out without row_slots");
+  hipError_t e = dsa::launch_rotate_quantize(x, x_dtype, n_rows, d, row_slots, num_out,
+                                             codes, scales, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rotate-quantize launch");
+  return ok();
+}
+
+int dsa_indexer_topk_fp8q(const dsa_batch* batch, const uint8_t* q_codes,
+                          const float* q_scale, const float* w, int32_t n_heads,
+                          int32_t d_idx, const void* k_cache, const float* k_scale,
+                          int32_t topk, int32_t* topk_idx, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  if (!q_scale) return fail(DSA_ERR_INVALID_ARG, "q_scale must be non-NULL");
+  int st = check_indexer(batch, q_codes, DSA_FP8_E4M3, w, n_heads, d_idx, k_cache, k_scale,
+                         DSA_FP8_E4M3, topk, topk_idx, workspace, ws_bytes, true, q_scale);
+  if (st) return st;
+  return run_indexer(batch, q_codes, DSA_FP8_E4M3, w, n_heads, d_idx, k_cache, k_scale,
+                     DSA_FP8_E4M3, topk, topk_idx, workspace,
+                     static_cast<hipStream_t>(stream), q_scale);
 }
 
 int dsa_indexer_topk_noalloc(const dsa_batch* batch, const void* q, int32_t q_dtype,

@@ -8,6 +8,9 @@
 // reduces amax = max |k| exactly, scale = fl32(amax / 448) (1 if amax == 0),
 // each lane divides its elements by scale (IEEE fp32 division) and rounds to
 // e4m3fn with round-to-nearest-even and saturation at +-448.
+#include <cmath>
+#include <type_traits>
+
 #include "common.h"
 
 namespace dsa {
@@ -85,6 +88,65 @@ __global__ __launch_bounds__(256) void k_quant_keys(const T* __restrict__ k_new,
   if (lane == 0) scale[slot] = s;
 }
 
+// Activation rotation and quantisation (page "GLM5 TensorCast 适配设计",
+// section "DSA Indexer fused semantic op": the FP8 path's rotate_activation
+// and activation quantisation; section "Performance model design", bucket
+// 5).  One 64-lane wave per row of d = 32 .. 256 (a power of two) elements:
+// element l + 64 m sits in lane l, slot m (EPL = max(1, d / 64) slots).  The
+// orthonormal Hadamard transform runs as butterflies over h = 1, 2, ...,
+// d / 2 in that order, (a, b) -> (a + b, a - b) for the pair (i, i + h) in
+// each block of 2 h, rounded to fp32 at every stage, then one multiply by
+// inv_sqrt_d = fl32(d^-1/2); pairs of h < 64 meet across lanes l and l ^ h,
+// pairs of h >= 64 inside a lane.  The rotated row is then quantised like a
+// key: amax, scale = fl32(amax / 448) (1 if amax == 0), e4m3(v / scale).
+template <typename T, int EPL>
+__global__ __launch_bounds__(256) void k_rotate_quantize(
+    const T* __restrict__ x, int64_t n_rows, int d, float inv_sqrt_d,
+    const int64_t* __restrict__ row_slots, int64_t num_out,
+    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows) return;
+  const int64_t dst = row_slots ? row_slots[row] : row;
+  if (dst < 0 || dst >= num_out) return;
+  const bool live = lane < d;            // d < 64: lanes d .. 63 hold nothing
+  float v[EPL];
+#pragma unroll
+  for (int m = 0; m < EPL; ++m)
+    v[m] = live ? load_as_f32(x, row * d + lane + 64 * m) : 0.0f;
+  for (int h = 1; h < 64 && h < d; h <<= 1) {
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+      const float other = __shfl_xor(v[m], h);
+      v[m] = (lane & h) ? other - v[m] : v[m] + other;
+    }
+  }
+#pragma unroll
+  for (int h = 1; h < EPL; h <<= 1) {    // element strides 64 h
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+      if (m & h) continue;
+      const float a = v[m], b = v[m + h];
+      v[m] = a + b;
+      v[m + h] = a - b;
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int m = 0; m < EPL; ++m) {
+    v[m] *= inv_sqrt_d;
+    amax = fmaxf(amax, fabsf(v[m]));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float sc = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  if (live) {
+#pragma unroll
+    for (int m = 0; m < EPL; ++m)
+      codes[dst * d + lane + 64 * m] = static_cast<uint8_t>(f32_to_e4m3(v[m] / sc));
+  }
+  if (lane == 0) scales[dst] = sc;
+}
+
 // Decodes e4m3 codes, 8 per thread, with the conversion and byte packing
 // the indexer's FP8 path uses (n is a multiple of 8).
 __global__ void k_fp8_decode_check(const uint8_t* __restrict__ codes,
@@ -122,6 +184,33 @@ hipError_t launch_cache_write(const void* k_new, int k_dtype, int n_new,
     k_copy_keys<float><<<grid, block, 0, stream>>>(
         static_cast<const float*>(k_new), n_new, d, slots, num_slots,
         static_cast<float*>(k_cache));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate_quantize(const void* x, int x_dtype, int64_t n_rows, int d,
+                                  const int64_t* row_slots, int64_t num_out, uint8_t* codes,
+                                  float* scales, hipStream_t stream) {
+  if (n_rows == 0) return hipSuccess;
+  // fl32(d^-1/2): the double square root and reciprocal are correctly
+  // rounded, then rounded once to float
+  const float inv = static_cast<float>(1.0 / std::sqrt(static_cast<double>(d)));
+  const dim3 grid(static_cast<unsigned>((n_rows + 3) / 4)), block(256);
+  auto go = [&](auto tag, auto epl) {
+    using T = decltype(tag);
+    constexpr int E = decltype(epl)::value;
+    k_rotate_quantize<T, E><<<grid, block, 0, stream>>>(
+        static_cast<const T*>(x), n_rows, d, inv, row_slots, num_out, codes, scales);
+  };
+  const int epl = d <= 64 ? 1 : d / 64;
+  if (x_dtype == DSA_BF16) {
+    if (epl == 1) go(uint16_t{}, std::integral_constant<int, 1>{});
+    else if (epl == 2) go(uint16_t{}, std::integral_constant<int, 2>{});
+    else go(uint16_t{}, std::integral_constant<int, 4>{});
+  } else {
+    if (epl == 1) go(float{}, std::integral_constant<int, 1>{});
+    else if (epl == 2) go(float{}, std::integral_constant<int, 2>{});
+    else go(float{}, std::integral_constant<int, 4>{});
   }
   return hipGetLastError();
 }

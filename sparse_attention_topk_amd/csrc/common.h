@@ -143,6 +143,7 @@ struct IndexerArgs {
   dsa_batch b;
   const void* q;
   int q_dtype;
+  const float* q_scale;   // e4m3 queries: [N, n_heads] scales; else null
   const float* w;
   int n_heads, d_idx;
   const void* k_cache;
@@ -196,6 +197,13 @@ bool mla_mfma_ok(const dsa_batch& b, int dtype, int n_heads, int R, int P);
 int mla_choose_split(const dsa_batch* b, int dtype, int n_heads, int R, int P,
                      int topk);
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);
+
+// Hadamard-rotates and quantises rows of d (a power of two, 32 .. 256)
+// elements; row i goes to output row row_slots[i] (or i when row_slots is
+// null), skipped when that is negative or >= num_out.
+hipError_t launch_rotate_quantize(const void* x, int x_dtype, int64_t n_rows, int d,
+                                  const int64_t* row_slots, int64_t num_out, uint8_t* codes,
+                                  float* scales, hipStream_t stream);
 
 hipError_t launch_fp8_decode_check(const uint8_t* codes, float* out, int n,
                                    hipStream_t stream);

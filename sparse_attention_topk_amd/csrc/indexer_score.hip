@@ -31,6 +31,8 @@
 namespace dsa {
 namespace {
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));   // 32 e4m3 codes
+
 constexpr int kTile = 32;      // keys per MFMA tile
 constexpr int kWaves = 4;      // waves per workgroup
 // Dim mapping of the MFMA operands.  Lane half hf = lane / 32 and K-step s
@@ -120,9 +122,12 @@ __device__ __forceinline__ void wait_tile(int later) {
 // MAXT: tiles per wave the LDS score buffer holds.  With 16 (launches of
 // several rounds) two workgroups share a CU, so one's start overlaps the
 // other's stream.
-template <int TQ, int MT, bool F8, int MAXT>
+// QF8: e4m3 queries (rotated, quantised per head, q_scale per token and
+// head) against an e4m3 cache, contracted on the fp8 matrix cores.
+template <int TQ, int MT, bool F8, int MAXT, bool QF8 = false>
 __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
-    const uint16_t* __restrict__ q, const float* __restrict__ w,
+    const uint16_t* __restrict__ q, const float* __restrict__ qscale,
+    const float* __restrict__ w,
     const uint8_t* __restrict__ kc, const float* __restrict__ kscale,
     const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ block_table,
@@ -131,6 +136,7 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
     int32_t tiles_per_wave, float* __restrict__ scores, int64_t row_stride,
     float2* __restrict__ crange, int32_t range_stride) {
   constexpr int H = 32 * MT;
+  static_assert(!QF8 || F8, "e4m3 queries go with an e4m3 cache");
   using DT = DmaTile<F8>;
   static_assert(kWaves == kRangeParts, "one range entry per wave and chunk");
   constexpr int RING = F8 ? kRingF8 : kRing;
@@ -188,25 +194,46 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   // The loads are unconditional (a block with one token loads that token
   // twice): the second token's scores are then never written out, and
   // branch-free loads leave the compiler's wait counting exact.
-  bf16x8 qa[TQ][MT][8];
+  // bf16 queries: qa[.][.][s] = dims dim_of(hf, s); e4m3 queries: qa8[.][.][s]
+  // = the 32 code bytes of dims 64 s + 32 hf .. + 31 (the key operand takes
+  // the same bytes of its row, so each product pairs equal dims)
+  constexpr int QS = QF8 ? 1 : 8;
+  constexpr int QS8 = QF8 ? 2 : 1;
+  bf16x8 qa[TQ][MT][QS];
+  i32x8 qa8[TQ][MT][QS8];
   float wr[TQ][MT][16];
 #pragma unroll
   for (int tt = 0; tt < TQ; ++tt) {
     const int64_t tok = tbeg + t0 + (tt < nt ? tt : 0);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const uint16_t* qrow = q + (tok * H + mt * 32 + col) * 128;
+      if constexpr (QF8) {
+        const uint8_t* qrow = reinterpret_cast<const uint8_t*>(q) + (tok * H + mt * 32 + col) * 128;
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        qa[tt][mt][s] = *reinterpret_cast<const bf16x8*>(qrow + dim_of<F8>(hf, s));
+        for (int s = 0; s < 2; ++s) {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(qrow + 64 * s + 32 * hf);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(qrow + 64 * s + 32 * hf + 16);
+          qa8[tt][mt][s] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                                 (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+      } else {
+        const uint16_t* qrow = q + (tok * H + mt * 32 + col) * 128;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          qa[tt][mt][s] = *reinterpret_cast<const bf16x8*>(qrow + dim_of<F8>(hf, s));
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float4 w4 =
-            *reinterpret_cast<const float4*>(w + tok * H + mt * 32 + 8 * g + 4 * hf);
-        wr[tt][mt][4 * g + 0] = w4.x;
-        wr[tt][mt][4 * g + 1] = w4.y;
-        wr[tt][mt][4 * g + 2] = w4.z;
-        wr[tt][mt][4 * g + 3] = w4.w;
+        const int64_t hw = tok * H + mt * 32 + 8 * g + 4 * hf;
+        const float4 w4 = *reinterpret_cast<const float4*>(w + hw);
+        float4 s4 = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        if constexpr (QF8) s4 = *reinterpret_cast<const float4*>(qscale + hw);
+        // the query's scale joins its head weight (both multiply the head's
+        // ReLU term; the scale is positive)
+        wr[tt][mt][4 * g + 0] = w4.x * s4.x;
+        wr[tt][mt][4 * g + 1] = w4.y * s4.y;
+        wr[tt][mt][4 * g + 2] = w4.z * s4.z;
+        wr[tt][mt][4 * g + 3] = w4.w * s4.w;
       }
     }
   }
@@ -263,8 +290,13 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   for (int tt = 0; tt < TQ; ++tt)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
+      if constexpr (QF8) {
 #pragma unroll
-      for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(qa[tt][mt][st]));
+        for (int st = 0; st < 2; ++st) asm volatile("" : "+v"(qa8[tt][mt][st]));
+      } else {
+#pragma unroll
+        for (int st = 0; st < 8; ++st) asm volatile("" : "+v"(qa[tt][mt][st]));
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(wr[tt][mt][r]));
     }
@@ -299,7 +331,8 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
         asm volatile("" ::: "memory");
         if (i + RING < ntiles) dma(j, r0[j]);
       };
-      bf16x8 kv[8];
+      bf16x8 kv[QF8 ? 1 : 8];
+      i32x8 kv8[QF8 ? 2 : 1];
       float kscl = 1.0f;
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if constexpr (!F8) {
@@ -318,18 +351,32 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
                    (__attribute__((address_space(3))) uint8_t*)(&ring[wave][j][0]))) +
                DT::kScaleOff + 4u * static_cast<uint32_t>(col));
         u32x4 raw[4];
+        // bf16 queries: pieces 4 hf + jj (dims 64 hf + 16 jj ..), widened;
+        // e4m3 queries: pieces 4 (jj / 2) + 2 hf + jj % 2 (dims 64 s + 32 hf
+        // .. for K-step s = jj / 2), kept as codes
         static_for<4>([&](auto jc2) {
           constexpr int jj = decltype(jc2)::value;
+          const int piece = QF8 ? 4 * (jj >> 1) + 2 * hf + (jj & 1) : 4 * hf + jj;
           raw[jj] = __builtin_bit_cast(
-              u32x4, lds_b128<0>(tb + 16u * static_cast<uint32_t>((4 * hf + jj) ^ csw)));
+              u32x4, lds_b128<0>(tb + 16u * static_cast<uint32_t>(piece ^ csw)));
         });
         static_for<4>([&](auto jc2) {
           constexpr int jj = decltype(jc2)::value;
           lgkm_keep<3 - jj>(raw[jj]);
           if constexpr (jj == 0) asm volatile("" : "+v"(kscl));
-          kv[2 * jj] = fp8x8_to_bf16x8(raw[jj][0], raw[jj][1]);
-          kv[2 * jj + 1] = fp8x8_to_bf16x8(raw[jj][2], raw[jj][3]);
+          if constexpr (!QF8) {
+            kv[2 * jj] = fp8x8_to_bf16x8(raw[jj][0], raw[jj][1]);
+            kv[2 * jj + 1] = fp8x8_to_bf16x8(raw[jj][2], raw[jj][3]);
+          }
         });
+        if constexpr (QF8) {
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const u32x4 lo = raw[2 * st], hi = raw[2 * st + 1];
+            kv8[st] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                            (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+          }
+        }
         refill();
       }
       float part[TQ];
@@ -340,6 +387,16 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
         f32x16 acc[TQ];
 #pragma unroll
         for (int tt = 0; tt < TQ; ++tt) acc[tt] = f32x16{};
+        if constexpr (QF8) {
+          // e4m3 x e4m3, 64 dims per instruction (format code 0 = e4m3 for
+          // both operands; block scales 127 = 2^0)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int tt = 0; tt < TQ; ++tt)
+              acc[tt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  qa8[tt][mt][st], kv8[st], acc[tt], 0, 0, 0, 127, 0, 127);
+        } else
         static_for<8>([&](auto sc) {
           constexpr int st = decltype(sc)::value;
 #pragma unroll
@@ -390,7 +447,7 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   }
 }
 
-template <int TQ, int MT, bool F8, int MAXT>
+template <int TQ, int MT, bool F8, int MAXT, bool QF8>
 hipError_t launch_dma_t(IndexerArgs& a, int qbpr, int nchunks, int64_t tpw,
                         hipStream_t stream) {
   const dsa_batch& b = a.b;
@@ -399,8 +456,8 @@ hipError_t launch_dma_t(IndexerArgs& a, int qbpr, int nchunks, int64_t tpw,
   a.range_stride = nchunks * kRangeParts;
   const int64_t grid = static_cast<int64_t>(b.num_reqs) * qbpr * nchunks;
   if (grid == 0) return hipSuccess;
-  k_score_dma<TQ, MT, F8, MAXT><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
-      static_cast<const uint16_t*>(a.q), a.w,
+  k_score_dma<TQ, MT, F8, MAXT, QF8><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
+      static_cast<const uint16_t*>(a.q), a.q_scale, a.w,
       static_cast<const uint8_t*>(a.k_cache), a.k_scale, b.seq_lens, b.cu_q,
       b.block_table, b.max_blocks, b.block_size, b.num_slots, b.max_seq_len,
       qbpr, nchunks, static_cast<int32_t>(tpw), a.scores, a.row_stride, a.chunk_range,
@@ -408,7 +465,7 @@ hipError_t launch_dma_t(IndexerArgs& a, int qbpr, int nchunks, int64_t tpw,
   return hipGetLastError();
 }
 
-template <int TQ, int MT, bool F8>
+template <int TQ, int MT, bool F8, bool QF8 = false>
 hipError_t launch_dma(IndexerArgs& a, hipStream_t stream) {
   const dsa_batch& b = a.b;
   const int qbpr = (b.max_q_len + TQ - 1) / TQ;
@@ -427,10 +484,10 @@ hipError_t launch_dma(IndexerArgs& a, hipStream_t stream) {
     if (groups * nchunks > 256 && tpw > 16) {
       tpw = 16;
       nchunks = static_cast<int>((tiles_total + tpw * kWaves - 1) / (tpw * kWaves));
-      return launch_dma_t<TQ, MT, F8, 16>(a, qbpr, nchunks, tpw, stream);
+      return launch_dma_t<TQ, MT, F8, 16, QF8>(a, qbpr, nchunks, tpw, stream);
     }
   }
-  return launch_dma_t<TQ, MT, F8, kMaxTpw>(a, qbpr, nchunks, tpw, stream);
+  return launch_dma_t<TQ, MT, F8, kMaxTpw, QF8>(a, qbpr, nchunks, tpw, stream);
 }
 
 // ---------------------------------------------------------------- vector path
@@ -442,7 +499,8 @@ __device__ __forceinline__ float ld(const void* p, int64_t i, int dt) {
 
 // one thread per (token, key); the token's query and weights sit in LDS
 __global__ __launch_bounds__(256) void k_score_vector(
-    const void* __restrict__ q, int q_dtype, const float* __restrict__ w,
+    const void* __restrict__ q, int q_dtype, const float* __restrict__ qscale,
+    const float* __restrict__ w,
     const void* __restrict__ kc, const float* __restrict__ kscale,
     int cache_dtype, int H, int D, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ cu_q, int32_t B,
@@ -458,7 +516,9 @@ __global__ __launch_bounds__(256) void k_score_vector(
   if (kb * 256 > pos) return;
   for (int i = threadIdx.x; i < H * D; i += 256)
     sq[i] = ld(q, static_cast<int64_t>(t) * H * D + i, q_dtype);
-  for (int i = threadIdx.x; i < H; i += 256) sw[i] = w[static_cast<int64_t>(t) * H + i];
+  for (int i = threadIdx.x; i < H; i += 256)   // e4m3 queries: times their scale
+    sw[i] = w[static_cast<int64_t>(t) * H + i] *
+            (qscale ? qscale[static_cast<int64_t>(t) * H + i] : 1.0f);
   __syncthreads();
   const int32_t s = kb * 256 + threadIdx.x;
   if (s > pos) return;
@@ -480,7 +540,8 @@ __global__ __launch_bounds__(256) void k_score_vector(
 }  // namespace
 
 bool indexer_mfma_ok(const IndexerArgs& a) {
-  return a.q_dtype == DSA_BF16 &&
+  const bool qf8 = a.q_dtype == DSA_FP8_E4M3 && a.cache_dtype == DSA_FP8_E4M3;
+  return (a.q_dtype == DSA_BF16 || qf8) &&
          (a.cache_dtype == DSA_BF16 || a.cache_dtype == DSA_FP8_E4M3) &&
          a.d_idx == 128 && (a.n_heads == 32 || a.n_heads == 64) &&
          a.b.block_size % kTile == 0;
@@ -498,6 +559,11 @@ hipError_t launch_indexer_score(IndexerArgs& a, hipStream_t stream) {
       if (one) return mt2 ? launch_dma<1, 2, false>(a, stream) : launch_dma<1, 1, false>(a, stream);
       return mt2 ? launch_dma<2, 2, false>(a, stream) : launch_dma<2, 1, false>(a, stream);
     }
+    if (a.q_dtype == DSA_FP8_E4M3) {
+      if (one) return mt2 ? launch_dma<1, 2, true, true>(a, stream)
+                          : launch_dma<1, 1, true, true>(a, stream);
+      return mt2 ? launch_dma<2, 2, true, true>(a, stream) : launch_dma<2, 1, true, true>(a, stream);
+    }
     if (one) return mt2 ? launch_dma<1, 2, true>(a, stream) : launch_dma<1, 1, true>(a, stream);
     return mt2 ? launch_dma<2, 2, true>(a, stream) : launch_dma<2, 1, true>(a, stream);
   }
@@ -505,7 +571,7 @@ hipError_t launch_indexer_score(IndexerArgs& a, hipStream_t stream) {
   const int key_blocks = (b.max_seq_len + 255) / 256;
   const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * key_blocks;
   k_score_vector<<<static_cast<unsigned>(grid), 256, 0, stream>>>(
-      a.q, a.q_dtype, a.w, a.k_cache, a.k_scale, a.cache_dtype, a.n_heads,
+      a.q, a.q_dtype, a.q_scale, a.w, a.k_cache, a.k_scale, a.cache_dtype, a.n_heads,
       a.d_idx, b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
       b.block_size, b.num_slots, b.max_seq_len, key_blocks, a.scores,
       a.row_stride);

@@ -20,6 +20,9 @@ Workloads (shapes and value distributions as given for the path):
                     query each; indexer keys N(0,1) -> bf16 -> e4m3 + fp32
                     scale (quantised by the cache write), bf16 q,
                     w ~ N(0,1)/sqrt(32); MLA as decode_32k_mtp.
+  fp8q_decode_32k_mtp  decode_32k_mtp with the FP8 indexer path: bf16
+                    queries and keys rotated and quantised to e4m3 by the
+                    library (per head / per token scales).
   indexshare_8layer 8 layers [full, shared, shared, shared] x 2, 64 requests
                     x 32768, one query each, per-layer bf16 indexer q, k, w
                     and latent rows.

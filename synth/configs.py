@@ -19,6 +19,7 @@ class Config:
     topk: int = 2048
     idx_dtype: str = "bf16"       # dtype of indexer q and new keys
     idx_cache_dtype: str = "bf16"
+    idx_q_fp8: bool = False       # queries and keys rotated and quantised to e4m3
     idx_values: str = "normal"    # "normal" or "int3" (uniform ints -3..3)
     w_values: str = "normal_over_sqrt_heads"   # or "normal", "one_two"
     n_heads: int = 64
@@ -59,6 +60,9 @@ CONFIGS = {
     "fp8_decode_varlen": Config(
         name="fp8_decode_varlen", cid=4, num_reqs=128, q_len=1, seq_len=None,
         seq_len_range=(1024, 131072), idx_cache_dtype="fp8"),
+    "fp8q_decode_32k_mtp": Config(
+        name="fp8q_decode_32k_mtp", cid=6, num_reqs=64, q_len=2, seq_len=32768,
+        idx_cache_dtype="fp8", idx_q_fp8=True),
     "indexshare_8layer": Config(
         name="indexshare_8layer", cid=5, num_reqs=64, q_len=1, seq_len=32768,
         indexer_types=["full", "shared", "shared", "shared",

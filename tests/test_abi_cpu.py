@@ -199,3 +199,18 @@ def test_noalloc_rejects_oversized_batches_on_the_host():
                                       None, 1, 2048, _FAKE, None)
     assert rc == -5
     assert "allocation-free" in dsa.dsa_last_error()
+
+
+def test_fp8_query_entry_points_reject_on_the_host():
+    dsa = ensure_library()
+    lib = dsa.load_library()
+    # rotation sizes: powers of two in 32..256 only
+    for d, code in ((100, -2), (16, -2), (512, -2)):
+        assert lib.dsa_rotate_quantize(_FAKE, 1, 4, d, None, 4, _FAKE, _FAKE, None) == code
+    assert lib.dsa_rotate_quantize(_FAKE, 2, 4, 128, None, 4, _FAKE, _FAKE, None) == -2
+    assert lib.dsa_rotate_quantize(_FAKE, 1, 8, 128, None, 4, _FAKE, _FAKE, None) == -1
+    cb = _batch(dsa)
+    assert lib.dsa_indexer_topk_fp8q(ctypes.byref(cb), _FAKE, None, _FAKE, 32, 128, _FAKE,
+                                     _FAKE, 16, _FAKE, _FAKE, 1 << 30, None) == -1
+    assert lib.dsa_indexer_topk_fp8q(ctypes.byref(cb), _FAKE, _FAKE, _FAKE, 32, 128, _FAKE,
+                                     None, 16, _FAKE, _FAKE, 1 << 30, None) == -1

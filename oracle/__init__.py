@@ -17,6 +17,8 @@ Modules
   indexer    key-cache write, indexer score, deterministic top-k
   fp8_indexer  the FP8-query variant: Hadamard rotation, per-row activation
              quantisation, score over e4m3 queries and keys
+  prologue   the indexer's inputs: q / k / w projections, RMSNorm k_norm,
+             rotate-half RoPE
   mla        absorbed sparse MLA over selected latent rows, and a dense
              causal MLA used only for the sparse == dense invariant
   indexshare GLM-5.2 IndexShare source-layer resolution and layer stack
@@ -42,7 +44,12 @@ one of these pins.
               dot products kept, the fp32 butterflies within their rounding
               bound, a hand-worked rotation / quantisation / score example
               (tests/golden), brute-force top-k over e4m3 codes
+  prologue    a hand-worked two-token example (tests/golden) with every
+              intermediate step; RMSNorm unit RMS and scale freedom; RoPE
+              norm keeping, identity at angle 0, inverse angle, dependence on
+              relative position only; planted interleaved pairs, RoPE on the
+              last dims and LayerNorm each fail the example
 No oracle function is "parity unpinned".
 """
 
-from . import codecs, indexer, mla, indexshare, fp8_indexer  # noqa: F401
+from . import codecs, indexer, mla, indexshare, fp8_indexer, prologue  # noqa: F401

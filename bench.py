@@ -127,6 +127,16 @@ def mla_flops(b, cfg):
     return 2 * _rows(b, cfg.topk) * cfg.n_heads * (cfg.d_latent + cfg.kv_lora_rank)
 
 
+def prologue_bytes(b, cfg):
+    """Weights read once (bf16), activations read once, q / k / w written
+    once, cos / sin read once, the new keys' cache rows written once."""
+    N, H, D = b.num_q_tokens, cfg.n_idx_heads, cfg.d_idx
+    weights = (H * D * cfg.q_lora_rank + D * cfg.hidden_dim + H * cfg.hidden_dim) * 2
+    acts = N * (cfg.hidden_dim + cfg.q_lora_rank) * 2 + N * cfg.idx_rope_dim * 4
+    outs = N * H * D * 2 + N * D * 2 + N * H * 4 + N * (D * 2 + 8)
+    return weights + acts + outs
+
+
 def cache_write_bytes(b, cfg):
     per = cfg.d_idx * (1 if cfg.idx_cache_dtype == "fp8" else 2)
     return b.num_q_tokens * (cfg.d_idx * 2 + per + 8)
@@ -563,6 +573,7 @@ def main():
 
     timer = HipTimer(stream.cuda_stream)
     flush = make_flush(torch, dev)
+    with_prologue = cfg.name in ("decode_32k_mtp", "fp8q_decode_32k_mtp")
     log("timing %d steps, caches evicted before each" % args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -572,6 +583,35 @@ def main():
     calls = {"cache_write": stats(timer.reps(cache_write, args.steps, flush)),
              "indexer_topk": stats(timer.reps(indexer, args.steps, flush)),
              "sparse_mla_attn": stats(timer.reps(attention, args.steps, flush))}
+    if with_prologue:
+        # the indexer prologue of this step's new tokens (projections, k_norm,
+        # RoPE, the keys' cache write); reported beside the step, not in it
+        from synth import make_prologue
+        pi = make_prologue(cfg, b, dev)
+        pq = torch.empty((N, cfg.n_idx_heads, cfg.d_idx), dtype=torch.bfloat16, device=dev)
+        pw = torch.empty((N, cfg.n_idx_heads), dtype=torch.float32, device=dev)
+        pws = torch.empty(max(256, dsa.load_library().dsa_indexer_prologue_workspace_size(
+            N, ctypes.byref(dsa._binding._CPrologueDims(
+                cfg.hidden_dim, cfg.q_lora_rank, cfg.n_idx_heads, cfg.d_idx,
+                cfg.idx_rope_dim, cfg.norm_eps)))), dtype=torch.uint8, device=dev)
+
+        def prologue():
+            dsa.dsa_indexer_prologue(pi.hidden, pi.qa_normed, pi.cos, pi.sin, pi.wq_b, pi.wk,
+                                     pi.weights_proj, pi.k_norm_weight, cfg.n_idx_heads,
+                                     cfg.idx_rope_dim, cfg.norm_eps,
+                                     slot_mapping=b.slot_mapping_t, k_cache=k_cache,
+                                     k_scale=k_scale, q_out=pq, w_out=pw, workspace=pws,
+                                     want_k=False)
+        prologue()
+        torch.cuda.synchronize()
+        pst = stats(timer.reps(prologue, args.steps, flush))
+        pb = prologue_bytes(b, cfg)
+        pst.update(bytes=pb, note="not part of the step: q / k / w projections, k_norm, "
+                                  "RoPE and the new keys' cache write (hidden %d, q_lora_rank "
+                                  "%d); bytes: weights, activations and outputs once"
+                                  % (cfg.hidden_dim, cfg.q_lora_rank))
+        pst["frac_hbm"] = pb / (pst["median_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS
+        calls["indexer_prologue"] = pst
     ms_step = st["median_ms"]
     ib, mb, cb = indexer_bytes(b, cfg), mla_bytes(b, cfg), cache_write_bytes(b, cfg)
     ifl, mfl = indexer_flops(b, cfg), mla_flops(b, cfg)

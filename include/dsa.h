@@ -206,6 +206,49 @@ int dsa_indexer_topk_fp8q(const dsa_batch* batch, const uint8_t* q_codes,
                           size_t ws_bytes, void* stream);
 
 /*
+ * Indexer prologue (section "DSA Indexer fused semantic op": the op's inputs
+ * hidden_states, qa_normed (the MLA path's normalised query low-rank
+ * activation, section "mlapo / mlapo_quant and qa_normed"), RoPE cos / sin,
+ * wq_b, wk, weights_proj, the k_norm weight, head_dim and qk_rope_head_dim,
+ * and the indexer cache it writes; section "Performance model design",
+ * buckets 1-4).  For N new tokens:
+ *     q = RoPE(qa_normed wq_b^T)                          -> q_out [N, H, D] bf16
+ *     k = RoPE(RMSNorm(hidden wk^T, eps) * k_norm_weight)  -> k_out [N, D] bf16
+ *     w = hidden weights_proj^T                           -> w_out [N, H] fp32
+ * and k is written to the indexer cache at slot_mapping[t] (skipped when -1
+ * or >= num_slots): a bf16 copy for a BF16 cache; for an FP8 cache the
+ * bf16 key rotated and quantised exactly as dsa_rotate_quantize does (the
+ * FP8 path), codes into k_cache and the scale into k_scale.
+ *   hidden        [N, hidden_dim] bf16;  qa_normed [N, q_lora_rank] bf16
+ *   cos, sin      [N, rope_dim / 2] fp32, the token's RoPE angles: dims j and
+ *                 j + rope_dim / 2 (j < rope_dim / 2) of each query head and
+ *                 of the key turn by angle j (rotate-half); dims past
+ *                 rope_dim are left alone
+ *   wq_b          [n_heads * head_dim, q_lora_rank] bf16 (linear-layer
+ *                 layout [out, in]); wk [head_dim, hidden_dim] bf16;
+ *                 weights_proj [n_heads, hidden_dim] bf16
+ *   k_norm_weight [head_dim] fp32
+ *   k_out         may be NULL; slot_mapping may be NULL (no cache write)
+ * Products accumulate in fp32 over the bf16 inputs, in a fixed order (the
+ * results are deterministic).  Supported: head_dim 128, rope_dim even and
+ * <= head_dim, q_lora_rank and hidden_dim multiples of 32, n_heads 1..64.
+ * workspace: at least dsa_indexer_prologue_workspace_size() bytes (fp32
+ * partial sums), 256-byte aligned, contents ignored.
+ */
+typedef struct dsa_prologue_dims {
+  int32_t hidden_dim, q_lora_rank, n_heads, head_dim, rope_dim;
+  float eps;
+} dsa_prologue_dims;
+size_t dsa_indexer_prologue_workspace_size(int32_t n_tokens, const dsa_prologue_dims* dims);
+int dsa_indexer_prologue(int32_t n_tokens, const dsa_prologue_dims* dims, const void* hidden,
+                         const void* qa_normed, const float* cos, const float* sin,
+                         const void* wq_b, const void* wk, const void* weights_proj,
+                         const float* k_norm_weight, const int64_t* slot_mapping,
+                         int64_t num_slots, void* k_cache, float* k_scale,
+                         int32_t cache_dtype, void* q_out, void* k_out, float* w_out,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * Allocation-free variant of dsa_indexer_topk, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments, results and errors as

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     DSAError, Batch, library_path, load_library, exported_symbols,
     dsa_indexer_cache_write, dsa_indexer_topk, dsa_indexer_topk_workspace_size,
     dsa_indexer_topk_noalloc, dsa_rotate_quantize, dsa_indexer_topk_fp8q,
+    dsa_indexer_prologue,
     sparse_mla_attn, sparse_mla_attn_workspace_size,
     dsa_resolve_indexer_sources, indexshare_forward,
     indexshare_forward_workspace_size, dsa_fp8_decode_check, dsa_last_error,

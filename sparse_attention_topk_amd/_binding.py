@@ -19,7 +19,8 @@ DSA_LAYER_FULL, DSA_LAYER_SHARED = 0, 1
 EXPORTS = [
     "dsa_indexer_cache_write", "dsa_indexer_topk_workspace_size",
     "dsa_indexer_topk", "dsa_indexer_topk_noalloc", "dsa_rotate_quantize",
-    "dsa_indexer_topk_fp8q", "sparse_mla_attn_workspace_size",
+    "dsa_indexer_topk_fp8q", "dsa_indexer_prologue_workspace_size", "dsa_indexer_prologue",
+    "sparse_mla_attn_workspace_size",
     "sparse_mla_attn",
     "dsa_resolve_indexer_sources", "indexshare_forward_workspace_size",
     "indexshare_forward", "dsa_fp8_decode_check", "dsa_last_error",
@@ -46,6 +47,12 @@ class _CLayer(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "q_idx", "w", "k_cache", "k_scale", "topk_idx", "q_mla", "kv_cache",
         "out", "lse")]
+
+
+class _CPrologueDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "hidden_dim", "q_lora_rank", "n_heads", "head_dim", "rope_dim")] + [
+        ("eps", ctypes.c_float)]
 
 
 class _CDims(ctypes.Structure):
@@ -82,6 +89,9 @@ def load_library():
         "dsa_indexer_topk_noalloc": (ctypes.c_int, [P, P, I32, P, I32, I32, P, P, I32, I32, P, P]),
         "dsa_rotate_quantize": (ctypes.c_int, [P, I32, I64, I32, P, I64, P, P, P]),
         "dsa_indexer_topk_fp8q": (ctypes.c_int, [P, P, P, P, I32, I32, P, P, I32, P, P, SZ, P]),
+        "dsa_indexer_prologue_workspace_size": (SZ, [I32, P]),
+        "dsa_indexer_prologue": (ctypes.c_int, [I32, P, P, P, P, P, P, P, P, P, P, I64, P, P,
+                                                I32, P, P, P, P, SZ, P]),
         "sparse_mla_attn_workspace_size": (SZ, [P, I32, I32, I32, I32, I32]),
         "sparse_mla_attn": (ctypes.c_int, [P, P, P, I32, I32, I32, I32, P, I32, F, P, P, P, SZ, P]),
         "dsa_resolve_indexer_sources": (ctypes.c_int, [I32, P, I32, P]),
@@ -300,6 +310,42 @@ def dsa_indexer_topk_fp8q(batch, q_codes, q_scale, w, k_cache, k_scale, topk,
         ctypes.byref(cb), _ptr(q_codes), _ptr(q_scale), _ptr(w), H, D, _ptr(k_cache),
         _ptr(k_scale), topk, _ptr(topk_idx), _ptr(ws), ws_bytes, _stream(stream)))
     return topk_idx
+
+
+def dsa_indexer_prologue(hidden, qa_normed, cos, sin, wq_b, wk, weights_proj, k_norm_weight,
+                         n_heads, rope_dim, eps, slot_mapping=None, k_cache=None, k_scale=None,
+                         q_out=None, k_out=None, w_out=None, workspace=None, want_k=True,
+                         stream=None):
+    """q [N, H, D] bf16, k [N, D] bf16 (or None), w [N, H] fp32 of N new tokens;
+    with slot_mapping, k is also written into k_cache (bf16 copy, or rotated
+    and quantised into an e4m3 cache with k_scale)."""
+    lib = load_library()
+    for n, t in (("hidden", hidden), ("qa_normed", qa_normed), ("cos", cos), ("sin", sin),
+                 ("wq_b", wq_b), ("wk", wk), ("weights_proj", weights_proj),
+                 ("k_norm_weight", k_norm_weight), ("k_cache", k_cache)):
+        _contig(n, t)
+    N, hidden_dim = hidden.shape
+    D = wk.shape[0]
+    dims = _CPrologueDims(hidden_dim=hidden_dim, q_lora_rank=qa_normed.shape[1],
+                          n_heads=n_heads, head_dim=D, rope_dim=rope_dim, eps=eps)
+    dev = hidden.device
+    if q_out is None:
+        q_out = torch.empty((N, n_heads, D), dtype=torch.bfloat16, device=dev)
+    if k_out is None and want_k:
+        k_out = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    if w_out is None:
+        w_out = torch.empty((N, n_heads), dtype=torch.float32, device=dev)
+    ws = _workspace(lib.dsa_indexer_prologue_workspace_size(N, ctypes.byref(dims)), dev,
+                    workspace, stream)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    cache_dtype = _dtype(k_cache) if k_cache is not None else DSA_BF16
+    num_slots = k_cache.shape[0] if k_cache is not None else 0
+    _check(lib.dsa_indexer_prologue(
+        N, ctypes.byref(dims), _ptr(hidden), _ptr(qa_normed), _ptr(cos), _ptr(sin), _ptr(wq_b),
+        _ptr(wk), _ptr(weights_proj), _ptr(k_norm_weight), _ptr(slot_mapping), num_slots,
+        _ptr(k_cache), _ptr(k_scale), cache_dtype, _ptr(q_out), _ptr(k_out), _ptr(w_out),
+        _ptr(ws), ws_bytes, _stream(stream)))
+    return q_out, k_out, w_out
 
 
 def sparse_mla_attn_workspace_size(batch, n_heads, kv_lora_rank, rope_dim,

@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
 SOURCES = ["api.hip", "cache_write.hip", "indexer_score.hip", "topk.hip",
-           "sparse_mla.hip"]
+           "sparse_mla.hip", "prologue.hip"]
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

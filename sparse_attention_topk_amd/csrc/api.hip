@@ -402,6 +402,57 @@ int dsa_indexer_topk_fp8q(const dsa_batch* batch, const uint8_t* q_codes,
                      static_cast<hipStream_t>(stream), q_scale);
 }
 
+size_t dsa_indexer_prologue_workspace_size(int32_t n_tokens, const dsa_prologue_dims* d) {
+  if (n_tokens < 0 || !d || d->n_heads < 1 || d->head_dim < 1) return 0;
+  return round_up(dsa::prologue_part_floats(n_tokens, d) * sizeof(float));
+}
+
+int dsa_indexer_prologue(int32_t n_tokens, const dsa_prologue_dims* d, const void* hidden,
+                         const void* qa_normed, const float* cos, const float* sin,
+                         const void* wq_b, const void* wk, const void* weights_proj,
+                         const float* k_norm_weight, const int64_t* slot_mapping,
+                         int64_t num_slots, void* k_cache, float* k_scale,
+                         int32_t cache_dtype, void* q_out, void* k_out, float* w_out,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  if (!d) return fail(DSA_ERR_INVALID_ARG, "dims is NULL");
+  if (n_tokens < 0) return fail(DSA_ERR_INVALID_ARG, "n_tokens < 0");
+  if (d->head_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "head_dim %d (the prologue supports 128)", d->head_dim);
+  if (d->n_heads < 1 || d->n_heads > 64)
+    return fail(DSA_ERR_UNSUPPORTED, "n_heads %d outside 1..64", d->n_heads);
+  if (d->rope_dim < 0 || d->rope_dim > d->head_dim || d->rope_dim % 2)
+    return fail(DSA_ERR_UNSUPPORTED, "rope_dim %d must be even and <= head_dim", d->rope_dim);
+  if (d->q_lora_rank < 32 || d->q_lora_rank % 32 || d->hidden_dim < 32 || d->hidden_dim % 32)
+    return fail(DSA_ERR_UNSUPPORTED, "q_lora_rank %d and hidden_dim %d must be multiples of 32",
+                d->q_lora_rank, d->hidden_dim);
+  if (!(d->eps >= 0.0f) || !std::isfinite(d->eps))
+    return fail(DSA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (n_tokens > 0 && (!hidden || !qa_normed || !wq_b || !wk || !weights_proj ||
+                       !k_norm_weight || !q_out || !w_out || (d->rope_dim && (!cos || !sin))))
+    return fail(DSA_ERR_INVALID_ARG, "input, weight and output pointers must be non-NULL");
+  if (slot_mapping) {
+    if (!k_cache || num_slots < 1)
+      return fail(DSA_ERR_INVALID_ARG, "a cache write needs k_cache and num_slots");
+    if (cache_dtype != DSA_BF16 && cache_dtype != DSA_FP8_E4M3)
+      return fail(DSA_ERR_UNSUPPORTED, "prologue cache dtype must be BF16 or FP8_E4M3");
+    if (cache_dtype == DSA_FP8_E4M3 && !k_scale)
+      return fail(DSA_ERR_INVALID_ARG, "FP8 cache needs k_scale");
+  }
+  const size_t need = dsa_indexer_prologue_workspace_size(n_tokens, d);
+  if (n_tokens > 0 && (!workspace || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace ? ws_bytes : static_cast<size_t>(0));
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+    return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  hipError_t e = dsa::launch_prologue(n_tokens, d, hidden, qa_normed, cos, sin, wq_b, wk,
+                                      weights_proj, k_norm_weight, slot_mapping, num_slots,
+                                      k_cache, k_scale, cache_dtype, q_out, k_out, w_out,
+                                      static_cast<float*>(workspace),
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prologue launch");
+  return ok();
+}
+
 int dsa_indexer_topk_noalloc(const dsa_batch* batch, const void* q, int32_t q_dtype,
                              const float* w, int32_t n_heads, int32_t d_idx,
                              const void* k_cache, const float* k_scale,

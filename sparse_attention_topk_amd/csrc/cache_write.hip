@@ -16,25 +16,6 @@
 namespace dsa {
 namespace {
 
-// fp32 -> OCP e4m3fn, round to nearest even, saturating, sign kept.
-// NaN is outside the contract (it saturates like a large value).
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  uint32_t bits = __float_as_uint(v);
-  uint32_t sign = (bits >> 24) & 0x80u;
-  uint32_t a = bits & 0x7FFFFFFFu;
-  if (a >= 0x43E00000u) return sign | 0x7Eu;          // |v| >= 448
-  if (a >= 0x3C800000u) {                             // |v| >= 2^-6: normal
-    // keep 3 mantissa bits: round the 20 dropped bits to nearest even; a
-    // carry moves into the exponent, which is the right result
-    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-    return sign | ((r >> 20) - (120u << 3));          // rebias 127 -> 7
-  }
-  // subnormal: value = m * 2^-9 with m = rne(|v| * 512) in 0..8
-  // (m == 8 is the smallest normal, code 0x08, which is also correct)
-  float m = rintf(__uint_as_float(a) * 512.0f);
-  return sign | static_cast<uint32_t>(m);
-}
-
 template <typename T>
 __device__ __forceinline__ float load_as_f32(const T* p, int64_t i);
 template <>
@@ -109,42 +90,11 @@ __global__ __launch_bounds__(256) void k_rotate_quantize(
   if (row >= n_rows) return;
   const int64_t dst = row_slots ? row_slots[row] : row;
   if (dst < 0 || dst >= num_out) return;
-  const bool live = lane < d;            // d < 64: lanes d .. 63 hold nothing
   float v[EPL];
 #pragma unroll
   for (int m = 0; m < EPL; ++m)
-    v[m] = live ? load_as_f32(x, row * d + lane + 64 * m) : 0.0f;
-  for (int h = 1; h < 64 && h < d; h <<= 1) {
-#pragma unroll
-    for (int m = 0; m < EPL; ++m) {
-      const float other = __shfl_xor(v[m], h);
-      v[m] = (lane & h) ? other - v[m] : v[m] + other;
-    }
-  }
-#pragma unroll
-  for (int h = 1; h < EPL; h <<= 1) {    // element strides 64 h
-#pragma unroll
-    for (int m = 0; m < EPL; ++m) {
-      if (m & h) continue;
-      const float a = v[m], b = v[m + h];
-      v[m] = a + b;
-      v[m + h] = a - b;
-    }
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int m = 0; m < EPL; ++m) {
-    v[m] *= inv_sqrt_d;
-    amax = fmaxf(amax, fabsf(v[m]));
-  }
-  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const float sc = (amax == 0.0f) ? 1.0f : amax / 448.0f;
-  if (live) {
-#pragma unroll
-    for (int m = 0; m < EPL; ++m)
-      codes[dst * d + lane + 64 * m] = static_cast<uint8_t>(f32_to_e4m3(v[m] / sc));
-  }
-  if (lane == 0) scales[dst] = sc;
+    v[m] = lane < d ? load_as_f32(x, row * d + lane + 64 * m) : 0.0f;
+  wave_rotate_quantize<EPL>(v, d, inv_sqrt_d, codes + dst * d, scales + dst);
 }
 
 // Decodes e4m3 codes, 8 per thread, with the conversion and byte packing

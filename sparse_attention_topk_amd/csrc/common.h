@@ -86,6 +86,75 @@ __device__ __forceinline__ void wave_minmax(float& lo, float& hi) {
   hi = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// fp32 -> OCP e4m3fn, round to nearest even, saturating, sign kept.
+// NaN is outside the contract (it saturates like a large value).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  uint32_t bits = __float_as_uint(v);
+  uint32_t sign = (bits >> 24) & 0x80u;
+  uint32_t a = bits & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;          // |v| >= 448
+  if (a >= 0x3C800000u) {                             // |v| >= 2^-6: normal
+    // keep 3 mantissa bits: round the 20 dropped bits to nearest even; a
+    // carry moves into the exponent, which is the right result
+    uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    return sign | ((r >> 20) - (120u << 3));          // rebias 127 -> 7
+  }
+  // subnormal: value = m * 2^-9 with m = rne(|v| * 512) in 0..8
+  // (m == 8 is the smallest normal, code 0x08, which is also correct)
+  float m = rintf(__uint_as_float(a) * 512.0f);
+  return sign | static_cast<uint32_t>(m);
+}
+
+// Activation rotation and quantisation of one row by one wave (the FP8
+// indexer path's rotate_activation and activation quantisation): element
+// l + 64 m of the row sits in lane l, slot m (EPL = max(1, d / 64) slots;
+// for d < 64 lanes d .. 63 hold zeros).  The orthonormal Hadamard transform
+// runs as butterflies over h = 1, 2, ..., d / 2 in that order, (a, b) ->
+// (a + b, a - b) for the pair (i, i + h) in each block of 2 h, rounded to
+// fp32 at every stage, then one multiply by inv_sqrt_d = fl32(d^-1/2);
+// pairs of h < 64 meet across lanes l and l ^ h, pairs of h >= 64 inside a
+// lane.  The rotated row is then quantised like a key: amax, scale =
+// fl32(amax / 448) (1 if amax == 0), code = e4m3(v / scale); the codes go to
+// codes_row[0 .. d) and the scale to *scale_out.  Every lane of the wave
+// must call it (it exchanges values across lanes).
+template <int EPL>
+__device__ __forceinline__ void wave_rotate_quantize(float (&v)[EPL], int d, float inv_sqrt_d,
+                                                     uint8_t* __restrict__ codes_row,
+                                                     float* __restrict__ scale_out) {
+  const int lane = threadIdx.x & 63;
+  for (int h = 1; h < 64 && h < d; h <<= 1) {
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+      const float other = __shfl_xor(v[m], h);
+      v[m] = (lane & h) ? other - v[m] : v[m] + other;
+    }
+  }
+#pragma unroll
+  for (int h = 1; h < EPL; h <<= 1) {    // element strides 64 h
+#pragma unroll
+    for (int m = 0; m < EPL; ++m) {
+      if (m & h) continue;
+      const float a = v[m], b = v[m + h];
+      v[m] = a + b;
+      v[m + h] = a - b;
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int m = 0; m < EPL; ++m) {
+    v[m] *= inv_sqrt_d;
+    amax = fmaxf(amax, fabsf(v[m]));
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float sc = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+  if (lane < d) {
+#pragma unroll
+    for (int m = 0; m < EPL; ++m)
+      codes_row[lane + 64 * m] = static_cast<uint8_t>(f32_to_e4m3(v[m] / sc));
+  }
+  if (lane == 0) *scale_out = sc;
+}
+
 // Physical cache row of logical position s of a request, or -1 when the
 // block id or slot falls outside the cache (treated as "no key").
 __device__ __forceinline__ int64_t slot_of(const int32_t* bt_row, int32_t s,
@@ -204,6 +273,16 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream);
 hipError_t launch_rotate_quantize(const void* x, int x_dtype, int64_t n_rows, int d,
                                   const int64_t* row_slots, int64_t num_out, uint8_t* codes,
                                   float* scales, hipStream_t stream);
+
+// indexer prologue: split counts, partial-sum floats, launch
+void prologue_splits(int32_t N, const dsa_prologue_dims* d, int* sq, int* sk);
+size_t prologue_part_floats(int32_t N, const dsa_prologue_dims* d);
+hipError_t launch_prologue(int32_t N, const dsa_prologue_dims* d, const void* hidden,
+                           const void* qa, const float* cos, const float* sin,
+                           const void* wq_b, const void* wk, const void* wp,
+                           const float* k_norm, const int64_t* slots, int64_t num_slots,
+                           void* k_cache, float* k_scale, int cache_dtype, void* q_out,
+                           void* k_out, float* w_out, float* part, hipStream_t stream);
 
 hipError_t launch_fp8_decode_check(const uint8_t* codes, float* out, int n,
                                    hipStream_t stream);

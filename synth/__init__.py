@@ -31,5 +31,5 @@ permutation of the physical blocks.
 """
 
 from .configs import CONFIGS, Config, get_config  # noqa: F401
-from .gen import (Batch, LayerInputs, make_batch, make_layer,  # noqa: F401
-                  make_random_indices, torch_gen)
+from .gen import (Batch, LayerInputs, PrologueInputs, make_batch, make_layer,  # noqa: F401
+                  make_prologue, make_random_indices, torch_gen)

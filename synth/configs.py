@@ -28,6 +28,11 @@ class Config:
     mla_dtype: str = "bf16"
     block_size: int = 64
     indexer_types: Optional[List[str]] = None  # None = one full layer
+    # indexer prologue (the projections that produce q, k and w)
+    hidden_dim: int = 6144
+    q_lora_rank: int = 2048
+    idx_rope_dim: int = 64
+    norm_eps: float = 1e-5
 
     @property
     def n_layers(self):

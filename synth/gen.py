@@ -11,6 +11,7 @@ _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 # tensor ids inside a config's seed space (seed = 1000 * cid + id + 100*layer)
 _ID_LENS, _ID_BLOCKS, _ID_Q, _ID_W, _ID_K, _ID_QM, _ID_KV, _ID_IDX = range(8)
+_ID_HID, _ID_QA, _ID_WQB, _ID_WK, _ID_WP, _ID_KNW = range(8, 14)
 
 
 def torch_gen(seed, device):
@@ -179,3 +180,46 @@ def make_random_indices(batch, topk, seed, device):
     if not rows:
         return torch.empty((0, topk), dtype=torch.int32, device=device)
     return torch.stack(rows)
+
+
+@dataclass
+class PrologueInputs:
+    hidden: torch.Tensor        # [N, hidden_dim] bf16
+    qa_normed: torch.Tensor     # [N, q_lora_rank] bf16
+    cos: torch.Tensor           # [N, R/2] fp32
+    sin: torch.Tensor
+    wq_b: torch.Tensor          # [H * D, q_lora_rank] bf16
+    wk: torch.Tensor            # [D, hidden_dim] bf16
+    weights_proj: torch.Tensor  # [H, hidden_dim] bf16
+    k_norm_weight: torch.Tensor  # [D] fp32
+
+
+def make_prologue(cfg, batch, device, layer=0, n_tokens=None):
+    """Synthetic inputs of the indexer prologue for the batch's query tokens:
+    activations N(0,1), weights N(0, 1/fan_in) (linear-layer layout), k_norm
+    weight 1 + N(0, 0.1^2), RoPE angles pos * 10000^(-2j/R) at each token's
+    position."""
+    base = 1000 * cfg.cid + 100 * layer
+    N = batch.num_q_tokens if n_tokens is None else n_tokens
+    H, D, R = cfg.n_idx_heads, cfg.d_idx, cfg.idx_rope_dim
+    bf = torch.bfloat16
+    hidden = _normal((N, cfg.hidden_dim), bf, base + _ID_HID, device)
+    qa = _normal((N, cfg.q_lora_rank), bf, base + _ID_QA, device)
+    wq_b = _normal((H * D, cfg.q_lora_rank), bf, base + _ID_WQB, device,
+                   scale=1.0 / math.sqrt(cfg.q_lora_rank))
+    wk = _normal((D, cfg.hidden_dim), bf, base + _ID_WK, device,
+                 scale=1.0 / math.sqrt(cfg.hidden_dim))
+    wp = _normal((H, cfg.hidden_dim), bf, base + _ID_WP, device,
+                 scale=1.0 / math.sqrt(cfg.hidden_dim))
+    knw = 1.0 + _normal((D,), torch.float32, base + _ID_KNW, device, scale=0.1)
+    pos = []
+    for b in range(batch.num_reqs):
+        L, ql = batch.seq_lens[b], batch.q_lens[b]
+        pos += [L - ql + i for i in range(ql)]
+    pos = (pos + [0] * N)[:N]
+    j = torch.arange(R // 2, dtype=torch.float64)
+    ang = torch.tensor(pos, dtype=torch.float64)[:, None] * torch.pow(10000.0, -2.0 * j / R)
+    return PrologueInputs(hidden=hidden, qa_normed=qa,
+                          cos=torch.cos(ang).to(torch.float32).to(device),
+                          sin=torch.sin(ang).to(torch.float32).to(device),
+                          wq_b=wq_b, wk=wk, weights_proj=wp, k_norm_weight=knw)

@@ -269,6 +269,185 @@ __device__ __forceinline__ u32x2 pack_bf16x4(const float* p) {
   return r;
 }
 
+// The workgroup's staged result leaves it.  stage holds the normalised
+// bf16 rows of its 64 heads (head h at byte h * kRowB, kRowB = 2 R + 16),
+// and every lse is stored already (into lse, or as a partial).  With one
+// split the rows are copied to out; with several, this split's rows are
+// stored as its partial, and the split that arrives last at the token's
+// word merges all of them.  Every thread of the workgroup calls it; stage
+// must have room behind the rows for the merge weights.
+constexpr int kRowB = kR * 2 + 16;
+__device__ __forceinline__ void mla_store_or_merge(
+    uint8_t* stage, uint32_t* counter, int t, int split, int n_split, bool partial,
+    uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
+    float* __restrict__ part_lse, unsigned long long* __restrict__ arrivals,
+    unsigned long long call_tag) {
+  const int tid = threadIdx.x;
+  constexpr int row_b = kRowB;
+  tile_barrier();
+  // Copy the staged block out.  The output: 16-byte pieces of a contiguous
+  // region.
+  if (!partial) {
+    constexpr int row_pieces = kR * 2 / 16;
+    constexpr int total = kH * row_pieces;
+    u32x4* dst = reinterpret_cast<u32x4*>(out + static_cast<int64_t>(t) * kH * kR);
+    for (int c = tid; c < total; c += kThreads) {
+      const int h = c / row_pieces, pc = c % row_pieces;
+      dst[c] = *reinterpret_cast<const u32x4*>(stage + h * row_b + 16 * pc);
+    }
+    return;
+  }
+  // Partials (bf16, normalised) are read back by another workgroup of this
+  // launch, maybe on another XCD: they are stored as relaxed device-scope
+  // atomics, which the hardware keeps coherent across XCDs by themselves,
+  // so no cache-wide write-back or invalidation is needed to hand them
+  // over.  8-byte words (4 dims), consecutive lanes on consecutive words,
+  // so every store instruction writes four whole 128-byte lines: thread tid
+  // takes word tid % 128 of head rows tid / 128 + 2 i.
+  constexpr int kWords = kR / 4;                   // 8-byte words per head row
+  constexpr int kRowsPer = kThreads / kWords;      // head rows per pass (4)
+  const int wq = tid % kWords;
+  const int h0 = tid / kWords;
+  unsigned long long* dst = reinterpret_cast<unsigned long long*>(
+      part_o + (static_cast<int64_t>(t) * n_split + split) * kH * kR);
+#pragma unroll 8
+  for (int i = 0; i < kH / kRowsPer; ++i) {
+    const int h = h0 + kRowsPer * i;
+    const unsigned long long v =
+        *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq);
+    __hip_atomic_store(dst + h * kWords + wq, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- the split that arrives last merges the token's partials.  Every
+  // thread waits until its partial stores have completed (reached the
+  // device-coherent level) before the workgroup counts its arrival; the
+  // merging workgroup loads the others' partials only after its own count
+  // came back, with device-scope atomic loads.
+  wait_vm<0>();
+  __syncthreads();
+  if (tid == 0) *counter = arrive(arrivals + t, call_tag, n_split) == static_cast<uint32_t>(n_split);
+  __syncthreads();
+  if (!*counter) return;
+  asm volatile("" ::: "memory");
+  // Thread tid merges dims 4 wq .. 4 wq + 3 of heads h0 + 2 i (as the
+  // partials were written: whole lines per instruction).  Splits are
+  // summed in split order (0, 1, ...) whichever finished last, so the
+  // result does not depend on the arrival order; this split's own partial
+  // comes from the staged block, rounded exactly as the others read theirs.
+  const unsigned long long* po = reinterpret_cast<const unsigned long long*>(
+      part_o + static_cast<int64_t>(t) * n_split * kH * kR) + wq;
+  auto word = [&](int s, int h) -> unsigned long long {
+    return __hip_atomic_load(const_cast<unsigned long long*>(po + (s * kH + h) * kWords),
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto own = [&](int h) -> unsigned long long {
+    return *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq);
+  };
+  auto unpack = [](unsigned long long v, float (&x)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      x[e] = __uint_as_float(static_cast<uint32_t>((v >> (16 * e)) & 0xFFFFu) << 16);
+  };
+  unsigned long long* ob = reinterpret_cast<unsigned long long*>(
+      out + static_cast<int64_t>(t) * kH * kR) + wq;
+  auto put = [&](int h, const float (&x)[4], float inv) {
+    const unsigned long long v =
+        static_cast<unsigned long long>(pack2_bf16(x[0] * inv, x[1] * inv)) |
+        (static_cast<unsigned long long>(pack2_bf16(x[2] * inv, x[3] * inv)) << 32);
+    ob[h * kWords] = v;
+  };
+  // with two splits, the other split's rows are in flight while the
+  // weights are made
+  unsigned long long u[kH / kRowsPer];
+  if (n_split == 2) {
+#pragma unroll
+    for (int i = 0; i < kH / kRowsPer; ++i) u[i] = word(1 - split, h0 + kRowsPer * i);
+  }
+  // split weights exp(lse_s - max) per head in place of the log-sum-exps,
+  // then 1 / their sum, behind the staged block
+  float* wt = reinterpret_cast<float*>(stage + kH * row_b);
+  for (int c = tid; c < n_split * kH; c += kThreads)
+    wt[c] = __hip_atomic_load(part_lse + static_cast<int64_t>(t) * n_split * kH + c,
+                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (tid < kH) {
+    float mx = -INFINITY;
+    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, wt[s * kH + tid]);
+    float sum = 0.0f;
+    for (int s = 0; s < n_split; ++s) {
+      const float wgt = mx == -INFINITY ? 0.0f : expf(wt[s * kH + tid] - mx);
+      wt[s * kH + tid] = wgt;
+      sum += wgt;
+    }
+    wt[n_split * kH + tid] = sum > 0.0f ? 1.0f / sum : 0.0f;
+    if (lse) lse[static_cast<int64_t>(t) * kH + tid] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
+  }
+  __syncthreads();
+  if (n_split == 2) {
+#pragma unroll
+    for (int i = 0; i < kH / kRowsPer; ++i) {
+      const int h = h0 + kRowsPer * i;
+      float m[4], o4[4], x[4];
+      unpack(own(h), m);
+      unpack(u[i], o4);
+      const float w0 = wt[h], w1 = wt[kH + h];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = split == 0 ? m[e] : o4[e];
+        const float p1 = split == 0 ? o4[e] : m[e];
+        x[e] = fmaf(w1, p1, w0 * p0);
+      }
+      put(h, x, wt[2 * kH + h]);
+    }
+  } else {
+    // Eight head rows at a time, splits in groups of four: the group's
+    // words (the eight rows of each of its splits) are requested before any
+    // is used, so a group costs one memory round trip rather than one per
+    // split.  The loads are unconditional (a split past the last re-reads
+    // the last, and this split's own words are read but taken from the
+    // staged block), so the compiler issues them back to back.  Splits are
+    // summed in split order.
+    for (int i0 = 0; i0 < kH / kRowsPer; i0 += 8) {
+      float acc[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i][e] = 0.0f;
+      for (int s0 = 0; s0 < n_split; s0 += 4) {
+        unsigned long long wv[4][8];
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            wv[g][i] = word(min(s0 + g, n_split - 1), h0 + kRowsPer * (i0 + i));
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int sg = s0 + g;
+          if (sg < n_split) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int h = h0 + kRowsPer * (i0 + i);
+              float p[4];
+              unpack(sg == split ? own(h) : wv[g][i], p);
+              const float wgt = wt[sg * kH + h];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wgt, p[e], acc[i][e]);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int h = h0 + kRowsPer * (i0 + i);
+        put(h, acc[i], wt[n_split * kH + h]);
+      }
+    }
+  }
+  // every split of this call has arrived: clear the word, so that a replay
+  // of the same launch (same tag) counts from zero again
+  if (tid == 0) __hip_atomic_store(arrivals + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // One workgroup = (query token, key split), all 64 heads, kWavesM waves (two
 // per SIMD).  Logits and softmax: wave w = 2 hg + kh, heads 16 kHT hg .. in
 // kHT 16-head tiles n (head 16 kHT hg + 16 n + lane % 16 in the query
@@ -708,168 +887,367 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
         lse[static_cast<int64_t>(t) * kH + h] = lse_h[n];
     }
   }
-  tile_barrier();
-  // Copy the staged block out.  The output: 16-byte pieces of a contiguous
-  // region.
-  if (!partial) {
-    constexpr int row_pieces = kR * 2 / 16;
-    constexpr int total = kH * row_pieces;
-    u32x4* dst = reinterpret_cast<u32x4*>(out + static_cast<int64_t>(t) * kH * kR);
-    for (int c = tid; c < total; c += kThreads) {
-      const int h = c / row_pieces, pc = c % row_pieces;
-      dst[c] = *reinterpret_cast<const u32x4*>(stage + h * row_b + 16 * pc);
-    }
-    return;
-  }
-  // Partials (bf16, normalised) are read back by another workgroup of this
-  // launch, maybe on another XCD: they are stored as relaxed device-scope
-  // atomics, which the hardware keeps coherent across XCDs by themselves,
-  // so no cache-wide write-back or invalidation is needed to hand them
-  // over.  8-byte words (4 dims), consecutive lanes on consecutive words,
-  // so every store instruction writes four whole 128-byte lines: thread tid
-  // takes word tid % 128 of head rows tid / 128 + 2 i.
-  constexpr int kWords = kR / 4;                   // 8-byte words per head row
-  constexpr int kRowsPer = kThreads / kWords;      // head rows per pass (4)
-  const int wq = tid % kWords;
-  const int h0 = tid / kWords;
-  unsigned long long* dst = reinterpret_cast<unsigned long long*>(
-      part_o + (static_cast<int64_t>(t) * n_split + split) * kH * kR);
-#pragma unroll 8
-  for (int i = 0; i < kH / kRowsPer; ++i) {
-    const int h = h0 + kRowsPer * i;
-    const unsigned long long v =
-        *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq);
-    __hip_atomic_store(dst + h * kWords + wq, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  mla_store_or_merge(stage, &sh.counter, t, split, n_split, partial, out, lse, part_o,
+                     part_lse, arrivals, call_tag);
+}
+
+// ------------------------------------------------- warp-specialised pipeline
+// The same contraction with the work of a tile split by role instead of by
+// phase.  Waves 0..3 (one per SIMD) are logit waves: wave hg holds the
+// queries of heads 16 hg .. 16 hg + 15 in registers and computes their
+// logits for all 32 keys of a tile (two 16-key blocks per K-step, the query
+// operand shared), the per-head tile maxima in-lane plus two permlane swaps,
+// and the bf16 probabilities; it also issues its 8-row group of the tile
+// DMAs.  Waves 4..7 are P.V waves: wave 4 + pq accumulates all 64 heads
+// over value dims 128 pq .. 128 pq + 127, so each value element is read from
+// LDS once and feeds four MFMAs (one per head group).  Iteration k: logit
+// waves work on tile k while P.V waves work on tile k - 1 with the
+// probabilities the logit waves published one iteration earlier (a double
+// buffer in LDS); one barrier per iteration.  Ring of four tiles: k - 1
+// (P.V), k (logits), k + 1 and k + 2 in flight (tile k + 2 is issued at the
+// start of iteration k, into the slot tile k - 2 left).
+// Reference maxima: as in k_mla_mfma, a head's reference is fixed by its
+// first key and may be exceeded by kMoveSlack before it moves; when it moves,
+// the logit wave rescales its sums and publishes the factor 2^(m_old -
+// m_new), and the P.V waves rescale that head group's accumulators in place
+// before adding the tile (no restart: each tile is processed once).
+constexpr int kWsSplitCap = 1024;       // indices per workgroup (slot table)
+struct MlaSharedWs {
+  uint16_t k[kBufs][kT * kD];           // row-major tiles, 4 x 36864 B
+  int32_t slots[kWsSplitCap];           // physical row of each index, or -1
+  uint32_t vbits[kWsSplitCap / kT];     // per tile: bit k = key k has a row
+  u32x4 xp[2][kHG][64];                 // probabilities [buffer][head group][lane]
+  float xf[2][kH];                      // per-head rescale factors
+  alignas(16) uint32_t xflag[2][kHG];   // per head group: its factors apply
+  float xl[kH];                         // per-head sums (epilogue)
+  uint32_t counter;
+};
+static_assert(sizeof(MlaSharedWs) <= 160 * 1024, "LDS budget");
+static_assert(kH * kRowB + (kMaxSplits + 1) * kH * 4 <= sizeof(MlaSharedWs::k),
+              "staged partials and merge weights fit in the tile buffers");
+
+__global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ topk_idx, int32_t topk, int32_t n_tokens,
+    int32_t n_split, int32_t split_len, float scale_log2,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
+    int32_t B, const int32_t* __restrict__ block_table, int32_t max_blocks,
+    int32_t block_size, int64_t num_slots, int32_t max_seq_len,
+    uint16_t* __restrict__ out, float* __restrict__ lse,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
+    unsigned long long* __restrict__ arrivals, unsigned long long call_tag) {
+  __shared__ MlaSharedWs sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int g16 = lane >> 4;
+  const bool logit = wave < kHG;        // waves 0..3; waves 4..7 are P.V waves
+  const int hg = wave & 3;              // logit wave: heads 16 hg ..; P.V wave: dims 128 hg ..
+
+  int vb = blockIdx.x;
+  if (n_split > 1 && (gridDim.x & 7) == 0)
+    vb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int t = vb / n_split;
+  const int split = vb % n_split;
+  if (t >= n_tokens) return;
+
+  const int32_t* idx_row = topk_idx + static_cast<int64_t>(t) * topk;
+  const int jbeg = split * split_len;
+  const int jend = min(topk, jbeg + split_len);
+  const int ntiles = jend > jbeg ? (jend - jbeg + kT - 1) / kT : 0;
+  const int jpad = jbeg + ntiles * kT;
+
+  // Logit waves' queries first (they depend only on t): heads 16 hg + l16,
+  // dims 32 st + 8 g16 .. + 7 of K-step st.
+  bf16x8 qb[kQSteps];
+  if (logit) {
+    const int64_t qbase = (static_cast<int64_t>(t) * kH + 16 * hg + l16) * kD;
+#pragma unroll
+    for (int st = 0; st < kQSteps; ++st)
+      qb[st] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * st + 8 * g16);
   }
 
-  // ---- the split that arrives last merges the token's partials.  Every
-  // thread waits until its partial stores have completed (reached the
-  // device-coherent level) before the workgroup counts its arrival; the
-  // merging workgroup loads the others' partials only after its own count
-  // came back, with device-scope atomic loads.
-  wait_vm<0>();
-  __syncthreads();
-  if (tid == 0) sh.counter = arrive(arrivals + t, call_tag, n_split) == static_cast<uint32_t>(n_split);
-  __syncthreads();
-  if (!sh.counter) return;
-  asm volatile("" ::: "memory");
-  // Thread tid merges dims 4 wq .. 4 wq + 3 of heads h0 + 2 i (as the
-  // partials were written: whole lines per instruction).  Splits are
-  // summed in split order (0, 1, ...) whichever finished last, so the
-  // result does not depend on the arrival order; this split's own partial
-  // comes from the staged block, rounded exactly as the others read theirs.
-  const unsigned long long* po = reinterpret_cast<const unsigned long long*>(
-      part_o + static_cast<int64_t>(t) * n_split * kH * kR) + wq;
-  auto word = [&](int s, int h) -> unsigned long long {
-    return __hip_atomic_load(const_cast<unsigned long long*>(po + (s * kH + h) * kWords),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto own = [&](int h) -> unsigned long long {
-    return *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq);
-  };
-  auto unpack = [](unsigned long long v, float (&x)[4]) {
+  // the split's physical rows and per-tile validity masks
+  constexpr int kIdxPer = kWsSplitCap / kThreads;    // 2
+  int32_t p[kIdxPer];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      x[e] = __uint_as_float(static_cast<uint32_t>((v >> (16 * e)) & 0xFFFFu) << 16);
-  };
-  unsigned long long* ob = reinterpret_cast<unsigned long long*>(
-      out + static_cast<int64_t>(t) * kH * kR) + wq;
-  auto put = [&](int h, const float (&x)[4], float inv) {
-    const unsigned long long v =
-        static_cast<unsigned long long>(pack2_bf16(x[0] * inv, x[1] * inv)) |
-        (static_cast<unsigned long long>(pack2_bf16(x[2] * inv, x[3] * inv)) << 32);
-    ob[h * kWords] = v;
-  };
-  // with two splits, the other split's rows are in flight while the
-  // weights are made
-  unsigned long long u[kH / kRowsPer];
-  if (n_split == 2) {
-#pragma unroll
-    for (int i = 0; i < kH / kRowsPer; ++i) u[i] = word(1 - split, h0 + kRowsPer * i);
+  for (int i = 0; i < kIdxPer; ++i) {
+    const int j = jbeg + kThreads * i + tid;
+    p[i] = j < jend ? idx_row[j] : -1;
   }
-  // split weights exp(lse_s - max) per head in place of the log-sum-exps,
-  // then 1 / their sum, behind the staged block
-  float* wt = reinterpret_cast<float*>(stage + kH * row_b);
-  for (int c = tid; c < n_split * kH; c += kThreads)
-    wt[c] = __hip_atomic_load(part_lse + static_cast<int64_t>(t) * n_split * kH + c,
-                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (tid < kH) {
-    float mx = -INFINITY;
-    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, wt[s * kH + tid]);
-    float sum = 0.0f;
-    for (int s = 0; s < n_split; ++s) {
-      const float wgt = mx == -INFINITY ? 0.0f : expf(wt[s * kH + tid] - mx);
-      wt[s * kH + tid] = wgt;
-      sum += wgt;
-    }
-    wt[n_split * kH + tid] = sum > 0.0f ? 1.0f / sum : 0.0f;
-    if (lse) lse[static_cast<int64_t>(t) * kH + tid] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
+  const int b = request_of_wave(cu_q, B, t);
+  const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
+  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
+  int32_t bid[kIdxPer];
+#pragma unroll
+  for (int i = 0; i < kIdxPer; ++i) {
+    const bool ok = p[i] >= 0 && p[i] <= pos && p[i] / block_size < max_blocks;
+    bid[i] = ok ? bt_row[p[i] / block_size] : -1;
+    if (!ok) p[i] = -1;
   }
-  __syncthreads();
-  if (n_split == 2) {
 #pragma unroll
-    for (int i = 0; i < kH / kRowsPer; ++i) {
-      const int h = h0 + kRowsPer * i;
-      float m[4], o4[4], x[4];
-      unpack(own(h), m);
-      unpack(u[i], o4);
-      const float w0 = wt[h], w1 = wt[kH + h];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = split == 0 ? m[e] : o4[e];
-        const float p1 = split == 0 ? o4[e] : m[e];
-        x[e] = fmaf(w1, p1, w0 * p0);
-      }
-      put(h, x, wt[2 * kH + h]);
+  for (int i = 0; i < kIdxPer; ++i) {
+    const int j = jbeg + kThreads * i + tid;
+    int32_t slot = -1;
+    if (p[i] >= 0) {
+      const int64_t s = static_cast<int64_t>(bid[i]) * block_size + p[i] % block_size;
+      slot = (s >= 0 && s < num_slots) ? static_cast<int32_t>(s) : -1;
     }
-  } else {
-    // Eight head rows at a time, splits in groups of four: the group's
-    // words (the eight rows of each of its splits) are requested before any
-    // is used, so a group costs one memory round trip rather than one per
-    // split.  The loads are unconditional (a split past the last re-reads
-    // the last, and this split's own words are read but taken from the
-    // staged block), so the compiler issues them back to back.  Splits are
-    // summed in split order.
-    for (int i0 = 0; i0 < kH / kRowsPer; i0 += 8) {
-      float acc[8][4];
+    if (j < jpad) sh.slots[j - jbeg] = slot;
+    const uint64_t m = __ballot(j < jpad && slot >= 0);
+    const int tw = (kThreads * i + 64 * wave) / kT;
+    if (lane == 0 && tw < ntiles) sh.vbits[tw] = static_cast<uint32_t>(m);
+    if (lane == 0 && tw + 1 < ntiles) sh.vbits[tw + 1] = static_cast<uint32_t>(m >> 32);
+  }
+  tile_barrier();
+
+  // DMA geometry (logit wave w fills row group w of a tile: nine
+  // instructions, one per 128-byte piece group; keys without a row load row
+  // 0 and are masked)
+  const int dpi = (lane >> 3) ^ (wave & 1);
+  const int drow = 8 * wave + ((lane & 7) ^ (4 * (dpi & 1)));
+  const uint32_t dcol = 16u * static_cast<uint32_t>(dpi);
+  auto dma_piece = [&](const uint8_t* src, uint8_t* dst, auto gc) {
+    constexpr int G = decltype(gc)::value;
+    __builtin_amdgcn_global_load_lds(
+        src + 128 * G, (__attribute__((address_space(3))) void*)(dst + 1024 * G), 16, 0, 0);
+  };
+  auto tile_src = [&](int tile) {
+    const int32_t sl = sh.slots[tile * kT + drow];
+    return reinterpret_cast<const uint8_t*>(kv) + static_cast<uint64_t>(max(sl, 0)) * (2 * kD) + dcol;
+  };
+
+  if (logit) {
+    // ================================================== logit waves
+    const uint8_t* s0 = ntiles > 0 ? tile_src(0) : nullptr;
+    const uint8_t* s1 = ntiles > 1 ? tile_src(1) : nullptr;
+    if (s0) static_for<kDmaPerWave>([&](auto g) {
+      dma_piece(s0, reinterpret_cast<uint8_t*>(sh.k[0]) + 9216 * wave, g); });
+    if (s1) static_for<kDmaPerWave>([&](auto g) {
+      dma_piece(s1, reinterpret_cast<uint8_t*>(sh.k[1]) + 9216 * wave, g); });
+    // the queries and tile 0 are in when at most tile 1's loads are pending
+    if (ntiles > 1) wait_vm<kDmaPerWave>(); else wait_vm<0>();
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][e] = 0.0f;
-      for (int s0 = 0; s0 < n_split; s0 += 4) {
-        unsigned long long wv[4][8];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            wv[g][i] = word(min(s0 + g, n_split - 1), h0 + kRowsPer * (i0 + i));
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int sg = s0 + g;
-          if (sg < n_split) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int h = h0 + kRowsPer * (i0 + i);
-              float p[4];
-              unpack(sg == split ? own(h) : wv[g][i], p);
-              const float wgt = wt[sg * kH + h];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wgt, p[e], acc[i][e]);
+    for (int st = 0; st < kQSteps; ++st) asm volatile("" : "+v"(qb[st]));
+    // K-operand rows of this lane: keys l16 (block 0) and 16 + l16 (block 1);
+    // K-step st reads piece 4 st + g16: group st >> 1 (an immediate) and one
+    // of two offsets per block
+    const uint32_t ko[2][2] = {{tile_byte(l16, g16), tile_byte(l16, 4 + g16)},
+                               {tile_byte(16 + l16, g16), tile_byte(16 + l16, 4 + g16)}};
+    float m_ref = -INFINITY;            // head 16 hg + l16
+    float l_part = 0.0f;
+    for (int k = 0; k <= ntiles; ++k) {
+      tile_barrier();                   // tile k landed; P(k - 1) read by the P.V waves
+      if (k >= ntiles) continue;
+      // refill: tile k + 2 into the slot tile k - 2 left, one DMA instruction
+      // after every second K-step
+      const bool refill = k + 2 < ntiles;
+      const uint8_t* rsrc = refill ? tile_src(k + 2) : nullptr;
+      uint8_t* rdst = reinterpret_cast<uint8_t*>(sh.k[(k + 2) % kBufs]) + 9216 * wave;
+      if (refill) asm volatile("" : "+v"(rsrc));
+      const uint32_t kb = lds_addr(sh.k[k % kBufs]);
+      const uint32_t vb32 = sh.vbits[k];
+      f32x4 part[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+      {
+        constexpr int kAhead = 3;       // K-steps of operands in flight
+        bf16x8 kr[kAhead][2];
+        lgkm_drain();
+        static_for<kAhead>([&](auto sc) {
+          constexpr int S = decltype(sc)::value;
+          kr[S][0] = b128_load<1024 * (S >> 1)>(kb + ko[0][S & 1]);
+          kr[S][1] = b128_load<1024 * (S >> 1)>(kb + ko[1][S & 1]);
+        });
+        static_for<kQSteps>([&](auto sc) {
+          constexpr int S = decltype(sc)::value;
+          constexpr int R = S % kAhead;
+          constexpr int kAfter = 2 * ((kQSteps - 1 - S) < (kAhead - 1) ? (kQSteps - 1 - S) : (kAhead - 1));
+          lgkm_keep<kAfter + 1>(kr[R][0]);
+          part[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[R][0], qb[S], part[0], 0, 0, 0);
+          lgkm_keep<kAfter>(kr[R][1]);
+          part[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[R][1], qb[S], part[1], 0, 0, 0);
+          if constexpr (S + kAhead < kQSteps) {
+            kr[R][0] = b128_load<1024 * ((S + kAhead) >> 1)>(kb + ko[0][(S + kAhead) & 1]);
+            kr[R][1] = b128_load<1024 * ((S + kAhead) >> 1)>(kb + ko[1][(S + kAhead) & 1]);
+          }
+          if constexpr (S % 2 == 1 && S / 2 < kDmaPerWave) {
+            if (refill) {
+              asm volatile("" ::: "memory");
+              dma_piece(rsrc, rdst, std::integral_constant<int, S / 2>{});
             }
           }
+        });
+      }
+      // ---- softmax: lane (l16, g16) holds head 16 hg + l16's logits of keys
+      // 4 g16 + i (block 0) and 16 + 4 g16 + i (block 1)
+      float zr[8];
+      if (__builtin_amdgcn_readfirstlane(vb32) == 0xFFFFFFFFu) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          zr[i] = part[0][i];
+          zr[4 + i] = part[1][i];
+        }
+      } else {
+        const uint32_t v0 = vb32 >> (4 * g16), v1 = vb32 >> (16 + 4 * g16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          zr[i] = ((v0 >> i) & 1u) ? part[0][i] : -INFINITY;
+          zr[4 + i] = ((v1 >> i) & 1u) ? part[1][i] : -INFINITY;
         }
       }
+      float mx = max_nn(max3_nn(zr[0], zr[1], zr[2]), max3_nn(zr[3], zr[4], zr[5]));
+      mx = max_x16_x32(max3_nn(mx, zr[6], zr[7])) * scale_log2;
+      // the reference moves on the head's first key, or when the tile beats
+      // it by more than the slack; a move of a live reference rescales
+      float factor = 1.0f;
+      bool moved = false;
+      if (m_ref == -INFINITY) {
+        m_ref = mx;                      // stays -inf while no key has a row
+      } else if (mx > m_ref + kMoveSlack) {
+        factor = __builtin_amdgcn_exp2f(m_ref - mx);
+        m_ref = mx;
+        moved = true;
+      }
+      const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
+      float pr[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int h = h0 + kRowsPer * (i0 + i);
-        put(h, acc[i], wt[n_split * kH + h]);
+      for (int i = 0; i < 8; ++i) pr[i] = __builtin_amdgcn_exp2f(fmaf(zr[i], scale_log2, -mu));
+      l_part *= factor;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) l_part += pr[i];
+      const int pb = k & 1;
+      u32x4 pk;
+      pk[0] = pack2_bf16(pr[0], pr[1]);
+      pk[1] = pack2_bf16(pr[2], pr[3]);
+      pk[2] = pack2_bf16(pr[4], pr[5]);
+      pk[3] = pack2_bf16(pr[6], pr[7]);
+      sh.xp[pb][hg][lane] = pk;
+      const bool any = __ballot(moved) != 0;
+      if (any && g16 == 0) sh.xf[pb][16 * hg + l16] = factor;
+      if (lane == 0) sh.xflag[pb][hg] = any ? 1u : 0u;
+      // tile k + 1 is in when at most tile k + 2's loads are pending
+      if (k + 1 < ntiles) {
+        if (refill) wait_vm<kDmaPerWave>(); else wait_vm<0>();
       }
     }
+    tile_barrier();                      // every P.V wave is done with the tiles
+    const float l = sum_x16_x32(l_part);
+    if (g16 == 0) {
+      sh.xl[16 * hg + l16] = l;
+      const float lh = l > 0.0f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+      const int h = 16 * hg + l16;
+      if (n_split > 1)
+        __hip_atomic_store(part_lse + (static_cast<int64_t>(t) * n_split + split) * kH + h,
+                           lh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else if (lse)
+        lse[static_cast<int64_t>(t) * kH + h] = lh;
+    }
+    tile_barrier();                      // sums published
+    tile_barrier();                      // rows staged
+  } else {
+    // ================================================== P.V waves
+    // O[n][nt]: heads 16 n + 4 g16 + i (i = 0..3), dims 128 pq + 16 nt + l16
+    const int pq = hg;
+    f32x4 o[kHG][kPvNT];
+#pragma unroll
+    for (int n = 0; n < kHG; ++n)
+#pragma unroll
+      for (int nt = 0; nt < kPvNT; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
+    // transpose-load offsets: rows 4 g16 + l16 / 4 (keys 0..15) and 16 + that
+    // (keys 16..31), dims 128 pq + 16 nt + 4 (l16 & 3)
+    const int vrow_a = 4 * g16 + (l16 >> 2);
+    const int vrow_b = 16 + vrow_a;
+    const int vb_lo = (l16 & 3) >> 1;
+    uint32_t voff_a[4], voff_b[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t half = 8u * static_cast<uint32_t>(l16 & 1);
+      voff_a[m] = tile_byte(vrow_a, 16 * pq + 2 * m + vb_lo) + half;
+      voff_b[m] = tile_byte(vrow_b, 16 * pq + 2 * m + vb_lo) + half;
+    }
+    for (int k = 0; k <= ntiles; ++k) {
+      tile_barrier();                   // P(k - 1) published
+      if (k == 0) continue;
+      const int j = k - 1;
+      const int pb = j & 1;
+      // a head group whose references moved: rescale its rows first
+      const u32x4 fl = *reinterpret_cast<const u32x4*>(&sh.xflag[pb][0]);
+      if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0u) {
+#pragma unroll
+        for (int n = 0; n < kHG; ++n) {
+          if (!fl[n]) continue;
+          float f[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) f[i] = sh.xf[pb][16 * n + 4 * g16 + i];
+#pragma unroll
+          for (int nt = 0; nt < kPvNT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[n][nt][i] *= f[i];
+        }
+      }
+      const uint32_t tb = lds_addr(sh.k[j % kBufs]);
+      uint32_t va[4], vb[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        va[m] = tb + voff_a[m];
+        vb[m] = tb + voff_b[m];
+      }
+      bf16x8 pa[kHG];
+      lgkm_drain();
+#pragma unroll
+      for (int n = 0; n < kHG; ++n)
+        pa[n] = __builtin_bit_cast(bf16x8, sh.xp[pb][n][lane]);
+      lgkm_drain();
+      constexpr int kLoads = 2 * kPvNT;               // 16
+      constexpr int kAhead = 8;
+      v4i16 vr[kAhead];
+      auto vload = [&](auto ld) -> v4i16 {
+        constexpr int L = decltype(ld)::value;
+        constexpr int NT = L >> 1;
+        return (L & 1) ? tr_load<1024 * (NT >> 2)>(vb[NT & 3])
+                       : tr_load<1024 * (NT >> 2)>(va[NT & 3]);
+      };
+      static_for<kAhead>([&](auto ld) { vr[decltype(ld)::value] = vload(ld); });
+      static_for<kPvNT>([&](auto ntc) {
+        constexpr int NT = decltype(ntc)::value;
+        v4i16& a0 = vr[(2 * NT) % kAhead];
+        v4i16& a1 = vr[(2 * NT + 1) % kAhead];
+        constexpr int kAfter = (kLoads - 2 - 2 * NT) < (kAhead - 2) ? (kLoads - 2 - 2 * NT) : (kAhead - 2);
+        lgkm_keep<kAfter>(a0);
+        lgkm_keep<kAfter>(a1);
+        const v8i16 v01 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, v01);
+#pragma unroll
+        for (int n = 0; n < kHG; ++n)
+          o[n][NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[n], vop, o[n][NT], 0, 0, 0);
+        if constexpr (2 * NT + kAhead < kLoads) {
+          a0 = vload(std::integral_constant<int, 2 * NT + kAhead>{});
+          a1 = vload(std::integral_constant<int, 2 * NT + kAhead + 1>{});
+        }
+      });
+    }
+    tile_barrier();                      // every wave is done with the tiles
+    tile_barrier();                      // sums published
+    // normalised bf16 rows into the staging block (over the ring)
+    uint8_t* stage = reinterpret_cast<uint8_t*>(&sh.k[0][0]);
+#pragma unroll
+    for (int n = 0; n < kHG; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * n + 4 * g16 + i;
+        const float l = sh.xl[h];
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < kPvNT; ++nt) {
+          const int d = 128 * pq + 16 * nt + l16;
+          *reinterpret_cast<uint16_t*>(stage + h * kRowB + 2 * d) = f32_to_bf16_rne(o[n][nt][i] * inv);
+        }
+      }
+    }
+    tile_barrier();                      // rows staged
   }
-  // every split of this call has arrived: clear the word, so that a replay
-  // of the same launch (same tag) counts from zero again
-  if (tid == 0) __hip_atomic_store(arrivals + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  mla_store_or_merge(reinterpret_cast<uint8_t*>(&sh.k[0][0]), &sh.counter, t, split, n_split,
+                     n_split > 1, out, lse, part_o, part_lse, arrivals, call_tag);
 }
 
 // ---------------------------------------------------------------- vector path
@@ -982,6 +1360,17 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
     if (n_split > 1 && (!a.part_o || !a.part_lse || !a.arrivals || !a.call_tag))
       return hipErrorInvalidValue;
     const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * n_split;
+    if (n_split > 1 && split_len <= kWsSplitCap) {
+      // key splits short enough for the warp-specialised pipeline's slot table
+      k_mla_ws<<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(
+          static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv),
+          a.idx, a.topk, b.num_q_tokens, n_split, split_len, a.scale * kLog2e,
+          b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
+          b.block_size, b.num_slots, b.max_seq_len,
+          static_cast<uint16_t*>(a.out), a.lse, a.part_o, a.part_lse, a.arrivals,
+          a.call_tag);
+      return hipGetLastError();
+    }
     k_mla_mfma<<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv),
         a.idx, a.topk, b.num_q_tokens, n_split, split_len, a.scale * kLog2e,

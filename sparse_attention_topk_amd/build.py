@@ -16,8 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["api.hip", "cache_write.hip", "indexer_score.hip", "topk.hip",
-           "sparse_mla.hip", "prologue.hip"]
+SOURCES = ["api.hip", "cache_write.hip", "indexer_score.hip", "indexer_prefill.hip",
+           "topk.hip", "sparse_mla.hip", "prologue.hip"]
 ARCH = os.environ.get("DSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -28,11 +28,17 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
+# per-source code generation options
+EXTRA = {
+    # the prefill score kernel keeps its MFMA accumulators in VGPRs, where
+    # the ReLU-weighted head sum reads them without accumulator moves
+    "indexer_prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src):
     obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + CFLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd),

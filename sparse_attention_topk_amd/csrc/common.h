@@ -243,6 +243,11 @@ inline int64_t indexer_range_stride_max(int32_t max_seq_len) {
 }
 bool indexer_mfma_ok(const IndexerArgs& a);
 hipError_t launch_indexer_score(IndexerArgs& a, hipStream_t stream);
+// prefill-shaped batches (bf16 queries and keys, 32 heads of 128 dims,
+// blocks of a multiple of 64 keys, at least 16 query tokens in a request):
+// each key tile is reused across 16 query tokens
+bool prefill_score_ok(const IndexerArgs& a);
+hipError_t launch_score_prefill(IndexerArgs& a, hipStream_t stream);
 hipError_t launch_topk(const IndexerArgs& a, hipStream_t stream);
 
 struct MlaArgs {

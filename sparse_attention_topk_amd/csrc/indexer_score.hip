@@ -551,6 +551,7 @@ hipError_t launch_indexer_score(IndexerArgs& a, hipStream_t stream) {
   const dsa_batch& b = a.b;
   if (b.num_q_tokens == 0) return hipSuccess;
   if (b.max_seq_len <= kTopkRegCap) a.chunk_range = nullptr;   // see kTopkRegCap
+  if (prefill_score_ok(a)) return launch_score_prefill(a, stream);
   if (indexer_mfma_ok(a)) {
     const bool fp8 = a.cache_dtype == DSA_FP8_E4M3;
     const bool one = b.max_q_len == 1;

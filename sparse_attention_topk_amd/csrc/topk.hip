@@ -52,21 +52,25 @@ __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-struct Shared {
+// LDS of a workgroup of T threads (the register path holds up to 32 T
+// positions: one bitmap word per thread)
+template <int T>
+struct ShrT {
   uint32_t hist[kBins];
   uint32_t cand[kCandCap];
-  uint32_t bm_sel[kRegCap / 32];   // register path: selected positions
-  uint32_t bm_eq[kRegCap / 32];    // register path: positions scoring == T
-  uint32_t wave_a[kWaves];
-  uint32_t wave_b[kWaves];
-  float red_min[kWaves];
-  float red_max[kWaves];
+  uint32_t bm_sel[T];     // register path: selected positions
+  uint32_t bm_eq[T];      // register path: positions scoring == T
+  uint32_t wave_a[T / 64];
+  uint32_t wave_b[T / 64];
+  float red_min[T / 64];
+  float red_max[T / 64];
   uint32_t ncand;
   uint32_t sel_bin;       // threshold bin
   uint32_t above_bin;     // keys in bins above it
   uint32_t digit;         // radix step result
   uint32_t digit_above;
 };
+using Shared = ShrT<kThreads>;
 
 __device__ __forceinline__ uint64_t lanes_below() {
   const int lane = threadIdx.x & 63;
@@ -90,7 +94,8 @@ __device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
 // Suffix scan helper: for a 256-bin histogram find digit d with
 // above(d) < r <= above(d) + h[d] (above = sum of higher bins).  Wave 0
 // scans; results land in s.digit / s.digit_above.
-__device__ __forceinline__ void find_digit(Shared& s, uint32_t r) {
+template <typename S>
+__device__ __forceinline__ void find_digit(S& s, uint32_t r) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     // lane owns digits 255 - 4*lane - i, i = 0..3 (top-down)
@@ -123,7 +128,8 @@ __device__ __forceinline__ int bin_of(float v, float vmin, float inv) {
 }
 
 // Workgroup-wide min / max of per-thread values (every thread gets both).
-__device__ __forceinline__ void range_reduce(Shared& s, float& vmin, float& vmax) {
+template <int T>
+__device__ __forceinline__ void range_reduce(ShrT<T>& s, float& vmin, float& vmax) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   wave_minmax(vmin, vmax);
@@ -135,22 +141,28 @@ __device__ __forceinline__ void range_reduce(Shared& s, float& vmin, float& vmax
   vmin = s.red_min[0];
   vmax = s.red_max[0];
 #pragma unroll
-  for (int wv = 1; wv < kWaves; ++wv) {
+  for (int wv = 1; wv < T / 64; ++wv) {
     vmin = fminf(vmin, s.red_min[wv]);
     vmax = fmaxf(vmax, s.red_max[wv]);
   }
 }
 
-// Thread tid owns bins 2047 - 2 tid and 2046 - 2 tid; the bin holding rank r
-// (counted from the top) and the number of keys above it go to s.sel_bin /
-// s.above_bin.  Ends with a barrier.
-__device__ __forceinline__ void find_threshold_bin(Shared& s, uint32_t r) {
+// Thread tid owns the kBins / T bins from 2047 - (kBins / T) tid down; the
+// bin holding rank r (counted from the top) and the number of keys above it
+// go to s.sel_bin / s.above_bin.  Ends with a barrier.
+template <int T>
+__device__ __forceinline__ void find_threshold_bin(ShrT<T>& s, uint32_t r) {
+  constexpr int kB = kBins / T;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const uint32_t h0 = s.hist[kBins - 1 - 2 * tid];
-  const uint32_t h1 = s.hist[kBins - 2 - 2 * tid];
-  const uint32_t tot = h0 + h1;
+  uint32_t h[kB];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < kB; ++i) {
+    h[i] = s.hist[kBins - 1 - kB * tid - i];
+    tot += h[i];
+  }
   uint32_t incl = wave_scan_incl(tot);
   if (lane == 63) s.wave_a[wave] = incl;
   lds_barrier();
@@ -158,15 +170,14 @@ __device__ __forceinline__ void find_threshold_bin(Shared& s, uint32_t r) {
   // DPP scan (instead of a serial run of LDS reads)
   const uint32_t base = __builtin_amdgcn_readlane(
       wave_scan_incl(lane < wave ? s.wave_a[lane] : 0u), 63);
-  const uint32_t above0 = base + incl - tot;    // above bin 2047 - 2 tid
-  if (above0 < r && r <= above0 + h0) {
-    s.sel_bin = kBins - 1 - 2 * tid;
-    s.above_bin = above0;
-  }
-  const uint32_t above1 = above0 + h0;
-  if (above1 < r && r <= above1 + h1) {
-    s.sel_bin = kBins - 2 - 2 * tid;
-    s.above_bin = above1;
+  uint32_t above = base + incl - tot;        // above bin 2047 - kB tid
+#pragma unroll
+  for (int i = 0; i < kB; ++i) {
+    if (above < r && r <= above + h[i]) {
+      s.sel_bin = kBins - 1 - kB * tid - i;
+      s.above_bin = above;
+    }
+    above += h[i];
   }
   lds_barrier();
 }
@@ -177,7 +188,7 @@ __device__ __forceinline__ void find_threshold_bin(Shared& s, uint32_t r) {
 // positions 0 .. L - 1 are combined; without them own(lo, hi) scans the
 // keys.  Both give the exact min / max of the row's scores, NaN skipped.
 // pre: entry threadIdx.x of the row, loaded early (before L was known).
-template <typename F>
+template <int T, typename F>
 __device__ __forceinline__ void row_range(const float2* __restrict__ rng, int32_t chunk_keys,
                                           int L, float2 pre, F&& own, float& vmin,
                                           float& vmax) {
@@ -186,7 +197,7 @@ __device__ __forceinline__ void row_range(const float2* __restrict__ rng, int32_
     const bool mine = static_cast<int>(threadIdx.x) < nent;
     vmin = mine ? pre.x : INFINITY;
     vmax = mine ? pre.y : -INFINITY;
-    for (int e = threadIdx.x + kThreads; e < nent; e += kThreads) {
+    for (int e = threadIdx.x + T; e < nent; e += T) {
       const float2 r = rng[e];
       vmin = fminf(vmin, r.x);
       vmax = fmaxf(vmax, r.y);
@@ -268,7 +279,8 @@ __device__ __forceinline__ void load_row_regs(const float* __restrict__ src,
 // counts below correct for them.  The selection is recorded in a bitmap of
 // positions (bit p & 31 of word p >> 5), emitted in position order at the
 // end.
-__device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int L,
+template <int T>
+__device__ __forceinline__ void select_row_regs(ShrT<T>& s, float (&f)[kKpt], int L,
                                                 int topk, const float2* __restrict__ rng,
                                                 int32_t chunk_keys, float2 pre,
                                                 int32_t* __restrict__ out) {
@@ -288,9 +300,13 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
       for (int e = 0; e < 4; ++e)
         if (reg_pos(wave, lane, j, e) >= L) f[4 * j + e] = __builtin_nanf("");
   }
-  const uint32_t absent = static_cast<uint32_t>(kRegCap - L);   // NaNs in bin 0
+  // 256-position blocks (wave-uniform: load j of a wave) lying wholly past
+  // the row take no part in the passes below; the row's last block holds
+  // the only NaNs that do, and they land in bin 0
+  auto live = [&](int j) { return 2048 * wave + 256 * j < L; };
+  const uint32_t absent = static_cast<uint32_t>((L + 255) / 256 * 256 - L);
   float vmin, vmax;
-  row_range(rng, chunk_keys, L, pre, [&](float& lo, float& hi) {
+  row_range<T>(rng, chunk_keys, L, pre, [&](float& lo, float& hi) {
     lo = f[0];
     hi = f[0];
 #pragma unroll
@@ -299,21 +315,23 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
       hi = fmaxf(hi, f[j]);
     }
   }, vmin, vmax);
-  for (int i = tid; i < kBins; i += kThreads) s.hist[i] = 0;
+  for (int i = tid; i < kBins; i += T) s.hist[i] = 0;
   s.bm_sel[tid] = 0;
   s.bm_eq[tid] = 0;
   if (tid == 0) s.ncand = 0;
-  range_reduce(s, vmin, vmax);
+  range_reduce<T>(s, vmin, vmax);
 
   uint32_t need = 0;          // positions still to take among those == T
   if (!(vmax > vmin)) {
     // every score is equal: the first topk positions
     need = static_cast<uint32_t>(topk);
 #pragma unroll
-    for (int j = 0; j < kKpt / 4; ++j)
+    for (int j = 0; j < kKpt / 4; ++j) {
+      if (!live(j)) continue;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         if (f[4 * j + e] == vmax) atomicOr(&s.bm_eq[word_of(j)], bit_of(e));
+    }
   } else {
     // ---- 2. histogram and threshold bin: bin = trunc(clamp(f * inv - vmin *
     // inv, 0, 2047)), monotone in f; NaN lands in bin 0.  The map needs a
@@ -331,11 +349,15 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
         return static_cast<int>(fminf(fmaxf(fmaf(x, inv, off), 0.0f), kBins - 1.0f));
       };
 #pragma unroll
-      for (int j = 0; j < kKpt; ++j) atomicAdd(&s.hist[bin(f[j])], 1u);
+      for (int j = 0; j < kKpt / 4; ++j) {
+        if (!live(j)) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(&s.hist[bin(f[4 * j + e])], 1u);
+      }
       lds_barrier();
-      if (tid == kThreads - 1) s.hist[0] -= absent;
+      if (tid == T - 1) s.hist[0] -= absent;
       lds_barrier();
-      find_threshold_bin(s, static_cast<uint32_t>(topk));
+      find_threshold_bin<T>(s, static_cast<uint32_t>(topk));
       const int sel = static_cast<int>(s.sel_bin);
       const uint32_t above_bin = s.above_bin;
       const uint32_t bin_count = s.hist[sel];
@@ -358,6 +380,7 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
         uint32_t cand_bits = 0;          // bit 4 j + e
 #pragma unroll
         for (int j = 0; j < kKpt / 4; ++j) {
+          if (!live(j)) continue;
           uint32_t take = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -399,10 +422,11 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
       uint32_t prefix = 0, mask = 0, gt_extra = 0;
       for (int shift = 24; shift >= 0; shift -= 8) {
         lds_barrier();
-        for (int i = tid2; i < 256; i += kThreads) s.hist[i] = 0;
+        for (int i = tid2; i < 256; i += T) s.hist[i] = 0;
         lds_barrier();
 #pragma unroll
         for (int j = 0; j < kKpt; ++j) {
+          if (!live(j / 4)) continue;
           const uint32_t kk = float_key(f[j]);
           if (f[j] == f[j] && (kk & mask) == prefix)
             atomicAdd(&s.hist[(kk >> shift) & 255u], 1u);
@@ -417,15 +441,16 @@ __device__ __forceinline__ void select_row_regs(Shared& s, float (&f)[kKpt], int
         prefix |= d << shift;
         mask |= 255u << shift;
       }
-      const float T = key_float(prefix);
+      const float thr = key_float(prefix);
       need = static_cast<uint32_t>(topk) - gt_extra;   // >= 1
 #pragma unroll
       for (int j = 0; j < kKpt / 4; ++j) {
+        if (!live(j)) continue;
         uint32_t gtm = 0, eqm = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (f[4 * j + e] > T) gtm |= bit_of(e);
-          if (f[4 * j + e] == T) eqm |= bit_of(e);
+          if (f[4 * j + e] > thr) gtm |= bit_of(e);
+          if (f[4 * j + e] == thr) eqm |= bit_of(e);
         }
         if (gtm) atomicOr(&s.bm_sel[word_of(j)], gtm);
         if (eqm) atomicOr(&s.bm_eq[word_of(j)], eqm);
@@ -548,7 +573,7 @@ __device__ __forceinline__ void select_row_stream(Shared& s, const float* __rest
 
   // ---- 1. range (a pass over the row only without the score pass's)
   float vmin, vmax;
-  row_range(rng, chunk_keys, L, pre, [&](float& lo, float& hi) {
+  row_range<kThreads>(rng, chunk_keys, L, pre, [&](float& lo, float& hi) {
     lo = INFINITY;
     hi = -INFINITY;
     for_each_key(src, L, [&](int, uint32_t k) {
@@ -796,7 +821,7 @@ __device__ __noinline__ bool select_row_long(Shared& s, uint32_t* __restrict__ d
 
   // ---- 1. range
   float vmin, vmax;
-  row_range(rng, chunk_keys, L, pre, [&](float& lo, float& hi) {
+  row_range<kThreads>(rng, chunk_keys, L, pre, [&](float& lo, float& hi) {
     lo = INFINITY;
     hi = -INFINITY;
     for_each_quad(src, L, [&](int i, const float4& v) {
@@ -946,7 +971,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
     return;
   }
   if (L <= kRegCap) {
-    select_row_regs(s, f, L, topk, rng, chunk_keys, pre, orow);
+    select_row_regs<kThreads>(s, f, L, topk, rng, chunk_keys, pre, orow);
     return;
   }
   if (L <= 32 * words_cap &&
@@ -956,10 +981,54 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
   select_row_stream(s, src, L, topk, rng, chunk_keys, pre, orow);
 }
 
+// Launches whose rows all fit 32 T positions (prefill-length rows): the
+// register path on a workgroup of T threads, several rows per CU.
+template <int T>
+__global__ __launch_bounds__(T, 2048 / T) void k_topk_reg(
+    const float* __restrict__ scores, int64_t row_stride,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
+    int32_t B, int32_t max_seq_len, int32_t topk, int32_t* __restrict__ out) {
+  __shared__ ShrT<T> s;
+  const int t = blockIdx.x;
+  const float* src = scores + static_cast<int64_t>(t) * row_stride;
+  const int lane = threadIdx.x & 63;
+  const int32_t c0 = cu_q[lane < B ? lane : B];      // cu_q has B + 1 entries
+  asm volatile("" ::: "memory");
+  float f[kKpt];
+  load_row_regs(src, row_stride, f);
+  int n = __popcll(__ballot(lane < B && c0 <= t));
+  for (int b0 = 64; b0 < B; b0 += 64) {
+    const int bb = b0 + lane;
+    const int32_t c = cu_q[bb < B ? bb : B];
+    n += __popcll(__ballot(bb < B && c <= t));
+  }
+  const int b = n - 1 < 0 ? 0 : (n - 1 >= B ? B - 1 : n - 1);
+  const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
+  const int L = pos + 1;
+  int32_t* orow = out + static_cast<int64_t>(t) * topk;
+  if (L <= topk) {
+    for (int j = threadIdx.x; j < topk; j += T) orow[j] = j < L ? j : -1;
+    return;
+  }
+  select_row_regs<T>(s, f, L, topk, nullptr, 0, make_float2(INFINITY, -INFINITY), orow);
+}
+
 }  // namespace
 
 hipError_t launch_topk(const IndexerArgs& a, hipStream_t stream) {
   if (a.b.num_q_tokens == 0) return hipSuccess;
+  if (a.b.max_seq_len <= 32 * 256) {
+    k_topk_reg<256><<<a.b.num_q_tokens, 256, 0, stream>>>(
+        a.scores, a.row_stride, a.b.seq_lens, a.b.cu_q, a.b.num_reqs, a.b.max_seq_len,
+        a.topk, a.topk_idx);
+    return hipGetLastError();
+  }
+  if (a.b.max_seq_len <= 32 * 512) {
+    k_topk_reg<512><<<a.b.num_q_tokens, 512, 0, stream>>>(
+        a.scores, a.row_stride, a.b.seq_lens, a.b.cu_q, a.b.num_reqs, a.b.max_seq_len,
+        a.topk, a.topk_idx);
+    return hipGetLastError();
+  }
   // long rows' bitmaps and candidate positions in dynamic LDS, sized for the
   // longest row this launch can hold (none when every row fits registers)
   const int32_t words_cap = a.b.max_seq_len > kRegCap

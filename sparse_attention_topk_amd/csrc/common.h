@@ -193,6 +193,37 @@ __device__ __forceinline__ int request_of_wave(const int32_t* cu_q, int32_t B, i
   return r < 0 ? 0 : (r >= B ? B - 1 : r);
 }
 
+// Request b and position of query token t in one memory round trip when
+// B < 128: cu_q[0..127] and seq_lens[0..127] are read two entries per lane
+// up front, b is counted with ballots and the entries it needs are taken
+// with v_readlane (every wave gets the same, wave-uniform values).  Larger
+// batches take request_of_wave and query_pos.
+__device__ __forceinline__ int32_t query_pos(const int32_t* seq_lens,
+                                             const int32_t* cu_q, int b,
+                                             int32_t t, int32_t max_seq_len);
+__device__ __forceinline__ void token_place(const int32_t* cu_q, const int32_t* seq_lens,
+                                            int32_t B, int32_t t, int32_t max_seq_len,
+                                            int& b, int32_t& pos) {
+  if (B < 128) {
+    const int lane = threadIdx.x & 63;
+    const int32_t c0 = cu_q[min(lane, B)], c1 = cu_q[min(lane + 64, B)];   // B + 1 entries
+    const int32_t s0 = seq_lens[min(lane, B - 1)], s1 = seq_lens[min(lane + 64, B - 1)];
+    const int n = __popcll(__ballot(lane < B && c0 <= t)) +
+                  __popcll(__ballot(lane + 64 < B && c1 <= t));
+    const int bb = n - 1 < 0 ? 0 : (n - 1 >= B ? B - 1 : n - 1);
+    auto pick = [&](int32_t v0, int32_t v1, int i) {
+      return i < 64 ? __builtin_amdgcn_readlane(v0, i) : __builtin_amdgcn_readlane(v1, i - 64);
+    };
+    const int32_t cb = pick(c0, c1, bb), ce = pick(c0, c1, bb + 1);
+    const int32_t L = min(pick(s0, s1, bb), max_seq_len);
+    pos = min(L - (ce - cb) + (t - cb), L - 1);
+    b = bb;
+    return;
+  }
+  b = request_of_wave(cu_q, B, t);
+  pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
+}
+
 // Position of query token t of request b, clamped into [-1, max_seq_len-1].
 __device__ __forceinline__ int32_t query_pos(const int32_t* seq_lens,
                                              const int32_t* cu_q, int b,

@@ -919,7 +919,7 @@ struct MlaSharedWs {
   u32x4 xp[2][kHG][64];                 // probabilities [buffer][head group][lane]
   float xf[2][kH];                      // per-head rescale factors
   alignas(16) uint32_t xflag[2][kHG];   // per head group: its factors apply
-  float xl[kH];                         // per-head sums (epilogue)
+  float xl[kH];                         // per-head 1 / sum (epilogue)
   uint32_t counter;
 };
 static_assert(sizeof(MlaSharedWs) <= 160 * 1024, "LDS budget");
@@ -958,17 +958,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
   const int ntiles = jend > jbeg ? (jend - jbeg + kT - 1) / kT : 0;
   const int jpad = jbeg + ntiles * kT;
 
-  // Logit waves' queries first (they depend only on t): heads 16 hg + l16,
-  // dims 32 st + 8 g16 .. + 7 of K-step st.
-  bf16x8 qb[kQSteps];
-  if (logit) {
-    const int64_t qbase = (static_cast<int64_t>(t) * kH + 16 * hg + l16) * kD;
-#pragma unroll
-    for (int st = 0; st < kQSteps; ++st)
-      qb[st] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * st + 8 * g16);
-  }
-
-  // the split's physical rows and per-tile validity masks
+  // The split's physical rows and per-tile validity masks, in two memory
+  // round trips: the indices beside the request's place (cu_q and seq_lens
+  // read whole), then the block-table entries.  The logit waves' queries
+  // are requested only behind those (loads return in order: ahead of them
+  // the 72 KiB of queries would delay both trips).
   constexpr int kIdxPer = kWsSplitCap / kThreads;    // 2
   int32_t p[kIdxPer];
 #pragma unroll
@@ -976,8 +970,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
     const int j = jbeg + kThreads * i + tid;
     p[i] = j < jend ? idx_row[j] : -1;
   }
-  const int b = request_of_wave(cu_q, B, t);
-  const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
+  int b;
+  int32_t pos;
+  token_place(cu_q, seq_lens, B, t, max_seq_len, b, pos);
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
   int32_t bid[kIdxPer];
 #pragma unroll
@@ -985,6 +980,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
     const bool ok = p[i] >= 0 && p[i] <= pos && p[i] / block_size < max_blocks;
     bid[i] = ok ? bt_row[p[i] / block_size] : -1;
     if (!ok) p[i] = -1;
+  }
+  asm volatile("" ::: "memory");
+  // logit waves' queries: heads 16 hg + l16, dims 32 st + 8 g16 .. + 7 of
+  // K-step st
+  bf16x8 qb[kQSteps];
+  if (logit) {
+    const int64_t qbase = (static_cast<int64_t>(t) * kH + 16 * hg + l16) * kD;
+#pragma unroll
+    for (int st = 0; st < kQSteps; ++st)
+      qb[st] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * st + 8 * g16);
   }
 #pragma unroll
   for (int i = 0; i < kIdxPer; ++i) {
@@ -1133,7 +1138,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
     tile_barrier();                      // every P.V wave is done with the tiles
     const float l = sum_x16_x32(l_part);
     if (g16 == 0) {
-      sh.xl[16 * hg + l16] = l;
+      sh.xl[16 * hg + l16] = l > 0.0f ? 1.0f / l : 0.0f;      // the P.V waves scale by it
       const float lh = l > 0.0f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
       const int h = 16 * hg + l16;
       if (n_split > 1)
@@ -1235,8 +1240,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 16 * n + 4 * g16 + i;
-        const float l = sh.xl[h];
-        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+        const float inv = sh.xl[h];
 #pragma unroll
         for (int nt = 0; nt < kPvNT; ++nt) {
           const int d = 128 * pq + 16 * nt + l16;

@@ -48,6 +48,20 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts
+// within each 16-lane row, then the gfx9 row broadcasts (lane 15 of a row
+// into the next row, lane 31 into the upper half).  Lanes a move does not
+// reach keep 0, so each step adds only what lies below them.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xF, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xA, 0xF, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xC, 0xF, false));
+  return v;
+}
+
 // Cross-lane reductions inside a wave with VALU moves only (no LDS round
 // trip, unlike a shuffle): DPP permutations inside each 16-lane row (lane
 // l ^ 1, l ^ 2, then the half-row and row mirrors), then gfx950's permlane

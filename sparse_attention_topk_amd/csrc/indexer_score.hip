@@ -124,8 +124,15 @@ __device__ __forceinline__ void wait_tile(int later) {
 // other's stream.
 // QF8: e4m3 queries (rotated, quantised per head, q_scale per token and
 // head) against an e4m3 cache, contracted on the fp8 matrix cores.
-template <int TQ, int MT, bool F8, int MAXT, bool QF8 = false>
-__global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
+// SPAN: launches of several rounds over requests of one query token each
+// (long varlen rows).  A fixed grid of workgroups (two per CU) splits the
+// batch's key tiles evenly: the requests' tiles, each request's rounded up
+// to whole 128-key range chunks, are laid end to end and workgroup g takes
+// the g-th equal share, in pieces of up to 4 MAXT tiles.  No workgroup is
+// launched without work and they all finish together; the score ranges
+// (for the top-k's long rows) are then recorded per 32-key tile.
+template <int TQ, int MT, bool F8, int MAXT, bool QF8 = false, bool SPAN = false>
+__global__ __launch_bounds__(256, MAXT <= 32 ? 2 : 1) void k_score_dma(
     const uint16_t* __restrict__ q, const float* __restrict__ qscale,
     const float* __restrict__ w,
     const uint8_t* __restrict__ kc, const float* __restrict__ kscale,
@@ -133,8 +140,8 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ block_table,
     int32_t max_blocks, int32_t block_size, int64_t num_slots,
     int32_t max_seq_len, int32_t qblocks_per_req, int32_t nchunks,
-    int32_t tiles_per_wave, float* __restrict__ scores, int64_t row_stride,
-    float2* __restrict__ crange, int32_t range_stride) {
+    int32_t tiles_per_wave_arg, float* __restrict__ scores, int64_t row_stride,
+    float2* __restrict__ crange, int32_t range_stride, int32_t B) {
   constexpr int H = 32 * MT;
   static_assert(!QF8 || F8, "e4m3 queries go with an e4m3 cache");
   using DT = DmaTile<F8>;
@@ -149,10 +156,12 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   const int hf = lane >> 5;
   const int col = lane & 31;
 
-  const int chunk = blockIdx.x % nchunks;
-  const int qbg = blockIdx.x / nchunks;
-  const int b = qbg / qblocks_per_req;
-  const int qb = qbg % qblocks_per_req;
+  static_assert(!SPAN || TQ == 1, "spans cover requests of one query token");
+  // One chunk: the tiles from key_beg up to key_lim (and the query block's
+  // last position) of request b, query block qb, tiles_per_wave per wave.
+  // chunk: its index among the request's range chunks (non-SPAN).
+  auto run = [&](const int b, const int qb, const int32_t key_beg, const int tiles_per_wave,
+                 const int32_t key_lim, const int chunk) {
   const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
 
   // The wave's tiles are first_tile + kWaves i, i < ntiles (<= 64).  A
@@ -164,8 +173,6 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   // chunk, so the load is issued first, beside the request's length and
   // query range, rather than behind them: the first tile's address then
   // waits for one memory round trip instead of two.
-  const int32_t chunk_keys = kTile * kWaves * tiles_per_wave;
-  const int32_t key_beg = chunk * chunk_keys;
   const int first_tile = key_beg / kTile + wave;
   int32_t bid_lane = -1;
   {
@@ -180,7 +187,7 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
   if (t0 >= qlen) return;
   const int nt = min(TQ, qlen - t0);
   const int32_t pos0 = L - qlen + t0;
-  const int32_t key_end = min(pos0 + nt, (chunk + 1) * chunk_keys);
+  const int32_t key_end = min(pos0 + nt, key_lim);
   if (key_beg >= key_end) return;
   const int end_tile = (key_end + kTile - 1) / kTile;
   const int ntiles = end_tile > first_tile
@@ -420,18 +427,29 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
       if (my_r0 < 0) v = 0.0f;
       if (crange) {   // uniform: recorded only for batches of long rows
         const bool causal = (first_tile + kWaves * i) * kTile + col <= my_pos;
-        rmin = fminf(rmin, causal ? v : INFINITY);
-        rmax = fmaxf(rmax, causal ? v : -INFINITY);
+        if constexpr (SPAN) {
+          // one entry per tile: range chunks of 128 keys, one part per tile
+          float lo = causal ? v : INFINITY, hi = causal ? v : -INFINITY;
+          half_minmax(lo, hi);
+          if (col == 0 && hf < nt)
+            crange[(tbeg + t0 + hf) * static_cast<int64_t>(range_stride) + first_tile +
+                   kWaves * i] = make_float2(lo, hi);
+        } else {
+          rmin = fminf(rmin, causal ? v : INFINITY);
+          rmax = fmaxf(rmax, causal ? v : -INFINITY);
+        }
       }
       if (hf < TQ) sc[hf < TQ ? hf : 0][(kWaves * i + wave) * kTile + col] = v;
     });
   }
 
   // ---- the wave's range entries: one per token of the block
-  if (crange) half_minmax(rmin, rmax);
-  if (crange && col == 0 && hf < nt)
-    crange[(tbeg + t0 + hf) * static_cast<int64_t>(range_stride) + chunk * kRangeParts + wave] =
-        make_float2(rmin, rmax);
+  if constexpr (!SPAN) {
+    if (crange) half_minmax(rmin, rmax);
+    if (crange && col == 0 && hf < nt)
+      crange[(tbeg + t0 + hf) * static_cast<int64_t>(range_stride) + chunk * kRangeParts + wave] =
+          make_float2(rmin, rmax);
+  }
 
   // ---- write the chunk's scores: token tt, keys key_beg .. key_end - 1
   // (up to the next multiple of 4, inside the padded row), 16 bytes per
@@ -445,23 +463,102 @@ __global__ __launch_bounds__(256, MAXT <= 16 ? 2 : 1) void k_score_dma(
     for (int c = threadIdx.x; c < n4; c += 256)
       reinterpret_cast<float4*>(row)[c] = reinterpret_cast<const float4*>(&sc[tt][0])[c];
   }
+  };   // run
+
+  if constexpr (SPAN) {
+    // tiles of request bb: its keys rounded up to whole 128-key chunks, or
+    // none without a query token
+    auto tiles_of = [&](int bb) -> uint32_t {
+      if (bb >= B) return 0u;
+      const int32_t L = min(seq_lens[bb], max_seq_len);
+      const int32_t ql = cu_q[bb + 1] - cu_q[bb];
+      return (ql > 0 && L > 0) ? static_cast<uint32_t>((L + 127) / 128 * 4) : 0u;
+    };
+    uint32_t total = 0;
+    for (int b0 = 0; b0 < B; b0 += 64)
+      total += __builtin_amdgcn_readlane(wave_scan_incl(tiles_of(b0 + lane)), 63);
+    const uint32_t beg = static_cast<uint32_t>(
+        static_cast<uint64_t>(blockIdx.x) * total / gridDim.x);
+    const uint32_t end = static_cast<uint32_t>(
+        static_cast<uint64_t>(blockIdx.x + 1) * total / gridDim.x);
+    uint32_t base = 0;           // tiles of the requests before b0
+    for (int b0 = 0; b0 < B && base < end; b0 += 64) {
+      const uint32_t n = tiles_of(b0 + lane);
+      const uint32_t incl = wave_scan_incl(n);
+      const uint32_t st = base + incl - n;
+      uint64_t m = __ballot(n > 0 && st < end && st + n > beg);
+      while (m) {
+        const int i = __builtin_ctzll(m);
+        m &= m - 1;
+        const uint32_t s_b = __builtin_amdgcn_readlane(st, i);
+        const uint32_t n_b = __builtin_amdgcn_readlane(n, i);
+        const uint32_t lt1 = min(end, s_b + n_b) - s_b;
+        for (uint32_t lt = max(beg, s_b) - s_b; lt < lt1; lt += kWaves * MAXT) {
+          const int cnt = static_cast<int>(min(lt1 - lt, static_cast<uint32_t>(kWaves * MAXT)));
+          run(b0 + i, 0, static_cast<int32_t>(lt) * kTile, (cnt + kWaves - 1) / kWaves,
+              static_cast<int32_t>(lt + cnt) * kTile, 0);
+          if (crange) {
+            // the piece's tiles past the row (up to its last 128-key chunk):
+            // empty ranges, so the top-k reads no stale entry
+            const int bb = b0 + i;
+            const uint32_t first_pad =
+                static_cast<uint32_t>((min(seq_lens[bb], max_seq_len) + kTile - 1) / kTile);
+            const int64_t rrow = static_cast<int64_t>(cu_q[bb]) * range_stride;
+            for (uint32_t tt = max(lt, first_pad) + threadIdx.x; tt < lt + cnt; tt += 256)
+              crange[rrow + tt] = make_float2(INFINITY, -INFINITY);
+          }
+          lds_barrier();           // the scores' LDS is free for the next piece
+        }
+      }
+      base += __builtin_amdgcn_readlane(incl, 63);
+    }
+  } else {
+    const int chunk = blockIdx.x % nchunks;
+    const int qbg = blockIdx.x / nchunks;
+    const int32_t chunk_keys = kTile * kWaves * tiles_per_wave_arg;
+    run(qbg / qblocks_per_req, qbg % qblocks_per_req, chunk * chunk_keys, tiles_per_wave_arg,
+        (chunk + 1) * chunk_keys, chunk);
+  }
 }
 
-template <int TQ, int MT, bool F8, int MAXT, bool QF8>
+// compute units of the current device (cached per device)
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int TQ, int MT, bool F8, int MAXT, bool QF8, bool SPAN = false>
 hipError_t launch_dma_t(IndexerArgs& a, int qbpr, int nchunks, int64_t tpw,
                         hipStream_t stream) {
   const dsa_batch& b = a.b;
-  // the range layout the top-k reads: kRangeParts entries per chunk
-  a.chunk_keys = static_cast<int32_t>(kTile * kWaves * tpw);
-  a.range_stride = nchunks * kRangeParts;
-  const int64_t grid = static_cast<int64_t>(b.num_reqs) * qbpr * nchunks;
+  int64_t grid;
+  if constexpr (SPAN) {
+    // per-tile range entries: chunks of 128 keys, one part per 32-key tile
+    a.chunk_keys = 4 * kTile;
+    a.range_stride = (b.max_seq_len + 4 * kTile - 1) / (4 * kTile) * kRangeParts;
+    grid = 2 * static_cast<int64_t>(device_cus());
+  } else {
+    // the range layout the top-k reads: kRangeParts entries per chunk
+    a.chunk_keys = static_cast<int32_t>(kTile * kWaves * tpw);
+    a.range_stride = nchunks * kRangeParts;
+    grid = static_cast<int64_t>(b.num_reqs) * qbpr * nchunks;
+  }
   if (grid == 0) return hipSuccess;
-  k_score_dma<TQ, MT, F8, MAXT, QF8><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
+  k_score_dma<TQ, MT, F8, MAXT, QF8, SPAN><<<static_cast<unsigned>(grid), 256, 0, stream>>>(
       static_cast<const uint16_t*>(a.q), a.q_scale, a.w,
       static_cast<const uint8_t*>(a.k_cache), a.k_scale, b.seq_lens, b.cu_q,
       b.block_table, b.max_blocks, b.block_size, b.num_slots, b.max_seq_len,
       qbpr, nchunks, static_cast<int32_t>(tpw), a.scores, a.row_stride, a.chunk_range,
-      a.range_stride);
+      a.range_stride, b.num_reqs);
   return hipGetLastError();
 }
 
@@ -478,14 +575,11 @@ hipError_t launch_dma(IndexerArgs& a, hipStream_t stream) {
   if (tpw < 1) tpw = 1;
   if (tpw > kMaxTpw) tpw = kMaxTpw;        // one block id per lane
   int nchunks = static_cast<int>((tiles_total + tpw * kWaves - 1) / (tpw * kWaves));
-  // several rounds: smaller workgroups, two per CU, where the registers
-  // allow it (one query token, one head group, e4m3 keys)
+  // several rounds of single-token requests (long varlen rows, e4m3 keys):
+  // an even split of the batch's tiles over two workgroups per CU
   if constexpr (TQ == 1 && MT == 1 && F8) {
-    if (groups * nchunks > 256 && tpw > 16) {
-      tpw = 16;
-      nchunks = static_cast<int>((tiles_total + tpw * kWaves - 1) / (tpw * kWaves));
-      return launch_dma_t<TQ, MT, F8, 16, QF8>(a, qbpr, nchunks, tpw, stream);
-    }
+    if (groups * nchunks > 256 && tpw > 16)
+      return launch_dma_t<TQ, MT, F8, 32, QF8, true>(a, qbpr, nchunks, tpw, stream);
   }
   return launch_dma_t<TQ, MT, F8, kMaxTpw, QF8>(a, qbpr, nchunks, tpw, stream);
 }

@@ -77,20 +77,6 @@ __device__ __forceinline__ uint64_t lanes_below() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts
-// within each 16-lane row, then the gfx9 row broadcasts (lane 15 of a row
-// into the next row, lane 31 into the upper half).  Lanes a move does not
-// reach keep 0, so each step adds only what lies below them.
-__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xF, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xF, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xF, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xF, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xA, 0xF, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xC, 0xF, false));
-  return v;
-}
-
 // Suffix scan helper: for a 256-bin histogram find digit d with
 // above(d) < r <= above(d) + h[d] (above = sum of higher bins).  Wave 0
 // scans; results land in s.digit / s.digit_above.

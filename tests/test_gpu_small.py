@@ -201,6 +201,46 @@ def test_fp8_cache_including_row_longer_than_lds(dsa):
     assert r >= 0.999
 
 
+def test_fp8_varlen_even_split_of_tiles(dsa):
+    """Many single-token requests over long, ragged e4m3 caches, as the
+    varlen decode workload has: the score pass splits the batch's key tiles
+    evenly over a fixed grid, so pieces start and end inside requests, rows
+    are padded to whole 128-key range chunks, and requests past the top-k's
+    register reach get per-tile score ranges.  A request without a query
+    token and one of a single key sit between the others.  Every row against
+    the oracle."""
+    g = np.random.default_rng(7)
+    lens = [int(x) for x in g.integers(100, 40000, size=64)]
+    lens[3], lens[4], lens[5] = 1, 32769, 39999
+    q_lens = [1] * 64
+    q_lens[9] = 0
+    cfg = _small_cfg(num_reqs=64, q_len=1, idx_cache_dtype="fp8", topk=2048)
+    b = make_batch(cfg, DEV, seq_lens=lens, q_lens=q_lens)
+    lay = make_layer(cfg, b, DEV)
+    cache = torch.zeros((b.num_slots, 128), dtype=torch.uint8, device=DEV)
+    scale = torch.zeros((b.num_slots,), dtype=torch.float32, device=DEV)
+    all_slots = torch.arange(b.num_slots, dtype=torch.int64, device=DEV)
+    dsa.dsa_indexer_cache_write(lay.k_src, all_slots, cache, scale)
+    idx = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), lay.q_idx, lay.w, cache, scale, 2048)
+    torch.cuda.synchronize()
+    # the oracle's own codes of the same keys (the cache must hold them)
+    codes, scales = OI.fp8_quantize_rows(np_f64(lay.k_src).astype(np.float32))
+    assert np.array_equal(np_bits(cache), codes)
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), scales.view(np.uint32))
+    ref = _oracle_topk(b, lay, cfg, codes, scales, OI.FP8, 2048)
+    got = idx.cpu().numpy()
+    t = 0
+    for bi in range(b.num_reqs):
+        for _ in range(b.q_lens[bi]):
+            pos = b.seq_lens[bi] - 1
+            check_row_invariants(got[t], pos, 2048)
+            if pos + 1 <= 2048:
+                assert np.array_equal(got[t], ref[t])
+            t += 1
+    r, worst = recall(got, ref)
+    assert r >= 0.999, (r, worst)
+
+
 def _crafted(dsa, L, topk, kind):
     """One request, one query, crafted so the scores are degenerate."""
     cfg = _small_cfg(num_reqs=1, q_len=1, topk=topk)

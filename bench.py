@@ -145,7 +145,7 @@ def cache_write_bytes(b, cfg):
 # ------------------------------------------------------------------ traffic
 CSRC = os.path.join(ROOT, "sparse_attention_topk_amd", "csrc")
 # the dominant call's kernels, and the sources they are built from
-INDEXER_KERNELS = ("k_score_dma", "k_topk")
+INDEXER_KERNELS = ("k_score_dma", "k_score_prefill", "k_topk", "k_topk_reg")
 INDEXER_SRCS = ("common.h", "indexer_score.hip", "topk.hip")
 CALIB_ELEMS = 1 << 28          # calibration: fp32 -> bf16 conversion of 1 GiB
 CALIB_READ, CALIB_WRITE = CALIB_ELEMS * 4, CALIB_ELEMS * 2
@@ -628,7 +628,7 @@ def main():
     ix_ms, ml_ms = calls["indexer_topk"]["median_ms"], calls["sparse_mla_attn"]["median_ms"]
     if prefill:
         # latent rows and keys stay cache-resident: matrix-core bound
-        roof = (mfma_roofline("sparse_mla_attn (k_mla_mfma)", mfl, ml_ms) if ml_ms >= ix_ms
+        roof = (mfma_roofline("sparse_mla_attn (k_mla_mfma: one workgroup per token)", mfl, ml_ms) if ml_ms >= ix_ms
                 else mfma_roofline("dsa_indexer_topk", ifl, ix_ms))
     elif cfg.idx_q_fp8:
         roof = hbm_roofline("dsa_rotate_quantize (queries) + dsa_indexer_topk_fp8q", ib, ix_ms)
@@ -746,7 +746,7 @@ def bench_indexshare(args, cfg, b, bb, dsa, torch, stream):
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": cfg.name, "layers": types, "requests": b.num_reqs,
                    "max_context": b.max_seq_len, "query_tokens": N, "topk": cfg.topk},
-        "roofline": hbm_roofline("sparse_mla_attn (k_mla_mfma), one layer", mb,
+        "roofline": hbm_roofline("sparse_mla_attn (k_mla_ws: four key splits per token), one layer", mb,
                                  ml["median_ms"]),
         "timing": {"protocol": "median over K reps, caches evicted before each rep, one "
                                "HIP event pair (no system fence) per rep", "stack": st},

@@ -628,7 +628,7 @@ def main():
     ix_ms, ml_ms = calls["indexer_topk"]["median_ms"], calls["sparse_mla_attn"]["median_ms"]
     if prefill:
         # latent rows and keys stay cache-resident: matrix-core bound
-        roof = (mfma_roofline("sparse_mla_attn (k_mla_mfma: one workgroup per token)", mfl, ml_ms) if ml_ms >= ix_ms
+        roof = (mfma_roofline("sparse_mla_attn (k_mla_prefill: one workgroup per token)", mfl, ml_ms) if ml_ms >= ix_ms
                 else mfma_roofline("dsa_indexer_topk", ifl, ix_ms))
     elif cfg.idx_q_fp8:
         roof = hbm_roofline("dsa_rotate_quantize (queries) + dsa_indexer_topk_fp8q", ib, ix_ms)

@@ -33,6 +33,11 @@ EXTRA = {
     # the prefill score kernel keeps its MFMA accumulators in VGPRs, where
     # the ReLU-weighted head sum reads them without accumulator moves
     "indexer_prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+    # the one-token-per-workgroup attention keeps its queries (the logits'
+    # B operands) in accumulator registers and its MFMA accumulators in
+    # VGPRs; in the default form the queries spill into copies around every
+    # MFMA.  The file's other kernels measure the same either way.
+    "sparse_mla.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -11,33 +11,23 @@
 //     out[t, h, :] = sum_j softmax_j(z[h, :]) * kv[j, 0:R]
 //     lse[t, h] = log sum_j exp z[h, j]
 //
-// Matrix-core path (bf16, R = 512, P = 64, 64 heads): one workgroup per
+// Matrix-core paths (bf16, R = 512, P = 64, 64 heads): one workgroup per
 // (query token, key split) covers all 64 heads, so every selected latent row
-// crosses HBM once per token.  Rows are gathered in 32-row tiles straight
-// from HBM into LDS (global_load_lds_dwordx4) through a ring of four tile
-// buffers (whole 128-byte lines per DMA instruction): three tiles are in
-// flight while one is multiplied.  Eight waves, two per SIMD; the first
-// four also issue the tile DMAs, so when one of them waits for room in the
-// memory queue the other wave on its SIMD keeps the matrix core busy:
-//   logits: wave w = 2 hg + kh: the 16 keys 16 kh .. 16 kh + 15 of the tile
-//           against the 16 heads of head group hg over all 576 dims
-//           (v_mfma_f32_16x16x32_bf16, queries in registers), so each tile
-//           row is read from LDS by four waves;
-//   softmax: the two waves of a head group swap their per-head maxima and
-//           publish their bf16 probabilities in LDS; the reference maximum
-//           moves rarely (only when a tile beats it by more than 64 in
-//           base-2 log units), so the common tile needs no rescale of the
-//           accumulators;
-//   P.V:    wave w = 4 php + pq: the 32 heads of head groups 2 php and
-//           2 php + 1 over value dims 128 pq .. 128 pq + 127 and all 32
-//           keys; each value fragment, read with the gfx950 LDS transpose
-//           load straight from the row-major tile, feeds two MFMAs (one per
-//           head group), so each value element is read by two waves instead
-//           of four.
-// With more than one key split, each split writes its normalised partial
-// output and log-sum-exp, and the split that finishes last merges them by
-// LSE weights (splits of a token are placed on one XCD, so the partials it
-// reads back are still in that XCD's L2).
+// crosses HBM once per token.  Rows are gathered into LDS straight from
+// memory (global_load_lds_dwordx4, whole 128-byte lines per instruction).
+//   k_mla_ws: splits of up to 1,024 indices (decode: a few tokens, many
+//     splits).  32-row tiles in a ring of four; eight waves, warp
+//     specialised: four logit waves on tile k, four P.V waves on tile k - 1.
+//   k_mla_prefill: up to 2,048 indices per workgroup (many tokens, one split,
+//     or long splits).  64-row tiles, two in LDS; four waves, each doing its
+//     share of the logits, softmax and P.V on v_mfma_f32_32x32x16_bf16.
+// Both keep a per-head reference maximum that a later key may exceed by a
+// fixed slack before it moves; a move rescales the running sums and
+// accumulators in place, so each tile is processed once.  With more than
+// one key split, each split writes its normalised partial output and
+// log-sum-exp, and the split that finishes last merges them by LSE weights
+// (splits of a token are placed on one XCD, so the partials it reads back
+// are still in that XCD's L2).
 //
 // Vector path (fp32 or other shapes): one workgroup per (token, head),
 // fp32 arithmetic, logits in LDS.
@@ -56,7 +46,6 @@ constexpr int kHT = 1;                  // 16-head tiles per wave
 constexpr int kHG = kH / (16 * kHT);    // head groups (4)
 constexpr int kWavesM = 2 * kHG;        // waves: head group x key half (8, two per SIMD)
 constexpr int kThreads = 64 * kWavesM;  // 512
-constexpr int kPvHT = 2;                // 16-head tiles per wave in P.V
 constexpr int kPvNT = kR / 4 / 16;      // 16-dim tiles per wave in P.V (128 dims)
 constexpr int kDmaWaves = 4;            // waves that issue the tile DMAs
 constexpr int kPieces = kD / 8;         // 16-byte pieces per latent row (72)
@@ -76,20 +65,6 @@ constexpr float kMoveSlack = 64.0f;
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
-
-struct MlaShared {
-  uint16_t k[kBufs][kT * kD];           // row-major tiles, 4 x 36864 B
-  int32_t slots[kMaxSplitLen];          // physical row of each index, or -1
-  uint32_t vbits[kMaxSplitLen / kT];    // per tile: bit k = key k has a row
-  u32x2 xp[kWavesM][kHT][64];           // bf16 probabilities, per wave / head tile / lane
-  float xm[kWavesM][kHT][64];           // per-head tile maxima (sums at the end)
-  alignas(16) uint32_t xf[kWavesM];     // per wave: a reference maximum moves
-  alignas(16) uint32_t xr[kWavesM];     // per wave: the split must restart
-  uint32_t counter;
-};
-static_assert(sizeof(MlaShared) <= 160 * 1024, "LDS budget");
-static_assert(kH * (kR * 2 + 16) + (kMaxSplits + 1) * kH * 4 <= sizeof(MlaShared::k),
-              "staged partials and merge weights fit in the tile buffers");
 
 // fp32 -> bf16, round to nearest even, with gfx950's conversion
 // instruction (v_cvt_pk_bf16_f32: two values per instruction)
@@ -136,6 +111,18 @@ template <int OFF>
 __device__ __forceinline__ v4i16 tr_load(uint32_t addr) {
   v4i16 r;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t b32_load(uint32_t addr) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 u128_load(uint32_t addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "n"(OFF));
   return r;
 }
 template <int OFF>
@@ -200,15 +187,7 @@ __device__ __forceinline__ float sum_x16_x32(float x) {
 // before, counts as no arrival.  A compare-and-swap fails only when another
 // split of the token changed the word after it was read, which each of them
 // does once, so the loop ends within n_split + 1 rounds (the first may
-// fail on the guess below).
-__device__ __forceinline__ float lo_f(unsigned long long u) {
-  return __uint_as_float(static_cast<uint32_t>(u));
-}
-__device__ __forceinline__ float hi_f(unsigned long long u) {
-  return __uint_as_float(static_cast<uint32_t>(u >> 32));
-}
-
-// The first compare-and-swap guesses that every other split has already
+// fail on the guess below).  The first compare-and-swap guesses that every other split has already
 // counted, so the split that arrives last (the one that merges, on the
 // kernel's critical path) usually needs a single round trip; a wrong guess
 // costs the others one more.
@@ -250,24 +229,7 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// whether any wave's flag word is set (kWavesM words, 16-byte aligned)
-__device__ __forceinline__ bool any_word(const uint32_t* w) {
-  static_assert(kWavesM % 4 == 0, "flag words are read four at a time");
-  uint32_t o = 0;
-#pragma unroll
-  for (int i = 0; i < kWavesM; i += 4) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(w + i);
-    o |= v[0] | v[1] | v[2] | v[3];
-  }
-  return o != 0;
-}
 
-__device__ __forceinline__ u32x2 pack_bf16x4(const float* p) {
-  u32x2 r;
-  r[0] = pack2_bf16(p[0], p[1]);
-  r[1] = pack2_bf16(p[2], p[3]);
-  return r;
-}
 
 // The workgroup's staged result leaves it.  stage holds the normalised
 // bf16 rows of its 64 heads (head h at byte h * kRowB, kRowB = 2 R + 16),
@@ -277,6 +239,7 @@ __device__ __forceinline__ u32x2 pack_bf16x4(const float* p) {
 // word merges all of them.  Every thread of the workgroup calls it; stage
 // must have room behind the rows for the merge weights.
 constexpr int kRowB = kR * 2 + 16;
+template <int NT>
 __device__ __forceinline__ void mla_store_or_merge(
     uint8_t* stage, uint32_t* counter, int t, int split, int n_split, bool partial,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
@@ -291,7 +254,7 @@ __device__ __forceinline__ void mla_store_or_merge(
     constexpr int row_pieces = kR * 2 / 16;
     constexpr int total = kH * row_pieces;
     u32x4* dst = reinterpret_cast<u32x4*>(out + static_cast<int64_t>(t) * kH * kR);
-    for (int c = tid; c < total; c += kThreads) {
+    for (int c = tid; c < total; c += NT) {
       const int h = c / row_pieces, pc = c % row_pieces;
       dst[c] = *reinterpret_cast<const u32x4*>(stage + h * row_b + 16 * pc);
     }
@@ -305,7 +268,7 @@ __device__ __forceinline__ void mla_store_or_merge(
   // so every store instruction writes four whole 128-byte lines: thread tid
   // takes word tid % 128 of head rows tid / 128 + 2 i.
   constexpr int kWords = kR / 4;                   // 8-byte words per head row
-  constexpr int kRowsPer = kThreads / kWords;      // head rows per pass (4)
+  constexpr int kRowsPer = NT / kWords;            // head rows per pass
   const int wq = tid % kWords;
   const int h0 = tid / kWords;
   unsigned long long* dst = reinterpret_cast<unsigned long long*>(
@@ -366,7 +329,7 @@ __device__ __forceinline__ void mla_store_or_merge(
   // split weights exp(lse_s - max) per head in place of the log-sum-exps,
   // then 1 / their sum, behind the staged block
   float* wt = reinterpret_cast<float*>(stage + kH * row_b);
-  for (int c = tid; c < n_split * kH; c += kThreads)
+  for (int c = tid; c < n_split * kH; c += NT)
     wt[c] = __hip_atomic_load(part_lse + static_cast<int64_t>(t) * n_split * kH + c,
                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
@@ -448,449 +411,6 @@ __device__ __forceinline__ void mla_store_or_merge(
   if (tid == 0) __hip_atomic_store(arrivals + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup = (query token, key split), all 64 heads, kWavesM waves (two
-// per SIMD).  Logits and softmax: wave w = 2 hg + kh, heads 16 kHT hg .. in
-// kHT 16-head tiles n (head 16 kHT hg + 16 n + lane % 16 in the query
-// operand).  P.V: wave w = 4 php + pq, heads 32 php .. 32 php + 31.
-//   logits:  S^T[16 keys, 16 heads] = K . Q^T per head tile over 18 K-steps,
-//            keys 16 kh + 4 g16 + i on the rows (lane group g16 = lane / 16),
-//            so lane (l16, g16) holds head l16's logits of 4 keys;
-//   softmax: max over the wave's 16 keys in-lane plus two permlane swaps,
-//            then the partner wave's (2 hg + 1 - kh) maxima through LDS;
-//   P.V:     O[16 heads, 16 dims] += P[16 heads, 32 keys] . V[32 keys, 16 dims]
-//            for each of the wave's two head tiles, with K-index 8 g16 + e =
-//            key 4 g16 + e (e < 4) or key 16 + 4 g16 + e - 4: lane (l16, g16)
-//            of the P operand takes the 4 probabilities that lane holds in
-//            the head group's kh = 0 wave, then those of its kh = 1 wave
-//            (both from LDS), and two transpose loads of rows 4 g16 + c and
-//            16 + 4 g16 + c give the value operand in the same key order.
-__global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
-    const int32_t* __restrict__ topk_idx, int32_t topk, int32_t n_tokens,
-    int32_t n_split, int32_t split_len, float scale_log2,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
-    int32_t B, const int32_t* __restrict__ block_table, int32_t max_blocks,
-    int32_t block_size, int64_t num_slots, int32_t max_seq_len,
-    uint16_t* __restrict__ out, float* __restrict__ lse,
-    uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-    unsigned long long* __restrict__ arrivals, unsigned long long call_tag) {
-  __shared__ MlaShared sh;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  // wave-uniform values live in scalar registers
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15;
-  const int g16 = lane >> 4;
-  const int hg = wave >> 1;             // heads 16 kHT hg .. 16 kHT hg + 16 kHT - 1
-  const int kh = wave & 1;
-  const int partner = wave ^ 1;
-
-  // Workgroups are dealt to the eight XCDs in turn (workgroup i to XCD
-  // i % 8); with a grid that divides by 8, the splits of a token take
-  // consecutive places in one XCD's share.
-  int vb = blockIdx.x;
-  if (n_split > 1 && (gridDim.x & 7) == 0)
-    vb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  const int t = vb / n_split;
-  const int split = vb % n_split;
-  if (t >= n_tokens) return;
-
-  const int32_t* idx_row = topk_idx + static_cast<int64_t>(t) * topk;
-  const int jbeg = split * split_len;
-  const int jend = min(topk, jbeg + split_len);
-  const int ntiles = jend > jbeg ? (jend - jbeg + kT - 1) / kT : 0;
-  const int jpad = jbeg + ntiles * kT;           // tile-aligned end
-
-  // Index loads first: they depend only on t.
-  constexpr int kIdxPer = kMaxSplitLen / kThreads;   // 4
-  int32_t p[kIdxPer];
-#pragma unroll
-  for (int i = 0; i < kIdxPer; ++i) {
-    const int j = jbeg + kThreads * i + tid;
-    p[i] = j < jend ? idx_row[j] : -1;
-  }
-  const int b = request_of_wave(cu_q, B, t);
-  const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
-  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
-  int32_t bid[kIdxPer];
-#pragma unroll
-  for (int i = 0; i < kIdxPer; ++i) {
-    const bool ok = p[i] >= 0 && p[i] <= pos && p[i] / block_size < max_blocks;
-    bid[i] = ok ? bt_row[p[i] / block_size] : -1;
-    if (!ok) p[i] = -1;
-  }
-
-  // Physical row of every index of this split (padded with -1 to whole
-  // tiles) and a 32-bit validity mask per tile, in LDS.
-#pragma unroll
-  for (int i = 0; i < kIdxPer; ++i) {
-    const int j = jbeg + kThreads * i + tid;      // a wave covers 64 aligned j
-    int32_t slot = -1;
-    if (p[i] >= 0) {
-      const int64_t s = static_cast<int64_t>(bid[i]) * block_size + p[i] % block_size;
-      slot = (s >= 0 && s < num_slots) ? static_cast<int32_t>(s) : -1;
-    }
-    if (j < jpad) sh.slots[j - jbeg] = slot;
-    const uint64_t m = __ballot(j < jpad && slot >= 0);
-    const int tw = (kThreads * i + 64 * wave) / kT;
-    if (lane == 0 && tw < ntiles) sh.vbits[tw] = static_cast<uint32_t>(m);
-    if (lane == 0 && tw + 1 < ntiles) sh.vbits[tw + 1] = static_cast<uint32_t>(m >> 32);
-  }
-  tile_barrier();
-
-  static_assert(kQSteps / 4 == 4 && kPvNT == 8 && kDmaPerWave == 9 && kHT == 1,
-                "the refill pieces 0..3 follow logit K-steps, 4..8 P.V dim tiles");
-  // DMA of local tile `tile` into buffer `buf`: wave w < kDmaWaves fills
-  // row group h = w, one instruction per piece group g (the other waves
-  // issue none).  Keys without a row load row 0 (finite cache data) and are
-  // masked out of the softmax.
-  const int dpi = (lane >> 3) ^ (wave & 1);
-  const int drow = 8 * wave + ((lane & 7) ^ (4 * (dpi & 1)));
-  const uint32_t dcol = 16u * static_cast<uint32_t>(dpi);
-  auto dma = [&](int tile, uint16_t* buf) {
-    if (wave >= kDmaWaves) return;
-    const int32_t sl = sh.slots[tile * kT + drow];
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(kv) +
-                         static_cast<uint64_t>(max(sl, 0)) * (2 * kD) + dcol;
-    uint8_t* dst = reinterpret_cast<uint8_t*>(buf) + 9216 * wave;
-    static_for<kDmaPerWave>([&](auto g) {
-      constexpr int G = decltype(g)::value;
-      __builtin_amdgcn_global_load_lds(
-          src + 128 * G, (__attribute__((address_space(3))) void*)(dst + 1024 * G), 16, 0, 0);
-    });
-  };
-
-  // Per-lane LDS byte offsets inside a tile buffer.  Logits: the lane's key
-  // row 16 kh + l16, even / odd K-steps.  Values: transpose-load rows
-  // 4 g16 + l16 / 4 (keys 0..15, a) and 16 + 4 g16 + l16 / 4 (keys 16..31,
-  // b) at dims 128 pq + 16 nt + 4 (l16 & 3), for nt & 3 = m.
-  const int krow = 16 * kh + l16;
-  const uint32_t kodd[2] = {tile_byte(krow, g16), tile_byte(krow, 4 + g16)};
-  const int php = wave >> 2;            // P.V: head groups 2 php, 2 php + 1
-  const int pq = wave & 3;              // P.V: value dims 128 pq .. 128 pq + 127
-  const int vrow_a = 4 * g16 + (l16 >> 2);
-  const int vrow_b = 16 + vrow_a;
-  const int vb_lo = (l16 & 3) >> 1;
-  uint32_t voff_a[4], voff_b[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    // piece 16 pq + 2 m + vb_lo (+ 8 (nt >> 2) as an immediate), half l16 & 1
-    const uint32_t half = 8u * static_cast<uint32_t>(l16 & 1);
-    voff_a[m] = tile_byte(vrow_a, 16 * pq + 2 * m + vb_lo) + half;
-    voff_b[m] = tile_byte(vrow_b, 16 * pq + 2 * m + vb_lo) + half;
-  }
-
-  f32x4 o[kPvHT][kPvNT];                  // heads 32 php + 16 n + 4 g16 + i, dims 128 pq + 16 nt + l16
-#pragma unroll
-  for (int n = 0; n < kPvHT; ++n)
-#pragma unroll
-    for (int nt = 0; nt < kPvNT; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
-  float m_ref[kHT], l_part[kHT];   // head 16 kHT hg + 16 n + l16: reference, this lane's sum
-#pragma unroll
-  for (int n = 0; n < kHT; ++n) {
-    m_ref[n] = -INFINITY;
-    l_part[n] = 0.0f;
-  }
-
-#pragma unroll
-  for (int i = 0; i < kBufs - 1; ++i)
-    if (i < ntiles) dma(i, sh.k[i]);
-
-  // The query rows (logit B operand: head 16 kHT hg + 16 n + l16, dims
-  // 32 st + 8 g16 .. +8) are loaded behind the first tiles' DMAs, so their
-  // 72 KB overlap the tiles' latency instead of delaying the slot table and
-  // the first DMAs.  The wait for them also covers those tiles (the count
-  // is in issue order), which land at about the same time; the registers
-  // are then re-defined by an empty asm, so the compiler's wait tracking
-  // no longer ties the logits of every tile to outstanding loads.
-  bf16x8 qb[kHT][kQSteps];
-#pragma unroll
-  for (int n = 0; n < kHT; ++n) {
-    const int64_t qbase = (static_cast<int64_t>(t) * kH + 16 * kHT * hg + 16 * n + l16) * kD;
-#pragma unroll
-    for (int s = 0; s < kQSteps; ++s)
-      qb[n][s] = *reinterpret_cast<const bf16x8*>(q + qbase + 32 * s + 8 * g16);
-  }
-  wait_vm<0>();
-#pragma unroll
-  for (int n = 0; n < kHT; ++n)
-#pragma unroll
-    for (int s = 0; s < kQSteps; ++s) asm volatile("" : "+v"(qb[n][s]));
-
-  for (int it = 0; it < ntiles; ++it) {
-    // this wave's part of tile `it` is in when at most the later tiles'
-    // loads are pending
-    const int later = min(ntiles - 1 - it, kBufs - 2);
-    if (later >= 2) wait_vm<2 * kDmaPerWave>();
-    else if (later == 1) wait_vm<kDmaPerWave>();
-    else wait_vm<0>();
-    tile_barrier();              // (A) tile `it` complete, tile it-1 released
-    const uint16_t* kt = sh.k[it % kBufs];
-    const uint32_t vb32 = sh.vbits[it];
-    // The ring's refill (tile it + kBufs - 1 into the buffer tile it - 1
-    // left) is issued one DMA instruction at a time, spread over the tile's
-    // MFMAs (after every fourth logit K-step: pieces 0..3; after P.V dim
-    // tiles 0, 2, 3, 5, 6: pieces 4..8) rather than all at once: with the memory
-    // queue full an issue waits for room, and spread out those waits
-    // overlap the MFMAs in flight.
-    // This lane's source row is read here, before the logits' LDS counting
-    // starts, and the value is tied so the read has returned by then.
-    const bool refill = wave < kDmaWaves && it + kBufs - 1 < ntiles;
-    int32_t rsl = wave < kDmaWaves ? sh.slots[min(it + kBufs - 1, ntiles - 1) * kT + drow] : 0;
-    asm volatile("" : "+v"(rsl));
-    const uint8_t* rsrc = reinterpret_cast<const uint8_t*>(kv) +
-                          static_cast<uint64_t>(max(rsl, 0)) * (2 * kD) + dcol;
-    uint8_t* rdst = reinterpret_cast<uint8_t*>(sh.k[(it + kBufs - 1) % kBufs]) + 9216 * wave;
-
-    // ---- logits: part[n][i] = head 16 kHT hg + 16 n + l16, key 16 kh + 4 g16 + i
-    // K-step st reads piece 4 st + g16 of the lane's row: group st >> 1 (an
-    // immediate 1024 (st >> 1)) and one of two per-lane offsets.
-    f32x4 part[kHT];
-#pragma unroll
-    for (int n = 0; n < kHT; ++n) part[n] = f32x4{0, 0, 0, 0};
-    {
-      const uint32_t kb = lds_addr(kt);
-      const uint32_t kbase[2] = {kb + kodd[0], kb + kodd[1]};
-      constexpr int kAhead = 4;
-      bf16x8 kr[kAhead];
-      lgkm_drain();
-      static_for<kAhead>([&](auto st) {
-        constexpr int S = decltype(st)::value;
-        kr[S] = b128_load<1024 * (S >> 1)>(kbase[S & 1]);
-      });
-      static_for<kQSteps>([&](auto st) {
-        constexpr int S = decltype(st)::value;
-        bf16x8& cur = kr[S % kAhead];
-        constexpr int kAfter = (kQSteps - 1 - S) < (kAhead - 1) ? (kQSteps - 1 - S) : (kAhead - 1);
-        lgkm_keep<kAfter>(cur);
-#pragma unroll
-        for (int n = 0; n < kHT; ++n)
-          part[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur, qb[n][S], part[n], 0, 0, 0);
-        if constexpr (S + kAhead < kQSteps)
-          cur = b128_load<1024 * ((S + kAhead) >> 1)>(kbase[(S + kAhead) & 1]);
-        if constexpr (S % 4 == 3) {               // pieces 0 .. 3
-          constexpr int G = S / 4;
-          if (refill) {
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_global_load_lds(
-                rsrc + 128 * G, (__attribute__((address_space(3))) void*)(rdst + 1024 * G), 16, 0, 0);
-          }
-        }
-      });
-      
-    }
-
-    // ---- softmax.  The scale is positive, so the raw logits order as the
-    // scaled ones: maxima are taken raw and scaled once, and each
-    // probability is exp2(fma(raw, scale, -reference)).  Keys without a row
-    // take -inf (skipped when the whole tile has rows, the usual case).
-    float zr[kHT][4], mx[kHT];
-    if (__builtin_amdgcn_readfirstlane(vb32) == 0xFFFFFFFFu) {
-#pragma unroll
-      for (int n = 0; n < kHT; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zr[n][i] = part[n][i];
-    } else {
-      const uint32_t vbl = vb32 >> (16 * kh + 4 * g16);
-#pragma unroll
-      for (int n = 0; n < kHT; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zr[n][i] = ((vbl >> i) & 1u) ? part[n][i] : -INFINITY;
-    }
-    bool need = false;
-#pragma unroll
-    for (int n = 0; n < kHT; ++n) {
-      const float r = max_nn(max3_nn(zr[n][0], zr[n][1], zr[n][2]), zr[n][3]);
-      mx[n] = max_x16_x32(r) * scale_log2;
-      need |= mx[n] > m_ref[n] + kMoveSlack;
-    }
-    // speculative probabilities against the current reference maxima
-    float pr[kHT][4];
-#pragma unroll
-    for (int n = 0; n < kHT; ++n) {
-      const float mu = m_ref[n] == -INFINITY ? 0.0f : m_ref[n];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        pr[n][i] = __builtin_amdgcn_exp2f(fmaf(zr[n][i], scale_log2, -mu));
-    }
-    const bool wave_need = __ballot(need) != 0;
-#pragma unroll
-    for (int n = 0; n < kHT; ++n) {
-      sh.xp[wave][n][lane] = pack_bf16x4(pr[n]);
-      sh.xm[wave][n][lane] = mx[n];
-    }
-    if (lane == 0) sh.xf[wave] = wave_need ? 1u : 0u;
-    tile_barrier();              // (B) maxima, flags and probabilities published
-    if (any_word(sh.xf)) {
-      // Some reference maximum of the workgroup moves; every wave takes this
-      // branch.  A head's first key sets its reference (its sums are still
-      // zero, nothing to rescale).  A head whose tile maximum beats its
-      // reference by more than kMoveSlack would overflow: then the new maxima
-      // become the references and the workgroup restarts its split from the
-      // first tile with zero sums (later restarts can only come from later
-      // tiles, so there are at most ntiles of them).  The accumulators are
-      // never rescaled in place.
-      bool restart = false;
-#pragma unroll
-      for (int n = 0; n < kHT; ++n) {
-        const float mfull = fmaxf(mx[n], sh.xm[partner][n][lane]);
-        const bool first = m_ref[n] == -INFINITY && mfull != -INFINITY;
-        const bool over = m_ref[n] != -INFINITY && mfull > m_ref[n] + kMoveSlack;
-        restart |= over;
-        if (first || over) m_ref[n] = mfull;
-        const float mu = m_ref[n] == -INFINITY ? 0.0f : m_ref[n];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pr[n][i] = __builtin_amdgcn_exp2f(fmaf(zr[n][i], scale_log2, -mu));
-      }
-#pragma unroll
-      for (int n = 0; n < kHT; ++n) sh.xp[wave][n][lane] = pack_bf16x4(pr[n]);
-      const bool wave_restart = __ballot(restart) != 0;   // all lanes vote
-      if (lane == 0) sh.xr[wave] = wave_restart ? 1u : 0u;
-      tile_barrier();            // (C) probabilities against the new maxima
-      if (any_word(sh.xr)) {
-#pragma unroll
-        for (int n = 0; n < kHT; ++n) l_part[n] = 0.0f;
-#pragma unroll
-        for (int n = 0; n < kPvHT; ++n)
-#pragma unroll
-          for (int nt = 0; nt < kPvNT; ++nt) o[n][nt] = f32x4{0, 0, 0, 0};
-        wait_vm<0>();
-        tile_barrier();          // every wave is done with the ring
-#pragma unroll
-        for (int i = 0; i < kBufs - 1; ++i)
-          if (i < ntiles) dma(i, sh.k[i]);
-        it = -1;
-        continue;
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < kHT; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) l_part[n] += pr[n][i];
-    // P operands of head groups 2 php + n: keys 0..15 from wave 2 (2 php + n),
-    // keys 16..31 from wave 2 (2 php + n) + 1, as published in LDS
-    bf16x8 pa[kPvHT];
-#pragma unroll
-    for (int n = 0; n < kPvHT; ++n) {
-      const u32x2 p0 = sh.xp[4 * php + 2 * n][0][lane];
-      const u32x2 p1 = sh.xp[4 * php + 2 * n + 1][0][lane];
-      const u32x4 v = {p0[0], p0[1], p1[0], p1[1]};
-      pa[n] = __builtin_bit_cast(bf16x8, v);
-    }
-
-    // ---- O += P . V: 8 dim tiles of both head tiles, two transpose loads
-    // per dim tile, 8 loads in flight.  Dim tile nt reads piece
-    // 16 pq + 2 nt + b of its rows: group 2 pq + (nt >> 2) (an immediate
-    // 1024 (nt >> 2)) and one of four per-lane offsets per row set.
-    {
-      const uint32_t tb = lds_addr(kt);
-      uint32_t va[4], vb[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        va[m] = tb + voff_a[m];
-        vb[m] = tb + voff_b[m];
-      }
-      constexpr int kLoads = 2 * kPvNT;               // 16
-      constexpr int kAhead = 8;
-      v4i16 vr[kAhead];
-      auto vload = [&](auto ld) -> v4i16 {
-        constexpr int L = decltype(ld)::value;
-        constexpr int NT = L >> 1;
-        return (L & 1) ? tr_load<1024 * (NT >> 2)>(vb[NT & 3])
-                       : tr_load<1024 * (NT >> 2)>(va[NT & 3]);
-      };
-      lgkm_drain();
-      static_for<kAhead>([&](auto ld) { vr[decltype(ld)::value] = vload(ld); });
-      static_for<kPvNT>([&](auto ntc) {
-        constexpr int NT = decltype(ntc)::value;
-        v4i16& a0 = vr[(2 * NT) % kAhead];
-        v4i16& a1 = vr[(2 * NT + 1) % kAhead];
-        // loads issued after load 2 NT + 1
-        constexpr int kAfter = (kLoads - 2 - 2 * NT) < (kAhead - 2) ? (kLoads - 2 - 2 * NT) : (kAhead - 2);
-        lgkm_keep<kAfter>(a0);
-        lgkm_keep<kAfter>(a1);
-        const v8i16 v01 = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, v01);
-#pragma unroll
-        for (int n = 0; n < kPvHT; ++n)
-          o[n][NT] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[n], vop, o[n][NT], 0, 0, 0);
-        if constexpr (2 * NT + kAhead < kLoads) {
-          a0 = vload(std::integral_constant<int, 2 * NT + kAhead>{});
-          a1 = vload(std::integral_constant<int, 2 * NT + kAhead + 1>{});
-        }
-        // pieces 4 .. 8 after dim tiles 0, 2, 3, 5, 6
-        constexpr int G = NT == 0 ? 4 : NT == 2 ? 5 : NT == 3 ? 6 : NT == 5 ? 7 : NT == 6 ? 8 : -1;
-        if constexpr (G >= 0) {
-          if (refill) {
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_global_load_lds(
-                rsrc + 128 * G, (__attribute__((address_space(3))) void*)(rdst + 1024 * G), 16, 0, 0);
-          }
-        }
-      });
-    }
-  }
-
-  // ---- epilogue: per-head sums, normalisation, staged coalesced stores
-#pragma unroll
-  for (int n = 0; n < kHT; ++n) l_part[n] = sum_x16_x32(l_part[n]);
-  tile_barrier();                // every wave is done with the tiles and xm
-#pragma unroll
-  for (int n = 0; n < kHT; ++n) sh.xm[wave][n][lane] = l_part[n];
-  tile_barrier();
-  float lse_h[kHT];                // head 16 kHT hg + 16 n + l16
-#pragma unroll
-  for (int n = 0; n < kHT; ++n) {
-    const float l = l_part[n] + sh.xm[partner][n][lane];
-    lse_h[n] = l > 0.0f ? (m_ref[n] + log2f(l)) * kLn2 : -INFINITY;
-  }
-  float inv_l[kPvHT];              // head 32 php + 16 n + l16
-#pragma unroll
-  for (int n = 0; n < kPvHT; ++n) {
-    const float l = sh.xm[4 * php + 2 * n][0][lane] + sh.xm[4 * php + 2 * n + 1][0][lane];
-    inv_l[n] = l > 0.0f ? 1.0f / l : 0.0f;
-  }
-  const bool partial = n_split > 1;
-  // rows of the staged block (bf16, the output's or the partial's values):
-  // head h (0..63) at byte h * row_b of the tile buffers (free now); 16
-  // bytes of padding per row spread the banks
-  constexpr int row_b = kR * 2 + 16;
-  uint8_t* stage = reinterpret_cast<uint8_t*>(&sh.k[0][0]);
-  // heads i and i + 1 of a lane are converted together
-#pragma unroll
-  for (int n = 0; n < kPvHT; ++n) {
-#pragma unroll
-    for (int i = 0; i < 4; i += 2) {
-      const int hl = 4 * g16 + i;
-      const float il0 = __shfl(inv_l[n], hl);
-      const float il1 = __shfl(inv_l[n], hl + 1);
-      const int h = 32 * php + 16 * n + hl;
-#pragma unroll
-      for (int nt = 0; nt < kPvNT; ++nt) {
-        const int d = 128 * pq + 16 * nt + l16;
-        const uint32_t pk = pack2_bf16(o[n][nt][i] * il0, o[n][nt][i + 1] * il1);
-        *reinterpret_cast<uint16_t*>(stage + h * row_b + 2 * d) = static_cast<uint16_t>(pk);
-        *reinterpret_cast<uint16_t*>(stage + (h + 1) * row_b + 2 * d) =
-            static_cast<uint16_t>(pk >> 16);
-      }
-    }
-  }
-  if (kh == 0 && g16 == 0) {
-#pragma unroll
-    for (int n = 0; n < kHT; ++n) {
-      const int h = 16 * kHT * hg + 16 * n + l16;
-      if (partial)
-        __hip_atomic_store(part_lse + (static_cast<int64_t>(t) * n_split + split) * kH + h,
-                           lse_h[n], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else if (lse)
-        lse[static_cast<int64_t>(t) * kH + h] = lse_h[n];
-    }
-  }
-  mla_store_or_merge(stage, &sh.counter, t, split, n_split, partial, out, lse, part_o,
-                     part_lse, arrivals, call_tag);
-}
-
 // ------------------------------------------------- warp-specialised pipeline
 // The same contraction with the work of a tile split by role instead of by
 // phase.  Waves 0..3 (one per SIMD) are logit waves: wave hg holds the
@@ -906,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(
 // buffer in LDS); one barrier per iteration.  Ring of four tiles: k - 1
 // (P.V), k (logits), k + 1 and k + 2 in flight (tile k + 2 is issued at the
 // start of iteration k, into the slot tile k - 2 left).
-// Reference maxima: as in k_mla_mfma, a head's reference is fixed by its
+// Reference maxima: a head's reference is fixed by its
 // first key and may be exceeded by kMoveSlack before it moves; when it moves,
 // the logit wave rescales its sums and publishes the factor 2^(m_old -
 // m_new), and the P.V waves rescale that head group's accumulators in place
@@ -1250,8 +770,454 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
     }
     tile_barrier();                      // rows staged
   }
-  mla_store_or_merge(reinterpret_cast<uint8_t*>(&sh.k[0][0]), &sh.counter, t, split, n_split,
+  mla_store_or_merge<kThreads>(reinterpret_cast<uint8_t*>(&sh.k[0][0]), &sh.counter, t, split, n_split,
                      n_split > 1, out, lse, part_o, part_lse, arrivals, call_tag);
+}
+
+// ------------------------------------------------------- one token per workgroup
+// The same contraction for batches of many tokens without key splits
+// (prefill), and for key splits longer than k_mla_ws takes: one workgroup
+// per (token, split) of up to 2,048 indices, 4 waves (one per SIMD), 64-key tiles
+// and v_mfma_f32_32x32x16_bf16, which one wave issues at the matrix cores'
+// full rate (the 16x16x32 shape reaches about two thirds of it).
+//  * Logits: wave w = (head group g = w & 1, key block kb = w >> 1) holds the
+//    queries of heads 32 g .. 32 g + 31 in accumulator registers (read by the
+//    MFMA directly) and computes their logits over keys 32 kb .. 32 kb + 31
+//    of the tile, keys on M and heads on N: a lane holds one head and 16 keys
+//    (8 j + 4 (l / 32) + i), so the per-head maxima and sums are in-lane
+//    plus one permlane swap.
+//  * Probabilities go to LDS as bf16 MFMA A operands: K-step u of key block
+//    kb covers keys 16 u + 4 (l / 32) + i and 16 u + 8 + 4 (l / 32) + i, which
+//    are exactly the lane's own keys j = 2 u, 2 u + 1.  They are taken
+//    against the head's current reference before the other key block's
+//    maximum is known; only when some maximum of the head group passes the
+//    reference by more than the slack (the first tile with a row, then
+//    rarely) does the group exchange maxima, move the reference, rescale
+//    and take them again (one barrier per tile besides the tile barrier).
+//  * P.V: wave w accumulates all 64 heads over value dims 128 w .. + 127
+//    (O in registers), each value fragment read once with the transpose
+//    load and feeding both head groups; operands three MFMA pairs ahead.
+// Two tiles in LDS: the current one and the next one's DMA.  Each wave's 18
+// DMA instructions of tile k + 1 are spread over tile k's MFMAs (issued all
+// at once, they hold the wave at the issue until the memory queue has room,
+// with no other wave on its SIMD).  The slot table holds half of the
+// indices at a time (the second half replaces the first at tile 14, once
+// the rows of tile 15 are read; rows are read one tile ahead of their DMA).
+constexpr int kPfT = 64;                 // keys per tile
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfHalf = 1024;            // slot-table entries resident at once
+constexpr int kPfQSteps = kD / 16;       // 36 K-steps of the logits
+struct MlaSharedPf {
+  uint16_t k[2][kPfT * kD];              // two tiles in the layout of tile_byte (8 row groups)
+  int32_t slots[kPfHalf];                // physical rows of one half of the indices, or -1
+  uint32_t vbits[kMaxSplitLen / 32];     // per 32-key block: bit i = key i has a row
+  u32x4 xp[2][2][2][64];                 // P: [head group][key block][K-step][lane]
+  float xm[2][2][32];                    // per-head maxima of a key block (sums at the end)
+  float xf[2][32];                       // per-head rescale factors (1 / sums at the end)
+  alignas(16) uint32_t xflag[2];         // per head group: its factors apply
+  alignas(16) uint32_t xneed[4];         // per wave: a maximum passed the reference
+  uint32_t counter;                      // split merge: this workgroup merges
+};
+// LDS operations of P.V pairs i + 1 .. i + lead (four with a K-step's first
+// pair, two otherwise), the count allowed outstanding when pair i's own
+// operands must have arrived
+constexpr int pv_ops_after(int i, int lead) {
+  int n = 0;
+  for (int j = i + 1; j <= i + lead && j < 16; ++j) n += (j % 4 == 0) ? 4 : 2;
+  return n;
+}
+static_assert(sizeof(MlaSharedPf) <= 160 * 1024, "LDS budget");
+static_assert(kH * kRowB + (kMaxSplits + 1) * kH * 4 <= sizeof(MlaSharedPf::k),
+              "staged rows and merge weights fit in the tile buffers");
+
+__global__ __launch_bounds__(kPfThreads, 1) void k_mla_prefill(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+    const int32_t* __restrict__ topk_idx, int32_t topk, int32_t n_tokens,
+    int32_t n_split, int32_t split_len, float scale_log2,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q, int32_t B,
+    const int32_t* __restrict__ block_table, int32_t max_blocks, int32_t block_size,
+    int64_t num_slots, int32_t max_seq_len, uint16_t* __restrict__ out,
+    float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
+    unsigned long long* __restrict__ arrivals, unsigned long long call_tag) {
+  __shared__ MlaSharedPf sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = wave & 1;               // logits: head group
+  const int kb = wave >> 1;             // logits: key block of the tile
+  const int n32 = lane & 31;            // logits: head 32 g + n32; P.V: dim column
+  const int hh = lane >> 5;             // lane half
+  // workgroup = (token, key split); the splits of a token on one XCD
+  int vb = blockIdx.x;
+  if (n_split > 1 && (gridDim.x & 7) == 0)
+    vb = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  const int t = vb / n_split;
+  const int split = vb % n_split;
+  if (t >= n_tokens) return;
+  // the split's indices: topk_idx[t][jbeg + j] for j < cnt (cnt <= 2048)
+  const int jbeg = split * split_len;
+  const int cnt = max(0, min(topk, jbeg + split_len) - jbeg);
+  const int32_t* idx_row = topk_idx + static_cast<int64_t>(t) * topk + jbeg;
+  const int ntiles = (cnt + kPfT - 1) / kPfT;             // <= 32 tiles
+
+  // ---- the token's physical rows (8 indices per thread, j = tid + 256 i):
+  // indices beside the request's place, then the block-table entries; the
+  // queries are requested behind those
+  constexpr int kPer = kMaxSplitLen / kPfThreads;          // 8
+  int32_t p[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = tid + kPfThreads * i;
+    p[i] = j < cnt ? idx_row[j] : -1;
+  }
+  int b;
+  int32_t pos;
+  token_place(cu_q, seq_lens, B, t, max_seq_len, b, pos);
+  const int32_t* bt_row = block_table + static_cast<int64_t>(b) * max_blocks;
+  int32_t sl[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const bool ok = p[i] >= 0 && p[i] <= pos && p[i] / block_size < max_blocks;
+    const int32_t bid = ok ? bt_row[p[i] / block_size] : -1;
+    const int64_t s0 = static_cast<int64_t>(bid) * block_size + (ok ? p[i] % block_size : 0);
+    sl[i] = (bid >= 0 && s0 < num_slots) ? static_cast<int32_t>(s0) : -1;
+  }
+  asm volatile("" ::: "memory");
+  // queries, the B operand of head group g: head 32 g + n32, dims 16 s + 8 hh
+  bf16x8 qb[kPfQSteps];
+  {
+    const int64_t qbase = (static_cast<int64_t>(t) * kH + 32 * g + n32) * kD + 8 * hh;
+#pragma unroll
+    for (int st = 0; st < kPfQSteps; ++st)
+      qb[st] = *reinterpret_cast<const bf16x8*>(q + qbase + 16 * st);
+  }
+  // slot table (first half) and validity masks of every 32-key block
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int j = tid + kPfThreads * i;
+    if (i < kPer / 2) sh.slots[j] = sl[i];
+    const uint64_t m = __ballot(j < cnt && sl[i] >= 0);
+    if (lane == 0) {
+      sh.vbits[(kPfThreads * i + 64 * wave) / 32] = static_cast<uint32_t>(m);
+      sh.vbits[(kPfThreads * i + 64 * wave) / 32 + 1] = static_cast<uint32_t>(m >> 32);
+    }
+  }
+  tile_barrier();
+
+  // DMA of a tile: wave w fills row groups 2 w and 2 w + 1 (nine 1 KB blocks
+  // each, the lane map of tile_byte); rows without a physical row read row 0
+  // A wave's 18 DMA instructions of a tile are issued one at a time, spread
+  // over the previous tile's MFMAs: a wave that issues many at once waits
+  // at the issue until the memory pipeline has room, with nothing else to
+  // run on its SIMD.  src[hr] is the lane's row of group 2 w + hr.
+  const uint8_t* src[2];
+  // LDS address of the slot-table entry of the lane's row in group 2 w + hr
+  // of a tile (entry 0 for a tile past the end)
+  auto slot_addr = [&](int tile, bool real, int hr) {
+    const int h = 2 * wave + hr;
+    const int pi = (lane >> 3) ^ (h & 1);
+    const int row = 8 * h + ((lane & 7) ^ (4 * (pi & 1)));
+    const int j = real ? tile * kPfT + row : 0;
+    return lds_addr(&sh.slots[j >= kPfHalf ? j - kPfHalf : j]);
+  };
+  auto set_src = [&](int hr, int32_t slot) {
+    const int h = 2 * wave + hr;
+    const int pi = (lane >> 3) ^ (h & 1);
+    src[hr] = reinterpret_cast<const uint8_t*>(kv) +
+              static_cast<uint64_t>(max(slot, 0)) * (2 * kD) + 16u * pi;
+  };
+  auto dma_rows = [&](int tile, bool real) {
+#pragma unroll
+    for (int hr = 0; hr < 2; ++hr) {
+      const int h = 2 * wave + hr;
+      const int pi = (lane >> 3) ^ (h & 1);
+      const int row = 8 * h + ((lane & 7) ^ (4 * (pi & 1)));
+      const int j = real ? tile * kPfT + row : 0;
+      set_src(hr, real ? sh.slots[j >= kPfHalf ? j - kPfHalf : j] : -1);
+    }
+  };
+  // instruction d = 9 hr + G9 of the wave's share of a tile into buffer buf
+  auto dma_one = [&](int buf, int d) {
+    const int hr = d / 9, G9 = d % 9;
+    uint8_t* dst = reinterpret_cast<uint8_t*>(sh.k[buf]) + 9216 * (2 * wave + hr) + 1024 * G9;
+    __builtin_amdgcn_global_load_lds(src[hr] + 128 * G9,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+  if (ntiles > 0) {
+    dma_rows(0, true);
+#pragma unroll
+    for (int d = 0; d < 18; ++d) dma_one(0, d);
+  }
+
+  // logit operand offsets: row 32 kb + n32, piece 2 s + hh (group s / 4, an
+  // immediate; four in-group offsets for s % 4)
+  uint32_t ko[4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const uint32_t full = tile_byte(32 * kb + n32, 2 * s4 + hh);
+    ko[s4] = full;
+  }
+  // value operand offsets (transpose loads): within each 16-lane group G,
+  // lane j supplies row 4 hh + j / 4 (+ 8 x) of a 16-key step and dims
+  // 128 w + 32 d + 16 (G & 1) + 4 (j & 3) .. + 3; vo[x][d & 1] holds the
+  // lane-dependent part, the rest is immediate
+  const int j16 = lane & 15;
+  const int G = lane >> 4;
+  uint32_t vo[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int d1 = 0; d1 < 2; ++d1) {
+      const int row = 8 * x + 4 * hh + (j16 >> 2);
+      const int piece = 16 * wave + 4 * d1 + 2 * (G & 1) + ((j16 & 3) >> 1);
+      vo[x][d1] = tile_byte(row, piece) + 8u * static_cast<uint32_t>(j16 & 1);
+    }
+
+  float m_ref = -INFINITY;              // head 32 g + n32
+  float l_part = 0.0f;
+  // O[g'][d]: heads 32 g' + 8 (r / 4) + 4 hh + r % 4, dims 128 w + 32 d + n32
+  f32x16 o[2][4];
+#pragma unroll
+  for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[g2][d] = f32x16{};
+
+  // the queries were requested before tile 0's DMA (18 loads per wave)
+  wait_vm<18>();
+#pragma unroll
+  for (int st = 0; st < kPfQSteps; ++st) asm volatile("" : "+a"(qb[st]));
+
+  // rows of tile 1, whose DMA is issued during tile 0
+  dma_rows(1, 1 < ntiles);
+
+  for (int k = 0; k < ntiles; ++k) {
+    wait_vm<0>();                       // this wave's DMAs of tile k
+    tile_barrier();                     // tile k landed; every wave is done with tile k - 1
+    if (k == kPfHalf / kPfT - 2 && ntiles > kPfHalf / kPfT) {
+      // the second half of the slot table: the rows of tile 15 were read at
+      // the end of tile 13, those of tile 16 are read at the end of this one
+#pragma unroll
+      for (int i = 0; i < kPer / 2; ++i) sh.slots[tid + kPfThreads * i] = sl[kPer / 2 + i];
+      tile_barrier();
+    }
+    const int nbuf = (k + 1) & 1;
+    const uint32_t tb = lds_addr(sh.k[k & 1]);
+    uint32_t vbw;
+
+    // ---- logits of key block kb, head group g: 36 MFMAs, operands 3 ahead,
+    // DMA instructions 0 .. 8 of tile k + 1 after every fourth
+    f32x16 sacc = f32x16{};
+    {
+      constexpr int kAhead = 3;
+      bf16x8 kr[kAhead];
+      lgkm_drain();
+      vbw = b32_load<0>(lds_addr(&sh.vbits[2 * k + kb]));   // completes before kr[0]
+      static_for<kAhead>([&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        kr[S] = b128_load<1024 * (S >> 2)>(tb + ko[S & 3]);
+      });
+      static_for<kPfQSteps>([&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        constexpr int R = S % kAhead;
+        constexpr int kAfter = (kPfQSteps - 1 - S) < (kAhead - 1) ? (kPfQSteps - 1 - S) : (kAhead - 1);
+        lgkm_keep<kAfter>(kr[R]);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[R], qb[S], sacc, 0, 0, 0);
+        if constexpr (S % 4 == 0) dma_one(nbuf, S / 4);
+        if constexpr (S + kAhead < kPfQSteps)
+          kr[R] = b128_load<1024 * ((S + kAhead) >> 2)>(tb + ko[(S + kAhead) & 3]);
+      });
+    }
+    // ---- softmax: lane (n32, hh) holds keys 8 j + 4 hh + i (register 4 j + i).
+    // The probabilities are first taken against the current reference,
+    // without waiting for the other key block's maximum: that is exact
+    // unless a maximum of the group passes the reference by more than the
+    // slack, which every wave of the group learns at the barrier, and then
+    // the group takes them again against the common new reference (the
+    // first tile with a row always does).
+    lgkm_keep<0>(vbw);
+    const uint32_t vbk = vbw >> (4 * hh);
+    float z[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      z[r] = ((vbk >> (8 * (r >> 2) + (r & 3))) & 1u) ? sacc[r] : -INFINITY;
+    float mx = z[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = max_nn(mx, z[r]);
+    {
+      const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+      mx = max_nn(__uint_as_float(c[0]), __uint_as_float(c[1])) * scale_log2;
+    }
+    if (hh == 0) sh.xm[g][kb][n32] = mx;
+    const bool need = mx > m_ref + kMoveSlack;          // -inf reference: any row
+    float psum;                         // the lane's share of the tile's sum
+    auto probs = [&]() {
+      const float mu = m_ref == -INFINITY ? 0.0f : m_ref;
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(fmaf(z[r], scale_log2, -mu));
+      psum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) psum += pr[r];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u32x4 pk;
+        pk[0] = pack2_bf16(pr[8 * u + 0], pr[8 * u + 1]);
+        pk[1] = pack2_bf16(pr[8 * u + 2], pr[8 * u + 3]);
+        pk[2] = pack2_bf16(pr[8 * u + 4], pr[8 * u + 5]);
+        pk[3] = pack2_bf16(pr[8 * u + 6], pr[8 * u + 7]);
+        sh.xp[g][kb][u][lane] = pk;
+      }
+    };
+    probs();
+    {
+      const bool any_need = __ballot(need) != 0;
+      if (lane == 0) sh.xneed[wave] = any_need ? 1u : 0u;
+    }
+    tile_barrier();                     // probabilities and the groups' flags published
+
+    // ---- P.V over the tile: 16 MFMA pairs (K-step st = i / 4, dim block
+    // d = i % 4; both head groups share the value operand).  Operands are
+    // requested three pairs ahead: the probabilities of both head groups
+    // with the first pair of a K-step, two value fragments with each pair.
+    // DMA instructions 9 .. 17 of tile k + 1 are spread over the pairs.
+    // The groups' flags and the slot-table entries of tile k + 2 are
+    // requested ahead of the first operands; the first three pairs'
+    // operands are requested again if a group takes its probabilities anew.
+    const uint32_t pb = lds_addr(&sh.xp[0][0][0][lane]);
+    {
+      constexpr int kLead = 3;
+      bf16x8 pa[2][2];
+      v4i16 vv[4][2];
+      auto issue = [&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        constexpr int ST = I >> 2, D = I & 3, KB2 = ST >> 1, U = ST & 1;
+        if constexpr (D == 0) {
+          pa[ST & 1][0] = b128_load<1024 * (0 * 4 + KB2 * 2 + U)>(pb);
+          pa[ST & 1][1] = b128_load<1024 * (1 * 4 + KB2 * 2 + U)>(pb);
+        }
+        constexpr int kVImm = 9216 * (4 * KB2 + 2 * U) + 1024 * (D >> 1);
+        vv[D][0] = tr_load<kVImm>(tb + vo[0][D & 1]);
+        vv[D][1] = tr_load<kVImm>(tb + vo[1][D & 1]);
+      };
+      const bool next_real = k + 2 < ntiles;
+      u32x4 nd = u128_load<0>(lds_addr(sh.xneed));
+      uint32_t sv0 = b32_load<0>(slot_addr(k + 2, next_real, 0));
+      uint32_t sv1 = b32_load<0>(slot_addr(k + 2, next_real, 1));
+      static_for<kLead>([&](auto ic) { issue(ic); });
+      lgkm_keep<2 + pv_ops_after(-1, kLead)>(nd);
+      if ((nd[0] | nd[1] | nd[2] | nd[3]) != 0) {
+        lgkm_drain();
+        // waves g and g + 2 hold head group g
+        if ((nd[g] | nd[g + 2]) != 0) {
+          const float mxa = max_nn(mx, sh.xm[g][kb ^ 1][n32]);
+          float factor = 1.0f;
+          bool moved = false;
+          if (m_ref == -INFINITY) {
+            m_ref = mxa;                // stays -inf while no key has a row
+          } else if (mxa > m_ref + kMoveSlack) {
+            factor = __builtin_amdgcn_exp2f(m_ref - mxa);
+            m_ref = mxa;
+            moved = true;
+          }
+          l_part *= factor;
+          probs();
+          const bool any = __ballot(moved) != 0;
+          if (kb == 0) {
+            if (any && hh == 0) sh.xf[g][n32] = factor;
+            if (lane == 0) sh.xflag[g] = any ? 1u : 0u;
+          }
+        } else if (kb == 0 && lane == 0) {
+          sh.xflag[g] = 0u;
+        }
+        tile_barrier();                 // probabilities and factors published
+        // a head group whose references moved is rescaled before P.V
+        const uint32_t f0 = sh.xflag[0], f1 = sh.xflag[1];
+        if (f0 | f1) {
+#pragma unroll
+          for (int g2 = 0; g2 < 2; ++g2) {
+            if (!(g2 ? f1 : f0)) continue;
+            float fr[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) fr[r] = sh.xf[g2][8 * (r >> 2) + 4 * hh + (r & 3)];
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[g2][d][r] *= fr[r];
+          }
+        }
+        lgkm_drain();
+        static_for<kLead>([&](auto ic) { issue(ic); });
+      }
+      l_part += psum;
+      static_for<16>([&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        constexpr int ST = I >> 2, D = I & 3;
+        if constexpr (I + kLead < 16) issue(std::integral_constant<int, I + kLead>{});
+        // operations issued after pair I's: those of pairs I + 1 .. I + kLead
+        constexpr int kAfter = pv_ops_after(I, kLead);
+        if constexpr (D == 0) {
+          lgkm_keep<kAfter + 2>(pa[ST & 1][0]);
+          lgkm_keep<kAfter + 2>(pa[ST & 1][1]);
+        }
+        lgkm_keep<kAfter>(vv[D][0]);
+        lgkm_keep<kAfter>(vv[D][1]);
+        const v8i16 v01 = __builtin_shufflevector(vv[D][0], vv[D][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, v01);
+        o[0][D] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ST & 1][0], vop, o[0][D], 0, 0, 0);
+        o[1][D] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ST & 1][1], vop, o[1][D], 0, 0, 0);
+        if constexpr (I < 9) dma_one(nbuf, 9 + I);
+      });
+      // rows of tile k + 2 for the DMA issued during tile k + 1 (row 0
+      // after the last tile)
+      lgkm_keep<0>(sv0);
+      lgkm_keep<0>(sv1);
+      set_src(0, next_real ? static_cast<int32_t>(sv0) : -1);
+      set_src(1, next_real ? static_cast<int32_t>(sv1) : -1);
+    }
+  }
+  wait_vm<0>();                          // the DMA issued during the last tile
+  tile_barrier();                        // every wave is done with the tiles
+
+  // ---- per-head sums, lse, 1 / sum
+  {
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part),
+                                                    false, false);
+    const float lw = __uint_as_float(c[0]) + __uint_as_float(c[1]);
+    if (hh == 0) sh.xm[g][kb][n32] = lw;
+  }
+  tile_barrier();
+  if (kb == 0 && hh == 0) {
+    const float l = sh.xm[g][0][n32] + sh.xm[g][1][n32];
+    sh.xf[g][n32] = l > 0.0f ? 1.0f / l : 0.0f;
+    const float lh = l > 0.0f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+    const int h = 32 * g + n32;
+    if (n_split > 1)
+      __hip_atomic_store(part_lse + (static_cast<int64_t>(t) * n_split + split) * kH + h,
+                         lh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else if (lse)
+      lse[static_cast<int64_t>(t) * kH + h] = lh;
+  }
+  tile_barrier();
+  // ---- normalised bf16 rows into the staging block (over the tiles), then
+  // out (or stored as this split's partial, the last split merging)
+  uint8_t* stage = reinterpret_cast<uint8_t*>(&sh.k[0][0]);
+#pragma unroll
+  for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int hl = 8 * (r >> 2) + 4 * hh + (r & 3);
+      const float inv = sh.xf[g2][hl];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int dim = 128 * wave + 32 * d + n32;
+        *reinterpret_cast<uint16_t*>(stage + (32 * g2 + hl) * kRowB + 2 * dim) =
+            f32_to_bf16_rne(o[g2][d][r] * inv);
+      }
+    }
+  mla_store_or_merge<kPfThreads>(stage, &sh.counter, t, split, n_split, n_split > 1, out, lse,
+                                 part_o, part_lse, arrivals, call_tag);
 }
 
 // ---------------------------------------------------------------- vector path
@@ -1375,7 +1341,8 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
           a.call_tag);
       return hipGetLastError();
     }
-    k_mla_mfma<<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(
+    // longer splits (up to kMaxSplitLen indices), or one per token
+    k_mla_prefill<<<static_cast<unsigned>(grid), kPfThreads, 0, stream>>>(
         static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kv),
         a.idx, a.topk, b.num_q_tokens, n_split, split_len, a.scale * kLog2e,
         b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,

@@ -370,6 +370,37 @@ def test_topk_4096_through_both_calls(dsa):
         assert attn_close(gl2[t], rl2[t], 1e-3, 1e-4) <= 0, t
 
 
+def test_long_splits_merge_over_any_workspace(dsa):
+    """Key splits of 2048 indices (top-k 4096 at 130 tokens: two splits per
+    token, too long for the warp-specialised pipeline) go to the 64-key
+    tile kernel with its partials merged by the last split: over a
+    workspace of random bytes, twice in a row on the same workspace (the
+    second call bit for bit), against the oracle on sampled tokens."""
+    topk = 4096
+    cfg = _small_cfg(num_reqs=65, q_len=2, topk=topk)
+    b = make_batch(cfg, DEV, seq_lens=[4100 + 7 * i for i in range(65)], q_lens=[2] * 65)
+    lay = make_layer(cfg, b, DEV, with_indexer=False)
+    idx = make_random_indices(b, topk, 4097, DEV)
+    idx[3::11, 100::9] = -1
+    bb = _dsa_batch(dsa, b)
+    nbytes = dsa.sparse_mla_attn_workspace_size(bb, 64, 512, 64, topk, 1)
+    g = torch.Generator(device="cpu").manual_seed(4097)
+    ws = torch.randint(0, 256, (max(nbytes, 1),), dtype=torch.uint8, generator=g).to(DEV)
+    o1, l1 = dsa.sparse_mla_attn(bb, lay.q_mla, lay.kv_cache, idx, 512, cfg.softmax_scale,
+                                 workspace=ws)
+    o1, l1 = o1.clone(), l1.clone()
+    o2, l2 = dsa.sparse_mla_attn(bb, lay.q_mla, lay.kv_cache, idx, 512, cfg.softmax_scale,
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    toks = [0, 1, 3, 14, 64, 99, 128, 129]
+    ro, rl = _oracle_mla(b, lay, idx.cpu().numpy(), 512, cfg.softmax_scale, tokens=toks)
+    go, gl = np_f64(o1), l1.cpu().numpy()
+    for t in toks:
+        assert attn_close(go[t], ro[t]) <= 0, t
+        assert attn_close(gl[t], rl[t], 1e-3, 1e-4) <= 0, t
+
+
 def test_ragged_batch_with_requests_without_queries(dsa):
     """Requests with no query token this step (q_len = 0, one of them with
     an empty cache) between others: both calls skip them and every other
@@ -481,6 +512,34 @@ def test_bf16_attention_matrix_core(dsa, n_req, q_len, topk):
     for t in toks:
         assert attn_close(go[t], ro[t]) <= 0, t
         assert attn_close(gl[t], rl[t], 1e-3, 1e-4) <= 0, t
+
+
+@pytest.mark.parametrize("topk", [64, 300, 1100, 2048])
+def test_attention_one_workgroup_per_token(dsa, topk):
+    """Batches of 256 or more query tokens take one workgroup per token
+    (64-key tiles, the whole index list in one pass).  Widths that end
+    inside a tile (300), that need the second half of the slot table
+    (1100, 2048), rows shorter than the width (a 150-token context), and
+    holes (-1) inside the lists, against the oracle on sampled tokens."""
+    cfg = _small_cfg(num_reqs=3, topk=topk)
+    b = make_batch(cfg, DEV, seq_lens=[3000, 150, 2600], q_lens=[120, 100, 60])
+    assert b.num_q_tokens >= 256
+    lay = make_layer(cfg, b, DEV, with_indexer=False)
+    idx = make_random_indices(b, topk, 3100 + topk, DEV)
+    # holes: every seventh entry of every fifth row
+    idx[::5, 3::7] = -1
+    out, lse = dsa.sparse_mla_attn(_dsa_batch(dsa, b), lay.q_mla, lay.kv_cache, idx,
+                                   cfg.kv_lora_rank, cfg.softmax_scale)
+    torch.cuda.synchronize()
+    toks = [0, 1, 5, 64, 119, 120, 121, 150, 219, 220, 250, b.num_q_tokens - 1]
+    ro, rl = _oracle_mla(b, lay, idx.cpu().numpy(), cfg.kv_lora_rank,
+                         cfg.softmax_scale, tokens=toks)
+    go = np_f64(out)
+    gl = lse.cpu().numpy()
+    for t in toks:
+        assert attn_close(go[t], ro[t]) <= 0, t
+        assert attn_close(gl[t], rl[t], 1e-3, 1e-4) <= 0, t
+    assert np.all(np.isfinite(go))
 
 
 @pytest.mark.parametrize("fill", ["random", "ones", "zeros"])

@@ -33,10 +33,12 @@
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked [host].  All device buffers
  *     belong to the caller; the library never allocates or frees device
- *     memory and never synchronises the device.  State kept between calls:
- *     the thread-local error text, a process-wide counter that tags each
- *     sparse_mla_attn call, and, once dsa_indexer_topk_noalloc has run on a
- *     device, that device's static scratch array and its address.
+ *     memory and never synchronises the device (dsa_debug_faults of the
+ *     checked build excepted).  State kept between calls: the thread-local
+ *     error text, a process-wide counter that tags each sparse_mla_attn
+ *     call, once dsa_indexer_topk_noalloc has run on a device, that
+ *     device's static scratch array and its address, and each device's
+ *     fault word (checked build).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it; inputs must stay valid until that work completes.
  *   - Return value: DSA_OK (0) or a negative dsa_status.  Every condition
@@ -375,6 +377,37 @@ int indexshare_forward(const dsa_batch* batch, int32_t n_layers,
  */
 int dsa_fp8_decode_check(const uint8_t* codes, float* out, int32_t n,
                          void* stream);
+
+/*
+ * Checked build.  libdsa_debug.so is the same library compiled with
+ * -DDSA_DEBUG: around every call it enqueues, on the call's stream, a
+ * validation of the device-resident metadata the call reads against the
+ * host-side bounds (the conditions the release library only clamps), canary
+ * fills of the outputs and the workspace, and after the call a check that
+ * every output element was written and every indexer row is a valid
+ * selection.  Violations accumulate in a per-device fault word:
+ */
+typedef enum {
+  DSA_FAULT_SEQ_LENS = 1,      /* a seq_len outside [0, max_seq_len]                 */
+  DSA_FAULT_CU_Q = 2,          /* cu_q not 0 .. num_q_tokens ascending, or a q_len
+                                  above max_q_len or above its request's seq_len    */
+  DSA_FAULT_BLOCK_TABLE = 4,   /* a block in use past max_blocks, negative, or with
+                                  rows past num_slots                                */
+  DSA_FAULT_SLOT_MAPPING = 8,  /* a cache-write slot neither -1 nor in [0, num_slots) */
+  DSA_FAULT_TOPK_INPUT = 16,   /* an attention index neither -1 nor in [0, pos]      */
+  DSA_FAULT_TOPK_OUTPUT = 32,  /* an indexer row that is not min(topk, pos + 1)
+                                  ascending positions in [0, pos] followed by -1     */
+  DSA_FAULT_UNWRITTEN = 64     /* an output element still holds its canary           */
+} dsa_fault;
+
+/*
+ * The calling device's fault word (OR of dsa_fault bits since the last
+ * clear) into *faults [host]; clear != 0 resets it.  Waits for the device
+ * to finish all queued work first (checked build only: the one call that
+ * synchronises).  The release library sets *faults = 0 and returns
+ * DSA_ERR_UNSUPPORTED.  NULL faults: DSA_ERR_INVALID_ARG.
+ */
+int dsa_debug_faults(uint32_t* faults, int32_t clear);
 
 /* Text of the last error raised on the calling thread ("" if none). */
 const char* dsa_last_error(void);

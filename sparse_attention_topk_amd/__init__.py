@@ -5,7 +5,10 @@ and the current HIP stream.
 
 The library is loaded from this directory (libdsa.so, built by
 ``python -m sparse_attention_topk_amd.build``).  There is no fallback: if the
-library is missing or cannot be loaded, using any entry point raises.
+library is missing or cannot be loaded, using any entry point raises.  The
+checked build libdsa_debug.so (same kernels, plus metadata validation and
+output canaries around every call) is selected with DSA_LIBRARY=debug or
+``use_library("debug")``; ``debug_faults()`` reads what it found.
 """
 
 from ._binding import (  # noqa: F401
@@ -17,4 +20,6 @@ from ._binding import (  # noqa: F401
     sparse_mla_attn, sparse_mla_attn_workspace_size,
     dsa_resolve_indexer_sources, indexshare_forward,
     indexshare_forward_workspace_size, dsa_fp8_decode_check, dsa_last_error,
-    Layer, StackDims)
+    Layer, StackDims, use_library, debug_faults,
+    DSA_FAULT_SEQ_LENS, DSA_FAULT_CU_Q, DSA_FAULT_BLOCK_TABLE, DSA_FAULT_SLOT_MAPPING,
+    DSA_FAULT_TOPK_INPUT, DSA_FAULT_TOPK_OUTPUT, DSA_FAULT_UNWRITTEN)

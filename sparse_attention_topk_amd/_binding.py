@@ -1,5 +1,6 @@
 """ctypes marshalling for include/dsa.h (no computation here)."""
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -8,7 +9,11 @@ from typing import List, Optional, Sequence
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_NAME = "libdsa.so"
+# "release": libdsa.so; "debug": the checked build libdsa_debug.so (metadata
+# validation and output canaries around every call, see dsa_debug_faults).
+# DSA_LIBRARY=debug in the environment selects the checked build.
+_LIB_NAMES = {"release": "libdsa.so", "debug": "libdsa_debug.so"}
+_variant = os.environ.get("DSA_LIBRARY", "release")
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED = 0, -1, -2
@@ -23,8 +28,11 @@ EXPORTS = [
     "sparse_mla_attn_workspace_size",
     "sparse_mla_attn",
     "dsa_resolve_indexer_sources", "indexshare_forward_workspace_size",
-    "indexshare_forward", "dsa_fp8_decode_check", "dsa_last_error",
+    "indexshare_forward", "dsa_fp8_decode_check", "dsa_debug_faults", "dsa_last_error",
 ]
+DSA_FAULT_SEQ_LENS, DSA_FAULT_CU_Q, DSA_FAULT_BLOCK_TABLE = 1, 2, 4
+DSA_FAULT_SLOT_MAPPING, DSA_FAULT_TOPK_INPUT, DSA_FAULT_TOPK_OUTPUT = 8, 16, 32
+DSA_FAULT_UNWRITTEN = 64
 
 
 class DSAError(RuntimeError):
@@ -62,22 +70,25 @@ class _CDims(ctypes.Structure):
         ("softmax_scale", ctypes.c_float)]
 
 
-_lib = None
+_loaded = {}
 
 
-def library_path():
-    return os.path.join(HERE, _LIB_NAME)
+def library_path(variant=None):
+    if variant not in _LIB_NAMES:
+        variant = _variant
+    return os.path.join(HERE, _LIB_NAMES[variant])
 
 
-def load_library():
-    """Load libdsa.so once; raises if it is missing (no fallback path)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    path = library_path()
+def load_library(variant=None):
+    """Load the active library (or `variant`) once; raises if it is missing
+    (no fallback path)."""
+    v = variant if variant in _LIB_NAMES else _variant
+    if v in _loaded:
+        return _loaded[v]
+    path = library_path() if variant is None else library_path(v)
     if not os.path.exists(path):
         raise RuntimeError(
-            "libdsa.so not found at %s; build it with "
+            "%s not found; build it with "
             "`python -m sparse_attention_topk_amd.build`" % path)
     lib = ctypes.CDLL(path)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -98,14 +109,38 @@ def load_library():
         "indexshare_forward_workspace_size": (SZ, [P, P]),
         "indexshare_forward": (ctypes.c_int, [P, I32, P, I32, P, P, P, P, SZ, P]),
         "dsa_fp8_decode_check": (ctypes.c_int, [P, P, I32, P]),
+        "dsa_debug_faults": (ctypes.c_int, [P, I32]),
         "dsa_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
         f.restype = res
         f.argtypes = args
-    _lib = lib
+    _loaded[v] = lib
     return lib
+
+
+@contextlib.contextmanager
+def use_library(variant):
+    """Make `variant` ("release" or "debug") the library every call goes
+    through inside the block."""
+    global _variant
+    if variant not in _LIB_NAMES:
+        raise ValueError("unknown library variant %r" % (variant,))
+    prev = _variant
+    _variant = variant
+    try:
+        yield load_library()
+    finally:
+        _variant = prev
+
+
+def debug_faults(clear=True):
+    """The checked build's fault word (DSA_FAULT_* bits) for the current
+    device; waits for the device.  Raises DSAError on the release build."""
+    out = ctypes.c_uint32(0)
+    _check(load_library().dsa_debug_faults(ctypes.byref(out), 1 if clear else 0))
+    return out.value
 
 
 def exported_symbols():

@@ -212,10 +212,25 @@ int run_indexer(const dsa_batch* b, const void* q, int q_dtype, const float* w,
   a.chunk_range = reinterpret_cast<float2*>(static_cast<char*>(ws) + topk_scores_bytes(b));
   a.range_stride = 0;
   a.chunk_keys = 0;
-  hipError_t e = dsa::launch_indexer_score(a, stream);
+  hipError_t e;
+#ifdef DSA_DEBUG
+  // checked build: metadata validated, output and workspace filled with
+  // canaries before the call, every row checked after it
+  e = dsa::debug_check_batch(*b, stream);
+  if (e == hipSuccess)
+    e = dsa::debug_fill(topk_idx, static_cast<size_t>(b->num_q_tokens) * topk * sizeof(int32_t),
+                        static_cast<uint32_t>(dsa::kCanaryIdx), stream);
+  if (e == hipSuccess) e = dsa::debug_fill(ws, topk_ws(b), dsa::kPoisonWorkspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "checked-build launch");
+#endif
+  e = dsa::launch_indexer_score(a, stream);
   if (e != hipSuccess) return hip_fail(e, "indexer score launch");
   e = dsa::launch_topk(a, stream);
   if (e != hipSuccess) return hip_fail(e, "top-k launch");
+#ifdef DSA_DEBUG
+  e = dsa::debug_check_topk_out(*b, topk_idx, topk, stream);
+  if (e != hipSuccess) return hip_fail(e, "checked-build launch");
+#endif
   return ok();
 }
 
@@ -250,8 +265,32 @@ int run_mla(const dsa_batch* b, const void* q, const void* kv, int dtype,
         round_up(th * sizeof(float)));
     a.call_tag = next_call_tag();
   }
-  hipError_t e = dsa::launch_sparse_mla(a, stream);
+  hipError_t e;
+#ifdef DSA_DEBUG
+  const size_t n_out = static_cast<size_t>(b->num_q_tokens) * n_heads * R;
+  const int out_bytes = dtype == DSA_BF16 ? 2 : 4;
+  const uint32_t out_canary = out_bytes == 2 ? dsa::kCanaryBf16 : dsa::kCanaryF32;
+  e = dsa::debug_check_batch(*b, stream);
+  if (e == hipSuccess) e = dsa::debug_check_topk_in(*b, idx, topk, stream);
+  if (e == hipSuccess)
+    e = dsa::debug_fill(out, n_out * out_bytes,
+                        out_bytes == 2 ? (out_canary | (out_canary << 16)) : out_canary, stream);
+  if (e == hipSuccess && lse)
+    e = dsa::debug_fill(lse, static_cast<size_t>(b->num_q_tokens) * n_heads * sizeof(float),
+                        dsa::kCanaryF32, stream);
+  if (e == hipSuccess)
+    e = dsa::debug_fill(ws, mla_ws(b, n_heads, R, P, topk, dtype), dsa::kPoisonWorkspace, stream);
+  if (e != hipSuccess) return hip_fail(e, "checked-build launch");
+#endif
+  e = dsa::launch_sparse_mla(a, stream);
   if (e != hipSuccess) return hip_fail(e, "sparse MLA launch");
+#ifdef DSA_DEBUG
+  e = dsa::debug_check_unwritten(out, n_out, out_bytes, out_canary, stream);
+  if (e == hipSuccess && lse)
+    e = dsa::debug_check_unwritten(lse, static_cast<size_t>(b->num_q_tokens) * n_heads, 4,
+                                   dsa::kCanaryF32, stream);
+  if (e != hipSuccess) return hip_fail(e, "checked-build launch");
+#endif
   return ok();
 }
 
@@ -341,6 +380,13 @@ int dsa_indexer_cache_write(const void* k_new, int32_t k_dtype, int32_t n_new,
     return fail(DSA_ERR_UNSUPPORTED, "a %s cache stores keys unchanged; key dtype differs",
                 cache_dtype == DSA_BF16 ? "BF16" : "F32");
   }
+#ifdef DSA_DEBUG
+  {
+    const hipError_t ec = dsa::debug_check_slots(slot_mapping, n_new, num_slots,
+                                                 static_cast<hipStream_t>(stream));
+    if (ec != hipSuccess) return hip_fail(ec, "checked-build launch");
+  }
+#endif
   hipError_t e = dsa::launch_cache_write(k_new, k_dtype, n_new, d_idx,
                                          slot_mapping, num_slots, k_cache,
                                          k_scale, cache_dtype,
@@ -444,6 +490,13 @@ int dsa_indexer_prologue(int32_t n_tokens, const dsa_prologue_dims* d, const voi
                 workspace ? ws_bytes : static_cast<size_t>(0));
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
     return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+#ifdef DSA_DEBUG
+  if (slot_mapping) {
+    const hipError_t ec = dsa::debug_check_slots(slot_mapping, n_tokens, num_slots,
+                                                 static_cast<hipStream_t>(stream));
+    if (ec != hipSuccess) return hip_fail(ec, "checked-build launch");
+  }
+#endif
   hipError_t e = dsa::launch_prologue(n_tokens, d, hidden, qa_normed, cos, sin, wq_b, wk,
                                       weights_proj, k_norm_weight, slot_mapping, num_slots,
                                       k_cache, k_scale, cache_dtype, q_out, k_out, w_out,
@@ -569,6 +622,19 @@ int dsa_fp8_decode_check(const uint8_t* codes, float* out, int32_t n,
                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "fp8 decode launch");
   return ok();
+}
+
+int dsa_debug_faults(uint32_t* faults, int32_t clear) {
+  if (!faults) return fail(DSA_ERR_INVALID_ARG, "faults is NULL");
+#ifdef DSA_DEBUG
+  const hipError_t e = dsa::debug_faults(faults, clear != 0);
+  if (e != hipSuccess) return hip_fail(e, "reading the fault word");
+  return ok();
+#else
+  (void)clear;
+  *faults = 0;
+  return fail(DSA_ERR_UNSUPPORTED, "not the checked build (libdsa_debug.so)");
+#endif
 }
 
 const char* dsa_last_error(void) { return g_err; }

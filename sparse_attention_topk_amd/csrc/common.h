@@ -247,6 +247,25 @@ __device__ __forceinline__ int32_t query_pos(const int32_t* seq_lens,
   return min(L - qlen + (t - cu_q[b]), L - 1);
 }
 
+// Checked build (debug.hip): launched around every call when compiled with
+// -DDSA_DEBUG.  Canaries: an index no row can hold, and NaNs with payloads
+// the arithmetic does not produce from finite inputs.
+constexpr int32_t kCanaryIdx = 0x7FFFFFF7;
+constexpr uint32_t kCanaryBf16 = 0xFFC1u;
+constexpr uint32_t kCanaryF32 = 0xFFC00001u;
+constexpr uint32_t kPoisonWorkspace = 0xA5A5A5A5u;
+hipError_t debug_check_batch(const dsa_batch& b, hipStream_t stream);
+hipError_t debug_check_slots(const int64_t* slots, int32_t n, int64_t num_slots,
+                             hipStream_t stream);
+hipError_t debug_check_topk_in(const dsa_batch& b, const int32_t* idx, int32_t topk,
+                               hipStream_t stream);
+hipError_t debug_check_topk_out(const dsa_batch& b, const int32_t* idx, int32_t topk,
+                                hipStream_t stream);
+hipError_t debug_fill(void* p, size_t bytes, uint32_t pattern, hipStream_t stream);
+hipError_t debug_check_unwritten(const void* p, size_t n, int elem_bytes, uint32_t canary,
+                                 hipStream_t stream);
+hipError_t debug_faults(uint32_t* faults, bool clear);   // synchronises the device
+
 // Launchers (each returns hipGetLastError() after its launches).
 hipError_t launch_cache_write(const void* k_new, int k_dtype, int n_new,
                               int d_idx, const int64_t* slot_mapping,

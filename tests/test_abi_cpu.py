@@ -29,6 +29,40 @@ def test_library_exports_every_declared_symbol():
     assert sorted(dsa.exported_symbols()) == declared
 
 
+def test_checked_build_exports_every_declared_symbol():
+    """libdsa_debug.so (the -DDSA_DEBUG build) carries the same ABI."""
+    dsa = ensure_library()
+    lib = dsa.load_library("debug")
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_fault_word_only_in_the_checked_build():
+    """The release library has no fault word: dsa_debug_faults sets 0 and
+    reports DSA_ERR_UNSUPPORTED; both builds reject a NULL destination on
+    the host (no device call is made in any of these)."""
+    dsa = ensure_library()
+    rel = dsa.load_library("release")
+    out = ctypes.c_uint32(77)
+    assert rel.dsa_debug_faults(ctypes.byref(out), 1) == -2
+    assert out.value == 0
+    assert "checked build" in dsa.dsa_last_error()
+    assert rel.dsa_debug_faults(None, 0) == -1
+    assert dsa.load_library("debug").dsa_debug_faults(None, 0) == -1
+    with pytest.raises(dsa.DSAError):
+        dsa.debug_faults()
+
+
+def test_checked_build_validates_arguments_on_the_host_first():
+    """The checked build rejects bad arguments before it enqueues its own
+    checks (fake device addresses are never touched)."""
+    dsa = ensure_library()
+    lib = dsa.load_library("debug")
+    assert _topk(lib, _batch(dsa), q=None) == -1
+    assert _topk(lib, _batch(dsa), ws_bytes=16) == -5
+    assert _topk(lib, _batch(dsa, num_reqs=-1)) == -1
+
+
 def test_resolve_sources_matches_the_oracle():
     from oracle import indexshare as ix
     dsa = ensure_library()

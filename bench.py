@@ -681,11 +681,10 @@ def bench_indexshare(args, cfg, b, bb, dsa, torch, stream):
     from synth import make_layer
     dev = "cuda"
     types = cfg.indexer_types
-    src = []
-    last = None
-    for i, t in enumerate(types):
-        last = i if t == "full" else last
-        src.append(last)
+    codes = [dsa.DSA_LAYER_FULL if t == "full" else dsa.DSA_LAYER_SHARED for t in types]
+    # each layer's top-k source, from the library (the layers that own an
+    # indexer are those that are their own source)
+    src = dsa.dsa_resolve_indexer_sources(codes, len(types))
     N = b.num_q_tokens
     layers, lays = [], []
     for i in range(len(types)):
@@ -702,7 +701,6 @@ def bench_indexshare(args, cfg, b, bb, dsa, torch, stream):
     dims = dsa.StackDims(cfg.n_idx_heads, cfg.d_idx, dsa.DSA_BF16, dsa.DSA_BF16, cfg.topk,
                          cfg.n_heads, cfg.kv_lora_rank, cfg.rope_dim, dsa.DSA_BF16,
                          cfg.softmax_scale)
-    codes = [dsa.DSA_LAYER_FULL if t == "full" else dsa.DSA_LAYER_SHARED for t in types]
     ws = torch.empty(max(256, dsa.indexshare_forward_workspace_size(bb, dims)),
                      dtype=torch.uint8, device=dev)
 

@@ -149,14 +149,21 @@ int dsa_indexer_cache_write(const void* k_new, int32_t k_dtype, int32_t n_new,
  * (FP8 queries: dsa_indexer_topk_fp8q);
  * n_heads 1..64 and d_idx 1..256 (the matrix-core path needs n_heads % 32 == 0
  * and d_idx == 128; other shapes take a slower vector path); topk 1..4096.
- * workspace: at least dsa_indexer_topk_workspace_size() bytes, 256-byte
- * aligned; contents on entry are ignored.  It holds the fp32 score rows
- * [N, max_seq_len rounded up to 64] and, behind them, the range (min, max)
- * of each token's scores in each key chunk, which the score pass writes
- * when rows can exceed 32768 keys so that the selection, which then streams
- * its rows from memory, needs no range pass of its own.
+ * workspace: 256-byte aligned; contents on entry are ignored.  Per query
+ * token it holds an fp32 score row (max_seq_len rounded up to 64) and,
+ * behind the rows, the range (min, max) of the token's scores in each key
+ * chunk, which the score pass writes when rows can exceed 32768 keys so that
+ * the selection, which then streams its rows from memory, needs no range
+ * pass of its own.  With dsa_indexer_topk_workspace_size() bytes the whole
+ * batch is scored and selected in one pass.  A smaller workspace, of at
+ * least dsa_indexer_topk_workspace_min() bytes (the rows of 16 query tokens,
+ * or of all of them when there are fewer), is used window by window: the
+ * query tokens go through score + selection in consecutive windows of as
+ * many tokens as it holds (whole blocks of 16 when it can), with the same
+ * result.  Below the minimum: DSA_ERR_WORKSPACE.
  */
 size_t dsa_indexer_topk_workspace_size(const dsa_batch* batch, int32_t topk);
+size_t dsa_indexer_topk_workspace_min(const dsa_batch* batch, int32_t topk);
 int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
                      const float* w, int32_t n_heads, int32_t d_idx,
                      const void* k_cache, const float* k_scale,

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     DSA_F32, DSA_BF16, DSA_FP8_E4M3, DSA_LAYER_FULL, DSA_LAYER_SHARED,
     DSAError, Batch, library_path, load_library, exported_symbols,
     dsa_indexer_cache_write, dsa_indexer_topk, dsa_indexer_topk_workspace_size,
+    dsa_indexer_topk_workspace_min,
     dsa_indexer_topk_noalloc, dsa_rotate_quantize, dsa_indexer_topk_fp8q,
     dsa_indexer_prologue,
     sparse_mla_attn, sparse_mla_attn_workspace_size,

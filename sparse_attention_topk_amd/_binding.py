@@ -23,6 +23,7 @@ DSA_LAYER_FULL, DSA_LAYER_SHARED = 0, 1
 
 EXPORTS = [
     "dsa_indexer_cache_write", "dsa_indexer_topk_workspace_size",
+    "dsa_indexer_topk_workspace_min",
     "dsa_indexer_topk", "dsa_indexer_topk_noalloc", "dsa_rotate_quantize",
     "dsa_indexer_topk_fp8q", "dsa_indexer_prologue_workspace_size", "dsa_indexer_prologue",
     "sparse_mla_attn_workspace_size",
@@ -96,6 +97,7 @@ def load_library(variant=None):
     sig = {
         "dsa_indexer_cache_write": (ctypes.c_int, [P, I32, I32, I32, P, I64, P, P, I32, P]),
         "dsa_indexer_topk_workspace_size": (SZ, [P, I32]),
+        "dsa_indexer_topk_workspace_min": (SZ, [P, I32]),
         "dsa_indexer_topk": (ctypes.c_int, [P, P, I32, P, I32, I32, P, P, I32, I32, P, P, SZ, P]),
         "dsa_indexer_topk_noalloc": (ctypes.c_int, [P, P, I32, P, I32, I32, P, P, I32, I32, P, P]),
         "dsa_rotate_quantize": (ctypes.c_int, [P, I32, I64, I32, P, I64, P, P, P]),
@@ -249,6 +251,13 @@ def dsa_indexer_cache_write(k_new, slot_mapping, k_cache, k_scale=None,
 def dsa_indexer_topk_workspace_size(batch, topk):
     cb = batch.c()
     return load_library().dsa_indexer_topk_workspace_size(ctypes.byref(cb), topk)
+
+
+def dsa_indexer_topk_workspace_min(batch, topk):
+    """The least workspace dsa_indexer_topk accepts (it then works through the
+    query tokens in windows)."""
+    cb = batch.c()
+    return load_library().dsa_indexer_topk_workspace_min(ctypes.byref(cb), topk)
 
 
 def _workspace(nbytes, device, workspace, stream=None):

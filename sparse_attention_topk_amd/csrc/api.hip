@@ -90,16 +90,37 @@ int64_t score_row_stride(const dsa_batch* b) {
   return (static_cast<int64_t>(b->max_seq_len) + 63) / 64 * 64;
 }
 
-// fp32 score rows, then the per-chunk score ranges
-size_t topk_scores_bytes(const dsa_batch* b) {
-  return round_up(static_cast<size_t>(b->num_q_tokens) *
-                  static_cast<size_t>(score_row_stride(b)) * sizeof(float));
+// fp32 score rows, then the per-chunk score ranges, of a window of n query
+// tokens
+size_t topk_scores_bytes(const dsa_batch* b, int64_t n) {
+  return round_up(static_cast<size_t>(n) * static_cast<size_t>(score_row_stride(b)) *
+                  sizeof(float));
 }
-size_t topk_ws(const dsa_batch* b) {
-  return topk_scores_bytes(b) +
-         round_up(static_cast<size_t>(b->num_q_tokens) *
+size_t topk_ws_n(const dsa_batch* b, int64_t n) {
+  return topk_scores_bytes(b, n) +
+         round_up(static_cast<size_t>(n) *
                   static_cast<size_t>(dsa::indexer_range_stride_max(b->max_seq_len)) *
                   2 * sizeof(float));
+}
+// the whole batch in one window (the fastest), and the least accepted: a
+// window of kMinWindow tokens (fewer when the batch has fewer)
+constexpr int64_t kMinWindow = 16;
+size_t topk_ws(const dsa_batch* b) { return topk_ws_n(b, b->num_q_tokens); }
+size_t topk_ws_min(const dsa_batch* b) {
+  return topk_ws_n(b, b->num_q_tokens < kMinWindow ? b->num_q_tokens : kMinWindow);
+}
+// the query tokens per window that a workspace of ws_bytes holds (>= 1 when
+// ws_bytes >= topk_ws_min): the whole batch, else whole blocks of 16 tokens
+int64_t topk_window(const dsa_batch* b, size_t ws_bytes) {
+  const int64_t n = b->num_q_tokens;
+  if (topk_ws_n(b, n) <= ws_bytes) return n;
+  const size_t per = static_cast<size_t>(score_row_stride(b)) * sizeof(float) +
+                     static_cast<size_t>(dsa::indexer_range_stride_max(b->max_seq_len)) *
+                         2 * sizeof(float);
+  int64_t w = static_cast<int64_t>(ws_bytes / per);
+  if (w >= kMinWindow) w = w / kMinWindow * kMinWindow;
+  while (w > 1 && topk_ws_n(b, w) > ws_bytes) w -= (w > kMinWindow ? kMinWindow : 1);
+  return w < 1 ? 1 : (w > n ? n : w);
 }
 
 size_t mla_ws(const dsa_batch* b, int n_heads, int R, int P, int topk, int dtype) {
@@ -157,9 +178,10 @@ int check_indexer(const dsa_batch* b, const void* q, int q_dtype,
   if (topk < 1 || topk > DSA_MAX_TOPK)
     return fail(DSA_ERR_UNSUPPORTED, "topk %d outside 1..%d", topk, DSA_MAX_TOPK);
   if (!check_ws) return DSA_OK;
-  if (b->num_q_tokens > 0 && (!ws || ws_bytes < topk_ws(b)))
-    return fail(DSA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", topk_ws(b),
-                ws ? ws_bytes : static_cast<size_t>(0));
+  if (b->num_q_tokens > 0 && (!ws || ws_bytes < topk_ws_min(b)))
+    return fail(DSA_ERR_WORKSPACE,
+                "workspace needs at least %zu bytes (%zu for the batch in one pass), got %zu",
+                topk_ws_min(b), topk_ws(b), ws ? ws_bytes : static_cast<size_t>(0));
   if (reinterpret_cast<uintptr_t>(ws) % kAlign)
     return fail(DSA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   return DSA_OK;
@@ -190,9 +212,11 @@ int check_mla(const dsa_batch* b, const void* q, const void* kv, int dtype,
   return DSA_OK;
 }
 
+// Score + top-k over the batch's query tokens, in windows of as many
+// tokens as the workspace holds (one window when it holds the batch).
 int run_indexer(const dsa_batch* b, const void* q, int q_dtype, const float* w,
                 int n_heads, int d_idx, const void* k_cache, const float* k_scale,
-                int cache_dtype, int topk, int32_t* topk_idx, void* ws,
+                int cache_dtype, int topk, int32_t* topk_idx, void* ws, size_t ws_bytes,
                 hipStream_t stream, const float* q_scale = nullptr) {
   dsa::IndexerArgs a;
   a.b = *b;
@@ -207,26 +231,33 @@ int run_indexer(const dsa_batch* b, const void* q, int q_dtype, const float* w,
   a.cache_dtype = cache_dtype;
   a.topk = topk;
   a.topk_idx = topk_idx;
-  a.scores = static_cast<float*>(ws);
   a.row_stride = score_row_stride(b);
-  a.chunk_range = reinterpret_cast<float2*>(static_cast<char*>(ws) + topk_scores_bytes(b));
-  a.range_stride = 0;
-  a.chunk_keys = 0;
+  const int64_t n = b->num_q_tokens;
+  const int64_t win = n > 0 ? topk_window(b, ws_bytes) : 0;
   hipError_t e;
 #ifdef DSA_DEBUG
   // checked build: metadata validated, output and workspace filled with
   // canaries before the call, every row checked after it
   e = dsa::debug_check_batch(*b, stream);
   if (e == hipSuccess)
-    e = dsa::debug_fill(topk_idx, static_cast<size_t>(b->num_q_tokens) * topk * sizeof(int32_t),
+    e = dsa::debug_fill(topk_idx, static_cast<size_t>(n) * topk * sizeof(int32_t),
                         static_cast<uint32_t>(dsa::kCanaryIdx), stream);
-  if (e == hipSuccess) e = dsa::debug_fill(ws, topk_ws(b), dsa::kPoisonWorkspace, stream);
+  if (e == hipSuccess && win > 0)
+    e = dsa::debug_fill(ws, topk_ws_n(b, win), dsa::kPoisonWorkspace, stream);
   if (e != hipSuccess) return hip_fail(e, "checked-build launch");
 #endif
-  e = dsa::launch_indexer_score(a, stream);
-  if (e != hipSuccess) return hip_fail(e, "indexer score launch");
-  e = dsa::launch_topk(a, stream);
-  if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  for (int64_t w0 = 0; w0 < n; w0 += win) {
+    a.win_lo = static_cast<int32_t>(w0);
+    a.win_hi = static_cast<int32_t>(w0 + win < n ? w0 + win : n);
+    a.scores = static_cast<float*>(ws);
+    a.chunk_range = reinterpret_cast<float2*>(static_cast<char*>(ws) + topk_scores_bytes(b, win));
+    a.range_stride = 0;
+    a.chunk_keys = 0;
+    e = dsa::launch_indexer_score(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "indexer score launch");
+    e = dsa::launch_topk(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+  }
 #ifdef DSA_DEBUG
   e = dsa::debug_check_topk_out(*b, topk_idx, topk, stream);
   if (e != hipSuccess) return hip_fail(e, "checked-build launch");
@@ -401,6 +432,12 @@ size_t dsa_indexer_topk_workspace_size(const dsa_batch* batch, int32_t topk) {
   return topk_ws(batch);
 }
 
+size_t dsa_indexer_topk_workspace_min(const dsa_batch* batch, int32_t topk) {
+  (void)topk;
+  if (!batch || batch->num_q_tokens < 0 || batch->max_seq_len < 0) return 0;
+  return topk_ws_min(batch);
+}
+
 int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
                      const float* w, int32_t n_heads, int32_t d_idx,
                      const void* k_cache, const float* k_scale,
@@ -410,7 +447,7 @@ int dsa_indexer_topk(const dsa_batch* batch, const void* q, int32_t q_dtype,
                          cache_dtype, topk, topk_idx, workspace, ws_bytes);
   if (st) return st;
   return run_indexer(batch, q, q_dtype, w, n_heads, d_idx, k_cache, k_scale,
-                     cache_dtype, topk, topk_idx, workspace,
+                     cache_dtype, topk, topk_idx, workspace, ws_bytes,
                      static_cast<hipStream_t>(stream));
 }
 
@@ -444,7 +481,7 @@ int dsa_indexer_topk_fp8q(const dsa_batch* batch, const uint8_t* q_codes,
                          DSA_FP8_E4M3, topk, topk_idx, workspace, ws_bytes, true, q_scale);
   if (st) return st;
   return run_indexer(batch, q_codes, DSA_FP8_E4M3, w, n_heads, d_idx, k_cache, k_scale,
-                     DSA_FP8_E4M3, topk, topk_idx, workspace,
+                     DSA_FP8_E4M3, topk, topk_idx, workspace, ws_bytes,
                      static_cast<hipStream_t>(stream), q_scale);
 }
 
@@ -525,7 +562,8 @@ int dsa_indexer_topk_noalloc(const dsa_batch* batch, const void* q, int32_t q_dt
   st = scratch_on_current_device(static_cast<hipStream_t>(stream), &ws);
   if (st) return st;
   return run_indexer(batch, q, q_dtype, w, n_heads, d_idx, k_cache, k_scale,
-                     cache_dtype, topk, topk_idx, ws, static_cast<hipStream_t>(stream));
+                     cache_dtype, topk, topk_idx, ws, topk_ws(batch),
+                     static_cast<hipStream_t>(stream));
 }
 
 size_t sparse_mla_attn_workspace_size(const dsa_batch* batch, int32_t n_heads,
@@ -598,7 +636,7 @@ int indexshare_forward(const dsa_batch* batch, int32_t n_layers,
     if (src_stack[i] == i) {
       st = run_indexer(batch, L.q_idx, d->q_idx_dtype, L.w, d->n_idx_heads,
                        d->d_idx, L.k_cache, L.k_scale, d->idx_cache_dtype,
-                       d->topk, L.topk_idx, workspace, s);
+                       d->topk, L.topk_idx, workspace, ws_bytes, s);
       if (st) return st;
       active = L.topk_idx;
     }

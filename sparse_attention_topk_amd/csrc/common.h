@@ -295,6 +295,11 @@ struct IndexerArgs {
   float2* chunk_range;
   int32_t range_stride;   // entries per token
   int32_t chunk_keys;     // keys per chunk
+  // Query-token window of this launch pair: only tokens t in [win_lo,
+  // win_hi) are scored and selected, and their score and range rows sit at
+  // row t - win_lo of the workspace (a workspace smaller than the whole
+  // batch's is used window by window).
+  int32_t win_lo = 0, win_hi = 0;
 };
 constexpr int kRangeParts = 4;   // entries per chunk (one per score wave)
 // Rows up to this many keys are selected from registers, where finding the

@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_score_prefill(
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ block_table,
     int32_t max_blocks, int32_t block_size, int64_t num_slots, int32_t max_seq_len,
     int32_t qbpr, int32_t num_reqs, int32_t chunk_keys, float* __restrict__ scores,
-    int64_t row_stride, float2* __restrict__ crange, int32_t range_stride) {
+    int64_t row_stride, float2* __restrict__ crange, int32_t range_stride, int32_t win_lo,
+    int32_t win_hi) {
   // Queries as MFMA B operands of v_mfma_f32_32x32x16_bf16 whose 32 columns
   // are the 16 tokens x one pair of heads: block (p, s) is 1 KB at
   // 1024 (8 p + s); lane l's 16 bytes at 16 l hold token l % 16, head
@@ -106,6 +107,11 @@ __global__ __launch_bounds__(kPThreads, 1) void k_score_prefill(
   const int32_t t0 = qb * kPT;
   if (t0 >= qlen) return;
   const int nt = min(kPT, qlen - t0);
+  // the block's tokens inside the window: tl_lo .. tl_hi - 1 (the others
+  // are computed with the block but not stored)
+  const int32_t tw = tbeg + t0;
+  const int tl_lo = max(tw, win_lo) - tw, tl_hi = min(tw + nt, win_hi) - tw;
+  if (tl_lo >= tl_hi) return;
   const int32_t pos0 = L - qlen + t0;
   const int32_t key_end = pos0 + nt;          // keys 0 .. key_end - 1
   if (key_end <= 0) return;
@@ -161,12 +167,12 @@ __global__ __launch_bounds__(kPThreads, 1) void k_score_prefill(
       for (int st = 0; st < 8; ++st)
         dst[kb][st] = *reinterpret_cast<const bf16x8*>(base + 32 * kb * kPD + 16 * st);
   };
-  // score rows t0 .. t0 + nt - 1 of the request as one buffer: byte offset
-  // 4 (row_stride tl + key).  The scores stream out non-temporally, so the
-  // key cache keeps its place in L2.
+  // score rows of the block's tokens tl_lo .. tl_hi - 1 as one buffer: byte
+  // offset 4 (row_stride (tl - tl_lo) + key).  The scores stream out
+  // non-temporally, so the key cache keeps its place in L2.
   const __amdgpu_buffer_rsrc_t srows = __builtin_amdgcn_make_buffer_rsrc(
-      scores + (tbeg + t0) * row_stride, 0,
-      static_cast<int>(static_cast<uint32_t>(nt * row_stride * 4)), 0x00020000);
+      scores + (tw + tl_lo - win_lo) * row_stride, 0,
+      static_cast<int>(static_cast<uint32_t>((tl_hi - tl_lo) * row_stride * 4)), 0x00020000);
   // The key registers are re-defined by an empty asm once their loads are
   // in (here and after each step's copy), so the wait counts inside the
   // head loop never tie it to the step's own stores or next loads.
@@ -288,8 +294,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_score_prefill(
             rmax = fmaxf(rmax, causal ? v[i] : -INFINITY);
           }
         }
-        const bool keep = tl < nt && key <= my_pos;
-        const int off = keep ? static_cast<int>(4 * (tl * row_stride + key)) : -1;
+        const bool keep = tl >= tl_lo && tl < tl_hi && key <= my_pos;
+        const int off = keep ? static_cast<int>(4 * ((tl - tl_lo) * row_stride + key)) : -1;
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), srows, off, 0, kStreamStore);
       }
     s_cur = s_next;
@@ -314,8 +320,8 @@ __global__ __launch_bounds__(kPThreads, 1) void k_score_prefill(
           const float2 o = rsh[e * (kPWaves / kRangeParts) + i][tt];
           r = make_float2(fminf(r.x, o.x), fmaxf(r.y, o.y));
         }
-        if (tt < nt)
-          crange[(tbeg + t0 + tt) * static_cast<int64_t>(range_stride) + chunk * kRangeParts + e] = r;
+        if (tt >= tl_lo && tt < tl_hi)
+          crange[(tw + tt - win_lo) * static_cast<int64_t>(range_stride) + chunk * kRangeParts + e] = r;
       }
       lds_barrier();
       rmin = INFINITY;
@@ -351,7 +357,7 @@ hipError_t launch_score_prefill(IndexerArgs& a, hipStream_t stream) {
       static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k_cache),
       b.seq_lens, b.cu_q, b.block_table, b.max_blocks, b.block_size, b.num_slots,
       b.max_seq_len, qbpr, b.num_reqs, chunk_keys, a.scores, a.row_stride,
-      a.chunk_range, a.range_stride);
+      a.chunk_range, a.range_stride, a.win_lo, a.win_hi);
   return hipGetLastError();
 }
 

@@ -141,7 +141,8 @@ __global__ __launch_bounds__(256, MAXT <= 32 ? 2 : 1) void k_score_dma(
     int32_t max_blocks, int32_t block_size, int64_t num_slots,
     int32_t max_seq_len, int32_t qblocks_per_req, int32_t nchunks,
     int32_t tiles_per_wave_arg, float* __restrict__ scores, int64_t row_stride,
-    float2* __restrict__ crange, int32_t range_stride, int32_t B) {
+    float2* __restrict__ crange, int32_t range_stride, int32_t B, int32_t win_lo,
+    int32_t win_hi) {
   constexpr int H = 32 * MT;
   static_assert(!QF8 || F8, "e4m3 queries go with an e4m3 cache");
   using DT = DmaTile<F8>;
@@ -186,6 +187,8 @@ __global__ __launch_bounds__(256, MAXT <= 32 ? 2 : 1) void k_score_dma(
   const int32_t t0 = qb * TQ;
   if (t0 >= qlen) return;
   const int nt = min(TQ, qlen - t0);
+  // the block's tokens tbeg + t0 .. + nt - 1: nothing to do outside the window
+  if (tbeg + t0 + nt <= win_lo || tbeg + t0 >= win_hi) return;
   const int32_t pos0 = L - qlen + t0;
   const int32_t key_end = min(pos0 + nt, key_lim);
   if (key_beg >= key_end) return;
@@ -431,8 +434,8 @@ __global__ __launch_bounds__(256, MAXT <= 32 ? 2 : 1) void k_score_dma(
           // one entry per tile: range chunks of 128 keys, one part per tile
           float lo = causal ? v : INFINITY, hi = causal ? v : -INFINITY;
           half_minmax(lo, hi);
-          if (col == 0 && hf < nt)
-            crange[(tbeg + t0 + hf) * static_cast<int64_t>(range_stride) + first_tile +
+          if (col == 0 && hf < nt && tbeg + t0 + hf >= win_lo && tbeg + t0 + hf < win_hi)
+            crange[(tbeg + t0 + hf - win_lo) * static_cast<int64_t>(range_stride) + first_tile +
                    kWaves * i] = make_float2(lo, hi);
         } else {
           rmin = fminf(rmin, causal ? v : INFINITY);
@@ -446,9 +449,9 @@ __global__ __launch_bounds__(256, MAXT <= 32 ? 2 : 1) void k_score_dma(
   // ---- the wave's range entries: one per token of the block
   if constexpr (!SPAN) {
     if (crange) half_minmax(rmin, rmax);
-    if (crange && col == 0 && hf < nt)
-      crange[(tbeg + t0 + hf) * static_cast<int64_t>(range_stride) + chunk * kRangeParts + wave] =
-          make_float2(rmin, rmax);
+    if (crange && col == 0 && hf < nt && tbeg + t0 + hf >= win_lo && tbeg + t0 + hf < win_hi)
+      crange[(tbeg + t0 + hf - win_lo) * static_cast<int64_t>(range_stride) +
+             chunk * kRangeParts + wave] = make_float2(rmin, rmax);
   }
 
   // ---- write the chunk's scores: token tt, keys key_beg .. key_end - 1
@@ -459,7 +462,9 @@ __global__ __launch_bounds__(256, MAXT <= 32 ? 2 : 1) void k_score_dma(
 #pragma unroll
   for (int tt = 0; tt < TQ; ++tt) {
     if (tt >= nt) break;
-    float* row = scores + (tbeg + t0 + tt) * row_stride + key_beg;
+    const int64_t tok = tbeg + t0 + tt;
+    if (tok < win_lo || tok >= win_hi) continue;
+    float* row = scores + (tok - win_lo) * row_stride + key_beg;
     for (int c = threadIdx.x; c < n4; c += 256)
       reinterpret_cast<float4*>(row)[c] = reinterpret_cast<const float4*>(&sc[tt][0])[c];
   }
@@ -471,8 +476,10 @@ __global__ __launch_bounds__(256, MAXT <= 32 ? 2 : 1) void k_score_dma(
     auto tiles_of = [&](int bb) -> uint32_t {
       if (bb >= B) return 0u;
       const int32_t L = min(seq_lens[bb], max_seq_len);
-      const int32_t ql = cu_q[bb + 1] - cu_q[bb];
-      return (ql > 0 && L > 0) ? static_cast<uint32_t>((L + 127) / 128 * 4) : 0u;
+      const int32_t c = cu_q[bb];
+      const int32_t ql = cu_q[bb + 1] - c;
+      return (ql > 0 && L > 0 && c >= win_lo && c < win_hi)
+                 ? static_cast<uint32_t>((L + 127) / 128 * 4) : 0u;
     };
     uint32_t total = 0;
     for (int b0 = 0; b0 < B; b0 += 64)
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(256, MAXT <= 32 ? 2 : 1) void k_score_dma(
             const int bb = b0 + i;
             const uint32_t first_pad =
                 static_cast<uint32_t>((min(seq_lens[bb], max_seq_len) + kTile - 1) / kTile);
-            const int64_t rrow = static_cast<int64_t>(cu_q[bb]) * range_stride;
+            const int64_t rrow = static_cast<int64_t>(cu_q[bb] - win_lo) * range_stride;
             for (uint32_t tt = max(lt, first_pad) + threadIdx.x; tt < lt + cnt; tt += 256)
               crange[rrow + tt] = make_float2(INFINITY, -INFINITY);
           }
@@ -558,7 +565,7 @@ hipError_t launch_dma_t(IndexerArgs& a, int qbpr, int nchunks, int64_t tpw,
       static_cast<const uint8_t*>(a.k_cache), a.k_scale, b.seq_lens, b.cu_q,
       b.block_table, b.max_blocks, b.block_size, b.num_slots, b.max_seq_len,
       qbpr, nchunks, static_cast<int32_t>(tpw), a.scores, a.row_stride, a.chunk_range,
-      a.range_stride, b.num_reqs);
+      a.range_stride, b.num_reqs, a.win_lo, a.win_hi);
   return hipGetLastError();
 }
 
@@ -600,10 +607,10 @@ __global__ __launch_bounds__(256) void k_score_vector(
     const int32_t* __restrict__ cu_q, int32_t B,
     const int32_t* __restrict__ block_table, int32_t max_blocks,
     int32_t block_size, int64_t num_slots, int32_t max_seq_len,
-    int32_t key_blocks, float* __restrict__ scores, int64_t row_stride) {
+    int32_t key_blocks, float* __restrict__ scores, int64_t row_stride, int32_t win_lo) {
   __shared__ float sq[8192];
   __shared__ float sw[64];
-  const int t = blockIdx.x / key_blocks;
+  const int t = win_lo + static_cast<int>(blockIdx.x / key_blocks);
   const int kb = blockIdx.x % key_blocks;
   const int b = request_of(cu_q, B, t);
   const int32_t pos = query_pos(seq_lens, cu_q, b, t, max_seq_len);
@@ -628,7 +635,7 @@ __global__ __launch_bounds__(256) void k_score_vector(
     }
     if (cache_dtype == DSA_FP8_E4M3) score *= kscale[slot];
   }
-  scores[static_cast<int64_t>(t) * row_stride + s] = score;
+  scores[static_cast<int64_t>(t - win_lo) * row_stride + s] = score;
 }
 
 }  // namespace
@@ -664,12 +671,13 @@ hipError_t launch_indexer_score(IndexerArgs& a, hipStream_t stream) {
   }
   a.chunk_range = nullptr;   // the top-k finds the range itself (vector path)
   const int key_blocks = (b.max_seq_len + 255) / 256;
-  const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * key_blocks;
+  const int64_t grid = static_cast<int64_t>(a.win_hi - a.win_lo) * key_blocks;
+  if (grid <= 0) return hipSuccess;
   k_score_vector<<<static_cast<unsigned>(grid), 256, 0, stream>>>(
       a.q, a.q_dtype, a.q_scale, a.w, a.k_cache, a.k_scale, a.cache_dtype, a.n_heads,
       a.d_idx, b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
       b.block_size, b.num_slots, b.max_seq_len, key_blocks, a.scores,
-      a.row_stride);
+      a.row_stride, a.win_lo);
   return hipGetLastError();
 }
 

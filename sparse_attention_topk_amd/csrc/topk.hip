@@ -923,11 +923,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
     const float2* __restrict__ crange, int32_t range_stride, int32_t chunk_keys,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
     int32_t B, int32_t max_seq_len, int32_t topk, int32_t* __restrict__ out,
-    int32_t words_cap) {
+    int32_t words_cap, int32_t t_lo) {
   __shared__ Shared s;
   extern __shared__ uint32_t dyn[];   // long rows: words_cap > 0
-  const int t = blockIdx.x;
-  const float* src = scores + static_cast<int64_t>(t) * row_stride;
+  // query token t_lo + blockIdx.x; its score and range rows are row blockIdx.x
+  const int t = t_lo + static_cast<int>(blockIdx.x);
+  const float* src = scores + static_cast<int64_t>(blockIdx.x) * row_stride;
   // The request lookup (the largest b with cu_q[b] <= t, counted with a
   // ballot over 64 entries per load) reads its first entries before the
   // row is requested: loads return in order, so behind the row's 128 KB it
@@ -939,7 +940,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_topk(
   float f[kKpt];
   load_row_regs(src, row_stride, f);
   // and the first kThreads of its score-range entries
-  const float2* rng = crange ? crange + static_cast<int64_t>(t) * range_stride : nullptr;
+  const float2* rng = crange ? crange + static_cast<int64_t>(blockIdx.x) * range_stride : nullptr;
   float2 pre = make_float2(INFINITY, -INFINITY);
   if (rng && static_cast<int>(threadIdx.x) < range_stride) pre = rng[threadIdx.x];
   int n = __popcll(__ballot(lane < B && c0 <= t));
@@ -973,10 +974,10 @@ template <int T>
 __global__ __launch_bounds__(T, 2048 / T) void k_topk_reg(
     const float* __restrict__ scores, int64_t row_stride,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
-    int32_t B, int32_t max_seq_len, int32_t topk, int32_t* __restrict__ out) {
+    int32_t B, int32_t max_seq_len, int32_t topk, int32_t* __restrict__ out, int32_t t_lo) {
   __shared__ ShrT<T> s;
-  const int t = blockIdx.x;
-  const float* src = scores + static_cast<int64_t>(t) * row_stride;
+  const int t = t_lo + static_cast<int>(blockIdx.x);
+  const float* src = scores + static_cast<int64_t>(blockIdx.x) * row_stride;
   const int lane = threadIdx.x & 63;
   const int32_t c0 = cu_q[lane < B ? lane : B];      // cu_q has B + 1 entries
   asm volatile("" ::: "memory");
@@ -1002,17 +1003,18 @@ __global__ __launch_bounds__(T, 2048 / T) void k_topk_reg(
 }  // namespace
 
 hipError_t launch_topk(const IndexerArgs& a, hipStream_t stream) {
-  if (a.b.num_q_tokens == 0) return hipSuccess;
+  const int rows = a.win_hi - a.win_lo;      // the window's query tokens
+  if (rows <= 0) return hipSuccess;
   if (a.b.max_seq_len <= 32 * 256) {
-    k_topk_reg<256><<<a.b.num_q_tokens, 256, 0, stream>>>(
+    k_topk_reg<256><<<rows, 256, 0, stream>>>(
         a.scores, a.row_stride, a.b.seq_lens, a.b.cu_q, a.b.num_reqs, a.b.max_seq_len,
-        a.topk, a.topk_idx);
+        a.topk, a.topk_idx, a.win_lo);
     return hipGetLastError();
   }
   if (a.b.max_seq_len <= 32 * 512) {
-    k_topk_reg<512><<<a.b.num_q_tokens, 512, 0, stream>>>(
+    k_topk_reg<512><<<rows, 512, 0, stream>>>(
         a.scores, a.row_stride, a.b.seq_lens, a.b.cu_q, a.b.num_reqs, a.b.max_seq_len,
-        a.topk, a.topk_idx);
+        a.topk, a.topk_idx, a.win_lo);
     return hipGetLastError();
   }
   // long rows' bitmaps and candidate positions in dynamic LDS, sized for the
@@ -1020,9 +1022,9 @@ hipError_t launch_topk(const IndexerArgs& a, hipStream_t stream) {
   const int32_t words_cap = a.b.max_seq_len > kRegCap
                                 ? (min(a.b.max_seq_len, kLongCap) + 31) / 32 : 0;
   const size_t dyn_bytes = words_cap > 0 ? (2 * static_cast<size_t>(words_cap) + kCandCap) * 4 : 0;
-  k_topk<<<a.b.num_q_tokens, kThreads, dyn_bytes, stream>>>(
+  k_topk<<<rows, kThreads, dyn_bytes, stream>>>(
       a.scores, a.row_stride, a.chunk_range, a.range_stride, a.chunk_keys, a.b.seq_lens,
-      a.b.cu_q, a.b.num_reqs, a.b.max_seq_len, a.topk, a.topk_idx, words_cap);
+      a.b.cu_q, a.b.num_reqs, a.b.max_seq_len, a.topk, a.topk_idx, words_cap, a.win_lo);
   return hipGetLastError();
 }
 

@@ -319,26 +319,32 @@ __device__ __forceinline__ void select_row_regs(ShrT<T>& s, float (&f)[kKpt], in
         if (f[4 * j + e] == vmax) atomicOr(&s.bm_eq[word_of(j)], bit_of(e));
     }
   } else {
-    // ---- 2. histogram and threshold bin: bin = trunc(clamp(f * inv - vmin *
-    // inv, 0, 2047)), monotone in f; NaN lands in bin 0.  The map needs a
-    // finite, non-zero inv and a finite offset: a range narrower than about
+    // ---- 2. histogram and threshold bin: 2048 value-linear bins of [vmin,
+    // vmax], monotone in f; NaN lands in bin 0.  The map needs a finite,
+    // non-zero inv and an offset below 2^23: a range narrower than about
     // 6e-36 (scores all in the subnormal range) overflows inv, one wider than
-    // the largest float underflows it.  Such rows (workgroup-uniform) take
-    // the exact radix select instead.
-    const float inv = static_cast<float>(kBins) / (vmax - vmin);
+    // the largest float underflows it, and one narrower than about 1e-3 of
+    // the scores' magnitude overflows the offset.  Such rows
+    // (workgroup-uniform) take the exact radix select instead.
+    const float inv = 8190.0f / (vmax - vmin);   // 4 per bin: see the bin map below
     const float off = -vmin * inv;
-    const bool linear = inv > 0.0f && inv < INFINITY && off > -INFINITY && off < INFINITY;
+    const bool linear = inv > 0.0f && inv < INFINITY && fabsf(off) < 8388608.0f;
     bool ranked = false;     // the selection is complete without the radix select
     if (linear) {
-      // fmaxf maps NaN to 0 (IEEE maxNum), so the conversion is always defined
-      auto bin = [&](float x) {
-        return static_cast<int>(fminf(fmaxf(fmaf(x, inv, off), 0.0f), kBins - 1.0f));
-      };
+      // t = x inv + off lies in [-0.5, 8190.5] for every key (|off| < 2^23
+      // rounds by at most 1/2), and the key's counter sits at byte offset
+      // trunc(t) & ~3: bin floor(t / 4), 0 .. 2047, monotone in x.  The
+      // conversion (v_cvt_u32_f32) sends negative t and NaN to 0.
 #pragma unroll
       for (int j = 0; j < kKpt / 4; ++j) {
         if (!live(j)) continue;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) atomicAdd(&s.hist[bin(f[4 * j + e])], 1u);
+        for (int e = 0; e < 4; ++e) {
+          uint32_t u;
+          asm("v_cvt_u32_f32 %0, %1" : "=v"(u) : "v"(fmaf(f[4 * j + e], inv, off)));
+          atomicAdd(reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(s.hist) +
+                                                (u & 0x1FFCu)), 1u);
+        }
       }
       lds_barrier();
       if (tid == T - 1) s.hist[0] -= absent;
@@ -352,13 +358,13 @@ __device__ __forceinline__ void select_row_regs(ShrT<T>& s, float (&f)[kKpt], in
       if (bin_count <= static_cast<uint32_t>(kRankCap)) {
         // ---- 3a. one pass: keys of higher bins are taken, keys of the
         // threshold bin become (score, position) candidates.  With t the same
-        // fma as in the bin map, bin > sel <=> t >= sel + 1 (sel < 2047) and
-        // bin >= sel <=> t >= sel (sel >= 1); for sel == 0 every non-NaN key
-        // has bin >= sel, which t >= -inf expresses.  NaN fails every test.
-        // Flags are collected branch-free; the rare candidates are appended
-        // after the pass.
-        const float thr_above = sel == kBins - 1 ? INFINITY : static_cast<float>(sel + 1);
-        const float thr_in = sel == 0 ? -INFINITY : static_cast<float>(sel);
+        // fma as in the bin map, bin > sel <=> t >= 4 (sel + 1) (sel < 2047)
+        // and bin >= sel <=> t >= 4 sel (sel >= 1); for sel == 0 every non-NaN
+        // key has bin >= sel, which t >= -inf expresses.  NaN fails every
+        // test.  Flags are collected branch-free; the rare candidates are
+        // appended after the pass.
+        const float thr_above = sel == kBins - 1 ? INFINITY : static_cast<float>(4 * (sel + 1));
+        const float thr_in = sel == 0 ? -INFINITY : static_cast<float>(4 * sel);
         // same values; the compiler is kept from holding the histogram pass's
         // 32 products in registers until here
         float inv2 = inv, off2 = off;

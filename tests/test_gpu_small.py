@@ -326,6 +326,33 @@ def test_subnormal_score_rows_exact(dsa, L, topk):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.parametrize("L,topk", [(3000, 512), (20000, 2048), (40000, 2048)])
+def test_narrow_range_score_rows_exact(dsa, L, topk):
+    """Scores 1000 + m / 16 for m in 0..7 (exact in fp32 on the vector
+    path): the range is far narrower than the scores' magnitude, so the
+    value-linear bin map's offset leaves its exact range and the selection
+    takes the radix path, with thousands of ties at the threshold.  Rows of
+    the 256-thread, 1024-thread and streaming selections must equal the
+    oracle's exactly."""
+    cfg = _small_cfg(num_reqs=1, q_len=1, topk=topk, n_idx_heads=2, d_idx=4,
+                     idx_dtype="f32", idx_cache_dtype="f32")
+    b = make_batch(cfg, DEV, seq_lens=[L], q_lens=[1])
+    g = torch.Generator(device="cpu").manual_seed(L)
+    q = torch.zeros(1, 2, 4)
+    q[0, :, 0] = 1.0
+    k = torch.zeros(b.num_slots, 4)
+    k[:, 0] = 1000.0 + torch.randint(0, 8, (b.num_slots,), generator=g).to(torch.float32) / 16
+    k[:, 1] = torch.randn(b.num_slots, generator=g)   # meets q = 0: no effect
+    w = torch.tensor([[1.0, 0.0]])
+    lay_q, lay_k, lay_w = q.to(DEV), k.to(DEV), w.to(DEV)
+    print("narrow range case: L %d topk %d" % (L, topk), flush=True)
+    idx = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), lay_q, lay_w, lay_k, None, topk)
+    torch.cuda.synchronize()
+    ref = OI.indexer_topk(b.seq_lens, b.cu_q_host, b.block_table_host, b.block_size,
+                          np_f64(lay_q), np_f64(lay_w), np_bits(lay_k), None, OI.F32, topk)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 def test_topk_4096_through_both_calls(dsa):
     """The largest top-k width: rows of 4096 positions from both selection
     paths (a row of 5000 keys in registers, one of 40000 streamed), rows

@@ -353,6 +353,50 @@ def test_narrow_range_score_rows_exact(dsa, L, topk):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+def test_long_rows_even_split_exact(dsa):
+    """Long single-token rows over an e4m3 cache in a batch large enough for
+    the even split of key tiles (the score pass records a range per 32-key
+    tile, which the selection of rows past 32768 keys reduces for the row's
+    range and streams the row against): each row has a run of keys above
+    every other (all taken), a run of zero scores and a spread between, with
+    many equal keys (bf16 values, so equal codes and scales).  The rows must
+    equal the oracle's exactly."""
+    g = np.random.default_rng(21)
+    R = 48
+    lens = [int(x) for x in g.integers(33000, 90000, size=R)]
+    cfg = _small_cfg(num_reqs=R, q_len=1, idx_cache_dtype="fp8", topk=2048)
+    b = make_batch(cfg, DEV, seq_lens=lens, q_lens=[1] * R)
+    bs = b.block_size
+    vals = np.zeros(b.num_slots, dtype=np.float32)
+    for bi, L in enumerate(lens):
+        pos = np.arange(L)
+        v = g.uniform(0.5, 8.0, size=L).astype(np.float32)
+        hot = int(g.integers(0, L - 1200))
+        v[hot:hot + 1100] = 100.0 + (pos[hot:hot + 1100] % 7)     # above every other key
+        cold = int(g.integers(0, L - 3000))
+        v[cold:cold + 2900] = -1.0                                 # ReLU: score 0
+        slots = b.block_table_host[bi, pos // bs].astype(np.int64) * bs + pos % bs
+        vals[slots] = v
+    k = torch.zeros(b.num_slots, 128)
+    k[:, 0] = torch.from_numpy(vals)
+    k_bf = k.to(torch.bfloat16).to(DEV)
+    q = torch.zeros(R, 32, 128)
+    q[:, :, 0] = 1.0
+    q_bf = q.to(torch.bfloat16).to(DEV)
+    w = torch.ones(R, 32, device=DEV)
+    cache = torch.zeros((b.num_slots, 128), dtype=torch.uint8, device=DEV)
+    scale = torch.zeros((b.num_slots,), dtype=torch.float32, device=DEV)
+    dsa.dsa_indexer_cache_write(k_bf, torch.arange(b.num_slots, dtype=torch.int64, device=DEV),
+                                cache, scale)
+    print("long even-split rows case: %d rows of %d..%d keys" % (R, min(lens), max(lens)), flush=True)
+    got = dsa.dsa_indexer_topk(_dsa_batch(dsa, b), q_bf, w, cache, scale, 2048)
+    torch.cuda.synchronize()
+    codes, scales = OI.fp8_quantize_rows(np_f64(k_bf).astype(np.float32))
+    ref = OI.indexer_topk(b.seq_lens, b.cu_q_host, b.block_table_host, bs, np_f64(q_bf),
+                          np_f64(w), codes, scales, OI.FP8, 2048)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
 def test_topk_4096_through_both_calls(dsa):
     """The largest top-k width: rows of 4096 positions from both selection
     paths (a row of 5000 keys in registers, one of 40000 streamed), rows

@@ -210,12 +210,12 @@ def pmc_summary(fetch_csv, write_csv):
     call = sum(v["fetch_bytes"] + v["write_bytes"] for k, v in kernels.items()
                if k.split("<")[0] in INDEXER_KERNELS)
     return {"commands": [
-                "rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc -o fetch --output-format csv"
+                "rocprofv3 --pmc FETCH_SIZE -d prof/pmc -o fetch --output-format csv"
                 " -- python3 -u bench.py --pmc-run --steps 3 --warmup 1 --no-cpu",
-                "rocprofv3 --pmc WRITE_SIZE -d gpurun_out/pmc -o write --output-format csv"
+                "rocprofv3 --pmc WRITE_SIZE -d prof/pmc -o write --output-format csv"
                 " -- python3 -u bench.py --pmc-run --steps 3 --warmup 1 --no-cpu",
-                "python3 bench.py --pmc-summary gpurun_out/pmc/fetch_counter_collection.csv"
-                " gpurun_out/pmc/write_counter_collection.csv"],
+                "python3 bench.py --pmc-summary prof/pmc/fetch_counter_collection.csv"
+                " prof/pmc/write_counter_collection.csv"],
             "note": "per-launch means; FETCH_SIZE and WRITE_SIZE scaled by the ratio of "
                     "known to counted bytes of the calibration kernel",
             "source_sha256": source_sha(), "sources": list(INDEXER_SRCS),

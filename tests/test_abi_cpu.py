@@ -174,6 +174,27 @@ def test_workspace_size_formula():
         up(th * 512 * 2) + up(th * 4) + up(128 * 8))
 
 
+def test_indexer_workspace_windows():
+    """The least accepted indexer workspace is a window of 16 query tokens
+    (score rows and range entries), or the whole batch when it has fewer;
+    one byte less is refused on the host before anything is enqueued."""
+    dsa = ensure_library()
+    lib = dsa.load_library()
+    def up(x):
+        return (x + 255) // 256 * 256
+    cb = _batch(dsa, num_reqs=64, num_q_tokens=128, max_q_len=2, max_seq_len=32768,
+                max_blocks=512, num_slots=64 * 32768)
+    full = lib.dsa_indexer_topk_workspace_size(ctypes.byref(cb), 2048)
+    least = lib.dsa_indexer_topk_workspace_min(ctypes.byref(cb), 2048)
+    assert full == up(128 * 32768 * 4) + up(128 * 4 * 256 * 8)
+    assert least == up(16 * 32768 * 4) + up(16 * 4 * 256 * 8)
+    assert _topk(lib, cb, topk=2048, ws_bytes=least - 1) == -5
+    assert "at least" in dsa.dsa_last_error()
+    small = _batch(dsa)                                  # 4 query tokens
+    assert (lib.dsa_indexer_topk_workspace_min(ctypes.byref(small), 16) ==
+            lib.dsa_indexer_topk_workspace_size(ctypes.byref(small), 16))
+
+
 def test_mla_and_cache_write_reject_on_host():
     dsa = ensure_library()
     lib = dsa.load_library()

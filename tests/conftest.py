@@ -27,3 +27,20 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _checked_build_finds_nothing(request):
+    """With DSA_LIBRARY=debug (every call through the checked build), each
+    GPU test must leave the checked build's fault word clear: no metadata
+    outside its bounds, no output element left unwritten, no invalid
+    selection row.  Tests that plant bad metadata read and clear the word
+    themselves."""
+    if os.environ.get("DSA_LIBRARY") != "debug" or "gpu" not in request.keywords:
+        yield
+        return
+    import sparse_attention_topk_amd as dsa
+    dsa.debug_faults(clear=True)
+    yield
+    faults = dsa.debug_faults(clear=True)
+    assert faults == 0, "checked build raised fault bits 0x%x" % faults

@@ -42,15 +42,15 @@ def test_fault_word_only_in_the_checked_build():
     reports DSA_ERR_UNSUPPORTED; both builds reject a NULL destination on
     the host (no device call is made in any of these)."""
     dsa = ensure_library()
-    rel = dsa.load_library("release")
-    out = ctypes.c_uint32(77)
-    assert rel.dsa_debug_faults(ctypes.byref(out), 1) == -2
-    assert out.value == 0
-    assert "checked build" in dsa.dsa_last_error()
-    assert rel.dsa_debug_faults(None, 0) == -1
+    with dsa.use_library("release") as rel:
+        out = ctypes.c_uint32(77)
+        assert rel.dsa_debug_faults(ctypes.byref(out), 1) == -2
+        assert out.value == 0
+        assert "checked build" in dsa.dsa_last_error()
+        assert rel.dsa_debug_faults(None, 0) == -1
+        with pytest.raises(dsa.DSAError):
+            dsa.debug_faults()
     assert dsa.load_library("debug").dsa_debug_faults(None, 0) == -1
-    with pytest.raises(dsa.DSAError):
-        dsa.debug_faults()
 
 
 def test_checked_build_validates_arguments_on_the_host_first():

@@ -81,3 +81,41 @@ def test_random_batch_both_calls(dsa, seed):
                            cfg.softmax_scale)
     assert attn_close(np_f64(out), ro) <= 0
     assert attn_close(lse.cpu().numpy(), rl, 1e-3, 1e-4) <= 0
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_batch_fp8_cache(dsa, seed):
+    """The same random batches over an e4m3 indexer cache written by
+    dsa_indexer_cache_write (normal keys): the cache's codes and scales equal
+    the oracle's bit for bit, every row keeps the selection invariants, and
+    the selected sets reach recall 0.999 against the oracle on the dequantised
+    keys (scores are no longer exact, so near-ties may resolve differently)."""
+    from _util import recall
+    lens, qls, topk, bs, heads, _ = _case(100 + seed)
+    cfg = get_config("decode_32k_mtp").scaled(
+        name="random_fp8", cid=90 + seed, num_reqs=len(lens), topk=topk, block_size=bs,
+        n_idx_heads=heads, idx_cache_dtype="fp8")
+    b = make_batch(cfg, DEV, seq_lens=lens, q_lens=qls)
+    print("random fp8 case %d: seq_lens %s q_lens %s topk %d block %d heads %d"
+          % (seed, lens, qls, topk, bs, heads), flush=True)
+    lay = make_layer(cfg, b, DEV)
+    cache = torch.zeros((b.num_slots, 128), dtype=torch.uint8, device=DEV)
+    scale = torch.zeros((b.num_slots,), dtype=torch.float32, device=DEV)
+    dsa.dsa_indexer_cache_write(lay.k_src, torch.arange(b.num_slots, dtype=torch.int64,
+                                                        device=DEV), cache, scale)
+    bb = dsa.Batch.from_synth(b)
+    idx = dsa.dsa_indexer_topk(bb, lay.q_idx, lay.w, cache, scale, topk)
+    torch.cuda.synchronize()
+    codes, scales = OI.fp8_quantize_rows(np_f64(lay.k_src).astype(np.float32))
+    assert np.array_equal(np_bits(cache), codes)
+    assert np.array_equal(scale.cpu().numpy().view(np.uint32), scales.view(np.uint32))
+    got = idx.cpu().numpy()
+    ref = OI.indexer_topk(b.seq_lens, b.cu_q_host, b.block_table_host, bs, np_f64(lay.q_idx),
+                          np_f64(lay.w), codes, scales, OI.FP8, topk)
+    t = 0
+    for bi in range(b.num_reqs):
+        for i in range(b.q_lens[bi]):
+            check_row_invariants(got[t], b.seq_lens[bi] - b.q_lens[bi] + i, topk)
+            t += 1
+    r, worst = recall(got, ref)
+    assert r >= 0.999, (r, worst)

@@ -305,11 +305,12 @@ int dsa_indexer_topk_noalloc(const dsa_batch* batch, const void* q, int32_t q_dt
  * which case workspace may be NULL), 256-byte aligned.  When the keys of a
  * token are split over several workgroups it holds their normalised bf16
  * partial outputs [N, n_split, n_heads, R], fp32 log-sum-exps [N, n_split,
- * n_heads] and one 8-byte arrival word per token; its prior contents do
- * not matter (arrivals are counted under a tag unique to the call, and each
- * call leaves its words cleared, so a call captured into a HIP graph may be
- * replayed with the tag it was captured with).  Calls that may run at the
- * same time must not share a workspace.
+ * n_heads] and, per token, a 128-byte line holding its arrival word; its
+ * prior contents do not matter (arrivals are counted under a tag unique to
+ * the call, and a word in which every split of the call has counted counts
+ * as none, so a call captured into a HIP graph may be replayed with the tag
+ * it was captured with).  Calls that may run at the same time must not
+ * share a workspace.
  */
 size_t sparse_mla_attn_workspace_size(const dsa_batch* batch, int32_t n_heads,
                                       int32_t kv_lora_rank, int32_t rope_dim,

@@ -128,7 +128,7 @@ size_t mla_ws(const dsa_batch* b, int n_heads, int R, int P, int topk, int dtype
   if (split <= 1) return 0;
   const size_t th = static_cast<size_t>(b->num_q_tokens) * split * n_heads;
   return round_up(th * R * sizeof(uint16_t)) + round_up(th * sizeof(float)) +
-         round_up(static_cast<size_t>(b->num_q_tokens) * sizeof(unsigned long long));
+         round_up(static_cast<size_t>(b->num_q_tokens) * 128);   // a 128-byte line per token
 }
 
 // 48-bit tag of a sparse MLA call: split arrivals counted under another tag

@@ -332,10 +332,25 @@ struct MlaArgs {
   float* lse;
   uint16_t* part_o;       // workspace [N, n_split, H, R] bf16 when n_split > 1
   float* part_lse;        // workspace [N, n_split, H]
-  unsigned long long* arrivals;   // workspace [N]: splits of the token done
+  unsigned long long* arrivals;   // workspace [N] x 128 B: the token's split arrivals
   unsigned long long call_tag;    // 48-bit tag of this call, never 0
   int n_split;
 };
+// compute units of the current device (cached per device; 256 if the
+// runtime cannot say)
+inline int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 bool mla_mfma_ok(const dsa_batch& b, int dtype, int n_heads, int R, int P);
 int mla_choose_split(const dsa_batch* b, int dtype, int n_heads, int R, int P,
                      int topk);

@@ -528,21 +528,6 @@ __global__ __launch_bounds__(256, MAXT <= 32 ? 2 : 1) void k_score_dma(
   }
 }
 
-// compute units of the current device (cached per device)
-int device_cus() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev] = n;
-  }
-  return cached[dev];
-}
-
 template <int TQ, int MT, bool F8, int MAXT, bool QF8, bool SPAN = false>
 hipError_t launch_dma_t(IndexerArgs& a, int qbpr, int nchunks, int64_t tpw,
                         hipStream_t stream) {

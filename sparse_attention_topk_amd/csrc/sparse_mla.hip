@@ -181,20 +181,34 @@ __device__ __forceinline__ float sum_x16_x32(float x) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-// Arrival count of a split at its token's word.  The word holds the tag of
-// the call that last counted there (upper 48 bits) and that call's
-// arrivals (lower 16): a word with another tag, whatever the workspace held
-// before, counts as no arrival.  A compare-and-swap fails only when another
-// split of the token changed the word after it was read, which each of them
-// does once, so the loop ends within n_split + 1 rounds (the first may
-// fail on the guess below).  The first compare-and-swap guesses that every other split has already
-// counted, so the split that arrives last (the one that merges, on the
-// kernel's critical path) usually needs a single round trip; a wrong guess
-// costs the others one more.
-__device__ uint32_t arrive(unsigned long long* word, unsigned long long tag, int n_split) {
-  unsigned long long cur = (tag << 16) | static_cast<unsigned long long>(n_split - 1);
-  for (int round = 0; round <= n_split + 1; ++round) {
-    const unsigned long long next = (cur >> 16) == tag ? cur + 1 : (tag << 16) | 1ull;
+// A token's splits meet at one 64-bit word in the workspace, alone on its
+// 128-byte line (kWordStride words apart), so that polls and counts of
+// different tokens never queue on one line: the tag of the call (upper 48
+// bits), the merge parts given up by their owners (bits 8..11) and the
+// splits arrived (bits 0..7).  A word with another tag, whatever the
+// workspace held before, counts as no arrival, and so does a finished word
+// of this call (every split arrived): that is what a replay of the same
+// launch (same tag) finds.  A compare-and-swap fails only when another
+// split changed the word after it was read; before the last arrival each
+// split changes it at most twice (its arrival, and giving up its part), so
+// the loop ends within 2 n_split + 1 rounds.  The first compare-and-swap
+// guesses the word the last arrival finds (`guess`), so the split that
+// arrives last, which merges and is on the kernel's critical path, usually
+// needs a single round trip.  A split that is not the last adds
+// `give_up` (its parts, merged by the last split instead); returns the
+// low 16 bits of the word it left, 0 if the loop ran out.
+constexpr int kWordStride = 16;
+constexpr int kParts = 4;                 // merge parts of 16 heads (three or more splits)
+static_assert(kMaxSplits < 256, "arrival count fits in 8 bits");
+__device__ uint32_t arrive(unsigned long long* word, unsigned long long tag, int n_split,
+                           uint32_t guess, uint32_t give_up) {
+  unsigned long long cur = (tag << 16) | (static_cast<unsigned long long>(guess) << 8) |
+                           static_cast<unsigned long long>(n_split - 1);
+  for (int round = 0; round <= 2 * n_split + 1; ++round) {
+    const bool counting = (cur >> 16) == tag && (cur & 0xFFu) < static_cast<uint32_t>(n_split);
+    unsigned long long next = (counting ? cur : tag << 16) + 1;
+    if ((next & 0xFFu) != static_cast<uint32_t>(n_split))
+      next |= static_cast<unsigned long long>(give_up) << 8;
     const unsigned long long prev = atomicCAS(word, cur, next);
     if (prev == cur) return static_cast<uint32_t>(next & 0xFFFFull);
     cur = prev;
@@ -231,17 +245,136 @@ __device__ __forceinline__ void tile_barrier() {
 
 
 
+// The merge's pieces.  A word holds 4 bf16 dims of a head row.
+__device__ __forceinline__ void unpack_bf16x4(unsigned long long v, float (&x)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    x[e] = __uint_as_float(static_cast<uint32_t>((v >> (16 * e)) & 0xFFFFu) << 16);
+}
+__device__ __forceinline__ unsigned long long pack_bf16x4(const float (&x)[4], float inv) {
+  return static_cast<unsigned long long>(pack2_bf16(x[0] * inv, x[1] * inv)) |
+         (static_cast<unsigned long long>(pack2_bf16(x[2] * inv, x[3] * inv)) << 32);
+}
+// Head h's split weights exp(lse_s - max) in place of its log-sum-exps
+// wt[s * kH + h], 1 / their sum into wt[n_split * kH + h], and the merged
+// log-sum-exp into lse (when given).
+__device__ __forceinline__ void merge_weights(float* wt, int h, int n_split, int t,
+                                              float* __restrict__ lse) {
+  float mx = -INFINITY;
+  for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, wt[s * kH + h]);
+  float sum = 0.0f;
+  for (int s = 0; s < n_split; ++s) {
+    const float wgt = mx == -INFINITY ? 0.0f : expf(wt[s * kH + h] - mx);
+    wt[s * kH + h] = wgt;
+    sum += wgt;
+  }
+  wt[n_split * kH + h] = sum > 0.0f ? 1.0f / sum : 0.0f;
+  if (lse) lse[static_cast<int64_t>(t) * kH + h] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
+}
+
+// Merges heads 16 p .. 16 p + 15 of token t over all its splits: the
+// weights of those heads, then every split's bf16 partial row summed in
+// split order (0, 1, ...) whichever split merges, with this split's own
+// rows taken from the staged block, rounded exactly as the others read
+// theirs; so the result does not depend on which split merges.  Thread tid
+// takes dims 4 wq .. 4 wq + 3 (wq = tid % 128) of heads 16 p + tid / 128 +
+// (NT / 128) i, as the partials were written.  The words of four splits
+// are requested before any is used, the first four splits' while the
+// weights are made.
+constexpr int kRowB = kR * 2 + 16;
+constexpr int kWords = kR / 4;            // 8-byte words (4 dims) of a head row
+template <int NT>
+__device__ void merge_part(const uint8_t* stage, int p, int t, int split, int n_split,
+                           uint16_t* __restrict__ out, float* __restrict__ lse,
+                           const uint16_t* __restrict__ part_o,
+                           const float* __restrict__ part_lse) {
+  constexpr int kRowsPer = NT / kWords;
+  constexpr int kPass = 16 / kRowsPer;
+  const int tid = threadIdx.x;
+  const int wq = tid % kWords;
+  const int hr = 16 * p + tid / kWords;
+  float* wt = reinterpret_cast<float*>(const_cast<uint8_t*>(stage) + kH * kRowB);
+  const unsigned long long* po = reinterpret_cast<const unsigned long long*>(
+      part_o + static_cast<int64_t>(t) * n_split * kH * kR) + wq;
+  unsigned long long wv[4][kPass];
+  auto load4 = [&](int s0) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int sg = s0 + g;
+      if (sg < n_split && sg != split) {
+#pragma unroll
+        for (int i = 0; i < kPass; ++i)
+          wv[g][i] = __hip_atomic_load(
+              const_cast<unsigned long long*>(po + (sg * kH + hr + kRowsPer * i) * kWords),
+              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kPass; ++i) wv[g][i] = 0;
+      }
+    }
+  };
+  load4(0);
+  for (int c = tid; c < n_split * 16; c += NT) {
+    const int s = c >> 4, h = 16 * p + (c & 15);
+    wt[s * kH + h] = __hip_atomic_load(
+        const_cast<float*>(part_lse) + (static_cast<int64_t>(t) * n_split + s) * kH + h,
+        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (tid < 16) merge_weights(wt, 16 * p + tid, n_split, t, lse);
+  __syncthreads();
+  float acc[kPass][4];
+#pragma unroll
+  for (int i = 0; i < kPass; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[i][e] = 0.0f;
+  for (int s0 = 0;;) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int sg = s0 + g;
+      if (sg < n_split) {
+#pragma unroll
+        for (int i = 0; i < kPass; ++i) {
+          const int h = hr + kRowsPer * i;
+          float x[4];
+          unpack_bf16x4(sg == split ? *reinterpret_cast<const unsigned long long*>(
+                                          stage + h * kRowB + 8 * wq)
+                                    : wv[g][i],
+                        x);
+          const float wgt = wt[sg * kH + h];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wgt, x[e], acc[i][e]);
+        }
+      }
+    }
+    s0 += 4;
+    if (s0 >= n_split) break;
+    load4(s0);
+  }
+  unsigned long long* ob = reinterpret_cast<unsigned long long*>(
+      out + static_cast<int64_t>(t) * kH * kR) + wq;
+#pragma unroll
+  for (int i = 0; i < kPass; ++i) {
+    const int h = hr + kRowsPer * i;
+    ob[h * kWords] = pack_bf16x4(acc[i], wt[n_split * kH + h]);
+  }
+}
+
+// Time an owner waits at most for the token's other splits before it gives
+// its part up (s_memrealtime ticks of 10 ns), and a bound on its polls.
+constexpr uint64_t kSpinTicks = 2000;
+constexpr int kSpinPolls = 4096;
+
 // The workgroup's staged result leaves it.  stage holds the normalised
 // bf16 rows of its 64 heads (head h at byte h * kRowB, kRowB = 2 R + 16),
 // and every lse is stored already (into lse, or as a partial).  With one
 // split the rows are copied to out; with several, this split's rows are
-// stored as its partial, and the split that arrives last at the token's
-// word merges all of them.  Every thread of the workgroup calls it; stage
-// must have room behind the rows for the merge weights.
-constexpr int kRowB = kR * 2 + 16;
+// stored as its partial and the token's splits merge them (see below).
+// Every thread of the workgroup calls it; stage must have room behind the
+// rows for the merge weights.
 template <int NT>
 __device__ __forceinline__ void mla_store_or_merge(
-    uint8_t* stage, uint32_t* counter, int t, int split, int n_split, bool partial,
+    uint8_t* stage, uint32_t* counter, int t, int split, int n_split, bool partial, bool coop,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_lse, unsigned long long* __restrict__ arrivals,
     unsigned long long call_tag) {
@@ -267,7 +400,6 @@ __device__ __forceinline__ void mla_store_or_merge(
   // over.  8-byte words (4 dims), consecutive lanes on consecutive words,
   // so every store instruction writes four whole 128-byte lines: thread tid
   // takes word tid % 128 of head rows tid / 128 + 2 i.
-  constexpr int kWords = kR / 4;                   // 8-byte words per head row
   constexpr int kRowsPer = NT / kWords;            // head rows per pass
   const int wq = tid % kWords;
   const int h0 = tid / kWords;
@@ -281,134 +413,118 @@ __device__ __forceinline__ void mla_store_or_merge(
     __hip_atomic_store(dst + h * kWords + wq, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // ---- the split that arrives last merges the token's partials.  Every
-  // thread waits until its partial stores have completed (reached the
-  // device-coherent level) before the workgroup counts its arrival; the
-  // merging workgroup loads the others' partials only after its own count
-  // came back, with device-scope atomic loads.
+  // ---- the token's splits merge their partials.  Every thread waits until
+  // its partial stores have completed (reached the device-coherent level)
+  // before the workgroup counts its arrival, and partials are loaded
+  // (device-scope atomic loads) only by a split that has seen every
+  // arrival.  With two splits the one that arrives last merges all 64
+  // heads.  With more, the heads are merged in kParts parts of 16: split p
+  // (p < kParts) owns part p, and parts without an owner (fewer splits
+  // than parts) fall to the last split.  With coop (set by the host when
+  // every workgroup of the launch is resident at once) an owner that is not
+  // last polls its token's word until every split has arrived (for a
+  // bounded time) and merges its own part; an owner that does not wait, or
+  // stops waiting, gives its part up in the word, and the last split merges
+  // every part given up.  Each part is merged exactly once, by a split that
+  // has seen every arrival.
   wait_vm<0>();
   __syncthreads();
-  if (tid == 0) *counter = arrive(arrivals + t, call_tag, n_split) == static_cast<uint32_t>(n_split);
+  const bool parts = n_split > 2;
+  const uint32_t mine = parts && split < kParts ? 1u << split : 0u;
+  const uint32_t unowned = parts && n_split < kParts ? 0xFu & ~((1u << n_split) - 1u) : 0u;
+  constexpr uint32_t kAllHeads = 0x10u;     // the two-split merge of all heads
+  if (tid == 0) {
+    unsigned long long* wp = arrivals + kWordStride * t;
+    // without coop every other owner gives its part up on arrival
+    const uint32_t guess = coop || !parts ? 0u : (0xFu & ~unowned & ~mine);
+    const uint32_t w = arrive(wp, call_tag, n_split, guess, coop ? 0u : mine);
+    uint32_t todo = 0;
+    if ((w & 0xFFu) == static_cast<uint32_t>(n_split)) {
+      todo = parts ? mine | unowned | ((w >> 8) & 0xFu) : kAllHeads;
+    } else if (coop && mine) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      unsigned long long cur = 0;
+      bool all = false;
+      for (int poll = 0; poll < kSpinPolls; ++poll) {
+        __builtin_amdgcn_s_sleep(2);
+        cur = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((cur & 0xFFu) == static_cast<uint32_t>(n_split)) {
+          all = true;
+          break;
+        }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) break;
+      }
+      if (all) {
+        todo = mine;
+      } else {
+        // give the part up, unless the last split has arrived meanwhile
+        // (after the last arrival the word no longer changes)
+        for (int round = 0; round <= 2 * n_split + 1; ++round) {
+          if ((cur & 0xFFu) == static_cast<uint32_t>(n_split)) {
+            todo = mine;
+            break;
+          }
+          const unsigned long long prev =
+              atomicCAS(wp, cur, cur | (static_cast<unsigned long long>(mine) << 8));
+          if (prev == cur) break;
+          cur = prev;
+        }
+      }
+    }
+    *counter = todo;
+  }
   __syncthreads();
-  if (!*counter) return;
+  const uint32_t todo = *counter;
+  if (todo == 0) return;
   asm volatile("" ::: "memory");
-  // Thread tid merges dims 4 wq .. 4 wq + 3 of heads h0 + 2 i (as the
-  // partials were written: whole lines per instruction).  Splits are
-  // summed in split order (0, 1, ...) whichever finished last, so the
-  // result does not depend on the arrival order; this split's own partial
-  // comes from the staged block, rounded exactly as the others read theirs.
+  if (todo != kAllHeads) {
+#pragma unroll 1
+    for (int p = 0; p < kParts; ++p)
+      if ((todo >> p) & 1u)
+        merge_part<NT>(stage, p, t, split, n_split, out, lse, part_o, part_lse);
+    return;
+  }
+  // Two splits.  Thread tid merges dims 4 wq .. 4 wq + 3 of heads
+  // h0 + kRowsPer i (as the partials were written: whole lines per
+  // instruction).  The splits are summed in split order (0, 1) whichever
+  // finished last, so the result does not depend on the arrival order;
+  // this split's own partial comes from the staged block, rounded exactly
+  // as the other reads its own.  The other split's rows are in flight
+  // while the weights are made.
   const unsigned long long* po = reinterpret_cast<const unsigned long long*>(
       part_o + static_cast<int64_t>(t) * n_split * kH * kR) + wq;
-  auto word = [&](int s, int h) -> unsigned long long {
-    return __hip_atomic_load(const_cast<unsigned long long*>(po + (s * kH + h) * kWords),
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  };
-  auto own = [&](int h) -> unsigned long long {
-    return *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq);
-  };
-  auto unpack = [](unsigned long long v, float (&x)[4]) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      x[e] = __uint_as_float(static_cast<uint32_t>((v >> (16 * e)) & 0xFFFFu) << 16);
-  };
-  unsigned long long* ob = reinterpret_cast<unsigned long long*>(
-      out + static_cast<int64_t>(t) * kH * kR) + wq;
-  auto put = [&](int h, const float (&x)[4], float inv) {
-    const unsigned long long v =
-        static_cast<unsigned long long>(pack2_bf16(x[0] * inv, x[1] * inv)) |
-        (static_cast<unsigned long long>(pack2_bf16(x[2] * inv, x[3] * inv)) << 32);
-    ob[h * kWords] = v;
-  };
-  // with two splits, the other split's rows are in flight while the
-  // weights are made
   unsigned long long u[kH / kRowsPer];
-  if (n_split == 2) {
 #pragma unroll
-    for (int i = 0; i < kH / kRowsPer; ++i) u[i] = word(1 - split, h0 + kRowsPer * i);
-  }
+  for (int i = 0; i < kH / kRowsPer; ++i)
+    u[i] = __hip_atomic_load(
+        const_cast<unsigned long long*>(po + ((1 - split) * kH + h0 + kRowsPer * i) * kWords),
+        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // split weights exp(lse_s - max) per head in place of the log-sum-exps,
   // then 1 / their sum, behind the staged block
   float* wt = reinterpret_cast<float*>(stage + kH * row_b);
-  for (int c = tid; c < n_split * kH; c += NT)
-    wt[c] = __hip_atomic_load(part_lse + static_cast<int64_t>(t) * n_split * kH + c,
+  for (int c = tid; c < 2 * kH; c += NT)
+    wt[c] = __hip_atomic_load(part_lse + static_cast<int64_t>(t) * 2 * kH + c,
                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (tid < kH) {
-    float mx = -INFINITY;
-    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, wt[s * kH + tid]);
-    float sum = 0.0f;
-    for (int s = 0; s < n_split; ++s) {
-      const float wgt = mx == -INFINITY ? 0.0f : expf(wt[s * kH + tid] - mx);
-      wt[s * kH + tid] = wgt;
-      sum += wgt;
-    }
-    wt[n_split * kH + tid] = sum > 0.0f ? 1.0f / sum : 0.0f;
-    if (lse) lse[static_cast<int64_t>(t) * kH + tid] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
-  }
+  if (tid < kH) merge_weights(wt, tid, 2, t, lse);
   __syncthreads();
-  if (n_split == 2) {
+  unsigned long long* ob = reinterpret_cast<unsigned long long*>(
+      out + static_cast<int64_t>(t) * kH * kR) + wq;
 #pragma unroll
-    for (int i = 0; i < kH / kRowsPer; ++i) {
-      const int h = h0 + kRowsPer * i;
-      float m[4], o4[4], x[4];
-      unpack(own(h), m);
-      unpack(u[i], o4);
-      const float w0 = wt[h], w1 = wt[kH + h];
+  for (int i = 0; i < kH / kRowsPer; ++i) {
+    const int h = h0 + kRowsPer * i;
+    float m[4], o4[4], x[4];
+    unpack_bf16x4(*reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq), m);
+    unpack_bf16x4(u[i], o4);
+    const float w0 = wt[h], w1 = wt[kH + h];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = split == 0 ? m[e] : o4[e];
-        const float p1 = split == 0 ? o4[e] : m[e];
-        x[e] = fmaf(w1, p1, w0 * p0);
-      }
-      put(h, x, wt[2 * kH + h]);
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = split == 0 ? m[e] : o4[e];
+      const float p1 = split == 0 ? o4[e] : m[e];
+      x[e] = fmaf(w1, p1, w0 * p0);
     }
-  } else {
-    // Eight head rows at a time, splits in groups of four: the group's
-    // words (the eight rows of each of its splits) are requested before any
-    // is used, so a group costs one memory round trip rather than one per
-    // split.  The loads are unconditional (a split past the last re-reads
-    // the last, and this split's own words are read but taken from the
-    // staged block), so the compiler issues them back to back.  Splits are
-    // summed in split order.
-    for (int i0 = 0; i0 < kH / kRowsPer; i0 += 8) {
-      float acc[8][4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][e] = 0.0f;
-      for (int s0 = 0; s0 < n_split; s0 += 4) {
-        unsigned long long wv[4][8];
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            wv[g][i] = word(min(s0 + g, n_split - 1), h0 + kRowsPer * (i0 + i));
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int sg = s0 + g;
-          if (sg < n_split) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const int h = h0 + kRowsPer * (i0 + i);
-              float p[4];
-              unpack(sg == split ? own(h) : wv[g][i], p);
-              const float wgt = wt[sg * kH + h];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(wgt, p[e], acc[i][e]);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int h = h0 + kRowsPer * (i0 + i);
-        put(h, acc[i], wt[n_split * kH + h]);
-      }
-    }
+    ob[h * kWords] = pack_bf16x4(x, wt[2 * kH + h]);
   }
-  // every split of this call has arrived: clear the word, so that a replay
-  // of the same launch (same tag) counts from zero again
-  if (tid == 0) __hip_atomic_store(arrivals + t, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------- warp-specialised pipeline
@@ -455,7 +571,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
     int32_t block_size, int64_t num_slots, int32_t max_seq_len,
     uint16_t* __restrict__ out, float* __restrict__ lse,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-    unsigned long long* __restrict__ arrivals, unsigned long long call_tag) {
+    unsigned long long* __restrict__ arrivals, unsigned long long call_tag, int32_t coop) {
   __shared__ MlaSharedWs sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -770,8 +886,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
     }
     tile_barrier();                      // rows staged
   }
-  mla_store_or_merge<kThreads>(reinterpret_cast<uint8_t*>(&sh.k[0][0]), &sh.counter, t, split, n_split,
-                     n_split > 1, out, lse, part_o, part_lse, arrivals, call_tag);
+  mla_store_or_merge<kThreads>(reinterpret_cast<uint8_t*>(&sh.k[0][0]), &sh.counter, t, split,
+                               n_split, n_split > 1, coop != 0, out, lse, part_o, part_lse,
+                               arrivals, call_tag);
 }
 
 // ------------------------------------------------------- one token per workgroup
@@ -839,7 +956,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_mla_prefill(
     const int32_t* __restrict__ block_table, int32_t max_blocks, int32_t block_size,
     int64_t num_slots, int32_t max_seq_len, uint16_t* __restrict__ out,
     float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-    unsigned long long* __restrict__ arrivals, unsigned long long call_tag) {
+    unsigned long long* __restrict__ arrivals, unsigned long long call_tag, int32_t coop) {
   __shared__ MlaSharedPf sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1216,8 +1333,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_mla_prefill(
             f32_to_bf16_rne(o[g2][d][r] * inv);
       }
     }
-  mla_store_or_merge<kPfThreads>(stage, &sh.counter, t, split, n_split, n_split > 1, out, lse,
-                                 part_o, part_lse, arrivals, call_tag);
+  mla_store_or_merge<kPfThreads>(stage, &sh.counter, t, split, n_split, n_split > 1, coop != 0,
+                                 out, lse, part_o, part_lse, arrivals, call_tag);
 }
 
 // ---------------------------------------------------------------- vector path
@@ -1330,6 +1447,11 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
     if (n_split > 1 && (!a.part_o || !a.part_lse || !a.arrivals || !a.call_tag))
       return hipErrorInvalidValue;
     const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * n_split;
+    // one workgroup per CU (both kernels take most of the LDS): when the
+    // grid fits the device every split of a token is resident at once, and
+    // with three or more splits the owners of the merge parts wait for the
+    // last split and merge their parts in parallel
+    const int32_t coop = grid <= device_cus() ? 1 : 0;
     if (n_split > 1 && split_len <= kWsSplitCap) {
       // key splits short enough for the warp-specialised pipeline's slot table
       k_mla_ws<<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(
@@ -1338,7 +1460,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
           b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
           b.block_size, b.num_slots, b.max_seq_len,
           static_cast<uint16_t*>(a.out), a.lse, a.part_o, a.part_lse, a.arrivals,
-          a.call_tag);
+          a.call_tag, coop);
       return hipGetLastError();
     }
     // longer splits (up to kMaxSplitLen indices), or one per token
@@ -1348,7 +1470,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
         b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
         b.block_size, b.num_slots, b.max_seq_len,
         static_cast<uint16_t*>(a.out), a.lse, a.part_o, a.part_lse, a.arrivals,
-        a.call_tag);
+        a.call_tag, coop);
     return hipGetLastError();
   }
   const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * a.n_heads;

@@ -162,16 +162,16 @@ def test_workspace_size_formula():
     # the matrix-core path with few workgroups splits the keys of a token:
     # 4 tokens -> 16 splits (at least 4 tiles of 32 keys each, enough
     # workgroups for 256 CUs); bf16 partials [N, split, H, R], their
-    # log-sum-exps [N, split, H] and one 8-byte arrival word per token, each
-    # region 256-byte aligned
+    # log-sum-exps [N, split, H] and a 128-byte line per token for its
+    # arrival word, each region 256-byte aligned
     th = 4 * 16 * 64
     assert lib.sparse_mla_attn_workspace_size(ctypes.byref(cb), 64, 512, 64, 2048, 1) == (
-        up(th * 512 * 2) + up(th * 4) + up(4 * 8))
+        up(th * 512 * 2) + up(th * 4) + up(4 * 128))
     # 128 decode tokens: 2 splits
     cb128 = _batch(dsa, num_reqs=64, num_q_tokens=128, max_q_len=2)
     th = 128 * 2 * 64
     assert lib.sparse_mla_attn_workspace_size(ctypes.byref(cb128), 64, 512, 64, 2048, 1) == (
-        up(th * 512 * 2) + up(th * 4) + up(128 * 8))
+        up(th * 512 * 2) + up(th * 4) + up(128 * 128))
 
 
 def test_indexer_workspace_windows():

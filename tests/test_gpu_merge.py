@@ -2,12 +2,15 @@
 
 When a token's keys are split over several workgroups, each split stores
 its bf16 partial rows and log-sum-exps, then counts its arrival at the
-token's word in the workspace (tagged with the call); the split that
-arrives last merges every split's partial in split order and clears the
-word.  The result must match the oracle and repeat bit for bit for every
-split count, for grids larger than the device holds at once, and for graph
-replays, which reuse the tag they were captured with and so must find the
-word cleared by their previous run."""
+token's word in the workspace (tagged with the call).  With two splits the
+split that arrives last merges all heads; with more, four parts of 16 heads
+are merged by their owners (splits 0..3) once every split has arrived, or
+by the last split when an owner gave its part up (always when the grid is
+larger than the device holds at once).  Every part is merged once, in split
+order, so the result must match the oracle and repeat bit for bit for every
+split count and grid size, and graph replays, which reuse the tag they were
+captured with, must find the word their previous run left (every split
+counted) as no arrival."""
 import numpy as np
 import pytest
 import torch
@@ -96,7 +99,7 @@ def test_merge_for_each_split_count(dsa, n_split):
 def test_merge_with_more_workgroups_than_the_device_holds(dsa, n_tokens, topk):
     """Grids past one workgroup per CU (320 splits of 256 indices; 600
     splits of 2,048 on the one-workgroup-per-token kernel), so some splits
-    start only after others have finished."""
+    start only after others have finished and nobody waits."""
     cfg, b, lay, idx, bb, nbytes = _setup(dsa, n_tokens, topk, 950 + n_tokens)
     assert _splits(nbytes, n_tokens) == 2
     print("merge case: %d tokens, top-k %d" % (n_tokens, topk), flush=True)
@@ -115,8 +118,8 @@ def test_merge_with_more_workgroups_than_the_device_holds(dsa, n_tokens, topk):
 @pytest.mark.parametrize("n_tokens,topk", [(16, 2048), (64, 2048), (128, 4096)])
 def test_graph_replays_match_eager(dsa, n_tokens, topk):
     """A captured call replays with the tag it was captured with, so each
-    replay must find the token words as its previous run left them (cleared
-    by the merging split) and count from zero.  Eager calls on the same
+    replay must find the token words as its previous run left them (every
+    split counted) and count from zero.  Eager calls on the same
     workspace (other tags) run between the replays; every replay equals the
     eager result bit for bit."""
     cfg, b, lay, idx, bb, nbytes = _setup(dsa, n_tokens, topk, 970 + n_tokens)

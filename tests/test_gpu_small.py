@@ -615,8 +615,9 @@ def test_attention_one_workgroup_per_token(dsa, topk):
 
 @pytest.mark.parametrize("fill", ["random", "ones", "zeros"])
 def test_split_merge_whatever_the_workspace_held(dsa, fill):
-    """With several key splits per token, the split that finishes last merges
-    the partials; arrivals are counted in a per-token word of the workspace.
+    """With several key splits per token (16 here), the splits merge the
+    partials once all have arrived; arrivals are counted in a per-token word
+    of the workspace.
     Whatever the workspace held before the first call, and over consecutive
     calls on the same workspace (the second with other queries), each result
     matches the oracle, and a repeated call repeats its result bit for bit."""

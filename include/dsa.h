@@ -311,6 +311,12 @@ int dsa_indexer_topk_noalloc(const dsa_batch* batch, const void* q, int32_t q_dt
  * as none, so a call captured into a HIP graph may be replayed with the tag
  * it was captured with).  Calls that may run at the same time must not
  * share a workspace.
+ * The splits of a token merge their partials a part of the heads each:
+ * when every workgroup of the launch fits the device at once, a split waits
+ * for its token's other splits for at most DSA_MERGE_WAIT_TICKS (from the
+ * environment, read at each call; ticks of 10 ns; default 2000, 0 for no
+ * wait) and otherwise leaves its part to the last split.  The result does
+ * not depend on the wait.
  */
 size_t sparse_mla_attn_workspace_size(const dsa_batch* batch, int32_t n_heads,
                                       int32_t kv_lora_rank, int32_t rope_dim,

@@ -25,12 +25,13 @@
 // fixed slack before it moves; a move rescales the running sums and
 // accumulators in place, so each tile is processed once.  With more than
 // one key split, each split writes its normalised partial output and
-// log-sum-exp, and the split that finishes last merges them by LSE weights
-// (splits of a token are placed on one XCD, so the partials it reads back
-// are still in that XCD's L2).
+// log-sum-exp, and the token's splits merge them by LSE weights, a part of
+// the heads each, once every split has arrived (see mla_store_or_merge;
+// splits of a token are placed on one XCD).
 //
 // Vector path (fp32 or other shapes): one workgroup per (token, head),
 // fp32 arithmetic, logits in LDS.
+#include <cstdlib>
 #include <type_traits>
 #include <utility>
 
@@ -272,34 +273,35 @@ __device__ __forceinline__ void merge_weights(float* wt, int h, int n_split, int
   if (lse) lse[static_cast<int64_t>(t) * kH + h] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
 }
 
-// Merges heads 16 p .. 16 p + 15 of token t over all its splits: the
+// Merges heads PH p .. PH p + PH - 1 of token t over all its splits: the
 // weights of those heads, then every split's bf16 partial row summed in
 // split order (0, 1, ...) whichever split merges, with this split's own
 // rows taken from the staged block, rounded exactly as the others read
 // theirs; so the result does not depend on which split merges.  Thread tid
-// takes dims 4 wq .. 4 wq + 3 (wq = tid % 128) of heads 16 p + tid / 128 +
-// (NT / 128) i, as the partials were written.  The words of four splits
-// are requested before any is used, the first four splits' while the
+// takes dims 4 wq .. 4 wq + 3 (wq = tid % 128) of heads PH p + tid / 128 +
+// (NT / 128) i, as the partials were written.  The words of kSr splits
+// are requested before any is used, the first kSr splits' while the
 // weights are made.
 constexpr int kRowB = kR * 2 + 16;
 constexpr int kWords = kR / 4;            // 8-byte words (4 dims) of a head row
-template <int NT>
+template <int NT, int PH>
 __device__ void merge_part(const uint8_t* stage, int p, int t, int split, int n_split,
                            uint16_t* __restrict__ out, float* __restrict__ lse,
                            const uint16_t* __restrict__ part_o,
                            const float* __restrict__ part_lse) {
   constexpr int kRowsPer = NT / kWords;
-  constexpr int kPass = 16 / kRowsPer;
+  constexpr int kPass = PH / kRowsPer;
   const int tid = threadIdx.x;
   const int wq = tid % kWords;
-  const int hr = 16 * p + tid / kWords;
+  const int hr = PH * p + tid / kWords;
   float* wt = reinterpret_cast<float*>(const_cast<uint8_t*>(stage) + kH * kRowB);
   const unsigned long long* po = reinterpret_cast<const unsigned long long*>(
       part_o + static_cast<int64_t>(t) * n_split * kH * kR) + wq;
-  unsigned long long wv[4][kPass];
+  constexpr int kSr = PH > 16 ? 2 : 4;      // splits per round of loads
+  unsigned long long wv[kSr][kPass];
   auto load4 = [&](int s0) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < kSr; ++g) {
       const int sg = s0 + g;
       if (sg < n_split && sg != split) {
 #pragma unroll
@@ -314,14 +316,14 @@ __device__ void merge_part(const uint8_t* stage, int p, int t, int split, int n_
     }
   };
   load4(0);
-  for (int c = tid; c < n_split * 16; c += NT) {
-    const int s = c >> 4, h = 16 * p + (c & 15);
+  for (int c = tid; c < n_split * PH; c += NT) {
+    const int s = c / PH, h = PH * p + c % PH;
     wt[s * kH + h] = __hip_atomic_load(
         const_cast<float*>(part_lse) + (static_cast<int64_t>(t) * n_split + s) * kH + h,
         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  if (tid < 16) merge_weights(wt, 16 * p + tid, n_split, t, lse);
+  if (tid < PH) merge_weights(wt, PH * p + tid, n_split, t, lse);
   __syncthreads();
   float acc[kPass][4];
 #pragma unroll
@@ -330,7 +332,7 @@ __device__ void merge_part(const uint8_t* stage, int p, int t, int split, int n_
     for (int e = 0; e < 4; ++e) acc[i][e] = 0.0f;
   for (int s0 = 0;;) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int g = 0; g < kSr; ++g) {
       const int sg = s0 + g;
       if (sg < n_split) {
 #pragma unroll
@@ -347,7 +349,7 @@ __device__ void merge_part(const uint8_t* stage, int p, int t, int split, int n_
         }
       }
     }
-    s0 += 4;
+    s0 += kSr;
     if (s0 >= n_split) break;
     load4(s0);
   }
@@ -360,9 +362,8 @@ __device__ void merge_part(const uint8_t* stage, int p, int t, int split, int n_
   }
 }
 
-// Time an owner waits at most for the token's other splits before it gives
-// its part up (s_memrealtime ticks of 10 ns), and a bound on its polls.
-constexpr uint64_t kSpinTicks = 2000;
+// A bound on the polls of an owner waiting for its token's other splits
+// (the wait is bounded in time too: wait_ticks).
 constexpr int kSpinPolls = 4096;
 
 // The workgroup's staged result leaves it.  stage holds the normalised
@@ -374,7 +375,8 @@ constexpr int kSpinPolls = 4096;
 // rows for the merge weights.
 template <int NT>
 __device__ __forceinline__ void mla_store_or_merge(
-    uint8_t* stage, uint32_t* counter, int t, int split, int n_split, bool partial, bool coop,
+    uint8_t* stage, uint32_t* counter, int t, int split, int n_split, bool partial,
+    int32_t wait_ticks,
     uint16_t* __restrict__ out, float* __restrict__ lse, uint16_t* __restrict__ part_o,
     float* __restrict__ part_lse, unsigned long long* __restrict__ arrivals,
     unsigned long long call_tag) {
@@ -393,137 +395,116 @@ __device__ __forceinline__ void mla_store_or_merge(
     }
     return;
   }
-  // Partials (bf16, normalised) are read back by another workgroup of this
+  // Partials (bf16, normalised) are read back by other workgroups of this
   // launch, maybe on another XCD: they are stored as relaxed device-scope
   // atomics, which the hardware keeps coherent across XCDs by themselves,
   // so no cache-wide write-back or invalidation is needed to hand them
   // over.  8-byte words (4 dims), consecutive lanes on consecutive words,
   // so every store instruction writes four whole 128-byte lines: thread tid
-  // takes word tid % 128 of head rows tid / 128 + 2 i.
+  // takes word tid % 128 of head rows tid / 128 + (NT / 128) i.
+  //
+  // The heads are merged in parts: with two splits two halves of 32 heads,
+  // split s owning half s; with more, kParts parts of 16, split p (p <
+  // kParts) owning part p, and parts without an owner (fewer splits than
+  // parts) falling to the last split.  With wait_ticks > 0 (the host sets
+  // it when every workgroup of the launch is resident at once) an owner
+  // waits, for at most wait_ticks s_memrealtime ticks (10 ns), until every
+  // split has arrived and merges its own parts, so a split stores only the
+  // rows of parts it does not own.  Otherwise, or once an owner stops
+  // waiting, the owner stores its own rows too
+  // and gives its parts up in the token's word, and the last split merges
+  // every part given up.  Every thread waits until its partial stores have
+  // completed (reached the device-coherent level) before the workgroup
+  // counts its arrival or gives a part up, and partials are loaded
+  // (device-scope atomic loads) only by a split that has seen every
+  // arrival, so each part is merged exactly once, from complete rows.
+  const int n_parts = n_split == 2 ? 2 : kParts;
+  const int ph = kH / n_parts;                     // heads per part
+  const uint32_t all_parts = (1u << n_parts) - 1u;
+  const uint32_t mine = split < n_parts ? 1u << split : 0u;
+  const uint32_t unowned = n_split < n_parts ? all_parts & ~((1u << n_split) - 1u) : 0u;
   constexpr int kRowsPer = NT / kWords;            // head rows per pass
+  constexpr uint32_t kGiveUp = 0x100u;
+  const bool coop = wait_ticks > 0;
   const int wq = tid % kWords;
   const int h0 = tid / kWords;
   unsigned long long* dst = reinterpret_cast<unsigned long long*>(
       part_o + (static_cast<int64_t>(t) * n_split + split) * kH * kR);
+  auto store_rows = [&](uint32_t parts_mask) {
 #pragma unroll 8
-  for (int i = 0; i < kH / kRowsPer; ++i) {
-    const int h = h0 + kRowsPer * i;
-    const unsigned long long v =
-        *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq);
-    __hip_atomic_store(dst + h * kWords + wq, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  // ---- the token's splits merge their partials.  Every thread waits until
-  // its partial stores have completed (reached the device-coherent level)
-  // before the workgroup counts its arrival, and partials are loaded
-  // (device-scope atomic loads) only by a split that has seen every
-  // arrival.  With two splits the one that arrives last merges all 64
-  // heads.  With more, the heads are merged in kParts parts of 16: split p
-  // (p < kParts) owns part p, and parts without an owner (fewer splits
-  // than parts) fall to the last split.  With coop (set by the host when
-  // every workgroup of the launch is resident at once) an owner that is not
-  // last polls its token's word until every split has arrived (for a
-  // bounded time) and merges its own part; an owner that does not wait, or
-  // stops waiting, gives its part up in the word, and the last split merges
-  // every part given up.  Each part is merged exactly once, by a split that
-  // has seen every arrival.
+    for (int i = 0; i < kH / kRowsPer; ++i) {
+      const int h = h0 + kRowsPer * i;
+      if ((parts_mask >> (h / ph)) & 1u) {         // uniform: h / ph = i / (ph / kRowsPer)
+        const unsigned long long v =
+            *reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq);
+        __hip_atomic_store(dst + h * kWords + wq, v, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  };
+  store_rows(coop ? all_parts & ~mine : all_parts);
   wait_vm<0>();
   __syncthreads();
-  const bool parts = n_split > 2;
-  const uint32_t mine = parts && split < kParts ? 1u << split : 0u;
-  const uint32_t unowned = parts && n_split < kParts ? 0xFu & ~((1u << n_split) - 1u) : 0u;
-  constexpr uint32_t kAllHeads = 0x10u;     // the two-split merge of all heads
+  unsigned long long* wp = arrivals + kWordStride * t;
   if (tid == 0) {
-    unsigned long long* wp = arrivals + kWordStride * t;
-    // without coop every other owner gives its part up on arrival
-    const uint32_t guess = coop || !parts ? 0u : (0xFu & ~unowned & ~mine);
+    // without coop every other owner gives its parts up on arrival
+    const uint32_t guess = coop ? 0u : all_parts & ~unowned & ~mine;
     const uint32_t w = arrive(wp, call_tag, n_split, guess, coop ? 0u : mine);
     uint32_t todo = 0;
     if ((w & 0xFFu) == static_cast<uint32_t>(n_split)) {
-      todo = parts ? mine | unowned | ((w >> 8) & 0xFu) : kAllHeads;
+      todo = mine | unowned | ((w >> 8) & all_parts);
     } else if (coop && mine) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      unsigned long long cur = 0;
-      bool all = false;
+      todo = kGiveUp;
       for (int poll = 0; poll < kSpinPolls; ++poll) {
         __builtin_amdgcn_s_sleep(2);
-        cur = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned long long cur =
+            __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if ((cur & 0xFFu) == static_cast<uint32_t>(n_split)) {
-          all = true;
+          todo = mine;
           break;
         }
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) break;
-      }
-      if (all) {
-        todo = mine;
-      } else {
-        // give the part up, unless the last split has arrived meanwhile
-        // (after the last arrival the word no longer changes)
-        for (int round = 0; round <= 2 * n_split + 1; ++round) {
-          if ((cur & 0xFFu) == static_cast<uint32_t>(n_split)) {
-            todo = mine;
-            break;
-          }
-          const unsigned long long prev =
-              atomicCAS(wp, cur, cur | (static_cast<unsigned long long>(mine) << 8));
-          if (prev == cur) break;
-          cur = prev;
-        }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > static_cast<uint64_t>(wait_ticks)) break;
       }
     }
     *counter = todo;
   }
   __syncthreads();
-  const uint32_t todo = *counter;
+  uint32_t todo = *counter;
+  if (todo == kGiveUp) {
+    // stop waiting: store this split's own rows, then give its parts up
+    // unless the last split has arrived meanwhile (after the last arrival
+    // the word no longer changes)
+    store_rows(mine);
+    wait_vm<0>();
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t res = mine;
+      unsigned long long cur = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int round = 0; round <= 2 * n_split + 1; ++round) {
+        if ((cur & 0xFFu) == static_cast<uint32_t>(n_split)) break;
+        const unsigned long long prev =
+            atomicCAS(wp, cur, cur | (static_cast<unsigned long long>(mine) << 8));
+        if (prev == cur) {
+          res = 0;
+          break;
+        }
+        cur = prev;
+      }
+      *counter = res;
+    }
+    __syncthreads();
+    todo = *counter;
+  }
   if (todo == 0) return;
   asm volatile("" ::: "memory");
-  if (todo != kAllHeads) {
 #pragma unroll 1
-    for (int p = 0; p < kParts; ++p)
-      if ((todo >> p) & 1u)
-        merge_part<NT>(stage, p, t, split, n_split, out, lse, part_o, part_lse);
-    return;
-  }
-  // Two splits.  Thread tid merges dims 4 wq .. 4 wq + 3 of heads
-  // h0 + kRowsPer i (as the partials were written: whole lines per
-  // instruction).  The splits are summed in split order (0, 1) whichever
-  // finished last, so the result does not depend on the arrival order;
-  // this split's own partial comes from the staged block, rounded exactly
-  // as the other reads its own.  The other split's rows are in flight
-  // while the weights are made.
-  const unsigned long long* po = reinterpret_cast<const unsigned long long*>(
-      part_o + static_cast<int64_t>(t) * n_split * kH * kR) + wq;
-  unsigned long long u[kH / kRowsPer];
-#pragma unroll
-  for (int i = 0; i < kH / kRowsPer; ++i)
-    u[i] = __hip_atomic_load(
-        const_cast<unsigned long long*>(po + ((1 - split) * kH + h0 + kRowsPer * i) * kWords),
-        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // split weights exp(lse_s - max) per head in place of the log-sum-exps,
-  // then 1 / their sum, behind the staged block
-  float* wt = reinterpret_cast<float*>(stage + kH * row_b);
-  for (int c = tid; c < 2 * kH; c += NT)
-    wt[c] = __hip_atomic_load(part_lse + static_cast<int64_t>(t) * 2 * kH + c,
-                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (tid < kH) merge_weights(wt, tid, 2, t, lse);
-  __syncthreads();
-  unsigned long long* ob = reinterpret_cast<unsigned long long*>(
-      out + static_cast<int64_t>(t) * kH * kR) + wq;
-#pragma unroll
-  for (int i = 0; i < kH / kRowsPer; ++i) {
-    const int h = h0 + kRowsPer * i;
-    float m[4], o4[4], x[4];
-    unpack_bf16x4(*reinterpret_cast<const unsigned long long*>(stage + h * row_b + 8 * wq), m);
-    unpack_bf16x4(u[i], o4);
-    const float w0 = wt[h], w1 = wt[kH + h];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p0 = split == 0 ? m[e] : o4[e];
-      const float p1 = split == 0 ? o4[e] : m[e];
-      x[e] = fmaf(w1, p1, w0 * p0);
-    }
-    ob[h * kWords] = pack_bf16x4(x, wt[2 * kH + h]);
+  for (int p = 0; p < n_parts; ++p) {
+    if (!((todo >> p) & 1u)) continue;
+    if (n_parts == 2)
+      merge_part<NT, kH / 2>(stage, p, t, split, n_split, out, lse, part_o, part_lse);
+    else
+      merge_part<NT, kH / kParts>(stage, p, t, split, n_split, out, lse, part_o, part_lse);
   }
 }
 
@@ -571,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
     int32_t block_size, int64_t num_slots, int32_t max_seq_len,
     uint16_t* __restrict__ out, float* __restrict__ lse,
     uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-    unsigned long long* __restrict__ arrivals, unsigned long long call_tag, int32_t coop) {
+    unsigned long long* __restrict__ arrivals, unsigned long long call_tag, int32_t wait_ticks) {
   __shared__ MlaSharedWs sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -887,7 +868,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_ws(
     tile_barrier();                      // rows staged
   }
   mla_store_or_merge<kThreads>(reinterpret_cast<uint8_t*>(&sh.k[0][0]), &sh.counter, t, split,
-                               n_split, n_split > 1, coop != 0, out, lse, part_o, part_lse,
+                               n_split, n_split > 1, wait_ticks, out, lse, part_o, part_lse,
                                arrivals, call_tag);
 }
 
@@ -956,7 +937,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_mla_prefill(
     const int32_t* __restrict__ block_table, int32_t max_blocks, int32_t block_size,
     int64_t num_slots, int32_t max_seq_len, uint16_t* __restrict__ out,
     float* __restrict__ lse, uint16_t* __restrict__ part_o, float* __restrict__ part_lse,
-    unsigned long long* __restrict__ arrivals, unsigned long long call_tag, int32_t coop) {
+    unsigned long long* __restrict__ arrivals, unsigned long long call_tag, int32_t wait_ticks) {
   __shared__ MlaSharedPf sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1333,7 +1314,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_mla_prefill(
             f32_to_bf16_rne(o[g2][d][r] * inv);
       }
     }
-  mla_store_or_merge<kPfThreads>(stage, &sh.counter, t, split, n_split, n_split > 1, coop != 0,
+  mla_store_or_merge<kPfThreads>(stage, &sh.counter, t, split, n_split, n_split > 1, wait_ticks,
                                  out, lse, part_o, part_lse, arrivals, call_tag);
 }
 
@@ -1436,6 +1417,16 @@ int mla_choose_split(const dsa_batch* b, int dtype, int n_heads, int R, int P,
   return max(min_split, min(split, max_split));
 }
 
+// How long (s_memrealtime ticks of 10 ns) a split waits for its token's
+// other splits before it leaves its part of the merge to the last split:
+// 20 us, or DSA_MERGE_WAIT_TICKS from the environment (0: never waits).
+static int32_t merge_wait_ticks() {
+  const char* e = getenv("DSA_MERGE_WAIT_TICKS");
+  if (!e || !*e) return 2000;
+  const long v = strtol(e, nullptr, 10);
+  return v < 0 ? 0 : (v > 1000000 ? 1000000 : static_cast<int32_t>(v));
+}
+
 hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
   const dsa_batch& b = a.b;
   if (b.num_q_tokens == 0) return hipSuccess;
@@ -1449,9 +1440,9 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
     const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * n_split;
     // one workgroup per CU (both kernels take most of the LDS): when the
     // grid fits the device every split of a token is resident at once, and
-    // with three or more splits the owners of the merge parts wait for the
-    // last split and merge their parts in parallel
-    const int32_t coop = grid <= device_cus() ? 1 : 0;
+    // the owners of the merge parts wait for the last split (at most
+    // merge_wait_ticks()) and merge their parts in parallel
+    const int32_t wait_ticks = grid <= device_cus() ? merge_wait_ticks() : 0;
     if (n_split > 1 && split_len <= kWsSplitCap) {
       // key splits short enough for the warp-specialised pipeline's slot table
       k_mla_ws<<<static_cast<unsigned>(grid), kThreads, 0, stream>>>(
@@ -1460,7 +1451,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
           b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
           b.block_size, b.num_slots, b.max_seq_len,
           static_cast<uint16_t*>(a.out), a.lse, a.part_o, a.part_lse, a.arrivals,
-          a.call_tag, coop);
+          a.call_tag, wait_ticks);
       return hipGetLastError();
     }
     // longer splits (up to kMaxSplitLen indices), or one per token
@@ -1470,7 +1461,7 @@ hipError_t launch_sparse_mla(const MlaArgs& a, hipStream_t stream) {
         b.seq_lens, b.cu_q, b.num_reqs, b.block_table, b.max_blocks,
         b.block_size, b.num_slots, b.max_seq_len,
         static_cast<uint16_t*>(a.out), a.lse, a.part_o, a.part_lse, a.arrivals,
-        a.call_tag, coop);
+        a.call_tag, wait_ticks);
     return hipGetLastError();
   }
   const int64_t grid = static_cast<int64_t>(b.num_q_tokens) * a.n_heads;

@@ -145,3 +145,34 @@ def test_graph_replays_match_eager(dsa, n_tokens, topk):
         torch.cuda.synchronize()
         assert torch.equal(o, o0) and torch.equal(l, l0), rep
     del graph
+
+
+@pytest.mark.parametrize("n_tokens,topk", [(128, 256), (64, 512), (16, 2048), (128, 4096)])
+def test_merge_does_not_depend_on_the_wait(dsa, n_tokens, topk, monkeypatch):
+    """DSA_MERGE_WAIT_TICKS bounds how long a split waits for its token's
+    other splits before it stores its own rows and leaves its part to the
+    last split.  With no wait (the last split merges every part), a wait
+    of one or five ticks (owners give their parts up about when the last
+    split arrives, so both outcomes of that race occur) and the default,
+    the bits are the same, and they match the oracle.  Shapes: two splits
+    on each kernel, four and sixteen splits."""
+    cfg, b, lay, idx, bb, nbytes = _setup(dsa, n_tokens, topk, 990 + n_tokens + topk)
+    print("merge wait case: %d tokens, top-k %d, %d splits" %
+          (n_tokens, topk, _splits(nbytes, n_tokens)), flush=True)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    got = []
+    for wait in (None, "0", "1", "5", "1", None):
+        if wait is None:
+            monkeypatch.delenv("DSA_MERGE_WAIT_TICKS", raising=False)
+        else:
+            monkeypatch.setenv("DSA_MERGE_WAIT_TICKS", wait)
+        o, l = _run(dsa, cfg, bb, lay, idx, ws)
+        torch.cuda.synchronize()
+        got.append((wait, o.clone(), l.clone()))
+    o0, l0 = got[0][1], got[0][2]
+    for wait, o, l in got[1:]:
+        assert torch.equal(o, o0) and torch.equal(l, l0), wait
+    tokens = sorted(set(np.linspace(0, n_tokens - 1, 8).astype(int).tolist()))
+    ro, rl = _oracle(b, lay, idx.cpu().numpy(), cfg.kv_lora_rank, cfg.softmax_scale, tokens)
+    assert attn_close(np_f64(o0)[tokens], ro[tokens]) <= 0
+    assert attn_close(l0.cpu().numpy()[tokens], rl[tokens], 1e-3, 1e-4) <= 0

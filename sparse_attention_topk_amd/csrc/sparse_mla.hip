@@ -1104,7 +1104,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_mla_prefill(
     uint32_t vbw;
 
     // ---- logits of key block kb, head group g: 36 MFMAs, operands 3 ahead,
-    // DMA instructions 0 .. 8 of tile k + 1 after every fourth
+    // DMA instructions 0 .. 11 of tile k + 1 after every third
     f32x16 sacc = f32x16{};
     {
       constexpr int kAhead = 3;
@@ -1121,7 +1121,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_mla_prefill(
         constexpr int kAfter = (kPfQSteps - 1 - S) < (kAhead - 1) ? (kPfQSteps - 1 - S) : (kAhead - 1);
         lgkm_keep<kAfter>(kr[R]);
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[R], qb[S], sacc, 0, 0, 0);
-        if constexpr (S % 4 == 0) dma_one(nbuf, S / 4);
+        if constexpr (S % 3 == 0) dma_one(nbuf, S / 3);
         if constexpr (S + kAhead < kPfQSteps)
           kr[R] = b128_load<1024 * ((S + kAhead) >> 2)>(tb + ko[(S + kAhead) & 3]);
       });
@@ -1179,7 +1179,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_mla_prefill(
     // d = i % 4; both head groups share the value operand).  Operands are
     // requested three pairs ahead: the probabilities of both head groups
     // with the first pair of a K-step, two value fragments with each pair.
-    // DMA instructions 9 .. 17 of tile k + 1 are spread over the pairs.
+    // DMA instructions 12 .. 17 of tile k + 1 follow pairs 0 .. 5.
     // The groups' flags and the slot-table entries of tile k + 2 are
     // requested ahead of the first operands; the first three pairs'
     // operands are requested again if a group takes its probabilities anew.
@@ -1265,7 +1265,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void k_mla_prefill(
         const bf16x8 vop = __builtin_bit_cast(bf16x8, v01);
         o[0][D] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ST & 1][0], vop, o[0][D], 0, 0, 0);
         o[1][D] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ST & 1][1], vop, o[1][D], 0, 0, 0);
-        if constexpr (I < 9) dma_one(nbuf, 9 + I);
+        if constexpr (I < 6) dma_one(nbuf, 12 + I);
       });
       // rows of tile k + 2 for the DMA issued during tile k + 1 (row 0
       // after the last tile)

@@ -1,16 +1,16 @@
 """GPU tests of the split merge of sparse MLA.
 
 When a token's keys are split over several workgroups, each split stores
-its bf16 partial rows and log-sum-exps, then counts its arrival at the
-token's word in the workspace (tagged with the call).  With two splits the
-split that arrives last merges all heads; with more, four parts of 16 heads
-are merged by their owners (splits 0..3) once every split has arrived, or
-by the last split when an owner gave its part up (always when the grid is
-larger than the device holds at once).  Every part is merged once, in split
-order, so the result must match the oracle and repeat bit for bit for every
-split count and grid size, and graph replays, which reuse the tag they were
-captured with, must find the word their previous run left (every split
-counted) as no arrival."""
+bf16 partial rows and log-sum-exps, then counts its arrival at the token's
+word in the workspace (tagged with the call).  The heads are merged in
+parts, two halves with two splits and four parts of 16 heads with more,
+each by its owner once every split has arrived, or by the last split when
+the owner gave its part up (always when the grid is larger than the device
+holds at once, or when the owner stopped waiting).  Every part is merged
+once, in split order, so the result must match the oracle and repeat bit
+for bit for every split count, grid size and wait bound, and graph replays,
+which reuse the tag they were captured with, must find the word their
+previous run left (every split counted) as no arrival."""
 import numpy as np
 import pytest
 import torch

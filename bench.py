@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--workload", default="decode_32k_mtp", choices=WORKLOADS)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--graph", action="store_true",
+                   help="also time the step captured in a HIP graph (replayed, same protocol)")
     p.add_argument("--warm", action="store_true",
                    help="also time K steps and calls back to back without eviction")
     p.add_argument("--pmc-run", action="store_true",
@@ -669,6 +671,21 @@ def main():
                           (ib + mb + cb) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS),
         "cpu_baseline": None,
     }
+    if args.graph:
+        # the same step captured once into a HIP graph (the library allocates
+        # nothing and enqueues no memset, so the capture holds only its
+        # kernels), replayed under the same protocol
+        log("graph pass: %d replays, caches evicted before each" % args.steps)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        gst = stats(timer.reps(graph.replay, args.steps, flush))
+        gst["value"] = N / (gst["median_ms"] * 1e-3)
+        res["graph_step"] = gst
+        del graph
     if args.warm:
         log("warm pass: %d steps and calls back to back" % args.steps)
         res["warm_back_to_back_ms"] = {

@@ -72,6 +72,8 @@ def parse():
     p.add_argument("--stats-summary", nargs=3, metavar=("STATS_CSV", "TITLE", "COMMAND"),
                    help="turn a rocprofv3 --stats kernel_stats.csv into the text table "
                         "kept under profiles/; no GPU needed")
+    p.add_argument("--mfma-counter", default="SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                   help="the flop counter --mfma-summary reads (_BF16 or _F8)")
     p.add_argument("--mfma-summary", metavar="CSV",
                    help="turn a rocprofv3 counter_collection.csv of SQ_INSTS_VALU_MFMA_"
                         "MOPS_BF16 and MfmaUtil into a per-kernel summary (JSON on "
@@ -229,13 +231,14 @@ def pmc_summary(fetch_csv, write_csv):
             "indexer_call_traffic_bytes": call, "kernels": kernels}
 
 
-def mfma_summary(csv_path):
-    """Per library kernel: bf16 matrix-core flops per dispatch (the counter
-    SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 flops) and the fraction
-    of cycles the matrix cores were busy while it ran (MfmaUtil = summed
-    SQ_VALU_MFMA_BUSY_CYCLES over every SIMD / (GRBM_GUI_ACTIVE x SIMDs))."""
+def mfma_summary(csv_path, counter="SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+    """Per library kernel: matrix-core flops per dispatch of one data type
+    (the counter, SQ_INSTS_VALU_MFMA_MOPS_BF16 or _F8, counts units of 512
+    flops) and the fraction of cycles the matrix cores were busy while it
+    ran (MfmaUtil = summed SQ_VALU_MFMA_BUSY_CYCLES over every SIMD /
+    (GRBM_GUI_ACTIVE x SIMDs))."""
     mops, util = {}, {}
-    for name, v, _ in _read_counters(csv_path, "SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+    for name, v, _ in _read_counters(csv_path, counter):
         if "dsa::" in name:
             mops.setdefault(_short(name), []).append(v * 512.0)
     for name, v, _ in _read_counters(csv_path, "MfmaUtil"):
@@ -482,7 +485,7 @@ def main():
         print(stats_summary(*args.stats_summary))
         return
     if args.mfma_summary:
-        print(json.dumps(mfma_summary(args.mfma_summary), indent=1))
+        print(json.dumps(mfma_summary(args.mfma_summary, args.mfma_counter), indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
